@@ -1,0 +1,108 @@
+"""50-digit brute-force twin of the decode-block oracle, for tiny shapes.
+
+TEST INFRASTRUCTURE ONLY (imported by the CPU tests, never by the library).
+
+Written independently of oracle/decode_step.py: explicit scalar loops over
+mpmath numbers, no numpy arithmetic, no shared helpers.  It follows the same
+statement of the block (RMSNorm with eps inside the root, one packed
+[Q | K | V] projection, rotate-half RoPE with angle pos * theta^(-2j/D),
+append of the new token, softmax attention with scale 1/sqrt(D) over the
+history and the new token, output projection plus residual), as described
+in the oracle's header, so that an indexing slip in either one shows up as a
+disagreement.
+"""
+from __future__ import annotations
+
+import mpmath
+
+mp = mpmath.mp
+
+
+def decode_step_brute(hidden, norm_w, w_qkv, w_o, k_hist, v_hist, pos, *,
+                      n_q_heads, n_kv_heads, head_dim, rope_theta, eps, digits=50):
+    """One sequence.  Plain nested lists (or anything indexable) of floats.
+
+    hidden [H], norm_w [H], w_qkv [H][(nq+2nkv)D], w_o [nq*D][H],
+    k_hist, v_hist [pos][nkv][D]  (the cached tokens before the new one).
+    Returns dict of nested lists of mpf: out [H], y [H], q [nq][D] (rotated),
+    k [nkv][D] (rotated), v [nkv][D], probs [nq][pos+1].
+    """
+    with mpmath.workdps(digits):
+        f = mpmath.mpf
+        H = len(hidden)
+        nq, nkv, D = n_q_heads, n_kv_heads, head_dim
+        x = [f(hidden[i]) for i in range(H)]
+
+        # RMSNorm
+        acc = f(0)
+        for i in range(H):
+            acc += x[i] * x[i]
+        scale = 1 / mpmath.sqrt(acc / H + f(eps))
+        xn = [x[i] * scale * f(norm_w[i]) for i in range(H)]
+
+        # packed projection, column by column
+        ncol = (nq + 2 * nkv) * D
+        u = []
+        for c in range(ncol):
+            s = f(0)
+            for i in range(H):
+                s += xn[i] * f(w_qkv[i][c])
+            u.append(s)
+        q = [[u[h * D + e] for e in range(D)] for h in range(nq)]
+        k = [[u[nq * D + g * D + e] for e in range(D)] for g in range(nkv)]
+        v = [[u[(nq + nkv) * D + g * D + e] for e in range(D)] for g in range(nkv)]
+
+        # rotate-half RoPE
+        half = D // 2
+
+        def rotate(vec):
+            res = [None] * D
+            for j in range(half):
+                ang = f(pos) * mpmath.power(f(rope_theta), -f(2 * j) / D)
+                c, s_ = mpmath.cos(ang), mpmath.sin(ang)
+                a, b = vec[j], vec[j + half]
+                res[j] = a * c - b * s_
+                res[j + half] = b * c + a * s_
+            return res
+
+        q = [rotate(q[h]) for h in range(nq)]
+        k = [rotate(k[g]) for g in range(nkv)]
+
+        # attention over pos history tokens plus the new one
+        group = nq // nkv
+        att = []
+        probs = []
+        for h in range(nq):
+            g = h // group
+            scores = []
+            for t in range(pos + 1):
+                key = k[g] if t == pos else [f(k_hist[t][g][e]) for e in range(D)]
+                dot = f(0)
+                for e in range(D):
+                    dot += q[h][e] * key[e]
+                scores.append(dot / mpmath.sqrt(D))
+            top = max(scores)
+            ex = [mpmath.exp(s - top) for s in scores]
+            tot = f(0)
+            for e_ in ex:
+                tot += e_
+            pr = [e_ / tot for e_ in ex]
+            probs.append(pr)
+            o = []
+            for e in range(D):
+                s = f(0)
+                for t in range(pos + 1):
+                    val = v[g][e] if t == pos else f(v_hist[t][g][e])
+                    s += pr[t] * val
+                o.append(s)
+            att.extend(o)
+
+        # output projection and residual
+        y = []
+        for c in range(H):
+            s = f(0)
+            for r in range(nq * D):
+                s += att[r] * f(w_o[r][c])
+            y.append(s)
+        out = [x[c] + y[c] for c in range(H)]
+        return {"out": out, "y": y, "q": q, "k": k, "v": v, "probs": probs}
