@@ -1,0 +1,227 @@
+"""attention_block_amd: the fused single-token decode attention block on MI355X.
+
+The compute lives in libdab.so (hand-written HIP kernels for gfx950 behind
+the C ABI of include/dab.h).  This module only marshals torch tensors into
+that ABI: torch provides device memory and the current stream, nothing
+else.  There is no CPU or torch fallback: without the built library every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+from . import _lib
+from ._lib import DAB_BF16, DAB_F32, DabConfig
+
+__all__ = ["DabError", "DabConfig", "make_config", "workspace_size", "Workspace", "decode_attn_block",
+           "decode_attn_block_timed", "read_device_error", "phase_names", "HipEvent", "lib_version"]
+
+
+class DabError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.load().dab_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.DAB_OK:
+        raise DabError(status, where)
+
+
+def lib_version() -> str:
+    return _lib.load().dab_version().decode()
+
+
+def make_config(*, batch: int, hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                cache_capacity: int, dtype: str, rope_theta: float, eps: float = 1e-6,
+                kv_chunk: int = 0) -> DabConfig:
+    """Build the C config struct.  dtype is "bf16" or "f32"."""
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
+    return DabConfig(batch, hidden, n_q_heads, n_kv_heads, head_dim, cache_capacity,
+                     DAB_BF16 if dtype == "bf16" else DAB_F32, rope_theta, eps, kv_chunk)
+
+
+def workspace_size(cfg: DabConfig) -> int:
+    n = _lib.load().dab_workspace_size(ctypes.byref(cfg))
+    if n == 0:
+        raise DabError(_lib.DAB_ERR_INVALID_ARG, "dab_workspace_size")
+    return n
+
+
+def phase_names(cfg: DabConfig) -> list:
+    lib = _lib.load()
+    return [lib.dab_phase_name(ctypes.byref(cfg), i).decode() for i in range(lib.dab_phase_count(ctypes.byref(cfg)))]
+
+
+class Workspace:
+    """Device scratch for the library (partials, counters, error flag).
+
+    Allocated once with torch, zeroed once by dab_workspace_init; every call
+    leaves its counters at zero, so one workspace serves any number of
+    calls on one stream at a time.
+    """
+
+    def __init__(self, nbytes: int, device):
+        import torch
+        self.nbytes = int(nbytes)
+        self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+        base = self._buf.data_ptr()
+        self.ptr = (base + 255) // 256 * 256
+        self.device = self._buf.device
+        _check(_lib.load().dab_workspace_init(ctypes.c_void_p(self.ptr), self.nbytes, _stream_ptr(self.device)),
+               "dab_workspace_init")
+
+
+_default_ws = {}
+
+
+def _workspace_for(cfg: DabConfig, device) -> Workspace:
+    need = workspace_size(cfg)
+    key = (device.type, device.index)
+    ws = _default_ws.get(key)
+    if ws is None or ws.nbytes < need:
+        ws = Workspace(max(need, 1 << 20), device)
+        _default_ws[key] = ws
+    return ws
+
+
+def _stream_ptr(device) -> ctypes.c_void_p:
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk):
+    import torch
+    if hidden.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("hidden must be bfloat16 or float32")
+    dt = hidden.dtype
+    dev = hidden.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    named = dict(hidden=hidden, norm_w=norm_w, w_qkv=w_qkv, w_o=w_o, k_cache=k_cache, v_cache=v_cache)
+    for name, t in named.items():
+        if t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+    if pos.dtype != torch.int32 or pos.device != dev or not pos.is_contiguous():
+        raise ValueError(f"pos must be a contiguous int32 tensor on {dev}")
+    if hidden.dim() != 2 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("hidden must be [B, H]; k_cache and v_cache [B, cap, nkv, D] of one shape")
+    B, H = hidden.shape
+    _, cap, nkv, D = k_cache.shape
+    if k_cache.shape[0] != B or pos.shape != (B,) or norm_w.shape != (H,):
+        raise ValueError("batch or hidden size mismatch")
+    n_qkv = w_qkv.shape[1]
+    if w_qkv.shape[0] != H or n_qkv % D or n_qkv // D <= 2 * nkv:
+        raise ValueError("w_qkv must be [H, (nq + 2 nkv) D]")
+    nq = n_qkv // D - 2 * nkv
+    if w_o.shape != (nq * D, H):
+        raise ValueError(f"w_o must be [{nq * D}, {H}]")
+    if out is None:
+        out = torch.empty_like(hidden)
+    elif out.shape != hidden.shape or out.dtype != dt or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must match hidden")
+    if dbg_y is not None and (dbg_y.shape != hidden.shape or dbg_y.dtype != torch.float32
+                              or dbg_y.device != dev or not dbg_y.is_contiguous()):
+        raise ValueError("dbg_y must be a contiguous float32 [B, H] tensor")
+    cfg = make_config(batch=B, hidden=H, n_q_heads=nq, n_kv_heads=nkv, head_dim=D, cache_capacity=cap,
+                      dtype="bf16" if dt == torch.bfloat16 else "f32", rope_theta=rope_theta, eps=eps,
+                      kv_chunk=kv_chunk)
+    return cfg, out
+
+
+def decode_attn_block(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta: float, eps: float = 1e-6,
+                      out=None, dbg_y=None, workspace: Optional[Workspace] = None, kv_chunk: int = 0):
+    """One decode step on the current stream; returns `out`.
+
+    Shapes: hidden [B, H]; norm_w [H]; w_qkv [H, (nq+2nkv)D]; w_o [nq D, H];
+    k_cache, v_cache [B, cap, nkv, D] (row pos[b] is written); pos int32 [B];
+    all but pos in one dtype (bfloat16 or float32) on one GPU.  dbg_y
+    (optional, float32 [B, H]) receives the pre-residual a @ W_o.
+    """
+    cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk)
+    ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)
+    _check(_lib.load().dab_decode_attn_block(
+        ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache), _ptr(v_cache),
+        _ptr(pos), _ptr(out), _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device)),
+        "dab_decode_attn_block")
+    return out
+
+
+class HipEvent:
+    """A raw hipEvent_t (timing only), so phases can be timed on the stream they run on."""
+
+    _hip = None
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            import torch  # noqa: F401  (loads the HIP runtime torch links against)
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        if self._rt().hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.handle = h
+
+    def record(self, stream_ptr) -> None:
+        if self._rt().hipEventRecord(self.handle, stream_ptr) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def synchronize(self) -> None:
+        self._rt().hipEventSynchronize(self.handle)
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        if self._rt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self._hip is not None and self.handle:
+                self._hip.hipEventDestroy(self.handle)
+        except Exception:
+            pass
+
+
+def decode_attn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos,
+                            rope_theta: float, eps: float = 1e-6, out=None, dbg_y=None,
+                            workspace: Optional[Workspace] = None, kv_chunk: int = 0):
+    """decode_attn_block that also records events[0] before the first kernel and events[i] after kernel i-1."""
+    cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk)
+    ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)
+    arr = (ctypes.c_void_p * len(events))(*[e.handle.value for e in events])
+    _check(_lib.load().dab_decode_attn_block_timed(
+        ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache), _ptr(v_cache),
+        _ptr(pos), _ptr(out), _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device),
+        arr, len(events)), "dab_decode_attn_block_timed")
+    return out
+
+
+def read_device_error(workspace: Optional[Workspace] = None, device=None) -> int:
+    """Read and clear the sticky device error flag (synchronises the stream)."""
+    import torch
+    if workspace is None:
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        workspace = _default_ws.get((dev.type, dev.index))
+        if workspace is None:
+            return 0
+    flag = ctypes.c_int32()
+    _check(_lib.load().dab_read_device_error(ctypes.c_void_p(workspace.ptr), _stream_ptr(workspace.device),
+                                             ctypes.byref(flag)), "dab_read_device_error")
+    return flag.value

@@ -1,0 +1,67 @@
+"""ctypes view of libdab.so (declarations mirror include/dab.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdab.so")
+
+DAB_OK, DAB_ERR_INVALID_ARG, DAB_ERR_UNSUPPORTED, DAB_ERR_WORKSPACE, DAB_ERR_HIP = range(5)
+DAB_F32, DAB_BF16 = 0, 1
+
+# every symbol include/dab.h declares
+EXPORTS = (
+    "dab_workspace_size", "dab_workspace_init", "dab_decode_attn_block", "dab_decode_attn_block_timed",
+    "dab_phase_count", "dab_phase_name", "dab_read_device_error", "dab_status_string", "dab_version",
+)
+
+
+class DabConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("cache_capacity", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("kv_chunk", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdab.so once.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_block_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, cfgp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(DabConfig)
+    lib.dab_workspace_size.argtypes = [cfgp]
+    lib.dab_workspace_size.restype = sz
+    lib.dab_workspace_init.argtypes = [vp, sz, vp]
+    lib.dab_workspace_init.restype = i32
+    call = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dab_decode_attn_block.argtypes = call
+    lib.dab_decode_attn_block.restype = i32
+    lib.dab_decode_attn_block_timed.argtypes = call + [ctypes.POINTER(vp), i32]
+    lib.dab_decode_attn_block_timed.restype = i32
+    lib.dab_phase_count.argtypes = [cfgp]
+    lib.dab_phase_count.restype = i32
+    lib.dab_phase_name.argtypes = [cfgp, i32]
+    lib.dab_phase_name.restype = ctypes.c_char_p
+    lib.dab_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.dab_read_device_error.restype = i32
+    lib.dab_status_string.argtypes = [i32]
+    lib.dab_status_string.restype = ctypes.c_char_p
+    lib.dab_version.argtypes = []
+    lib.dab_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib

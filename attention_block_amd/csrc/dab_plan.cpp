@@ -1,0 +1,160 @@
+// Host-side validation and launch planning (no HIP calls).
+#include "dab_plan.h"
+
+#include <math.h>
+
+namespace dab {
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Split a [K, N] GEMV over `batch` input rows into workgroup tiles: slabs of
+// kSlab columns, `rows` rows of W each, `bg` batch rows per workgroup.
+// Aims for at least four workgroups per compute unit (1024 on 256 CUs).
+void plan_gemv(int K, int N, int batch, GemvPlan* g) {
+    g->K = K;
+    g->N = N;
+    g->slabs = ceil_div(N, kSlab);
+    g->bg = batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
+    g->nbg = ceil_div(batch, g->bg);
+    g->rows = (K % 128 == 0 && (long long)g->slabs * (K / 128) * g->nbg >= 1024) ? 128 : 64;
+    g->ksplit = K / g->rows;
+    g->tiles = g->slabs * g->ksplit;
+    // With several batch groups the tiles are padded to a multiple of 8 so
+    // that the groups sharing one weight tile land on one XCD (see the
+    // workgroup-id decoding in the GEMV kernel).
+    g->grid = g->nbg == 1 ? g->tiles : (int)align_up((size_t)g->tiles, 8) * g->nbg;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+dab_status make_plan(const dab_config* cfg, Plan* p) {
+    if (!cfg || !p) return DAB_ERR_INVALID_ARG;
+    *p = Plan();
+    const dab_config& c = *cfg;
+    if (c.batch < 0 || c.hidden <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 ||
+        c.cache_capacity <= 0)
+        return DAB_ERR_INVALID_ARG;
+    if (c.dtype != DAB_F32 && c.dtype != DAB_BF16) return DAB_ERR_INVALID_ARG;
+    if (!(c.rope_theta > 0.f) || !isfinite(c.rope_theta) || !(c.eps >= 0.f) || !isfinite(c.eps))
+        return DAB_ERR_INVALID_ARG;
+    if (c.n_q_heads % c.n_kv_heads != 0) return DAB_ERR_INVALID_ARG;
+    if (c.head_dim != 64 && c.head_dim != 128) return DAB_ERR_UNSUPPORTED;
+    if (c.hidden % 64 != 0) return DAB_ERR_UNSUPPORTED;
+    if (c.n_q_heads / c.n_kv_heads > kMaxGroup) return DAB_ERR_UNSUPPORTED;
+    if (c.kv_chunk != 0 && (c.kv_chunk < 64 || c.kv_chunk > 4096 || c.kv_chunk % 64 != 0))
+        return DAB_ERR_INVALID_ARG;
+    // keep every element offset of the caches and weights inside int64 and
+    // the per-dimension products inside int32
+    const long long n_qkv = (long long)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+    if (n_qkv > (1 << 24) || c.hidden > (1 << 20) || c.cache_capacity > (1 << 24) || c.batch > 4096)
+        return DAB_ERR_UNSUPPORTED;
+
+    p->B = c.batch;
+    p->H = c.hidden;
+    p->nq = c.n_q_heads;
+    p->nkv = c.n_kv_heads;
+    p->D = c.head_dim;
+    p->cap = c.cache_capacity;
+    p->dtype = c.dtype;
+    p->G = c.n_q_heads / c.n_kv_heads;
+    p->n_qkv = (int)n_qkv;
+    p->n_q = c.n_q_heads * c.head_dim;
+    p->theta = c.rope_theta;
+    p->eps = c.eps;
+    p->elem = c.dtype == DAB_BF16 ? 2 : 4;
+
+    const int B = p->B > 0 ? p->B : 1;  // plan a batch-0 call as batch 1; nothing is launched
+    plan_gemv(p->H, p->n_qkv, B, &p->qkv);
+    plan_gemv(p->n_q, p->H, B, &p->oproj);
+
+    // split-KV chunk: the largest of 256/128/64 tokens that still gives at
+    // least 1024 work items over the batch and KV heads, then grown until
+    // the chunk count per sequence fits the merge step
+    int T = c.kv_chunk;
+    if (T == 0) {
+        T = 64;
+        for (int cand : {256, 128}) {
+            if ((long long)B * p->nkv * ceil_div(p->cap, cand) >= 1024) { T = cand; break; }
+        }
+        while (ceil_div(p->cap, T) > kMaxChunks && T < 4096) T *= 2;
+    }
+    p->kv_chunk = T;
+    p->max_chunks = ceil_div(p->cap, T);
+    if (p->max_chunks > kMaxChunks) return DAB_ERR_UNSUPPORTED;
+    const long long attn_grid = (long long)B * p->nkv * p->max_chunks;
+    if (attn_grid > (1LL << 30)) return DAB_ERR_UNSUPPORTED;
+    p->attn_grid = (int)attn_grid;
+
+    // workspace layout
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    p->off_flags = take(256);
+    p->off_qkv_cnt = take(sizeof(int32_t) * p->qkv.slabs * p->qkv.nbg);
+    p->off_attn_cnt = take(sizeof(int32_t) * B * p->nkv);
+    p->off_oproj_cnt = take(sizeof(int32_t) * p->oproj.slabs * p->oproj.nbg);
+    p->off_qkv_part = take(sizeof(float) * (size_t)p->qkv.ksplit * B * p->n_qkv);
+    p->off_ssq = take(sizeof(float) * (size_t)p->qkv.slabs * p->qkv.ksplit * B);
+    p->off_q = take(sizeof(float) * (size_t)B * p->n_q);
+    p->off_attn_o = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * p->D);
+    p->off_attn_ml = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * 2);
+    p->off_a = take(sizeof(float) * (size_t)B * p->n_q);
+    p->off_oproj_part = take(sizeof(float) * (size_t)p->oproj.ksplit * B * p->H);
+    p->ws_bytes = off;
+
+    const size_t e = (size_t)p->elem;
+    p->bytes_hidden = e * p->B * p->H;
+    p->bytes_norm = e * p->H;
+    p->bytes_wqkv = e * (size_t)p->H * p->n_qkv;
+    p->bytes_wo = e * (size_t)p->n_q * p->H;
+    p->bytes_cache = e * (size_t)p->B * p->cap * p->nkv * p->D;
+    p->bytes_pos = sizeof(int32_t) * p->B;
+    p->bytes_out = e * p->B * p->H;
+    p->bytes_dbg = sizeof(float) * p->B * p->H;
+    return DAB_OK;
+}
+
+dab_status check_call(const Plan& p, const void* hidden, const void* norm_w, const void* w_qkv,
+                      const void* w_o, const void* k_cache, const void* v_cache, const int32_t* pos,
+                      const void* out, const float* dbg_y, const void* workspace, size_t ws_bytes) {
+    if (!workspace) return DAB_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DAB_ERR_INVALID_ARG;
+    if (ws_bytes < p.ws_bytes) return DAB_ERR_WORKSPACE;
+    if (p.B == 0) return DAB_OK;  // nothing is read or written
+    const void* req[] = {hidden, norm_w, w_qkv, w_o, k_cache, v_cache, out};
+    for (const void* q : req)
+        if (!q || !aligned(q, 16)) return DAB_ERR_INVALID_ARG;
+    if (!pos || !aligned(pos, 4)) return DAB_ERR_INVALID_ARG;
+    if (dbg_y && !aligned(dbg_y, 16)) return DAB_ERR_INVALID_ARG;
+
+    struct Span { const void* p; size_t n; bool written; };
+    const Span spans[] = {
+        {hidden, p.bytes_hidden, false}, {norm_w, p.bytes_norm, false}, {w_qkv, p.bytes_wqkv, false},
+        {w_o, p.bytes_wo, false},        {pos, p.bytes_pos, false},     {k_cache, p.bytes_cache, true},
+        {v_cache, p.bytes_cache, true},  {out, p.bytes_out, true},      {dbg_y, p.bytes_dbg, true},
+        {workspace, p.ws_bytes, true},
+    };
+    const int n = (int)(sizeof(spans) / sizeof(spans[0]));
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if ((spans[i].written || spans[j].written) &&
+                overlaps(spans[i].p, spans[i].n, spans[j].p, spans[j].n))
+                return DAB_ERR_INVALID_ARG;
+    return DAB_OK;
+}
+
+}  // namespace dab

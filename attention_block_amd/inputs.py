@@ -120,11 +120,14 @@ def make_inputs(cfg: BlockConfig, seed: int, *, cap: Optional[int] = None,
     """
     rng = np.random.default_rng(seed)
     B, H, nq, nkv, D = cfg.batch, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    drawn = None
     if cfg.ragged is not None:
         lo, hi = cfg.ragged
         drawn = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
-    else:
+    elif cfg.pos is not None:
         drawn = np.full(B, cfg.pos, dtype=np.int32)
+    if pos is None and drawn is None:
+        raise ValueError(f"{cfg.name} has no configured length: pass pos")
     p = np.asarray(pos, dtype=np.int32) if pos is not None else drawn
     if p.shape != (B,):
         raise ValueError(f"pos must have shape ({B},)")

@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused single-token decode attention block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one decode-block call (RMSNorm, QKV projection, RoPE, KV append,
+split-KV attention, output projection + residual) on one batch.  Inputs are
+synthetic (seeded on the GPU with the shapes and distributions of the
+configuration) and already resident in HBM when timing starts.  The step
+cycles over R distinct layer-sets (weights, caches, hidden, out) whose total
+size exceeds twice the 256 MiB Infinity Cache, so no step is served from it.
+
+Prints one JSON line: microseconds per step (the metric), achieved HBM GB/s
+and % of the 8 TB/s peak over the algorithmic bytes, a roofline entry for
+the dominant kernel (its average duration from HIP events recorded on the
+stream it runs on), and the fp64 CPU oracle timed on the host as a
+baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+from attention_block_amd.inputs import (CONFIGS, HEADLINE, BlockConfig, algorithmic_bytes,  # noqa: E402
+                                        algorithmic_flops, positions)
+
+METRIC = "µs per decode block step and achieved HBM GB/s (% of peak), 7B layer bs1 4K"
+PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 1024 * 1024
+
+
+def phase_bytes(cfg: BlockConfig, pos) -> dict:
+    """Algorithmic bytes of each kernel; they add up to algorithmic_bytes()."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    B, H, nq, nkv, D = cfg.batch, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    tot = int(np.sum(pos))
+    qkv = s * H * cfg.n_qkv + s * H + s * B * H + s * 2 * nkv * D * B + 4 * B
+    attn = s * 2 * nkv * D * tot
+    # the hidden row is counted once, with the QKV kernel; the O-projection writes out
+    oproj = s * nq * D * H + s * B * H
+    return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj}
+
+
+def make_layer_set(cfg: BlockConfig, pos, cap: int, gen, device):
+    import torch
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    B, H, nq, nkv, D = cfg.batch, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    std = 1.0 / math.sqrt(H)
+
+    def randn(*shape, scale=1.0, shift=0.0):
+        return (torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * scale + shift).to(dt)
+
+    ls = {
+        "hidden": randn(B, H),
+        "norm_w": randn(H, scale=0.1, shift=1.0),
+        "w_qkv": randn(H, cfg.n_qkv, scale=std),
+        "w_o": randn(nq * D, H, scale=std),
+        "k_cache": torch.zeros(B, cap, nkv, D, dtype=dt, device=device),
+        "v_cache": torch.zeros(B, cap, nkv, D, dtype=dt, device=device),
+        "pos": torch.tensor(np.asarray(pos, dtype=np.int32), device=device),
+    }
+    for b in range(B):
+        p = int(pos[b])
+        ls["k_cache"][b, :p] = randn(p, nkv, D)
+        ls["v_cache"][b, :p] = randn(p, nkv, D)
+    ls["out"] = torch.empty_like(ls["hidden"])
+    return ls
+
+
+def cpu_baseline(cfg: BlockConfig, seed: int, budget_s: float) -> dict:
+    """The fp64 oracle on the host, on the full step of this workload."""
+    import oracle
+    from attention_block_amd.inputs import make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    inp = make_inputs(cfg, seed)
+    st = cfg.dtype
+    pos = inp["pos"]
+    B, nkv, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    # exact upcast of the stored bits, outside the timed region
+    kc = np.zeros((B, int(pos.max()) + 1, nkv, D))
+    vc = np.zeros_like(kc)
+    for b in range(B):
+        kc[b, :pos[b]] = oracle.to_f64(inp["k_cache"][b, :pos[b]], st)
+        vc[b, :pos[b]] = oracle.to_f64(inp["v_cache"][b, :pos[b]], st)
+    args = (oracle.to_f64(inp["hidden"], st), oracle.to_f64(inp["norm_w"], st), oracle.to_f64(inp["w_qkv"], st),
+            oracle.to_f64(inp["w_o"], st), kc, vc, pos)
+    kw = dict(n_q_heads=cfg.n_q_heads, n_kv_heads=nkv, head_dim=D, rope_theta=cfg.rope_theta, eps=cfg.eps,
+              storage=st)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_step_fp64(*args, **kw)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 200:
+            break
+    med = float(np.median(times))
+    return {"value": med * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} full {cfg.name} steps (seed {seed}) of the fp64 numpy oracle, median; "
+                      f"bf16->fp64 upcast outside the timing"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default=HEADLINE, choices=sorted(CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-phase-timing", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode block runs on a single MI355X here "
+              "(sharding across GPUs is described in the design notes but not built). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import attention_block_amd as ab
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS[args.config]
+    pos = positions(cfg, args.seed)
+    cap = int(pos.max()) + 1
+    nbytes = algorithmic_bytes(cfg, pos)
+    flops = algorithmic_flops(cfg, pos)
+    R = max(3, math.ceil(2 * MALL_BYTES / nbytes) + 1)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234 + args.seed)
+    sets = [make_layer_set(cfg, pos, cap, gen, dev) for _ in range(R)]
+    c = ab.make_config(batch=cfg.batch, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                       head_dim=cfg.head_dim, cache_capacity=cap, dtype=cfg.dtype, rope_theta=cfg.rope_theta,
+                       eps=cfg.eps, kv_chunk=args.kv_chunk)
+    ws = ab.Workspace(ab.workspace_size(c), dev)
+    phases = ab.phase_names(c)
+
+    def step(i, events=None):
+        s = sets[i % R]
+        if events is None:
+            ab.decode_attn_block(s["hidden"], s["norm_w"], s["w_qkv"], s["w_o"], s["k_cache"], s["v_cache"],
+                                 s["pos"], cfg.rope_theta, cfg.eps, out=s["out"], workspace=ws,
+                                 kv_chunk=args.kv_chunk)
+        else:
+            ab.decode_attn_block_timed(events, s["hidden"], s["norm_w"], s["w_qkv"], s["w_o"], s["k_cache"],
+                                       s["v_cache"], s["pos"], cfg.rope_theta, cfg.eps, out=s["out"],
+                                       workspace=ws, kv_chunk=args.kv_chunk)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if ab.read_device_error(ws) != 0:
+        print("device error flag raised during warm-up", file=sys.stderr)
+        return 1
+
+    # The timed steps replay HIP graphs (one captured launch sequence per
+    # step, over all layer-sets), so host-side marshalling never starves the
+    # GPU: graph of L steps replayed K // L times plus a remainder graph,
+    # exactly K steps in all.
+    L = min(args.steps, R * max(1, math.ceil(64 / R)))
+
+    def capture(nsteps, first):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(first)                     # warm call on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(nsteps):
+                step(first + i)
+        torch.cuda.synchronize()
+        return g
+
+    g_main = capture(L, 0)
+    n_main, rem = divmod(args.steps, L)
+    g_rem = capture(rem, 0) if rem else None
+    g_main.replay()
+    torch.cuda.synchronize()
+
+    start, end = ab.HipEvent(), ab.HipEvent()
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    start.record(stream.cuda_stream)
+    for _ in range(n_main):
+        g_main.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    end.record(stream.cuda_stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    us = start.elapsed_ms(end) * 1e3 / args.steps
+    if ab.read_device_error(ws) != 0:
+        print("device error flag raised during timing", file=sys.stderr)
+        return 1
+
+    # Per-kernel durations: K eager steps with events between the kernels,
+    # enqueued behind a spin kernel so they run back to back on the GPU.
+    phase_us = None
+    if not args.no_phase_timing:
+        ev = [[ab.HipEvent() for _ in range(len(phases) + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(2.4e9 * 1e-4 * args.steps))   # ~100 us of spinning per queued step
+        for i in range(args.steps):
+            step(i, ev[i])
+        torch.cuda.synchronize()
+        phase_us = [float(np.mean([ev[i][k].elapsed_ms(ev[i][k + 1]) * 1e3 for i in range(args.steps)]))
+                    for k in range(len(phases))]
+
+    gbps = nbytes / (us * 1e-6) / 1e9
+    pb = phase_bytes(cfg, pos)
+    roofline = None
+    phase_report = None
+    if phase_us is not None:
+        dom = max(phases, key=lambda n: pb[n])
+        k = phases.index(dom)
+        ach = pb[dom] / (phase_us[k] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_GBPS, 4), "traffic": None, "kernel": dom,
+                    "bytes_per_launch": pb[dom], "avg_launch_us": round(phase_us[k], 3)}
+        phase_report = {n: {"us": round(phase_us[i], 3), "bytes": pb[n],
+                            "gbps": round(pb[n] / (phase_us[i] * 1e-6) / 1e9, 1)} for i, n in enumerate(phases)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.seed, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "hidden": cfg.hidden,
+                   "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
+                   "kv_tokens": int(pos[0]) if cfg.ragged is None else f"ragged sum {int(np.sum(pos))}",
+                   "layer_sets": R, "parallelism": "single GPU"},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "algorithmic_bytes": nbytes,
+        "algorithmic_flops": flops,
+        "roofline": roofline,
+        "phases": phase_report,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,157 @@
+/*
+ * dab.h - C ABI of the fused single-token decode attention block for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, for every sequence b of a batch, the decode step of a
+ * pre-norm transformer attention block (the block composition listed in the
+ * operator-fusion article, "LayerNorm + Attention" CUDA kernel page,
+ * section 1; the fused dataflow of the ClusterFusion page, section 3.2):
+ *
+ *   r      = (mean_i x_i^2 + eps)^(-1/2),  xh = x * r * norm_w        RMSNorm
+ *   u      = xh @ W_qkv          (packed columns [Q | K | V])           QKV GEMV
+ *   q, k   = RoPE(q, pos_b), RoPE(k, pos_b)   (rotate-half pairing)     RoPE
+ *   cache  : K[b, pos_b] = k, V[b, pos_b] = v                           KV append
+ *   a_h    = softmax(q_h . K[b, 0..pos_b, g(h)] / sqrt(D)) @ V[...]     attention
+ *   out    = x + a @ W_o                                                O-proj + residual
+ *
+ * with g(h) = h / (n_q_heads / n_kv_heads) (grouped-query mapping of the
+ * operator-fusion page, section 3).  RoPE angle for pair (j, j + D/2) is
+ * pos_b * theta^(-2j/D).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise,
+ *     16-byte aligned, to memory of the device that is current when the
+ *     call is made.  The caller owns every buffer; the library never
+ *     allocates or frees device memory in these calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; no call below synchronises the
+ *     device except dab_read_device_error.  The enqueue sequence contains
+ *     only kernel launches, so it may be captured into a HIP graph.
+ *   - Storage dtype DAB_BF16: hidden, norm_w, W_qkv, W_o, both caches and out
+ *     hold bf16; every intermediate is fp32 and accumulation is fp32.
+ *     DAB_F32: every tensor is fp32.
+ *   - Errors a host can see (bad shapes, null or misaligned pointers,
+ *     overlapping output, short workspace) return a status before anything
+ *     is enqueued, and no buffer is touched.  A launch failure returns
+ *     DAB_ERR_HIP.  An out-of-range pos[b] can only be seen on the device:
+ *     that sequence is skipped (no cache write, its out row is left
+ *     unwritten) and a sticky flag is raised in the workspace, readable with
+ *     dab_read_device_error.
+ */
+#ifndef DAB_H
+#define DAB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DAB_OK = 0,
+    DAB_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, aliasing */
+    DAB_ERR_UNSUPPORTED = 2,  /* shape outside what the kernels implement     */
+    DAB_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required   */
+    DAB_ERR_HIP = 4           /* the HIP runtime reported an error            */
+} dab_status;
+
+typedef enum { DAB_F32 = 0, DAB_BF16 = 1 } dab_dtype;
+
+/* Shape and numerics of one decode-block call. */
+typedef struct {
+    int32_t batch;           /* B >= 0 sequences (0: nothing to do)                     */
+    int32_t hidden;          /* H, multiple of 64                                       */
+    int32_t n_q_heads;       /* nq >= 1                                                 */
+    int32_t n_kv_heads;      /* nkv >= 1, divides nq, nq / nkv <= 8                     */
+    int32_t head_dim;        /* D: 64 or 128                                            */
+    int32_t cache_capacity;  /* cap: token rows per sequence in each cache              */
+    int32_t dtype;           /* dab_dtype                                               */
+    float rope_theta;        /* RoPE base, > 0                                          */
+    float eps;               /* RMSNorm epsilon, >= 0 (1e-6 in the pages' kernels)      */
+    int32_t kv_chunk;        /* tokens per split-KV work item: 0 = automatic, else a    */
+                             /* multiple of 64 in [64, 4096]                            */
+} dab_config;
+
+/*
+ * Bytes of device workspace one call with this configuration needs (0 when
+ * the configuration is invalid).  The workspace holds split partial sums,
+ * arrival counters and the device error flag.  It must be initialised once
+ * with dab_workspace_init; every call leaves its counters at zero again, so
+ * it can be reused by later calls (on one stream at a time) without
+ * re-initialising.
+ */
+size_t dab_workspace_size(const dab_config* cfg);
+
+/*
+ * Zero `bytes` of workspace at `workspace` (device) with a fill kernel on
+ * `stream`.  Returns DAB_ERR_INVALID_ARG for a null or misaligned pointer.
+ */
+dab_status dab_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/*
+ * One decode step (all of the steps listed at the top of this header).
+ *
+ *   hidden   [B, H]              input hidden state x (read only)
+ *   norm_w   [H]                 RMSNorm weight (read only)
+ *   w_qkv    [H, (nq+2nkv)*D]    row-major; column blocks Q (nq*D), K (nkv*D),
+ *                                V (nkv*D), head-major inside each block
+ *   w_o      [nq*D, H]           row-major; row h*D + d belongs to query head h
+ *   k_cache, v_cache [B, cap, nkv, D]  token-major per sequence.  Rows
+ *                                t < pos[b] are read; row pos[b] is written with
+ *                                the new token's rotated k (resp. v), rounded to
+ *                                the storage dtype; no other element changes.
+ *   pos      int32 [B]           tokens already cached = index of the new token,
+ *                                0 <= pos[b] < cap; attention covers pos[b] + 1
+ *                                tokens (the history and the new one)
+ *   out      [B, H]              x + a @ W_o, rounded to the storage dtype; must
+ *                                not overlap any other argument
+ *   dbg_y    [B, H] fp32 or NULL the pre-residual a @ W_o in fp32 (a test tap)
+ *   workspace, workspace_bytes   device scratch of at least dab_workspace_size
+ *                                bytes, initialised once by dab_workspace_init
+ */
+dab_status dab_decode_attn_block(const dab_config* cfg,
+                                 const void* hidden, const void* norm_w,
+                                 const void* w_qkv, const void* w_o,
+                                 void* k_cache, void* v_cache,
+                                 const int32_t* pos, void* out, float* dbg_y,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * Same as dab_decode_attn_block, and also records `n_events` hipEvent_t
+ * (passed as void*) on `stream`: events[0] before the first kernel and
+ * events[i] after kernel i-1.  n_events must equal dab_phase_count(cfg) + 1.
+ * Used to time the phases of the step on the stream they run on.
+ */
+dab_status dab_decode_attn_block_timed(const dab_config* cfg,
+                                       const void* hidden, const void* norm_w,
+                                       const void* w_qkv, const void* w_o,
+                                       void* k_cache, void* v_cache,
+                                       const int32_t* pos, void* out, float* dbg_y,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream, void* const* events, int n_events);
+
+/* Number of kernels one call enqueues for this configuration (0 if invalid). */
+int dab_phase_count(const dab_config* cfg);
+
+/* Name of kernel `i` (0-based) of a call, or NULL. */
+const char* dab_phase_name(const dab_config* cfg, int i);
+
+/*
+ * Copy the workspace's sticky device error flag to *flag (host pointer) and
+ * clear it.  Synchronises `stream`.  Bit 0: some pos[b] was outside [0, cap).
+ */
+dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag);
+
+/* Static, human-readable description of a status code. */
+const char* dab_status_string(dab_status status);
+
+/* Library version string. */
+const char* dab_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAB_H */

@@ -1,0 +1,151 @@
+"""The C ABI library: loads, exports what include/dab.h declares, and rejects
+bad arguments on the host before any HIP call (no compute on the CPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from attention_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dab.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from attention_block_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dab_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dab_[a-z_]+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_library_targets_gfx950(lib):
+    # the embedded device code object names its target triple
+    blob = open(_lib.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def cfg(**kw):
+    base = dict(batch=1, hidden=256, n_q_heads=4, n_kv_heads=4, head_dim=64, cache_capacity=129,
+                dtype=_lib.DAB_F32, rope_theta=1e4, eps=1e-6, kv_chunk=0)
+    base.update(kw)
+    return _lib.DabConfig(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=0), dict(hidden=100), dict(head_dim=96), dict(n_q_heads=6, n_kv_heads=4),
+    dict(n_q_heads=32, n_kv_heads=2), dict(dtype=7), dict(rope_theta=0.0), dict(eps=-1.0),
+    dict(cache_capacity=0), dict(kv_chunk=100), dict(batch=-1), dict(rope_theta=float("inf")),
+    dict(eps=float("nan")),
+])
+def test_invalid_configs_have_no_workspace(lib, bad):
+    c = cfg(**bad)
+    assert lib.dab_workspace_size(ctypes.byref(c)) == 0
+    assert lib.dab_phase_count(ctypes.byref(c)) == 0
+
+
+def test_workspace_size_valid(lib):
+    c = cfg()
+    n = lib.dab_workspace_size(ctypes.byref(c))
+    assert n > 0 and n % 256 == 0
+    big = cfg(batch=32, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, cache_capacity=8193,
+              dtype=_lib.DAB_BF16, rope_theta=5e5)
+    assert lib.dab_workspace_size(ctypes.byref(big)) > n
+    assert lib.dab_phase_count(ctypes.byref(c)) == 3
+    assert [lib.dab_phase_name(ctypes.byref(c), i) for i in range(4)][-1] is None
+
+
+class FakePtrs:
+    """Distinct, aligned, never-dereferenced addresses for the pointer checks."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def take(self, nbytes, align=256):
+        p = self.next
+        self.next += (nbytes + 2 * align) // align * align + (1 << 30)
+        return p
+
+
+def call(lib, c, **over):
+    f = FakePtrs()
+    ptrs = dict(hidden=f.take(1 << 20), norm_w=f.take(1 << 20), w_qkv=f.take(1 << 24), w_o=f.take(1 << 24),
+                k_cache=f.take(1 << 24), v_cache=f.take(1 << 24), pos=f.take(64), out=f.take(1 << 20),
+                dbg_y=0, ws=f.take(1 << 26))
+    ws_bytes = lib.dab_workspace_size(ctypes.byref(c))
+    ptrs.update(over)
+    ws_bytes = over.pop("ws_bytes", ws_bytes)
+    vp = ctypes.c_void_p
+    return lib.dab_decode_attn_block(ctypes.byref(c), vp(ptrs["hidden"]), vp(ptrs["norm_w"]), vp(ptrs["w_qkv"]),
+                                     vp(ptrs["w_o"]), vp(ptrs["k_cache"]), vp(ptrs["v_cache"]), vp(ptrs["pos"]),
+                                     vp(ptrs["out"]), vp(ptrs["dbg_y"]), vp(ptrs["ws"]), ws_bytes, None)
+
+
+def test_null_and_misaligned_pointers(lib):
+    c = cfg()
+    for name in ("hidden", "norm_w", "w_qkv", "w_o", "k_cache", "v_cache", "pos", "out"):
+        assert call(lib, c, **{name: 0}) == _lib.DAB_ERR_INVALID_ARG, name
+    for name in ("hidden", "w_qkv", "out", "k_cache"):
+        assert call(lib, c, **{name: (1 << 40) + 8}) == _lib.DAB_ERR_INVALID_ARG, name
+    assert call(lib, c, pos=(1 << 41) + 2) == _lib.DAB_ERR_INVALID_ARG
+    assert call(lib, c, dbg_y=(1 << 42) + 4) == _lib.DAB_ERR_INVALID_ARG
+
+
+def test_workspace_checks(lib):
+    c = cfg()
+    assert call(lib, c, ws=0) == _lib.DAB_ERR_WORKSPACE
+    need = lib.dab_workspace_size(ctypes.byref(c))
+    assert call(lib, c, ws_bytes=need - 256) == _lib.DAB_ERR_WORKSPACE
+    assert call(lib, c, ws=(1 << 43) + 128) == _lib.DAB_ERR_INVALID_ARG
+
+
+def test_output_aliasing_rejected(lib):
+    c = cfg()
+    f = FakePtrs()
+    shared = f.take(1 << 20)
+    assert call(lib, c, hidden=shared, out=shared) == _lib.DAB_ERR_INVALID_ARG
+    assert call(lib, c, k_cache=shared, v_cache=shared + 256) == _lib.DAB_ERR_INVALID_ARG
+    assert call(lib, c, out=shared, dbg_y=shared + 512) == _lib.DAB_ERR_INVALID_ARG
+
+
+def test_unsupported_shapes(lib):
+    assert call(lib, cfg(head_dim=96)) == _lib.DAB_ERR_UNSUPPORTED
+    assert call(lib, cfg(n_q_heads=36, n_kv_heads=4)) == _lib.DAB_ERR_UNSUPPORTED
+
+
+def test_batch_zero_is_a_no_op(lib):
+    # nothing is enqueued, so this is safe without a device
+    assert call(lib, cfg(batch=0)) == _lib.DAB_OK
+
+
+def test_timed_variant_checks_events(lib):
+    c = cfg()
+    vp = ctypes.c_void_p
+    args = [ctypes.byref(c)] + [vp(1 << 40)] * 9 + [vp(1 << 44), lib.dab_workspace_size(ctypes.byref(c)), None]
+    assert lib.dab_decode_attn_block_timed(*args, None, 0) == _lib.DAB_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.dab_status_string(s)
+    assert lib.dab_version().startswith(b"dab")

@@ -1,0 +1,190 @@
+"""HIP path versus the fp64 oracle, element by element, on seeded inputs.
+
+Gates (per tensor, relative L2 over the whole tensor): out, the fp32
+pre-residual tap y, the appended K rows and V rows; <= 1e-2 with bf16
+storage and fp32 accumulation, <= 1e-5 in fp32 mode.  Every cache element
+other than the appended rows must keep its exact bits, including the NaN
+sentinel tail beyond each sequence's position.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from attention_block_amd.inputs import CONFIGS, BlockConfig, make_inputs
+from gpu_util import check_errs, compare, run_gpu, small_cfg, storage_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def parity_case(cfg: BlockConfig, seed: int, *, cap=None, pos=None, kv_chunk=0, label=""):
+    label = label or f"{cfg.name} seed={seed} cap={cap} pos={pos} kv_chunk={kv_chunk}"
+    say(f"[parity] {label}")
+    inp = make_inputs(cfg, seed, cap=cap, pos=pos)
+    ref = oracle.decode_step_from_inputs(inp)
+    dev = to_device(inp)
+    before = (storage_bits(dev["k_cache"]), storage_bits(dev["v_cache"]))
+    out, dbg = run_gpu(dev, cfg, kv_chunk=kv_chunk)
+    errs = compare(inp, ref, dev, out, dbg, before)
+    say(f"[parity] {label}: " + ", ".join(f"{k}={v:.2e}" if isinstance(v, float) else f"{k}={v}"
+                                          for k, v in errs.items()))
+    check_errs(errs, cfg.dtype, label)
+    return errs
+
+
+# ---------------------------------------------------------------------------
+# the workload configurations, full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_config_parity(name, seed):
+    parity_case(CONFIGS[name], seed)
+
+
+# ---------------------------------------------------------------------------
+# edge cases: several tiles, ragged tails, degenerate positions
+# ---------------------------------------------------------------------------
+
+EDGE = [
+    # (label, cfg, cap, pos, kv_chunk)
+    ("single token, empty history", small_cfg("e1", 1, 256, 4, 4, 64, "f32"), 4, [0], 0),
+    ("single token bf16 gqa", small_cfg("e2", 2, 512, 8, 2, 128, "bf16"), 3, [0, 0], 0),
+    ("chunk multiple", small_cfg("e3", 1, 256, 4, 2, 64, "f32"), 200, [127], 64),
+    ("chunk multiple + 1", small_cfg("e4", 1, 256, 4, 2, 64, "f32"), 200, [128], 64),
+    ("odd cap stride", small_cfg("e5", 3, 320, 3, 1, 64, "f32", 5e5), 301, [5, 299, 64], 64),
+    ("partial slabs H=320 bf16", small_cfg("e6", 5, 320, 3, 1, 64, "bf16", 5e5), 97, [96, 1, 63, 64, 65], 0),
+    ("group 8", small_cfg("e7", 2, 1024, 16, 2, 64, "bf16", 1e4), 600, [599, 300], 128),
+    ("batch 9 groups", small_cfg("e8", 9, 512, 4, 4, 128, "bf16"), 130, list(range(0, 129, 16)), 64),
+    ("fp32 d128 gqa", small_cfg("e9", 3, 512, 8, 2, 128, "f32", 5e5), 1100, [1099, 512, 3], 0),
+    ("many chunks", small_cfg("e10", 1, 256, 2, 1, 128, "bf16"), 4097 * 2, [8000], 64),
+]
+
+
+@pytest.mark.parametrize("label,cfg,cap,pos,kv_chunk", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_parity(label, cfg, cap, pos, kv_chunk):
+    parity_case(cfg, 7, cap=cap, pos=pos, kv_chunk=kv_chunk, label=label)
+
+
+def test_tiny_fp32_tolerance_is_met_tightly():
+    errs = parity_case(CONFIGS["tiny_mha_f32"], 3)
+    assert errs["out"] < 1e-6 and errs["y"] < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# properties of the HIP path
+# ---------------------------------------------------------------------------
+
+def test_split_count_invariance():
+    """Different KV chunk sizes give the same result up to fp32 rounding."""
+    import torch
+    cfg = small_cfg("inv", 2, 512, 8, 2, 128, "f32", 5e5)
+    inp = make_inputs(cfg, 11, cap=1500, pos=[1499, 700])
+    say("[split invariance] chunks 64/128/256/1024/4096")
+    outs = []
+    for ch in (64, 128, 256, 1024, 4096):
+        dev = to_device(inp)
+        _, dbg = run_gpu(dev, cfg, kv_chunk=ch)
+        outs.append(dbg.cpu().numpy().astype(np.float64))
+    for o in outs[1:]:
+        assert np.linalg.norm(o - outs[0]) / np.linalg.norm(outs[0]) < 1e-6
+
+
+def test_repeat_calls_are_bit_identical():
+    """Deterministic merges, and counters back at zero after each call."""
+    import torch
+    cfg = CONFIGS["llama3_8b_gqa_bs16_4k"]
+    cfg = BlockConfig("rep", 4, 4096, 32, 8, 128, "bf16", 5e5, pos=1000)
+    inp = make_inputs(cfg, 5)
+    dev = to_device(inp)
+    say("[repeat] three calls on one workspace")
+    res = []
+    for _ in range(3):
+        out, dbg = run_gpu(dev, cfg)
+        res.append((out.clone(), dbg.clone()))
+    for o, d in res[1:]:
+        assert torch.equal(o, res[0][0]) and torch.equal(d, res[0][1])
+
+
+def test_workspace_counters_return_to_zero():
+    import torch
+    import attention_block_amd as ab
+    cfg = small_cfg("ws", 3, 512, 8, 2, 128, "bf16", 5e5)
+    inp = make_inputs(cfg, 2, cap=300, pos=[299, 10, 150])
+    dev = to_device(inp)
+    c = ab.make_config(batch=3, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, cache_capacity=300,
+                       dtype="bf16", rope_theta=5e5)
+    ws = ab.Workspace(ab.workspace_size(c), dev["hidden"].device)
+    say("[counters] call then inspect workspace counters")
+    run_gpu(dev, cfg, workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws._buf[ws.ptr - ws._buf.data_ptr():][: 1024].cpu().numpy().view(np.int32)
+    # the workspace starts with four 256-byte regions: the flags word and the
+    # arrival counters of the three phases (each fits in 256 bytes at this shape)
+    assert np.all(raw == 0)
+
+
+def test_bad_position_sets_flag_and_skips_sequence():
+    import torch
+    import attention_block_amd as ab
+    cfg = small_cfg("badpos", 3, 256, 4, 2, 64, "f32")
+    inp = make_inputs(cfg, 4, cap=40, pos=[10, 20, 30])
+    dev = to_device(inp)
+    dev["pos"][1] = 40                                 # == cap: out of range, seen only on the device
+    before = (storage_bits(dev["k_cache"]), storage_bits(dev["v_cache"]))
+    out = torch.full_like(dev["hidden"], 12345.0)
+    say("[bad pos] sequence 1 at pos == cap")
+    ab.read_device_error()                             # clear any earlier flag
+    ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"], dev["v_cache"],
+                         dev["pos"], cfg.rope_theta, cfg.eps, out=out)
+    flag = ab.read_device_error()
+    assert flag & 1
+    assert torch.all(out[1] == 12345.0)               # its output row was left unwritten
+    kb, vb = storage_bits(dev["k_cache"]), storage_bits(dev["v_cache"])
+    assert np.array_equal(kb[1], before[0][1]) and np.array_equal(vb[1], before[1][1])
+    # the other sequences are still right
+    ref = oracle.decode_step_from_inputs({**inp, "pos": np.array([10, 20, 30])})
+    got = out.cpu().numpy().astype(np.float64)
+    for b in (0, 2):
+        assert np.linalg.norm(got[b] - ref["out"][b]) / np.linalg.norm(ref["out"][b]) < 1e-5
+    assert ab.read_device_error() == 0                 # reading cleared it
+
+
+def test_graph_replay_matches_eager():
+    import torch
+    import attention_block_amd as ab
+    cfg = small_cfg("graph", 2, 512, 8, 2, 128, "bf16", 5e5)
+    inp = make_inputs(cfg, 9, cap=700, pos=[699, 333])
+    dev = to_device(inp)
+    say("[graph] eager, capture, 4 replays")
+    eager, _ = run_gpu(dev, cfg)
+    eager = eager.clone()
+    out = torch.empty_like(dev["hidden"])
+    c = ab.make_config(batch=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, cache_capacity=700,
+                       dtype="bf16", rope_theta=5e5)
+    ws = ab.Workspace(ab.workspace_size(c), dev["hidden"].device)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up call outside capture
+        ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
+                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
+                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws)
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        _ = (dev["hidden"].float() * 2).sum().item()   # unrelated eager work between replays

@@ -64,3 +64,12 @@ def test_bf16_round_trip():
 def test_headline_bytes():
     cfg = CONFIGS["llama2_7b_bs1_4k"]
     assert algorithmic_bytes(cfg, [4096]) == 201_367_556
+
+
+def test_position_override_without_configured_length():
+    cfg = BlockConfig("free", 2, 64, 2, 1, 64, "f32", 1e4)
+    inp = make_inputs(cfg, 0, cap=9, pos=[0, 8])
+    assert list(inp["pos"]) == [0, 8] and inp["k_cache"].shape == (2, 9, 1, 64)
+    assert np.all(np.isnan(inp["k_cache"][0])) and np.all(np.isfinite(inp["k_cache"][1, :8]))
+    with pytest.raises(ValueError):
+        make_inputs(cfg, 0)
