@@ -21,7 +21,10 @@ __all__ = ["DabError", "DabConfig", "make_config", "workspace_size", "Workspace"
 class DabError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        msg = _lib.load().dab_status_string(status).decode()
+        lib = _lib.load()
+        msg = lib.dab_status_string(status).decode()
+        if status == _lib.DAB_ERR_HIP:
+            msg += f" [{lib.dab_last_hip_error().decode()}]"
         super().__init__(f"{where}: {msg} (status {status})")
 
 
@@ -36,12 +39,15 @@ def lib_version() -> str:
 
 def make_config(*, batch: int, hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                 cache_capacity: int, dtype: str, rope_theta: float, eps: float = 1e-6,
-                kv_chunk: int = 0) -> DabConfig:
-    """Build the C config struct.  dtype is "bf16" or "f32"."""
+                kv_chunk: int = 0, schedule: str = "auto") -> DabConfig:
+    """Build the C config struct.  dtype is "bf16" or "f32"; schedule "auto", "fused" or "phased"."""
     if dtype not in ("bf16", "f32"):
         raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
+    if schedule not in _lib.SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(_lib.SCHEDULES)}")
     return DabConfig(batch, hidden, n_q_heads, n_kv_heads, head_dim, cache_capacity,
-                     DAB_BF16 if dtype == "bf16" else DAB_F32, rope_theta, eps, kv_chunk)
+                     DAB_BF16 if dtype == "bf16" else DAB_F32, rope_theta, eps, kv_chunk,
+                     _lib.SCHEDULES[schedule])
 
 
 def workspace_size(cfg: DabConfig) -> int:
@@ -97,7 +103,8 @@ def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
 
 
-def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk):
+def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
+             schedule):
     import torch
     if hidden.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("hidden must be bfloat16 or float32")
@@ -132,20 +139,24 @@ def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps,
         raise ValueError("dbg_y must be a contiguous float32 [B, H] tensor")
     cfg = make_config(batch=B, hidden=H, n_q_heads=nq, n_kv_heads=nkv, head_dim=D, cache_capacity=cap,
                       dtype="bf16" if dt == torch.bfloat16 else "f32", rope_theta=rope_theta, eps=eps,
-                      kv_chunk=kv_chunk)
+                      kv_chunk=kv_chunk, schedule=schedule)
     return cfg, out
 
 
 def decode_attn_block(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta: float, eps: float = 1e-6,
-                      out=None, dbg_y=None, workspace: Optional[Workspace] = None, kv_chunk: int = 0):
+                      out=None, dbg_y=None, workspace: Optional[Workspace] = None, kv_chunk: int = 0,
+                      schedule: str = "auto"):
     """One decode step on the current stream; returns `out`.
 
     Shapes: hidden [B, H]; norm_w [H]; w_qkv [H, (nq+2nkv)D]; w_o [nq D, H];
     k_cache, v_cache [B, cap, nkv, D] (row pos[b] is written); pos int32 [B];
     all but pos in one dtype (bfloat16 or float32) on one GPU.  dbg_y
-    (optional, float32 [B, H]) receives the pre-residual a @ W_o.
+    (optional, float32 [B, H]) receives the pre-residual a @ W_o.  schedule:
+    "fused" (one persistent launch), "phased" (one kernel per phase) or
+    "auto" (fused where it applies).
     """
-    cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk)
+    cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
+                        schedule)
     ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)
     _check(_lib.load().dab_decode_attn_block(
         ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache), _ptr(v_cache),
@@ -201,9 +212,10 @@ class HipEvent:
 
 def decode_attn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos,
                             rope_theta: float, eps: float = 1e-6, out=None, dbg_y=None,
-                            workspace: Optional[Workspace] = None, kv_chunk: int = 0):
+                            workspace: Optional[Workspace] = None, kv_chunk: int = 0, schedule: str = "auto"):
     """decode_attn_block that also records events[0] before the first kernel and events[i] after kernel i-1."""
-    cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk)
+    cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
+                        schedule)
     ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)
     arr = (ctypes.c_void_p * len(events))(*[e.handle.value for e in events])
     _check(_lib.load().dab_decode_attn_block_timed(

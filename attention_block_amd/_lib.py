@@ -5,15 +5,18 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdab.so")
+# DAB_LIBRARY names another build of the same library (e.g. to compare builds)
+LIB_PATH = os.environ.get("DAB_LIBRARY") or os.path.join(HERE, "libdab.so")
 
 DAB_OK, DAB_ERR_INVALID_ARG, DAB_ERR_UNSUPPORTED, DAB_ERR_WORKSPACE, DAB_ERR_HIP = range(5)
 DAB_F32, DAB_BF16 = 0, 1
+SCHEDULES = {"auto": 0, "fused": 1, "phased": 2}
 
 # every symbol include/dab.h declares
 EXPORTS = (
     "dab_workspace_size", "dab_workspace_init", "dab_decode_attn_block", "dab_decode_attn_block_timed",
     "dab_phase_count", "dab_phase_name", "dab_read_device_error", "dab_status_string", "dab_version",
+    "dab_last_hip_error",
 )
 
 
@@ -29,6 +32,7 @@ class DabConfig(ctypes.Structure):
         ("rope_theta", ctypes.c_float),
         ("eps", ctypes.c_float),
         ("kv_chunk", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
     ]
 
 
@@ -42,6 +46,9 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_block_amd.build`")
+    # torch ships its own HIP runtime under the same soname; load it first so
+    # that the library and torch's streams and allocations share one runtime
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32, cfgp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(DabConfig)
     lib.dab_workspace_size.argtypes = [cfgp]
@@ -63,5 +70,7 @@ def load() -> ctypes.CDLL:
     lib.dab_status_string.restype = ctypes.c_char_p
     lib.dab_version.argtypes = []
     lib.dab_version.restype = ctypes.c_char_p
+    lib.dab_last_hip_error.argtypes = []
+    lib.dab_last_hip_error.restype = ctypes.c_char_p
     _lib = lib
     return lib

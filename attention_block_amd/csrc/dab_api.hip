@@ -1,9 +1,10 @@
 // C ABI of the decode attention block (declared in include/dab.h).
-// Validates on the host, then enqueues the three phase kernels on the
-// caller's stream.  No allocation, no synchronisation (except in
-// dab_read_device_error).
+// Validates on the host, then enqueues the fused kernel (or the three phase
+// kernels) on the caller's stream.  No allocation, no synchronisation
+// (except in dab_read_device_error).
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdio.h>
 
 #include "dab.h"
 #include "dab_kernels.h"
@@ -13,98 +14,107 @@ using dab::Plan;
 
 namespace {
 
-constexpr int kPhases = 3;
-const char* const kPhaseNames[kPhases] = {"qkv_rmsnorm_rope_append", "attention_split_kv", "oproj_residual"};
+#ifdef DAB_TRACE
+unsigned long long* g_trace = nullptr;
+#endif
 
-dab_status hip_status(hipError_t e) { return e == hipSuccess ? DAB_OK : DAB_ERR_HIP; }
+const char* const kPhasedNames[3] = {"qkv_rmsnorm_rope_append", "attention_split_kv", "oproj_residual"};
+const char* const kFusedName = "decode_block_fused";
+
+thread_local char g_last_error[256] = "no error";
+
+dab_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return DAB_OK;
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return DAB_ERR_HIP;
+}
+
+int phase_count(const Plan& p) { return p.fused ? 1 : 3; }
 
 dab_status record(void* const* events, int i, hipStream_t s) {
     if (!events) return DAB_OK;
     return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
 }
 
-dab_status enqueue(const Plan& p, const void* hidden, const void* norm_w, const void* w_qkv, const void* w_o,
-                   void* k_cache, void* v_cache, const int32_t* pos, void* out, float* dbg_y, void* workspace,
-                   hipStream_t s, void* const* events) {
+dab::GemvPlanDev gemv_dev(const dab::GemvPlan& g) {
+    dab::GemvPlanDev d;
+    d.slabs = g.slabs;
+    d.ksplit = g.ksplit;
+    d.rows = g.rows;
+    d.nbg = g.nbg;
+    d.tiles = g.tiles;
+    d.items = g.grid;
+    return d;
+}
+
+dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, const void* w_qkv, const void* w_o,
+                        void* k_cache, void* v_cache, const int32_t* pos, void* out, float* dbg_y, void* workspace) {
     char* ws = static_cast<char*>(workspace);
+    auto f = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    auto n = [&](size_t off) { return reinterpret_cast<int*>(ws + off); };
+    dab::StepArgs a{};
+    a.hidden = hidden;
+    a.norm_w = norm_w;
+    a.w_qkv = w_qkv;
+    a.w_o = w_o;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.pos = pos;
+    a.out = out;
+    a.dbg_y = dbg_y;
+    a.flags = n(p.off_flags);
+    a.done_all = a.flags + 1;
+    a.done = n(p.off_done);
+    a.qkv_cnt = n(p.off_qkv_cnt);
+    a.attn_cnt = n(p.off_attn_cnt);
+    a.oproj_cnt = n(p.off_oproj_cnt);
+    a.qkv_part = f(p.off_qkv_part);
+    a.ssq = f(p.off_ssq);
+    a.q = f(p.off_q);
+    a.kv_new = f(p.off_kv_new);
+    a.attn_o = f(p.off_attn_o);
+    a.attn_ml = f(p.off_attn_ml);
+    a.a = f(p.off_a);
+    a.oproj_part = f(p.off_oproj_part);
+    a.B = p.B;
+    a.H = p.H;
+    a.nq = p.nq;
+    a.nkv = p.nkv;
+    a.D = p.D;
+    a.G = p.G;
+    a.cap = p.cap;
+    a.n_qkv = p.n_qkv;
+    a.n_q = p.n_q;
+    a.eps = p.eps;
+    a.qscale = (float)(1.4426950408889634 / sqrt((double)p.D));
+    a.log2_theta = log2((double)p.theta);
+    a.qkv = gemv_dev(p.qkv);
+    a.oproj = gemv_dev(p.oproj);
+    a.qkv_bg = p.qkv.bg;
+    a.T = p.kv_chunk;
+    a.maxc = p.max_chunks;
+    a.attn_items = p.attn_grid;
+    a.total_items = p.total_items;
+#ifdef DAB_TRACE
+    a.trace = g_trace;
+    a.trace_base = 0;
+#endif
+    return a;
+}
+
+dab_status enqueue(const Plan& p, const dab::StepArgs& a, hipStream_t s, void* const* events) {
     const bool bf16 = p.dtype == DAB_BF16;
-    int* flags = reinterpret_cast<int*>(ws + p.off_flags);
-    float* q = reinterpret_cast<float*>(ws + p.off_q);
-    float* a = reinterpret_cast<float*>(ws + p.off_a);
-    dab_status st;
-
-    dab::GemvArgs g{};
-    g.W = w_qkv;
-    g.hidden = hidden;
-    g.norm_w = norm_w;
-    g.part = reinterpret_cast<float*>(ws + p.off_qkv_part);
-    g.ssq = reinterpret_cast<float*>(ws + p.off_ssq);
-    g.cnt = reinterpret_cast<int*>(ws + p.off_qkv_cnt);
-    g.flags = flags;
-    g.pos = pos;
-    g.q = q;
-    g.k_cache = k_cache;
-    g.v_cache = v_cache;
-    g.B = p.B;
-    g.K = p.H;
-    g.N = p.n_qkv;
-    g.slabs = p.qkv.slabs;
-    g.ksplit = p.qkv.ksplit;
-    g.nbg = p.qkv.nbg;
-    g.tiles = p.qkv.tiles;
-    g.cap = p.cap;
-    g.n_q = p.n_q;
-    g.nkv = p.nkv;
-    g.D = p.D;
-    g.eps = p.eps;
-    g.log2_theta = log2((double)p.theta);
-
-    if ((st = record(events, 0, s)) != DAB_OK) return st;
-    if ((st = hip_status(dab::launch_gemv(g, bf16, true, p.qkv.bg, p.qkv.rows, p.qkv.grid, s))) != DAB_OK) return st;
-    if ((st = record(events, 1, s)) != DAB_OK) return st;
-
-    dab::AttnArgs at{};
-    at.q = q;
-    at.k_cache = k_cache;
-    at.v_cache = v_cache;
-    at.pos = pos;
-    at.part_o = reinterpret_cast<float*>(ws + p.off_attn_o);
-    at.part_ml = reinterpret_cast<float*>(ws + p.off_attn_ml);
-    at.cnt = reinterpret_cast<int*>(ws + p.off_attn_cnt);
-    at.a_out = a;
-    at.nq = p.nq;
-    at.nkv = p.nkv;
-    at.cap = p.cap;
-    at.T = p.kv_chunk;
-    at.maxc = p.max_chunks;
-    at.qscale = (float)(1.4426950408889634 / sqrt((double)p.D));
-    if ((st = hip_status(dab::launch_attn(at, bf16, p.D, p.G, p.attn_grid, s))) != DAB_OK) return st;
-    if ((st = record(events, 2, s)) != DAB_OK) return st;
-
-    dab::GemvArgs o{};
-    o.W = w_o;
-    o.hidden = hidden;
-    o.xin = a;
-    o.part = reinterpret_cast<float*>(ws + p.off_oproj_part);
-    o.cnt = reinterpret_cast<int*>(ws + p.off_oproj_cnt);
-    o.flags = flags;
-    o.pos = pos;
-    o.out = out;
-    o.dbg_y = dbg_y;
-    o.B = p.B;
-    o.K = p.n_q;
-    o.N = p.H;
-    o.slabs = p.oproj.slabs;
-    o.ksplit = p.oproj.ksplit;
-    o.nbg = p.oproj.nbg;
-    o.tiles = p.oproj.tiles;
-    o.cap = p.cap;
-    o.n_q = p.n_q;
-    o.nkv = p.nkv;
-    o.D = p.D;
-    if ((st = hip_status(dab::launch_gemv(o, bf16, false, p.oproj.bg, p.oproj.rows, p.oproj.grid, s))) != DAB_OK)
-        return st;
-    return record(events, 3, s);
+    dab_status st = record(events, 0, s);
+    if (st != DAB_OK) return st;
+    if (p.fused) {
+        if ((st = hip_status(dab::launch_fused(a, bf16, s))) != DAB_OK) return st;
+        return record(events, 1, s);
+    }
+    for (int phase = 0; phase < 3; ++phase) {
+        if ((st = hip_status(dab::launch_phase(a, bf16, phase, s))) != DAB_OK) return st;
+        if ((st = record(events, phase + 1, s)) != DAB_OK) return st;
+    }
+    return DAB_OK;
 }
 
 dab_status call(const dab_config* cfg, const void* hidden, const void* norm_w, const void* w_qkv, const void* w_o,
@@ -117,18 +127,23 @@ dab_status call(const dab_config* cfg, const void* hidden, const void* norm_w, c
                          workspace_bytes);
     if (st != DAB_OK) return st;
     if (events) {
-        if (n_events != kPhases + 1) return DAB_ERR_INVALID_ARG;
+        if (n_events != phase_count(p) + 1) return DAB_ERR_INVALID_ARG;
         for (int i = 0; i < n_events; ++i)
             if (!events[i]) return DAB_ERR_INVALID_ARG;
     }
     if (p.B == 0) return DAB_OK;
-    return enqueue(p, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y, workspace,
-                   static_cast<hipStream_t>(stream), events);
+    const dab::StepArgs a = step_args(p, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y, workspace);
+    return enqueue(p, a, static_cast<hipStream_t>(stream), events);
 }
 
 }  // namespace
 
 extern "C" {
+
+#ifdef DAB_TRACE
+// Profiling builds only: device buffer of [grid, 4] timestamps for later calls (null: off).
+void dab_trace_set_buffer(void* p) { g_trace = static_cast<unsigned long long*>(p); }
+#endif
 
 size_t dab_workspace_size(const dab_config* cfg) {
     Plan p;
@@ -159,12 +174,13 @@ dab_status dab_decode_attn_block_timed(const dab_config* cfg, const void* hidden
 
 int dab_phase_count(const dab_config* cfg) {
     Plan p;
-    return dab::make_plan(cfg, &p) == DAB_OK ? kPhases : 0;
+    return dab::make_plan(cfg, &p) == DAB_OK ? phase_count(p) : 0;
 }
 
 const char* dab_phase_name(const dab_config* cfg, int i) {
-    if (dab_phase_count(cfg) == 0 || i < 0 || i >= kPhases) return nullptr;
-    return kPhaseNames[i];
+    Plan p;
+    if (dab::make_plan(cfg, &p) != DAB_OK || i < 0 || i >= phase_count(p)) return nullptr;
+    return p.fused ? kFusedName : kPhasedNames[i];
 }
 
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag) {
@@ -172,11 +188,11 @@ dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t host = 0;
     // the flags word sits at offset 0 of every workspace layout
-    if (hipMemcpyAsync(&host, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return DAB_ERR_HIP;
-    if (hipStreamSynchronize(s) != hipSuccess) return DAB_ERR_HIP;
+    dab_status st = hip_status(hipMemcpyAsync(&host, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    if (st == DAB_OK) st = hip_status(hipStreamSynchronize(s));
+    if (st != DAB_OK) return st;
     *flag = host;
-    if (dab::launch_fill_zero(workspace, sizeof(int32_t), s) != hipSuccess) return DAB_ERR_HIP;
-    return DAB_OK;
+    return hip_status(dab::launch_fill_zero(workspace, sizeof(int32_t), s));
 }
 
 const char* dab_status_string(dab_status status) {
@@ -190,6 +206,8 @@ const char* dab_status_string(dab_status status) {
     }
     return "unknown status";
 }
+
+const char* dab_last_hip_error(void) { return g_last_error; }
 
 const char* dab_version(void) { return "dab 0.1.0 (gfx950)"; }
 

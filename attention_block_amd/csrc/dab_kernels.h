@@ -9,44 +9,68 @@
 
 namespace dab {
 
-// One GEMV phase: QKV (RMSNorm folded in, RoPE + cache append in the
-// finaliser) or O-projection (residual in the finaliser).
-struct GemvArgs {
-    const void* W;          // [K, N] storage type, row-major
-    const void* hidden;     // [B, H] storage type
-    const void* norm_w;     // [H] storage type (QKV)
-    const float* xin;       // [B, K] fp32 input rows (O-projection: attention output)
-    float* part;            // [ksplit, B, N] fp32 partial sums
-    float* ssq;             // [slabs, ksplit, B] partial sums of x^2 (QKV)
-    int* cnt;               // [slabs * nbg] arrival counters, zero between calls
-    int* flags;             // device error flags
-    const int* pos;         // [B]
-    float* q;               // [B, nq*D] rotated q, fp32 (QKV)
-    void* k_cache;          // [B, cap, nkv, D] (QKV)
-    void* v_cache;
-    void* out;              // [B, H] (O-projection)
-    float* dbg_y;           // [B, H] fp32 or null (O-projection)
-    int B, K, N, slabs, ksplit, nbg, tiles;
-    int cap, n_q, nkv, D;
-    float eps;
-    double log2_theta;
+// Finish counting in the fused schedule: sub-counters on separate 256-byte lines.
+constexpr int kDoneShards = 16;
+constexpr int kDoneStride = 64;
+
+// Tiling of one GEMV phase as the kernels see it.
+struct GemvPlanDev {
+    int slabs;     // 256-column slabs
+    int ksplit;    // row blocks (K / rows)
+    int rows;      // KR: rows of W per tile (64 or 128)
+    int nbg;       // batch groups
+    int tiles;     // slabs * ksplit
+    int items;     // work indices (tiles, padded per batch group)
 };
 
-struct AttnArgs {
-    const float* q;         // [B, nq*D] rotated q
-    const void* k_cache;    // [B, cap, nkv, D]
-    const void* v_cache;
+// Everything one decode step needs, for every kernel of either schedule.
+struct StepArgs {
+    // caller tensors
+    const void* hidden;     // [B, H]
+    const void* norm_w;     // [H]
+    const void* w_qkv;      // [H, n_qkv]
+    const void* w_o;        // [n_q, H]
+    void* k_cache;          // [B, cap, nkv, D]
+    void* v_cache;
     const int* pos;         // [B]
-    float* part_o;          // [B, nq, maxc, D] unnormalised chunk outputs
-    float* part_ml;         // [B, nq, maxc, 2] chunk (max, sum) in log2 units
-    int* cnt;               // [B * nkv] arrival counters
-    float* a_out;           // [B, nq*D] attention output
-    int nq, nkv, cap, T, maxc;
-    float qscale;           // log2(e) / sqrt(D)
+    void* out;              // [B, H]
+    float* dbg_y;           // [B, H] or null
+    // workspace
+    int* flags;             // error bits
+    int* done;              // fused schedule: finished items, kDoneShards counters kDoneStride ints apart
+    int* done_all;          // fused schedule: finished shards
+    int* qkv_cnt;           // [q slabs * nbg] tile arrivals (+1 when the slab is final)
+    int* attn_cnt;          // [B * nkv] chunk arrivals (+1 when merged)
+    int* oproj_cnt;         // [o slabs * nbg] tile arrivals
+    float* qkv_part;        // [q ksplit, B, n_qkv]
+    float* ssq;             // [q slabs, q ksplit, B]
+    float* q;               // [B, n_q] rotated q
+    float* kv_new;          // [B, 2, nkv, D] the new token's rotated k and v
+    float* attn_o;          // [B, nq, maxc, D]
+    float* attn_ml;         // [B, nq, maxc, 2]
+    float* a;               // [B, n_q] attention output
+    float* oproj_part;      // [o ksplit, B, H]
+    // shapes and numerics
+    int B, H, nq, nkv, D, G, cap, n_qkv, n_q;
+    float eps, qscale;      // qscale = log2(e) / sqrt(D)
+    double log2_theta;
+    // plan
+    GemvPlanDev qkv, oproj;
+    int qkv_bg;             // batch rows per GEMV tile
+    int T, maxc, attn_items;
+    int total_items;        // fused schedule: grid size
+#ifdef DAB_TRACE
+    unsigned long long* trace;   // [items, 4] timestamps per workgroup (profiling builds only)
+    int trace_base;              // item number of this launch's workgroup 0
+#endif
 };
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-hipError_t launch_gemv(const GemvArgs& a, bool bf16, bool qkv, int bg, int rows, int grid, hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, bool bf16, int D, int G, int grid, hipStream_t s);
+hipError_t launch_fused(const StepArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_phase(const StepArgs& a, bool bf16, int phase, hipStream_t s);
+
+// per-dtype instantiations of the fused kernel (separate translation units)
+hipError_t launch_fused_bf16(const StepArgs& a, hipStream_t s);
+hipError_t launch_fused_f32(const StepArgs& a, hipStream_t s);
 
 }  // namespace dab

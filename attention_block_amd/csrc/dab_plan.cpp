@@ -11,20 +11,22 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // Split a [K, N] GEMV over `batch` input rows into workgroup tiles: slabs of
-// kSlab columns, `rows` rows of W each, `bg` batch rows per workgroup.
-// Aims for at least four workgroups per compute unit (1024 on 256 CUs).
-void plan_gemv(int K, int N, int batch, GemvPlan* g) {
+// kSlab columns, `rows` rows of W each (128 where K allows: 64 KB bf16 tiles,
+// and half the partials of 64-row tiles to sum at the end), `bg` batch rows
+// per workgroup.
+void plan_gemv(int K, int N, int batch, bool fused, GemvPlan* g) {
     g->K = K;
     g->N = N;
     g->slabs = ceil_div(N, kSlab);
     g->bg = batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
     g->nbg = ceil_div(batch, g->bg);
-    g->rows = (K % 128 == 0 && (long long)g->slabs * (K / 128) * g->nbg >= 1024) ? 128 : 64;
+    (void)fused;
+    g->rows = K % 128 == 0 ? 128 : 64;
     g->ksplit = K / g->rows;
     g->tiles = g->slabs * g->ksplit;
     // With several batch groups the tiles are padded to a multiple of 8 so
-    // that the groups sharing one weight tile land on one XCD (see the
-    // workgroup-id decoding in the GEMV kernel).
+    // that the groups sharing one weight tile land on one XCD (see
+    // gemv_decode).
     g->grid = g->nbg == 1 ? g->tiles : (int)align_up((size_t)g->tiles, 8) * g->nbg;
 }
 
@@ -52,7 +54,7 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     if (c.head_dim != 64 && c.head_dim != 128) return DAB_ERR_UNSUPPORTED;
     if (c.hidden % 64 != 0) return DAB_ERR_UNSUPPORTED;
     if (c.n_q_heads / c.n_kv_heads > kMaxGroup) return DAB_ERR_UNSUPPORTED;
-    if (c.kv_chunk != 0 && (c.kv_chunk < 64 || c.kv_chunk > 4096 || c.kv_chunk % 64 != 0))
+    if (c.kv_chunk != 0 && (c.kv_chunk < 32 || c.kv_chunk > 4096 || c.kv_chunk % 16 != 0))
         return DAB_ERR_INVALID_ARG;
     // keep every element offset of the caches and weights inside int64 and
     // the per-dimension products inside int32
@@ -75,26 +77,46 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     p->elem = c.dtype == DAB_BF16 ? 2 : 4;
 
     const int B = p->B > 0 ? p->B : 1;  // plan a batch-0 call as batch 1; nothing is launched
-    plan_gemv(p->H, p->n_qkv, B, &p->qkv);
-    plan_gemv(p->n_q, p->H, B, &p->oproj);
 
-    // split-KV chunk: the largest of 256/128/64 tokens that still gives at
-    // least 1024 work items over the batch and KV heads, then grown until
-    // the chunk count per sequence fits the merge step
+    // schedule: fused only where its fixed chunk and group sizes apply
+    const int fchunk = fused_chunk(p->D);
+    const bool fused_ok = (p->G == 1 || p->G == 2 || p->G == 4 || p->G == 8) &&
+                          (c.kv_chunk == 0 || c.kv_chunk == fchunk) &&
+                          (p->cap - 1 + fchunk - 1) / fchunk <= kMaxChunks;
+    if (c.schedule == DAB_SCHEDULE_FUSED && !fused_ok) return DAB_ERR_UNSUPPORTED;
+    if (c.schedule != DAB_SCHEDULE_AUTO && c.schedule != DAB_SCHEDULE_FUSED && c.schedule != DAB_SCHEDULE_PHASED)
+        return DAB_ERR_INVALID_ARG;
+    // AUTO takes the phased schedule: it measures faster on MI355X so far
+    p->fused = c.schedule == DAB_SCHEDULE_FUSED;
+
+    plan_gemv(p->H, p->n_qkv, B, p->fused, &p->qkv);
+    plan_gemv(p->n_q, p->H, B, p->fused, &p->oproj);
+
+    // split-KV chunk over the cached tokens (at most cap - 1; the new token
+    // rides with the last chunk).  Fused: one batch of loads per item.
+    // Phased: about 1024 items per pass over the batch and KV heads (one
+    // wave of resident workgroups, four per CU), chunks of 32..256 tokens in
+    // steps of 16; a chunk count just above a wave boundary would leave a
+    // nearly empty second wave.
+    const int hist = p->cap - 1 > 0 ? p->cap - 1 : 1;
     int T = c.kv_chunk;
-    if (T == 0) {
-        T = 64;
-        for (int cand : {256, 128}) {
-            if ((long long)B * p->nkv * ceil_div(p->cap, cand) >= 1024) { T = cand; break; }
-        }
-        while (ceil_div(p->cap, T) > kMaxChunks && T < 4096) T *= 2;
+    if (p->fused) {
+        T = fchunk;
+    } else if (T == 0) {
+        const int want = (1024 + B * p->nkv - 1) / (B * p->nkv);     // chunks per sequence and kv head
+        T = (ceil_div(hist, want) + 15) / 16 * 16;
+        if (T < 32) T = 32;
+        if (T > 256) T = 256;
+        while (ceil_div(hist, T) > kMaxChunks) T += 256;
     }
     p->kv_chunk = T;
-    p->max_chunks = ceil_div(p->cap, T);
+    p->max_chunks = ceil_div(hist, T);
     if (p->max_chunks > kMaxChunks) return DAB_ERR_UNSUPPORTED;
     const long long attn_grid = (long long)B * p->nkv * p->max_chunks;
-    if (attn_grid > (1LL << 30)) return DAB_ERR_UNSUPPORTED;
+    const long long total = attn_grid + p->qkv.grid + p->oproj.grid;
+    if (total > (1LL << 30)) return DAB_ERR_UNSUPPORTED;
     p->attn_grid = (int)attn_grid;
+    p->total_items = (int)total;
 
     // workspace layout
     size_t off = 0;
@@ -104,12 +126,14 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
         return at;
     };
     p->off_flags = take(256);
+    p->off_done = take(256 * 16);
     p->off_qkv_cnt = take(sizeof(int32_t) * p->qkv.slabs * p->qkv.nbg);
     p->off_attn_cnt = take(sizeof(int32_t) * B * p->nkv);
     p->off_oproj_cnt = take(sizeof(int32_t) * p->oproj.slabs * p->oproj.nbg);
     p->off_qkv_part = take(sizeof(float) * (size_t)p->qkv.ksplit * B * p->n_qkv);
     p->off_ssq = take(sizeof(float) * (size_t)p->qkv.slabs * p->qkv.ksplit * B);
     p->off_q = take(sizeof(float) * (size_t)B * p->n_q);
+    p->off_kv_new = take(sizeof(float) * (size_t)B * 2 * p->nkv * p->D);
     p->off_attn_o = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * p->D);
     p->off_attn_ml = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * 2);
     p->off_a = take(sizeof(float) * (size_t)B * p->n_q);

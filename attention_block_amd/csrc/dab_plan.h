@@ -18,6 +18,9 @@ constexpr int kThreads = 256;
 constexpr int kMaxChunks = 1024;
 // Largest query-head group per KV head the attention kernel keeps in registers.
 constexpr int kMaxGroup = 8;
+// Tokens per attention chunk in the fused schedule: one batch of loads,
+// 256 / (D/8) row slots x 8 tokens.
+inline int fused_chunk(int head_dim) { return 8 * 256 / (head_dim / 8); }
 
 struct GemvPlan {
     int K = 0, N = 0;     // reduction length, output columns
@@ -27,7 +30,7 @@ struct GemvPlan {
     int bg = 0;           // batch rows per workgroup (1, 2, 4 or 8)
     int nbg = 0;          // ceil(B / bg)
     int tiles = 0;        // slabs * ksplit
-    int grid = 0;         // workgroups launched
+    int grid = 0;         // work indices: tiles, padded per batch group
 };
 
 struct Plan {
@@ -36,12 +39,16 @@ struct Plan {
     float theta = 0.f, eps = 0.f;
     int elem = 0;                // bytes per stored element
 
+    bool fused = false;          // one persistent launch (else one kernel per phase)
     GemvPlan qkv, oproj;
     int kv_chunk = 0, max_chunks = 0, attn_grid = 0;
+    int total_items = 0;         // fused: qkv.grid + attn_grid + oproj.grid
 
-    // workspace layout, byte offsets (each 256-byte aligned)
-    size_t off_flags = 0, off_qkv_cnt = 0, off_attn_cnt = 0, off_oproj_cnt = 0;
-    size_t off_qkv_part = 0, off_ssq = 0, off_q = 0;
+    // workspace layout, byte offsets (each 256-byte aligned).  The flags
+    // word is at offset 0, the finished-shard count at 4; the 16 finish
+    // sub-counters follow, one per 256 bytes.
+    size_t off_flags = 0, off_done = 0, off_qkv_cnt = 0, off_attn_cnt = 0, off_oproj_cnt = 0;
+    size_t off_qkv_part = 0, off_ssq = 0, off_q = 0, off_kv_new = 0;
     size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0, off_oproj_part = 0;
     size_t ws_bytes = 0;
 

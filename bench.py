@@ -47,7 +47,8 @@ def phase_bytes(cfg: BlockConfig, pos) -> dict:
     attn = s * 2 * nkv * D * tot
     # the hidden row is counted once, with the QKV kernel; the O-projection writes out
     oproj = s * nq * D * H + s * B * H
-    return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj}
+    return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj,
+            "decode_block_fused": qkv + attn + oproj}
 
 
 def make_layer_set(cfg: BlockConfig, pos, cap: int, gen, device):
@@ -121,6 +122,7 @@ def main() -> int:
     ap.add_argument("--config", default=HEADLINE, choices=sorted(CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "fused", "phased"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true")
@@ -152,7 +154,7 @@ def main() -> int:
     sets = [make_layer_set(cfg, pos, cap, gen, dev) for _ in range(R)]
     c = ab.make_config(batch=cfg.batch, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
                        head_dim=cfg.head_dim, cache_capacity=cap, dtype=cfg.dtype, rope_theta=cfg.rope_theta,
-                       eps=cfg.eps, kv_chunk=args.kv_chunk)
+                       eps=cfg.eps, kv_chunk=args.kv_chunk, schedule=args.schedule)
     ws = ab.Workspace(ab.workspace_size(c), dev)
     phases = ab.phase_names(c)
 
@@ -161,11 +163,11 @@ def main() -> int:
         if events is None:
             ab.decode_attn_block(s["hidden"], s["norm_w"], s["w_qkv"], s["w_o"], s["k_cache"], s["v_cache"],
                                  s["pos"], cfg.rope_theta, cfg.eps, out=s["out"], workspace=ws,
-                                 kv_chunk=args.kv_chunk)
+                                 kv_chunk=args.kv_chunk, schedule=args.schedule)
         else:
             ab.decode_attn_block_timed(events, s["hidden"], s["norm_w"], s["w_qkv"], s["w_o"], s["k_cache"],
                                        s["v_cache"], s["pos"], cfg.rope_theta, cfg.eps, out=s["out"],
-                                       workspace=ws, kv_chunk=args.kv_chunk)
+                                       workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule)
 
     for i in range(args.warmup):
         step(i)
@@ -264,7 +266,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "batch": cfg.batch, "hidden": cfg.hidden,
                    "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "kv_tokens": int(pos[0]) if cfg.ragged is None else f"ragged sum {int(np.sum(pos))}",
-                   "layer_sets": R, "parallelism": "single GPU"},
+                   "layer_sets": R, "parallelism": "single GPU", "schedule": "+".join(phases)},
         "hbm_gbps": round(gbps, 1),
         "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         "algorithmic_bytes": nbytes,

@@ -69,9 +69,22 @@ typedef struct {
     int32_t dtype;           /* dab_dtype                                               */
     float rope_theta;        /* RoPE base, > 0                                          */
     float eps;               /* RMSNorm epsilon, >= 0 (1e-6 in the pages' kernels)      */
-    int32_t kv_chunk;        /* tokens per split-KV work item: 0 = automatic, else a    */
-                             /* multiple of 64 in [64, 4096]                            */
+    int32_t kv_chunk;        /* cached tokens per split-KV work item: 0 = automatic,    */
+                             /* else a multiple of 16 in [32, 4096]                     */
+    int32_t schedule;        /* dab_schedule: how the step is laid out on the GPU        */
 } dab_config;
+
+/*
+ * DAB_SCHEDULE_FUSED runs the whole step as one persistent launch: workgroups
+ * take work items in dependency order (QKV tiles, attention chunks, output
+ * tiles), issue their HBM loads first and then wait on device-side counters,
+ * so the three weight/cache streams overlap.  It needs n_q_heads / n_kv_heads
+ * in {1, 2, 4, 8} and kv_chunk 0 (the chunk is 128 tokens for D = 128, 256
+ * for D = 64).  DAB_SCHEDULE_PHASED runs one kernel per phase.  AUTO picks
+ * the schedule measured faster on MI355X (currently PHASED).  The two split their sums differently, so results
+ * agree to fp32 rounding, not bit for bit; each is deterministic.
+ */
+typedef enum { DAB_SCHEDULE_AUTO = 0, DAB_SCHEDULE_FUSED = 1, DAB_SCHEDULE_PHASED = 2 } dab_schedule;
 
 /*
  * Bytes of device workspace one call with this configuration needs (0 when
@@ -121,7 +134,8 @@ dab_status dab_decode_attn_block(const dab_config* cfg,
 /*
  * Same as dab_decode_attn_block, and also records `n_events` hipEvent_t
  * (passed as void*) on `stream`: events[0] before the first kernel and
- * events[i] after kernel i-1.  n_events must equal dab_phase_count(cfg) + 1.
+ * events[i] after kernel i-1.  n_events must equal dab_phase_count(cfg) + 1
+ * (2 for the fused schedule, 4 for the phased one).
  * Used to time the phases of the step on the stream they run on.
  */
 dab_status dab_decode_attn_block_timed(const dab_config* cfg,
@@ -141,11 +155,20 @@ const char* dab_phase_name(const dab_config* cfg, int i);
 /*
  * Copy the workspace's sticky device error flag to *flag (host pointer) and
  * clear it.  Synchronises `stream`.  Bit 0: some pos[b] was outside [0, cap).
+ * Bit 1: a workgroup of the fused schedule gave up waiting for a dependency
+ * (a bounded wait that cannot expire in a correct run; results are invalid).
  */
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag);
 
 /* Static, human-readable description of a status code. */
 const char* dab_status_string(dab_status status);
+
+/*
+ * Name and description of the last HIP error that made a call on this
+ * thread return DAB_ERR_HIP ("no error" if none).  The string is owned by
+ * the library and valid until the next call on this thread.
+ */
+const char* dab_last_hip_error(void);
 
 /* Library version string. */
 const char* dab_version(void);

@@ -44,13 +44,13 @@ def storage_values(t):
         t.cpu().numpy().astype(np.float64)
 
 
-def run_gpu(dev: dict, cfg: BlockConfig, kv_chunk=0, workspace=None):
+def run_gpu(dev: dict, cfg: BlockConfig, kv_chunk=0, workspace=None, schedule="auto"):
     import torch
     import attention_block_amd as ab
     dbg = torch.empty(dev["hidden"].shape, dtype=torch.float32, device=dev["hidden"].device)
     out = ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
                                dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, dbg_y=dbg,
-                               kv_chunk=kv_chunk, workspace=workspace)
+                               kv_chunk=kv_chunk, workspace=workspace, schedule=schedule)
     torch.cuda.synchronize()
     return out, dbg
 

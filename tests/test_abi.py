@@ -71,8 +71,25 @@ def test_workspace_size_valid(lib):
     big = cfg(batch=32, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, cache_capacity=8193,
               dtype=_lib.DAB_BF16, rope_theta=5e5)
     assert lib.dab_workspace_size(ctypes.byref(big)) > n
-    assert lib.dab_phase_count(ctypes.byref(c)) == 3
-    assert [lib.dab_phase_name(ctypes.byref(c), i) for i in range(4)][-1] is None
+    fu = cfg(schedule=1)
+    assert lib.dab_phase_count(ctypes.byref(fu)) == 1
+    assert lib.dab_phase_name(ctypes.byref(fu), 0) == b"decode_block_fused"
+    assert lib.dab_phase_count(ctypes.byref(c)) == 3                    # auto: phased
+    ph = cfg(schedule=2)
+    assert lib.dab_phase_count(ctypes.byref(ph)) == 3
+    assert [lib.dab_phase_name(ctypes.byref(ph), i) for i in range(4)] == [
+        b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual", None]
+
+
+def test_schedule_selection(lib):
+    # a group of 3 query heads per kv head runs phased under auto, and cannot run fused
+    g3 = cfg(n_q_heads=6, n_kv_heads=2)
+    assert lib.dab_phase_count(ctypes.byref(g3)) == 3
+    assert call(lib, cfg(n_q_heads=6, n_kv_heads=2, schedule=1)) == _lib.DAB_ERR_UNSUPPORTED
+    # the fused chunk is 256 tokens for D = 64: another explicit chunk needs the phased schedule
+    assert call(lib, cfg(kv_chunk=64, schedule=1)) == _lib.DAB_ERR_UNSUPPORTED
+    assert lib.dab_phase_count(ctypes.byref(cfg(kv_chunk=64))) == 3
+    assert lib.dab_workspace_size(ctypes.byref(cfg(schedule=7))) == 0
 
 
 class FakePtrs:
