@@ -19,6 +19,7 @@ unsigned long long* g_trace = nullptr;
 #endif
 
 const char* const kPhasedNames[3] = {"qkv_rmsnorm_rope_append", "attention_split_kv", "oproj_residual"};
+const char* const kTwoStageNames[2] = {"qkv_rmsnorm_rope_append", "attention_oproj_fused"};
 const char* const kFusedName = "decode_block_fused";
 
 thread_local char g_last_error[256] = "no error";
@@ -29,7 +30,9 @@ dab_status hip_status(hipError_t e) {
     return DAB_ERR_HIP;
 }
 
-int phase_count(const Plan& p) { return p.fused ? 1 : 3; }
+int phase_count(const Plan& p) {
+    return p.schedule == DAB_SCHEDULE_FUSED ? 1 : p.schedule == DAB_SCHEDULE_TWO_STAGE ? 2 : 3;
+}
 
 dab_status record(void* const* events, int i, hipStream_t s) {
     if (!events) return DAB_OK;
@@ -64,6 +67,7 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.dbg_y = dbg_y;
     a.flags = n(p.off_flags);
     a.done_all = a.flags + 1;
+    a.epoch = a.flags + 2;
     a.done = n(p.off_done);
     a.qkv_cnt = n(p.off_qkv_cnt);
     a.attn_cnt = n(p.off_attn_cnt);
@@ -95,6 +99,12 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.maxc = p.max_chunks;
     a.attn_items = p.attn_grid;
     a.total_items = p.total_items;
+    a.item_lo = 0;
+    a.units = p.units;
+    a.unit_items = p.unit_items;
+    a.unit_slabs = p.unit_slabs;
+    a.unit_kv = p.unit_kv;
+    a.unit_oks = p.unit_oks;
 #ifdef DAB_TRACE
     a.trace = g_trace;
     a.trace_base = 0;
@@ -106,9 +116,16 @@ dab_status enqueue(const Plan& p, const dab::StepArgs& a, hipStream_t s, void* c
     const bool bf16 = p.dtype == DAB_BF16;
     dab_status st = record(events, 0, s);
     if (st != DAB_OK) return st;
-    if (p.fused) {
+    if (p.schedule == DAB_SCHEDULE_FUSED) {
         if ((st = hip_status(dab::launch_fused(a, bf16, s))) != DAB_OK) return st;
         return record(events, 1, s);
+    }
+    if (p.schedule == DAB_SCHEDULE_TWO_STAGE) {
+        for (int stage = 0; stage < 2; ++stage) {
+            if ((st = hip_status(dab::launch_two_stage(a, bf16, stage, s))) != DAB_OK) return st;
+            if ((st = record(events, stage + 1, s)) != DAB_OK) return st;
+        }
+        return DAB_OK;
     }
     for (int phase = 0; phase < 3; ++phase) {
         if ((st = hip_status(dab::launch_phase(a, bf16, phase, s))) != DAB_OK) return st;
@@ -180,7 +197,8 @@ int dab_phase_count(const dab_config* cfg) {
 const char* dab_phase_name(const dab_config* cfg, int i) {
     Plan p;
     if (dab::make_plan(cfg, &p) != DAB_OK || i < 0 || i >= phase_count(p)) return nullptr;
-    return p.fused ? kFusedName : kPhasedNames[i];
+    return p.schedule == DAB_SCHEDULE_FUSED ? kFusedName
+         : p.schedule == DAB_SCHEDULE_TWO_STAGE ? kTwoStageNames[i] : kPhasedNames[i];
 }
 
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag) {

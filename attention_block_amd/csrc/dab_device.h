@@ -38,11 +38,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_inff();
 
 // Profiling builds (-DDAB_TRACE) record a 100 MHz timestamp per workgroup at
-// four points: 0 start, 1 loads issued, 2 dependencies met, 3 end.
+// up to eight points: 0 start, 1 loads issued, 2 dependencies met, 3 end;
+// in the workgroup that finishes a slab or merges a group: 4 its start,
+// 5 its inputs fetched, 6 its results published.
 #ifdef DAB_TRACE
 #define DAB_TRACE_POINT(args, slot) \
     do { if (threadIdx.x == 0 && (args).trace) \
-        (args).trace[((args).trace_base + blockIdx.x) * 4 + (slot)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+        (args).trace[((args).trace_base + blockIdx.x) * 8 + (slot)] = __builtin_amdgcn_s_memrealtime(); } while (0)
 #else
 #define DAB_TRACE_POINT(args, slot) do { } while (0)
 #endif
@@ -183,22 +185,6 @@ __device__ inline void drain_and_sync() {
     __syncthreads();
 }
 
-// Arrival at a counter shared by `expected` workgroups; true in exactly one
-// workgroup, the last to arrive.  With `rearm` that workgroup also resets
-// the counter (nobody waits on it); otherwise it stays at `expected` until
-// the finaliser signals completion with one more bump.
-__device__ inline bool arrive_last(int* counter, int expected, bool rearm, int* s_flag) {
-    drain_and_sync();
-    if (threadIdx.x == 0) {
-        const int prev = bump(counter);
-        const bool last = prev == expected - 1;
-        *s_flag = last;
-        if (last && rearm) set_counter(counter, 0);
-    }
-    __syncthreads();
-    return *s_flag != 0;
-}
-
 // Thread 0 waits (bounded) until *p >= target.  The bound cannot be reached
 // in a correct run; if it is, bit 1 of the error flags is raised and the
 // caller carries on, so every wave still exits.
@@ -210,20 +196,118 @@ __device__ inline void wait_at_least(const int* p, int target, int* flags) {
     __hip_atomic_fetch_or(flags, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Sum of n published floats p[0], p[stride], ... in index order.  Loads go
-// out NB at a time so their round trips to the memory-side cache overlap;
-// with n <= NB the whole sum costs one round trip.
-template <int NB>
-__device__ inline float fetch_sum(const float* p, size_t stride, int n) {
+// ---------------------------------------------------------------------------
+// Published values.  The phased schedule publishes plain floats (each kernel
+// boundary orders them); the fused schedule publishes 8-byte words
+// {value, tag} with one 64-bit device-coherent store, the low-latency
+// message format of RCCL's LL protocol.  A reader checks the tag against
+// this call's tag and re-reads a word that has not landed yet, so a producer
+// bumps its arrival counter without waiting for its stores to be
+// acknowledged.  The tag is a signalling-NaN bit pattern derived from the
+// call epoch, which no arithmetic result (and no float another call left in
+// the workspace) can equal.  Buffers hold 8 bytes per element in both
+// schedules; the phased one uses the low half as a float array.
+
+__device__ inline uint32_t ll_tag(uint32_t epoch) { return 0x7F800001u + epoch % 0x3FFFFFu; }
+
+template <bool LL>
+__device__ inline void put(float* base, size_t i, float v, uint32_t tag) {
+    if constexpr (LL) {
+        const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(base) + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        publish(base + i, v);
+    }
+}
+
+__device__ inline uint64_t load_ll(const float* base, size_t i) {
+    return __hip_atomic_load(reinterpret_cast<const uint64_t*>(base) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Value of an LL word once it carries `tag` (re-read with a bounded wait).
+__device__ inline float ll_value(uint64_t w, const float* base, size_t i, uint32_t tag, int* flags) {
+    for (int it = 0; (uint32_t)(w >> 32) != tag; ++it) {
+        if (it == kSpinLimit) {
+            __hip_atomic_fetch_or(flags, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        w = load_ll(base, i);
+    }
+    return __uint_as_float((uint32_t)w);
+}
+
+template <bool LL>
+__device__ inline float get(const float* base, size_t i, uint32_t tag, int* flags) {
+    if constexpr (LL) return ll_value(load_ll(base, i), base, i, tag, flags);
+    else return fetch(base + i);
+}
+
+// Published values base[i0 + j * stride] for the j < N whose bit is set in
+// `valid` (the others are neither read nor waited for and come back 0), all
+// requested before any is checked: a check may re-read, and later loads must
+// not queue behind it.
+template <bool LL, int N>
+__device__ inline void get_n(const float* base, size_t i0, size_t stride, uint32_t valid, float* out, uint32_t tag,
+                             int* flags) {
+    if constexpr (LL) {
+        uint64_t w[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) w[j] = (valid >> j) & 1u ? load_ll(base, i0 + j * stride) : 0;
+#pragma unroll
+        for (int j = 0; j < N; ++j) out[j] = (valid >> j) & 1u ? ll_value(w[j], base, i0 + j * stride, tag, flags) : 0.f;
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; ++j) out[j] = (valid >> j) & 1u ? fetch(base + i0 + j * stride) : 0.f;
+    }
+}
+
+__device__ inline uint32_t low_bits(int n) { return n >= 32 ? 0xffffffffu : n <= 0 ? 0u : (1u << n) - 1u; }
+
+// Sum of n published values base[i0], base[i0 + stride], ... in index order.
+// Loads go out NB at a time so their round trips to the memory-side cache
+// overlap; with n <= NB the whole sum costs one round trip.
+template <int NB, bool LL>
+__device__ inline float fetch_sum(const float* base, size_t i0, size_t stride, int n, uint32_t tag, int* flags) {
     float acc = 0.f;
-    for (int k0 = 0; k0 < n; k0 += NB) {
-        float v[NB];
+    constexpr int NW = LL ? NB / 2 : NB;   // a tagged word takes two registers
+    for (int k0 = 0; k0 < n; k0 += NW) {
+        if constexpr (LL) {
+            uint64_t w[NW];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) v[j] = (k0 + j < n) ? fetch(p + (size_t)(k0 + j) * stride) : 0.f;
+            for (int j = 0; j < NW; ++j) w[j] = (k0 + j < n) ? load_ll(base, i0 + (size_t)(k0 + j) * stride) : 0;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc += v[j];
+            for (int j = 0; j < NW; ++j)
+                if (k0 + j < n) acc += ll_value(w[j], base, i0 + (size_t)(k0 + j) * stride, tag, flags);
+        } else {
+            float v[NW];
+#pragma unroll
+            for (int j = 0; j < NW; ++j) v[j] = (k0 + j < n) ? fetch(base + i0 + (size_t)(k0 + j) * stride) : 0.f;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) acc += v[j];
+        }
     }
     return acc;
+}
+
+// Arrival at a counter shared by `expected` workgroups; true in exactly one
+// workgroup, the last to arrive.  Phased: every thread's stores are
+// acknowledged first.  Fused: readers check tags, so no wait.  With `rearm`
+// the last arriver resets the counter (nobody waits on it); otherwise it
+// stays at `expected` until the finaliser signals completion with one more
+// bump.
+template <bool LL>
+__device__ inline bool arrive_last(int* counter, int expected, bool rearm, int* s_flag) {
+    if constexpr (LL) __syncthreads();
+    else drain_and_sync();
+    if (threadIdx.x == 0) {
+        const int prev = bump(counter);
+        const bool last = prev == expected - 1;
+        *s_flag = last;
+        if (last && rearm) set_counter(counter, 0);
+    }
+    __syncthreads();
+    return *s_flag != 0;
 }
 
 __device__ inline bool pos_valid(const StepArgs& a, int b, int* p_out) {
@@ -253,30 +337,33 @@ struct GemvShared {
     float r[BG];
 };
 
-// Decode a GEMV work index into (tile, batch group); false for padding.
-__device__ inline bool gemv_decode(const GemvPlanDev& g, int idx, int* tile, int* bgi) {
-    if (g.nbg == 1) {
+// Decode a GEMV work index over `tiles` tiles into (tile, batch group);
+// false for padding.  Batch groups sharing a weight tile get work indices 8
+// apart, so they run on one XCD and share its L2.
+__device__ inline bool gemv_decode(int nbg, int tiles, int idx, int* tile, int* bgi) {
+    if (nbg == 1) {
         *tile = idx;
         *bgi = 0;
-        return idx < g.tiles;
+        return idx < tiles;
     }
-    // batch groups sharing a weight tile get work indices 8 apart (same XCD)
     const int lo = idx & 7, rest = idx >> 3;
-    *bgi = rest % g.nbg;
-    *tile = (rest / g.nbg) * 8 + lo;
-    return *tile < g.tiles;
+    *bgi = rest % nbg;
+    *tile = (rest / nbg) * 8 + lo;
+    return *tile < tiles;
 }
 
-template <typename T, int BG, bool QKV>
-__device__ void gemv_tile(const StepArgs& a, int tile, int bgi, bool fused, GemvShared<BG>& sm, int* s_flag) {
+// Work indices a GEMV over `tiles` tiles takes (padding included).
+__device__ __host__ inline int gemv_items(int nbg, int tiles) {
+    return nbg == 1 ? tiles : (tiles + 7) / 8 * 8 * nbg;
+}
+
+template <typename T, int BG, bool QKV, bool FUSED>
+__device__ void gemv_tile(const StepArgs& a, int slab, int ks, int bgi, uint32_t tag, GemvShared<BG>& sm,
+                          int* s_flag) {
     const GemvPlanDev& g = QKV ? a.qkv : a.oproj;
     const int K = QKV ? a.H : a.n_q;
     const int N = QKV ? a.n_qkv : a.H;
     const int KR = g.rows;
-    // K-split-major: concurrent tiles cover whole rows of W (all slabs of a
-    // row block), so HBM pages are read whole; slab-major order measured
-    // about 1.5x slower for the QKV stream
-    const int slab = tile % g.slabs, ks = tile / g.slabs;
     const int t = threadIdx.x, c8 = t & 31, rg = t >> 5, lane = t & 63, wave = t >> 6;
     const int n0 = slab * 256 + c8 * 8;
     const bool col_ok = n0 < N;
@@ -321,7 +408,7 @@ __device__ void gemv_tile(const StepArgs& a, int tile, int bgi, bool fused, Gemv
     } else {
         // attention output rows [kb, kb+KR) = heads kb/D .. ; in the fused
         // schedule wait until every sequence of the group has them
-        if (fused && t == 0) {
+        if (FUSED && t == 0) {
             for (int j = 0; j < BG; ++j) {
                 const int bb = b0 + j;
                 int p;
@@ -333,11 +420,18 @@ __device__ void gemv_tile(const StepArgs& a, int tile, int bgi, bool fused, Gemv
         }
         __syncthreads();
         if (t < KR) {
+            // rows of sequences with a valid position only (the others have
+            // no attention output and no output row)
+            uint32_t valid = 0;
 #pragma unroll
             for (int j = 0; j < BG; ++j) {
-                const int bb = b0 + j;
-                sm.xs[j][t] = bb < B ? fetch(&a.a[(size_t)bb * K + kb + t]) : 0.f;
+                int p;
+                if (b0 + j < B && pos_valid(a, b0 + j, &p)) valid |= 1u << j;
             }
+            float xv[BG];
+            get_n<FUSED, BG>(a.a, (size_t)b0 * K + kb + t, K, valid, xv, tag, a.flags);
+#pragma unroll
+            for (int j = 0; j < BG; ++j) sm.xs[j][t] = b0 + j < B ? xv[j] : 0.f;
         }
     }
     __syncthreads();
@@ -386,29 +480,35 @@ __device__ void gemv_tile(const StepArgs& a, int tile, int bgi, bool fused, Gemv
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) s += redf[(w * BG + j) * 256 + t];
-            publish(&part[((size_t)ks * B + bb) * N + n], s);
+            put<FUSED>(part, ((size_t)ks * B + bb) * N + n, s, tag);
         }
         if constexpr (QKV) {
             if (t == 0 && bb < B)
-                publish(&a.ssq[((size_t)slab * g.ksplit + ks) * B + bb],
-                        sm.ssq[j][0] + sm.ssq[j][1] + sm.ssq[j][2] + sm.ssq[j][3]);
+                put<FUSED>(a.ssq, ((size_t)slab * g.ksplit + ks) * B + bb,
+                           sm.ssq[j][0] + sm.ssq[j][1] + sm.ssq[j][2] + sm.ssq[j][3], tag);
         }
     }
 
     // 5. the last tile of this slab finishes it
     int* cnt = (QKV ? a.qkv_cnt : a.oproj_cnt) + slab * g.nbg + bgi;
-    if (!arrive_last(cnt, g.ksplit, !(QKV && fused), s_flag)) return;
+    if (!arrive_last<FUSED>(cnt, g.ksplit, !(QKV && FUSED), s_flag)) return;
+    DAB_TRACE_POINT(a, 4);
 
     // every partial sum of this slab: one round trip per batch row (32 wide)
 #pragma unroll
     for (int j = 0; j < BG; ++j) {
         const int bb = b0 + j;
-        sm.val[j][t] = (bb < B && n < N) ? fetch_sum<32>(part + (size_t)bb * N + n, (size_t)B * N, g.ksplit) : 0.f;
+        sm.val[j][t] = (bb < B && n < N)
+                           ? fetch_sum<32, FUSED>(part, (size_t)bb * N + n, (size_t)B * N, g.ksplit, tag, a.flags)
+                           : 0.f;
     }
+    DAB_TRACE_POINT(a, 5);
     if constexpr (QKV) {
         if (t < BG) {
             const int bb = b0 + t;
-            const float ss = bb < B ? fetch_sum<32>(a.ssq + (size_t)slab * g.ksplit * B + bb, B, g.ksplit) : 0.f;
+            const float ss =
+                bb < B ? fetch_sum<32, FUSED>(a.ssq, (size_t)slab * g.ksplit * B + bb, B, g.ksplit, tag, a.flags)
+                       : 0.f;
             sm.r[t] = 1.0f / sqrtf(ss / (float)K + a.eps);
         }
         __syncthreads();
@@ -438,22 +538,23 @@ __device__ void gemv_tile(const StepArgs& a, int tile, int bgi, bool fused, Gemv
                 v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
             }
             if (n < a.n_q) {
-                publish(&a.q[(size_t)bb * a.n_q + n], v);
+                put<FUSED>(a.q, (size_t)bb * a.n_q + n, v, tag);
             } else {
                 const int kvn = n - a.n_q;
                 const int is_v = kvn >= a.nkv * D;
                 const int col = is_v ? kvn - a.nkv * D : kvn;
-                publish(&a.kv_new[((size_t)bb * 2 + is_v) * a.nkv * D + col], v);
+                put<FUSED>(a.kv_new, ((size_t)bb * 2 + is_v) * a.nkv * D + col, v, tag);
                 if (ok) {
                     T* dst = static_cast<T*>(is_v ? a.v_cache : a.k_cache);
                     dst[((size_t)bb * a.cap + p) * a.nkv * D + col] = from_f32<T>(v);
                 }
             }
         }
-        if (fused) {
-            drain_and_sync();
+        if constexpr (FUSED) {
+            __syncthreads();
             if (t == 0) bump(cnt);                       // slab ready: counter = ksplit + 1
         }
+        DAB_TRACE_POINT(a, 6);
     } else {
 #pragma unroll
         for (int j = 0; j < BG; ++j) {
@@ -500,8 +601,8 @@ struct AttnGeom {
 // Which QKV slab (of 256 columns) holds column `col`.
 __device__ inline int slab_of(int col) { return col >> 8; }
 
-template <typename T, int D, int G>
-__device__ void attn_item(const StepArgs& a, int b, int g, int c, bool fused, AttnShared<D, G>& sm, int* s_flag) {
+template <typename T, int D, int G, bool FUSED>
+__device__ void attn_item(const StepArgs& a, int b, int g, int c, uint32_t tag, AttnShared<D, G>& sm, int* s_flag) {
     using Geo = AttnGeom<D>;
     constexpr int LPR = Geo::LPR, NSLOT = Geo::NSLOT, U = Geo::U;
     const int nkv = a.nkv;
@@ -540,7 +641,7 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, bool fused, At
     DAB_TRACE_POINT(a, 1);
 
     // 2. wait for q of this group's heads (and the new k, v in the last chunk)
-    if (fused) {
+    if constexpr (FUSED) {
         if (t == 0) {
             const int bq = b / a.qkv_bg;
             const GemvPlanDev& q = a.qkv;
@@ -559,9 +660,9 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, bool fused, At
     float qv[G][8];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-        const float* qp = a.q + (size_t)b * a.n_q + (size_t)(g * G + j) * D + l * 8;
+        get_n<FUSED, 8>(a.q, (size_t)b * a.n_q + (size_t)(g * G + j) * D + l * 8, 1, 0xffu, qv[j], tag, a.flags);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[j][e] = fetch(qp + e) * a.qscale;
+        for (int e = 0; e < 8; ++e) qv[j][e] *= a.qscale;
     }
     float m[G], ls[G], o[G][8];
 #pragma unroll
@@ -628,13 +729,15 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, bool fused, At
     // workspace copy the QKV finaliser published, rounded to the storage type
     // exactly as the appended cache row
     if (has_new && slot == 0) {
-        const float* kn = a.kv_new + ((size_t)b * 2 * nkv + g) * D + l * 8;
-        const float* vn = kn + (size_t)nkv * D;
+        const size_t kn = ((size_t)b * 2 * nkv + g) * D + l * 8;
+        const size_t vn = kn + (size_t)nkv * D;
         float kf[8], vf[8];
+        get_n<FUSED, 8>(a.kv_new, kn, 1, 0xffu, kf, tag, a.flags);
+        get_n<FUSED, 8>(a.kv_new, vn, 1, 0xffu, vf, tag, a.flags);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            kf[e] = to_f32(from_f32<T>(fetch(kn + e)));
-            vf[e] = to_f32(from_f32<T>(fetch(vn + e)));
+            kf[e] = to_f32(from_f32<T>(kf[e]));
+            vf[e] = to_f32(from_f32<T>(vf[e]));
         }
         float s[G][U];
         Vec8<T> vv[U];
@@ -691,10 +794,10 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, bool fused, At
             O += sm.o[w][j][d] * wt;
         }
         const size_t pi = ((size_t)b * a.nq + g * G + j) * a.maxc + c;
-        publish(&a.attn_o[pi * D + d], O);
+        put<FUSED>(a.attn_o, pi * D + d, O, tag);
         if (d == 0) {
-            publish(&a.attn_ml[pi * 2], M);
-            publish(&a.attn_ml[pi * 2 + 1], L);
+            put<FUSED>(a.attn_ml, pi * 2, M, tag);
+            put<FUSED>(a.attn_ml, pi * 2 + 1, L, tag);
         }
     }
 
@@ -702,25 +805,28 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, bool fused, At
     // statistics (m, l) and the first OB weighted outputs of every thread
     // are requested together, so short merges cost one round trip.
     int* cnt = &a.attn_cnt[b * nkv + g];
-    if (!arrive_last(cnt, nchunk, !fused, s_flag)) return;
+    if (!arrive_last<FUSED>(cnt, nchunk, !FUSED, s_flag)) return;
+    DAB_TRACE_POINT(a, 4);
     constexpr int PARTS = 256 / D;       // threads per output element
-    constexpr int OB = 16;               // chunks per thread in the first request
+    constexpr int OB = 8;                // chunks per thread in the first request
     const int d = t % D, part = t / D;
     for (int j = 0; j < G; ++j) {
         const int h = g * G + j;
         const size_t pbase = ((size_t)b * a.nq + h) * a.maxc;
+        // this thread's chunks part, part + PARTS, ... below nchunk
         float ov[OB];
-#pragma unroll
-        for (int q = 0; q < OB; ++q) {
-            const int cc = part + q * PARTS;
-            ov[q] = cc < nchunk ? fetch(&a.attn_o[(pbase + cc) * D + d]) : 0.f;
+        {
+            const int nv = part < nchunk ? (nchunk - part + PARTS - 1) / PARTS : 0;
+            get_n<FUSED, OB>(a.attn_o, (pbase + part) * D + d, (size_t)PARTS * D, low_bits(nv), ov, tag, a.flags);
         }
+        DAB_TRACE_POINT(a, 5);
         float mloc = kNegInf;
         for (int cc = t; cc < nchunk; cc += 256) {
-            const float mc = fetch(&a.attn_ml[(pbase + cc) * 2]);
-            sm.cm[cc] = mc;
-            sm.cw[cc] = fetch(&a.attn_ml[(pbase + cc) * 2 + 1]);   // l for now, weight below
-            mloc = fmaxf(mloc, mc);
+            float ml[2];
+            get_n<FUSED, 2>(a.attn_ml, (pbase + cc) * 2, 1, 0x3u, ml, tag, a.flags);
+            sm.cm[cc] = ml[0];
+            sm.cw[cc] = ml[1];            // l for now, weight below
+            mloc = fmaxf(mloc, ml[0]);
         }
         mloc = wave_max(mloc);
         if (lane == 0) sm.red[wave] = mloc;
@@ -743,13 +849,13 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, bool fused, At
         }
         for (int c0 = part + OB * PARTS; c0 < nchunk; c0 += 8 * PARTS) {
             float v[8];
+            get_n<FUSED, 8>(a.attn_o, (pbase + c0) * D + d, (size_t)PARTS * D,
+                            low_bits((nchunk - c0 + PARTS - 1) / PARTS), v, tag, a.flags);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int cc = c0 + q * PARTS;
-                v[q] = cc < nchunk ? sm.cw[cc] * fetch(&a.attn_o[(pbase + cc) * D + d]) : 0.f;
+                if (cc < nchunk) acc += sm.cw[cc] * v[q];
             }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc += v[q];
         }
         sm.acc[t] = acc;
         __syncthreads();
@@ -758,14 +864,15 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, bool fused, At
             float tot = 0.f;
 #pragma unroll
             for (int q = 0; q < PARTS; ++q) tot += sm.acc[q * D + t];
-            publish(&a.a[(size_t)b * a.n_q + (size_t)h * D + t], tot / L);
+            put<FUSED>(a.a, (size_t)b * a.n_q + (size_t)h * D + t, tot / L, tag);
         }
         __syncthreads();
     }
-    if (fused) {
-        drain_and_sync();
+    if constexpr (FUSED) {
+        __syncthreads();
         if (t == 0) bump(cnt);                          // group ready: counter = nchunk + 1
     }
+    DAB_TRACE_POINT(a, 6);
 }
 
 }  // namespace dev

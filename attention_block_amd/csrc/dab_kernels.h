@@ -39,9 +39,12 @@ struct StepArgs {
     int* flags;             // error bits
     int* done;              // fused schedule: finished items, kDoneShards counters kDoneStride ints apart
     int* done_all;          // fused schedule: finished shards
+    int* epoch;             // fused schedule: calls completed (message tags derive from it)
     int* qkv_cnt;           // [q slabs * nbg] tile arrivals (+1 when the slab is final)
     int* attn_cnt;          // [B * nkv] chunk arrivals (+1 when merged)
     int* oproj_cnt;         // [o slabs * nbg] tile arrivals
+    // published buffers hold 8 bytes per element: {value, tag} words in the
+    // fused schedule, a float array in the low half in the phased one
     float* qkv_part;        // [q ksplit, B, n_qkv]
     float* ssq;             // [q slabs, q ksplit, B]
     float* q;               // [B, n_q] rotated q
@@ -58,19 +61,30 @@ struct StepArgs {
     GemvPlanDev qkv, oproj;
     int qkv_bg;             // batch rows per GEMV tile
     int T, maxc, attn_items;
-    int total_items;        // fused schedule: grid size
+    int total_items;        // fused schedule: work items of the whole step
+    int item_lo;            // fused schedule: first work item of this launch (its workgroup 0)
+    // fused schedule, unit order (one unit = all heads when not unitised)
+    int units;              // number of units
+    int unit_items;         // work items per unit
+    int unit_slabs;         // QKV slabs per unit
+    int unit_kv;            // kv heads per unit
+    int unit_oks;           // output-projection row blocks per unit
 #ifdef DAB_TRACE
-    unsigned long long* trace;   // [items, 4] timestamps per workgroup (profiling builds only)
+    unsigned long long* trace;   // [items, 8] timestamps per workgroup (profiling builds only)
     int trace_base;              // item number of this launch's workgroup 0
 #endif
 };
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fused(const StepArgs& a, bool bf16, hipStream_t s);
+// two-stage schedule: QKV tiles alone, then attention and output tiles
+hipError_t launch_two_stage(const StepArgs& a, bool bf16, int stage, hipStream_t s);
 hipError_t launch_phase(const StepArgs& a, bool bf16, int phase, hipStream_t s);
 
 // per-dtype instantiations of the fused kernel (separate translation units)
 hipError_t launch_fused_bf16(const StepArgs& a, hipStream_t s);
 hipError_t launch_fused_f32(const StepArgs& a, hipStream_t s);
+hipError_t launch_stage_qkv_bf16(const StepArgs& a, hipStream_t s);
+hipError_t launch_stage_qkv_f32(const StepArgs& a, hipStream_t s);
 
 }  // namespace dab

@@ -15,10 +15,14 @@ template <typename T, int BG, bool QKV>
 __global__ __launch_bounds__(256) void phased_gemv_kernel(StepArgs a) {
     __shared__ GemvShared<BG> sm;
     __shared__ int s_flag;
+    const GemvPlanDev& g = QKV ? a.qkv : a.oproj;
     int tile, bgi;
     DAB_TRACE_POINT(a, 0);
-    if (gemv_decode(QKV ? a.qkv : a.oproj, blockIdx.x, &tile, &bgi))
-        gemv_tile<T, BG, QKV>(a, tile, bgi, false, sm, &s_flag);
+    // K-split-major: concurrent tiles cover whole rows of W (all slabs of a
+    // row block), so HBM pages are read whole; slab-major order measured
+    // about 1.5x slower for the QKV stream
+    if (gemv_decode(g.nbg, g.tiles, blockIdx.x, &tile, &bgi))
+        gemv_tile<T, BG, QKV, false>(a, tile % g.slabs, tile / g.slabs, bgi, 0u, sm, &s_flag);
     DAB_TRACE_POINT(a, 3);
 }
 
@@ -28,8 +32,8 @@ __global__ __launch_bounds__(256) void phased_attn_kernel(StepArgs a) {
     __shared__ int s_flag;
     int b, g, c;
     DAB_TRACE_POINT(a, 0);
-    attn_decode(a, blockIdx.x, &b, &g, &c);
-    attn_item<T, D, G>(a, b, g, c, false, sm, &s_flag);
+    attn_decode(a, a.nkv, blockIdx.x, &b, &g, &c);
+    attn_item<T, D, G, false>(a, b, g, c, 0u, sm, &s_flag);
     DAB_TRACE_POINT(a, 3);
 }
 
@@ -89,6 +93,24 @@ hipError_t launch_phase(const StepArgs& a, bool bf16, int phase, hipStream_t s) 
 
 hipError_t launch_fused(const StepArgs& a, bool bf16, hipStream_t s) {
     return bf16 ? launch_fused_bf16(a, s) : launch_fused_f32(a, s);
+}
+
+hipError_t launch_two_stage(const StepArgs& a, bool bf16, int stage, hipStream_t s) {
+    if (stage == 0) {
+#ifdef DAB_TRACE
+        StepArgs t = a;
+        t.trace_base = 0;
+        return bf16 ? launch_stage_qkv_bf16(t, s) : launch_stage_qkv_f32(t, s);
+#else
+        return bf16 ? launch_stage_qkv_bf16(a, s) : launch_stage_qkv_f32(a, s);
+#endif
+    }
+    StepArgs b = a;   // attention and output tiles: items from the first attention chunk on
+    b.item_lo = a.qkv.items;
+#ifdef DAB_TRACE
+    b.trace_base = b.item_lo;
+#endif
+    return bf16 ? launch_fused_bf16(b, s) : launch_fused_f32(b, s);
 }
 
 }  // namespace dab

@@ -40,6 +40,11 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
+// The schedule AUTO resolves to, from measurements on MI355X: one kernel per
+// phase beats both fused layouts on every configuration timed so far (the
+// fused hand-offs cost more than the kernel boundaries they remove).
+int auto_schedule(bool /*fused_ok*/) { return DAB_SCHEDULE_PHASED; }
+
 dab_status make_plan(const dab_config* cfg, Plan* p) {
     if (!cfg || !p) return DAB_ERR_INVALID_ARG;
     *p = Plan();
@@ -83,11 +88,12 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     const bool fused_ok = (p->G == 1 || p->G == 2 || p->G == 4 || p->G == 8) &&
                           (c.kv_chunk == 0 || c.kv_chunk == fchunk) &&
                           (p->cap - 1 + fchunk - 1) / fchunk <= kMaxChunks;
-    if (c.schedule == DAB_SCHEDULE_FUSED && !fused_ok) return DAB_ERR_UNSUPPORTED;
-    if (c.schedule != DAB_SCHEDULE_AUTO && c.schedule != DAB_SCHEDULE_FUSED && c.schedule != DAB_SCHEDULE_PHASED)
-        return DAB_ERR_INVALID_ARG;
-    // AUTO takes the phased schedule: it measures faster on MI355X so far
-    p->fused = c.schedule == DAB_SCHEDULE_FUSED;
+    if (c.schedule < DAB_SCHEDULE_AUTO || c.schedule > DAB_SCHEDULE_TWO_STAGE) return DAB_ERR_INVALID_ARG;
+    if ((c.schedule == DAB_SCHEDULE_FUSED || c.schedule == DAB_SCHEDULE_TWO_STAGE) && !fused_ok)
+        return DAB_ERR_UNSUPPORTED;
+    // AUTO: the schedule that measures fastest on MI355X where it applies
+    p->schedule = c.schedule != DAB_SCHEDULE_AUTO ? c.schedule : auto_schedule(fused_ok);
+    p->fused = p->schedule != DAB_SCHEDULE_PHASED;
 
     plan_gemv(p->H, p->n_qkv, B, p->fused, &p->qkv);
     plan_gemv(p->n_q, p->H, B, p->fused, &p->oproj);
@@ -113,10 +119,26 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     p->max_chunks = ceil_div(hist, T);
     if (p->max_chunks > kMaxChunks) return DAB_ERR_UNSUPPORTED;
     const long long attn_grid = (long long)B * p->nkv * p->max_chunks;
-    const long long total = attn_grid + p->qkv.grid + p->oproj.grid;
-    if (total > (1LL << 30)) return DAB_ERR_UNSUPPORTED;
+    if (attn_grid + p->qkv.grid + p->oproj.grid > (1LL << 30)) return DAB_ERR_UNSUPPORTED;
     p->attn_grid = (int)attn_grid;
-    p->total_items = (int)total;
+
+    // fused unit order.  A unit is the kv heads of one 256-column key slab
+    // (256/D heads); it needs the query block and both kv blocks to start on
+    // slab boundaries and the output row blocks to hold whole units.
+    // Unit order measured 2.3x slower than phase order on MI355X (units wait
+    // on long hand-off chains while holding their slots), so it is off.
+    constexpr bool kUnitOrder = false;
+    const int kvu = 256 / p->D;
+    const bool unitise = kUnitOrder && p->fused && p->n_q % 256 == 0 && p->nkv % kvu == 0 && p->nkv > kvu &&
+                         (kvu * p->G * p->D) % p->oproj.rows == 0;
+    p->units = unitise ? p->nkv / kvu : 1;
+    p->unit_kv = p->nkv / p->units;
+    p->unit_slabs = unitise ? p->G + 2 : p->qkv.slabs;
+    p->unit_oks = p->oproj.ksplit / p->units;
+    auto items = [&](int tiles) { return p->qkv.nbg == 1 ? tiles : (tiles + 7) / 8 * 8 * p->qkv.nbg; };
+    p->unit_items = items(p->unit_slabs * p->qkv.ksplit) + B * p->unit_kv * p->max_chunks +
+                    items(p->unit_oks * p->oproj.slabs);
+    p->total_items = p->units * p->unit_items;
 
     // workspace layout
     size_t off = 0;
@@ -130,14 +152,16 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     p->off_qkv_cnt = take(sizeof(int32_t) * p->qkv.slabs * p->qkv.nbg);
     p->off_attn_cnt = take(sizeof(int32_t) * B * p->nkv);
     p->off_oproj_cnt = take(sizeof(int32_t) * p->oproj.slabs * p->oproj.nbg);
-    p->off_qkv_part = take(sizeof(float) * (size_t)p->qkv.ksplit * B * p->n_qkv);
-    p->off_ssq = take(sizeof(float) * (size_t)p->qkv.slabs * p->qkv.ksplit * B);
-    p->off_q = take(sizeof(float) * (size_t)B * p->n_q);
-    p->off_kv_new = take(sizeof(float) * (size_t)B * 2 * p->nkv * p->D);
-    p->off_attn_o = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * p->D);
-    p->off_attn_ml = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * 2);
-    p->off_a = take(sizeof(float) * (size_t)B * p->n_q);
-    p->off_oproj_part = take(sizeof(float) * (size_t)p->oproj.ksplit * B * p->H);
+    // published buffers: 8 bytes per element (tagged words in the fused schedule)
+    const size_t w = 8;
+    p->off_qkv_part = take(w * (size_t)p->qkv.ksplit * B * p->n_qkv);
+    p->off_ssq = take(w * (size_t)p->qkv.slabs * p->qkv.ksplit * B);
+    p->off_q = take(w * (size_t)B * p->n_q);
+    p->off_kv_new = take(w * (size_t)B * 2 * p->nkv * p->D);
+    p->off_attn_o = take(w * (size_t)B * p->nq * p->max_chunks * p->D);
+    p->off_attn_ml = take(w * (size_t)B * p->nq * p->max_chunks * 2);
+    p->off_a = take(w * (size_t)B * p->n_q);
+    p->off_oproj_part = take(w * (size_t)p->oproj.ksplit * B * p->H);
     p->ws_bytes = off;
 
     const size_t e = (size_t)p->elem;

@@ -39,14 +39,18 @@ struct Plan {
     float theta = 0.f, eps = 0.f;
     int elem = 0;                // bytes per stored element
 
-    bool fused = false;          // one persistent launch (else one kernel per phase)
+    int schedule = DAB_SCHEDULE_PHASED;   // resolved: FUSED, TWO_STAGE or PHASED
+    bool fused = false;          // FUSED or TWO_STAGE: tagged hand-offs, fused device code
     GemvPlan qkv, oproj;
     int kv_chunk = 0, max_chunks = 0, attn_grid = 0;
-    int total_items = 0;         // fused: qkv.grid + attn_grid + oproj.grid
+    int total_items = 0;         // fused: qkv.grid + attn_grid + oproj.grid (+ unit padding)
+    // fused unit order: units of unit_kv kv heads, each with unit_slabs QKV
+    // slabs, its attention chunks and unit_oks output row blocks
+    int units = 1, unit_items = 0, unit_slabs = 0, unit_kv = 0, unit_oks = 0;
 
     // workspace layout, byte offsets (each 256-byte aligned).  The flags
-    // word is at offset 0, the finished-shard count at 4; the 16 finish
-    // sub-counters follow, one per 256 bytes.
+    // word is at offset 0, the finished-shard count at 4, the call epoch at
+    // 8; the 16 finish sub-counters follow, one per 256 bytes.
     size_t off_flags = 0, off_done = 0, off_qkv_cnt = 0, off_attn_cnt = 0, off_oproj_cnt = 0;
     size_t off_qkv_part = 0, off_ssq = 0, off_q = 0, off_kv_new = 0;
     size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0, off_oproj_part = 0;

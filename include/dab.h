@@ -80,11 +80,20 @@ typedef struct {
  * tiles), issue their HBM loads first and then wait on device-side counters,
  * so the three weight/cache streams overlap.  It needs n_q_heads / n_kv_heads
  * in {1, 2, 4, 8} and kv_chunk 0 (the chunk is 128 tokens for D = 128, 256
- * for D = 64).  DAB_SCHEDULE_PHASED runs one kernel per phase.  AUTO picks
- * the schedule measured faster on MI355X (currently PHASED).  The two split their sums differently, so results
- * agree to fp32 rounding, not bit for bit; each is deterministic.
+ * for D = 64).  DAB_SCHEDULE_TWO_STAGE runs the QKV tiles as a kernel of
+ * their own, then the rest of the fused launch (same requirements).
+ * DAB_SCHEDULE_PHASED runs one kernel per phase.  AUTO picks the schedule
+ * measured fastest on MI355X among those that apply (at present PHASED).
+ * FUSED and TWO_STAGE share their device code and give identical bits; PHASED
+ * splits its sums differently, so it agrees with them to fp32 rounding, not
+ * bit for bit.  Each schedule is deterministic.
  */
-typedef enum { DAB_SCHEDULE_AUTO = 0, DAB_SCHEDULE_FUSED = 1, DAB_SCHEDULE_PHASED = 2 } dab_schedule;
+typedef enum {
+    DAB_SCHEDULE_AUTO = 0,
+    DAB_SCHEDULE_FUSED = 1,
+    DAB_SCHEDULE_PHASED = 2,
+    DAB_SCHEDULE_TWO_STAGE = 3
+} dab_schedule;
 
 /*
  * Bytes of device workspace one call with this configuration needs (0 when
@@ -135,7 +144,7 @@ dab_status dab_decode_attn_block(const dab_config* cfg,
  * Same as dab_decode_attn_block, and also records `n_events` hipEvent_t
  * (passed as void*) on `stream`: events[0] before the first kernel and
  * events[i] after kernel i-1.  n_events must equal dab_phase_count(cfg) + 1
- * (2 for the fused schedule, 4 for the phased one).
+ * (2 for the fused schedule, 3 for the two-stage one, 4 for the phased one).
  * Used to time the phases of the step on the stream they run on.
  */
 dab_status dab_decode_attn_block_timed(const dab_config* cfg,

@@ -74,7 +74,9 @@ def test_workspace_size_valid(lib):
     fu = cfg(schedule=1)
     assert lib.dab_phase_count(ctypes.byref(fu)) == 1
     assert lib.dab_phase_name(ctypes.byref(fu), 0) == b"decode_block_fused"
-    assert lib.dab_phase_count(ctypes.byref(c)) == 3                    # auto: phased
+    ts = cfg(schedule=3)
+    assert [lib.dab_phase_name(ctypes.byref(ts), i) for i in range(3)] == [
+        b"qkv_rmsnorm_rope_append", b"attention_oproj_fused", None]
     ph = cfg(schedule=2)
     assert lib.dab_phase_count(ctypes.byref(ph)) == 3
     assert [lib.dab_phase_name(ctypes.byref(ph), i) for i in range(4)] == [
@@ -90,6 +92,12 @@ def test_schedule_selection(lib):
     assert call(lib, cfg(kv_chunk=64, schedule=1)) == _lib.DAB_ERR_UNSUPPORTED
     assert lib.dab_phase_count(ctypes.byref(cfg(kv_chunk=64))) == 3
     assert lib.dab_workspace_size(ctypes.byref(cfg(schedule=7))) == 0
+    assert call(lib, cfg(n_q_heads=6, n_kv_heads=2, schedule=3)) == _lib.DAB_ERR_UNSUPPORTED
+    # auto resolves to one kernel per phase, the layout measured fastest
+    head = cfg(batch=1, hidden=4096, n_q_heads=32, n_kv_heads=32, head_dim=128, cache_capacity=4097,
+               dtype=_lib.DAB_BF16)
+    assert [lib.dab_phase_name(ctypes.byref(head), i) for i in range(3)] == [
+        b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual"]
 
 
 class FakePtrs:

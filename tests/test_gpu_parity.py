@@ -42,7 +42,7 @@ def parity_case(cfg: BlockConfig, seed: int, *, cap=None, pos=None, kv_chunk=0, 
 # the workload configurations, full size
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("schedule", ["fused", "phased"])
+@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
 @pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_config_parity(name, seed, schedule):
@@ -73,6 +73,7 @@ def test_edge_parity(label, cfg, cap, pos, kv_chunk):
     parity_case(cfg, 7, cap=cap, pos=pos, kv_chunk=kv_chunk, label=label, schedule="phased")
     if cfg.group in (1, 2, 4, 8):
         parity_case(cfg, 7, cap=cap, pos=pos, label=label, schedule="fused")
+        parity_case(cfg, 7, cap=cap, pos=pos, label=label, schedule="two_stage")
 
 
 FUSED_VS_PHASED = [
@@ -91,10 +92,13 @@ def test_fused_and_phased_agree(cfg):
     inp = make_inputs(cfg, 13, cap=701, pos=pos)
     say(f"[fused vs phased] {cfg.name}")
     res = {}
-    for sched in ("fused", "phased"):
+    for sched in ("fused", "two_stage", "phased"):
         dev = to_device(inp)
         out, dbg = run_gpu(dev, cfg, schedule=sched)
         res[sched] = (dbg.double(), dev["k_cache"].double(), dev["v_cache"].double())
+    # the fused and two-stage schedules run the same work items in the same order
+    for i in range(3):   # raw bits: the caches hold NaN sentinels
+        assert torch.equal(res["fused"][i].view(torch.int64), res["two_stage"][i].view(torch.int64)), i
     f, p = res["fused"], res["phased"]
     assert torch.linalg.norm(f[0] - p[0]) / torch.linalg.norm(p[0]) < 1e-5
     rows = (torch.arange(cfg.batch), torch.tensor(pos))
@@ -129,7 +133,7 @@ def test_split_count_invariance():
         assert np.linalg.norm(o - outs[0]) / np.linalg.norm(outs[0]) < 1e-6
 
 
-@pytest.mark.parametrize("schedule", ["fused", "phased"])
+@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
 def test_repeat_calls_are_bit_identical(schedule):
     """Deterministic merges, and counters back at zero after each call."""
     import torch
@@ -145,7 +149,7 @@ def test_repeat_calls_are_bit_identical(schedule):
         assert torch.equal(o, res[0][0]) and torch.equal(d, res[0][1])
 
 
-@pytest.mark.parametrize("schedule", ["fused", "phased"])
+@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
 def test_workspace_counters_return_to_zero(schedule):
     import torch
     import attention_block_amd as ab
@@ -158,14 +162,17 @@ def test_workspace_counters_return_to_zero(schedule):
     say(f"[counters] {schedule}: call then inspect workspace counters")
     run_gpu(dev, cfg, workspace=ws, schedule=schedule)
     torch.cuda.synchronize()
-    raw = ws._buf[ws.ptr - ws._buf.data_ptr():][: 256 + 4096 + 3 * 256].cpu().numpy().view(np.int32)
+    raw = ws._buf[ws.ptr - ws._buf.data_ptr():][: 256 + 4096 + 3 * 256].cpu().numpy().view(np.int32).copy()
     # the workspace starts with the flags words (256 bytes), the 16 finish
     # sub-counters (256 bytes each), then the arrival counters of the three
-    # phases (each fits in 256 bytes at this shape)
+    # phases (each fits in 256 bytes at this shape).  Word 2 is the call
+    # epoch, which the fused schedule advances once per call.
+    assert raw[2] == (0 if schedule == "phased" else 1)
+    raw[2] = 0
     assert np.all(raw == 0)
 
 
-@pytest.mark.parametrize("schedule", ["fused", "phased"])
+@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
 def test_bad_position_sets_flag_and_skips_sequence(schedule):
     import torch
     import attention_block_amd as ab
@@ -192,7 +199,7 @@ def test_bad_position_sets_flag_and_skips_sequence(schedule):
     assert ab.read_device_error() == 0                 # reading cleared it
 
 
-@pytest.mark.parametrize("schedule", ["fused", "phased"])
+@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
 def test_graph_replay_matches_eager(schedule):
     import torch
     import attention_block_amd as ab
