@@ -40,7 +40,7 @@ def lib_version() -> str:
 def make_config(*, batch: int, hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                 cache_capacity: int, dtype: str, rope_theta: float, eps: float = 1e-6,
                 kv_chunk: int = 0, schedule: str = "auto") -> DabConfig:
-    """Build the C config struct.  dtype is "bf16" or "f32"; schedule "auto", "fused" or "phased"."""
+    """Build the C config struct.  dtype is "bf16" or "f32"; schedule "auto" or "phased"."""
     if dtype not in ("bf16", "f32"):
         raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
     if schedule not in _lib.SCHEDULES:
@@ -124,12 +124,14 @@ def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps,
     _, cap, nkv, D = k_cache.shape
     if k_cache.shape[0] != B or pos.shape != (B,) or norm_w.shape != (H,):
         raise ValueError("batch or hidden size mismatch")
-    n_qkv = w_qkv.shape[1]
-    if w_qkv.shape[0] != H or n_qkv % D or n_qkv // D <= 2 * nkv:
-        raise ValueError("w_qkv must be [H, (nq + 2 nkv) D]")
+    if w_qkv.dim() != 2 or w_o.dim() != 2:
+        raise ValueError("w_qkv and w_o must be 2-D")
+    n_qkv = w_qkv.shape[0]
+    if w_qkv.shape[1] != H or n_qkv % D or n_qkv // D <= 2 * nkv:
+        raise ValueError("w_qkv must be [(nq + 2 nkv) D, H] (one output feature per row)")
     nq = n_qkv // D - 2 * nkv
-    if w_o.shape != (nq * D, H):
-        raise ValueError(f"w_o must be [{nq * D}, {H}]")
+    if w_o.shape != (H, nq * D):
+        raise ValueError(f"w_o must be [{H}, {nq * D}] (one output feature per row)")
     if out is None:
         out = torch.empty_like(hidden)
     elif out.shape != hidden.shape or out.dtype != dt or out.device != dev or not out.is_contiguous():
@@ -148,12 +150,13 @@ def decode_attn_block(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_th
                       schedule: str = "auto"):
     """One decode step on the current stream; returns `out`.
 
-    Shapes: hidden [B, H]; norm_w [H]; w_qkv [H, (nq+2nkv)D]; w_o [nq D, H];
+    Shapes: hidden [B, H]; norm_w [H]; w_qkv [(nq+2nkv)D, H] and w_o [H, nq D]
+    (one output feature per row, as torch.nn.Linear stores its weight);
     k_cache, v_cache [B, cap, nkv, D] (row pos[b] is written); pos int32 [B];
     all but pos in one dtype (bfloat16 or float32) on one GPU.  dbg_y
-    (optional, float32 [B, H]) receives the pre-residual a @ W_o.  schedule:
-    "fused" (one persistent launch), "phased" (one kernel per phase) or
-    "auto" (fused where it applies).
+    (optional, float32 [B, H]) receives the pre-residual a @ W_o^T.
+    schedule: "phased" (one kernel per phase) or "auto" (the fastest that
+    applies).
     """
     cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
                         schedule)

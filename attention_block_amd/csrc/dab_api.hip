@@ -1,6 +1,6 @@
 // C ABI of the decode attention block (declared in include/dab.h).
-// Validates on the host, then enqueues the fused kernel (or the three phase
-// kernels) on the caller's stream.  No allocation, no synchronisation
+// Validates on the host, then enqueues the three phase kernels on the
+// caller's stream.  No allocation, no synchronisation
 // (except in dab_read_device_error).
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -19,8 +19,6 @@ unsigned long long* g_trace = nullptr;
 #endif
 
 const char* const kPhasedNames[3] = {"qkv_rmsnorm_rope_append", "attention_split_kv", "oproj_residual"};
-const char* const kTwoStageNames[2] = {"qkv_rmsnorm_rope_append", "attention_oproj_fused"};
-const char* const kFusedName = "decode_block_fused";
 
 thread_local char g_last_error[256] = "no error";
 
@@ -30,22 +28,18 @@ dab_status hip_status(hipError_t e) {
     return DAB_ERR_HIP;
 }
 
-int phase_count(const Plan& p) {
-    return p.schedule == DAB_SCHEDULE_FUSED ? 1 : p.schedule == DAB_SCHEDULE_TWO_STAGE ? 2 : 3;
-}
+int phase_count(const Plan&) { return 3; }
 
 dab_status record(void* const* events, int i, hipStream_t s) {
     if (!events) return DAB_OK;
     return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
 }
 
-dab::GemvPlanDev gemv_dev(const dab::GemvPlan& g) {
-    dab::GemvPlanDev d;
-    d.slabs = g.slabs;
-    d.ksplit = g.ksplit;
-    d.rows = g.rows;
+dab::PanelPlanDev panel_dev(const dab::PanelPlan& g) {
+    dab::PanelPlanDev d;
+    d.panels = g.panels;
+    d.nb = g.nb;
     d.nbg = g.nbg;
-    d.tiles = g.tiles;
     d.items = g.grid;
     return d;
 }
@@ -66,20 +60,12 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.out = out;
     a.dbg_y = dbg_y;
     a.flags = n(p.off_flags);
-    a.done_all = a.flags + 1;
-    a.epoch = a.flags + 2;
-    a.done = n(p.off_done);
-    a.qkv_cnt = n(p.off_qkv_cnt);
     a.attn_cnt = n(p.off_attn_cnt);
-    a.oproj_cnt = n(p.off_oproj_cnt);
-    a.qkv_part = f(p.off_qkv_part);
-    a.ssq = f(p.off_ssq);
     a.q = f(p.off_q);
     a.kv_new = f(p.off_kv_new);
     a.attn_o = f(p.off_attn_o);
     a.attn_ml = f(p.off_attn_ml);
     a.a = f(p.off_a);
-    a.oproj_part = f(p.off_oproj_part);
     a.B = p.B;
     a.H = p.H;
     a.nq = p.nq;
@@ -92,19 +78,11 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.eps = p.eps;
     a.qscale = (float)(1.4426950408889634 / sqrt((double)p.D));
     a.log2_theta = log2((double)p.theta);
-    a.qkv = gemv_dev(p.qkv);
-    a.oproj = gemv_dev(p.oproj);
-    a.qkv_bg = p.qkv.bg;
+    a.qkv = panel_dev(p.qkv);
+    a.oproj = panel_dev(p.oproj);
     a.T = p.kv_chunk;
     a.maxc = p.max_chunks;
     a.attn_items = p.attn_grid;
-    a.total_items = p.total_items;
-    a.item_lo = 0;
-    a.units = p.units;
-    a.unit_items = p.unit_items;
-    a.unit_slabs = p.unit_slabs;
-    a.unit_kv = p.unit_kv;
-    a.unit_oks = p.unit_oks;
 #ifdef DAB_TRACE
     a.trace = g_trace;
     a.trace_base = 0;
@@ -113,22 +91,10 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
 }
 
 dab_status enqueue(const Plan& p, const dab::StepArgs& a, hipStream_t s, void* const* events) {
-    const bool bf16 = p.dtype == DAB_BF16;
     dab_status st = record(events, 0, s);
     if (st != DAB_OK) return st;
-    if (p.schedule == DAB_SCHEDULE_FUSED) {
-        if ((st = hip_status(dab::launch_fused(a, bf16, s))) != DAB_OK) return st;
-        return record(events, 1, s);
-    }
-    if (p.schedule == DAB_SCHEDULE_TWO_STAGE) {
-        for (int stage = 0; stage < 2; ++stage) {
-            if ((st = hip_status(dab::launch_two_stage(a, bf16, stage, s))) != DAB_OK) return st;
-            if ((st = record(events, stage + 1, s)) != DAB_OK) return st;
-        }
-        return DAB_OK;
-    }
     for (int phase = 0; phase < 3; ++phase) {
-        if ((st = hip_status(dab::launch_phase(a, bf16, phase, s))) != DAB_OK) return st;
+        if ((st = hip_status(dab::launch_phase(a, p, phase, s))) != DAB_OK) return st;
         if ((st = record(events, phase + 1, s)) != DAB_OK) return st;
     }
     return DAB_OK;
@@ -154,6 +120,37 @@ dab_status call(const dab_config* cfg, const void* hidden, const void* norm_w, c
 }
 
 }  // namespace
+
+namespace dab {
+namespace {
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+    const size_t words = bytes / 4;
+    if (words == 0) return hipSuccess;
+    size_t blocks = (words + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint32_t*>(p), words);
+    return hipGetLastError();
+}
+
+hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s) {
+#ifdef DAB_TRACE
+    StepArgs t = a;   // phases trace at consecutive item numbers: QKV, attention, output
+    t.trace_base = phase == 0 ? 0 : phase == 1 ? p.qkv.grid : p.qkv.grid + p.attn_grid;
+    return p.dtype == DAB_BF16 ? launch_phase_bf16(t, p, phase, s) : launch_phase_f32(t, p, phase, s);
+#else
+    return p.dtype == DAB_BF16 ? launch_phase_bf16(a, p, phase, s) : launch_phase_f32(a, p, phase, s);
+#endif
+}
+
+}  // namespace dab
 
 extern "C" {
 
@@ -197,8 +194,7 @@ int dab_phase_count(const dab_config* cfg) {
 const char* dab_phase_name(const dab_config* cfg, int i) {
     Plan p;
     if (dab::make_plan(cfg, &p) != DAB_OK || i < 0 || i >= phase_count(p)) return nullptr;
-    return p.schedule == DAB_SCHEDULE_FUSED ? kFusedName
-         : p.schedule == DAB_SCHEDULE_TWO_STAGE ? kTwoStageNames[i] : kPhasedNames[i];
+    return kPhasedNames[i];
 }
 
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag) {
@@ -218,7 +214,8 @@ const char* dab_status_string(dab_status status) {
         case DAB_OK: return "ok";
         case DAB_ERR_INVALID_ARG: return "invalid argument (null, misaligned or overlapping pointer, bad size)";
         case DAB_ERR_UNSUPPORTED: return "unsupported shape (head_dim not 64/128, hidden not a multiple of 64, "
-                                         "group > 8, or too many KV chunks)";
+                                         "hidden or n_q_heads * head_dim above 16384, group > 8, "
+                                         "or too many KV chunks)";
         case DAB_ERR_WORKSPACE: return "workspace missing or too small";
         case DAB_ERR_HIP: return "HIP runtime error";
     }

@@ -1,0 +1,366 @@
+// Row-panel GEMVs of the decode step (gfx950, wave64).
+//
+// W is stored [N, K]: one output feature per row, its K weights contiguous
+// (the torch.nn.Linear layout).  A workgroup owns 4 waves x RW rows and all
+// of K for NB batch rows.  Lane l of a wave reads the 16-byte vectors l,
+// l + 64, l + 128, ... of each of its rows, so one wave-wide load covers
+// 1 KB of a row and a row of 4096 bf16 weights is 8 loads per lane.  Every
+// weight load of the first K-block is issued before anything else; the
+// fp32 inputs are staged in LDS meanwhile, and each output is one wave
+// reduction.  No partial sum leaves the workgroup: the kernel ends when its
+// last weight bytes arrive, with no second pass over partials.
+//
+//   QKV panel   wave w of panel i takes RoPE pair 4i + w: rows e and e + D/2
+//               of one head (q heads, then k heads, then v heads), so both
+//               halves of a rotation meet in one wave.  RMSNorm is applied
+//               as a scale after the sum, u = r * ((x .* norm_w) . W[n]),
+//               r = (mean x^2 + eps)^(-1/2) (the operator-fusion page,
+//               section 3, stage 1; the one-shot all-reduce page, section
+//               2.2), so the weight stream never waits for the norm.  Then
+//               RoPE (rotate-half pairing, angle pos * theta^(-2e/D), formed
+//               and reduced to [-pi, pi] in fp64), q and the new k, v to the
+//               workspace, k and v appended to the caches (operator-fusion
+//               page, section 3, stages 2-3).
+//   O panel     rows of W_o; out = x + a . W_o[n] (ClusterFusion page,
+//               section 1.1; operator-fusion page, section 1).
+#pragma once
+
+#include "dab_device.h"
+
+namespace dab {
+namespace dev {
+
+// 16 bytes of weights: 8 bf16 or 4 fp32, streamed once (nontemporal).
+template <typename T> struct W16;
+
+template <> struct W16<uint16_t> {
+    static constexpr int N = 8;
+    u32x4 r;
+    __device__ void load(const uint16_t* p) { r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+    __device__ void load_cached(const uint16_t* p) { r = *reinterpret_cast<const u32x4*>(p); }
+    __device__ void zero() { r = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ void unpack(float* f) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(r[i] << 16);
+            f[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+        }
+    }
+};
+
+template <> struct W16<float> {
+    static constexpr int N = 4;
+    f32x4 r;
+    __device__ void load(const float* p) { r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)); }
+    __device__ void load_cached(const float* p) { r = *reinterpret_cast<const f32x4*>(p); }
+    __device__ void zero() { r = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ void unpack(float* f) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = r[i];
+    }
+};
+
+constexpr int kPanelVecs = 8;    // weight vectors per lane, row and K-block
+
+// Work index -> (panel, batch group); false for padding.  The batch groups
+// of one panel get work indices 8 apart, so they run on one XCD (blocks are
+// dealt to the eight XCDs round-robin) and read the panel through its L2.
+__device__ inline bool panel_decode(int nbg, int panels, int idx, int* panel, int* bgi) {
+    if (nbg == 1) {
+        *panel = idx;
+        *bgi = 0;
+        return idx < panels;
+    }
+    const int lo = idx & 7, rest = idx >> 3;
+    *bgi = rest % nbg;
+    *panel = (rest / nbg) * 8 + lo;
+    return *panel < panels;
+}
+
+// RW rows of W against NB fp32 input rows staged in LDS (xs, row stride K).
+// EXACT: K is a whole number of K-blocks, so every lane's every vector is in
+// range and the loads go out with no bounds checks (and no branches, which
+// would make the compiler wait for every load at the first use).
+template <typename T, int RW, int NB, bool EXACT>
+struct PanelDot {
+    static constexpr int N = W16<T>::N;
+    static constexpr int KB = 64 * kPanelVecs * N;   // K per block: 4096 bf16, 2048 fp32
+    W16<T> w[RW][kPanelVecs];
+    float acc[RW][NB];
+
+    __device__ void issue(const T* const (&rows)[RW], int k0, int K, int lane) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int v = 0; v < kPanelVecs; ++v) {
+                const int k = k0 + (v * 64 + lane) * N;
+                if (EXACT || k < K) w[r][v].load(rows[r] + k);
+                else w[r][v].zero();
+            }
+    }
+
+    __device__ void accumulate(const float* xs, int k0, int K, int lane) {
+#pragma unroll
+        for (int v = 0; v < kPanelVecs; ++v) {
+            const int k = k0 + (v * 64 + lane) * N;
+            if (EXACT || k < K) {
+                float wf[RW][N];
+#pragma unroll
+                for (int r = 0; r < RW; ++r) w[r][v].unpack(wf[r]);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    float xv[N];
+#pragma unroll
+                    for (int i = 0; i < N / 4; ++i) {
+                        const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs + (size_t)j * K + k + 4 * i);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xv[4 * i + e] = x4[e];
+                    }
+#pragma unroll
+                    for (int r = 0; r < RW; ++r)
+#pragma unroll
+                        for (int e = 0; e < N; ++e) acc[r][j] = fmaf(wf[r][e], xv[e], acc[r][j]);
+                }
+            }
+        }
+    }
+
+    // The whole dot product: block 0 must already be issued.  Every lane
+    // ends with every sum.
+    __device__ void run(const T* const (&rows)[RW], const float* xs, int K, int lane) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[r][j] = 0.f;
+        for (int k0 = 0; k0 < K; k0 += KB) {
+            if (k0 > 0) issue(rows, k0, K, lane);
+            accumulate(xs, k0, K, lane);
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[r][j] = wave_sum(acc[r][j]);
+    }
+};
+
+// Staging of NB input rows of K values into LDS as fp32.  The first SI
+// vectors of every thread are loaded into registers before the weight
+// stream is issued (one round trip to L2 in front of the weights instead of
+// one behind them: a wave's loads complete in issue order); the rest, for
+// large K only, are loaded afterwards.
+constexpr int kStageAhead = 2;
+
+template <typename T, int NB>
+struct QkvShared {
+    float ss[NB][4];
+};
+
+// QKV panel `panel` for batch rows [bgi * NB, +NB).  xs: NB x H floats of LDS.
+template <typename T, int NB, bool EXACT>
+__device__ void qkv_panel(const StepArgs& a, int panel, int bgi, float* xs, QkvShared<T, NB>& sm) {
+    constexpr int N = W16<T>::N;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int H = a.H, D = a.D, half = D >> 1;
+    const int pr = panel * 4 + wave;                 // this wave's RoPE pair
+    const int hd = pr / half, e = pr - hd * half;    // head (q, then k, then v heads), dim
+    const int row0 = hd * D + e;
+    const T* W = static_cast<const T*>(a.w_qkv);
+    const T* const rows[2] = {W + (size_t)row0 * H, W + (size_t)(row0 + half) * H};
+    const T* hid = static_cast<const T*>(a.hidden);
+    const T* nw = static_cast<const T*>(a.norm_w);
+    const int b0 = bgi * NB;
+
+    // 1. this thread's first input vectors, then the weight stream
+    W16<T> xr[kStageAhead][NB], wr[kStageAhead];
+#pragma unroll
+    for (int i = 0; i < kStageAhead; ++i) {
+        const int k = (i * 256 + t) * N;
+        if (k < H) {
+            wr[i].load_cached(nw + k);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (b0 + j < a.B) xr[i][j].load_cached(hid + (size_t)(b0 + j) * H + k);
+                else xr[i][j].zero();
+            }
+        }
+    }
+    PanelDot<T, 2, NB, EXACT> dot;
+    dot.issue(rows, 0, H, lane);
+    DAB_TRACE_POINT(a, 1);
+
+    // 2. x .* norm_w into LDS, and sum of x^2 per sequence
+    float ss[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) ss[j] = 0.f;
+    auto stage = [&](int k, const W16<T>& wv, const W16<T> (&xv)[NB]) {
+        float wn[N];
+        wv.unpack(wn);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            float x[N];
+            xv[j].unpack(x);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                ss[j] = fmaf(x[i], x[i], ss[j]);
+                x[i] *= wn[i];
+            }
+#pragma unroll
+            for (int i = 0; i < N / 4; ++i)
+                *reinterpret_cast<f32x4*>(xs + (size_t)j * H + k + 4 * i) =
+                    f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < kStageAhead; ++i) {
+        const int k = (i * 256 + t) * N;
+        if (k < H) stage(k, wr[i], xr[i]);
+    }
+    for (int k = (kStageAhead * 256 + t) * N; k < H; k += 256 * N) {
+        W16<T> wv, xv[NB];
+        wv.load_cached(nw + k);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if (b0 + j < a.B) xv[j].load_cached(hid + (size_t)(b0 + j) * H + k);
+            else xv[j].zero();
+        }
+        stage(k, wv, xv);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const float s = wave_sum(ss[j]);
+        if (lane == 0) sm.ss[j][wave] = s;
+    }
+    __syncthreads();
+    DAB_TRACE_POINT(a, 2);
+
+    // 3. both rows against every staged sequence
+    dot.run(rows, xs, H, lane);
+
+    // 4. lane j finishes sequence b0 + j
+    float u0 = 0.f, u1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+        if (lane == j) {
+            u0 = dot.acc[0][j];
+            u1 = dot.acc[1][j];
+        }
+    const int bb = b0 + lane;
+    if (lane >= NB || bb >= a.B) return;
+    const float sum_sq = sm.ss[lane][0] + sm.ss[lane][1] + sm.ss[lane][2] + sm.ss[lane][3];
+    const float r = 1.0f / sqrtf(sum_sq / (float)H + a.eps);
+    u0 *= r;
+    u1 *= r;
+    int p;
+    const bool ok = pos_valid(a, bb, &p);
+    if (!ok && panel == 0 && wave == 0) __hip_atomic_fetch_or(a.flags, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (hd < a.nq + a.nkv) {
+        // q and k rows rotate: angle pos * theta^(-2e/D) in fp64, reduced to
+        // [-pi, pi] (fp32 would lose ~1e-3 rad at pos 16K), sin/cos in fp32
+        const double ang = (double)p * exp2(-(2.0 * e / D) * a.log2_theta);
+        const double two_pi = 6.283185307179586;
+        float sn, cs;
+        sincosf((float)(ang - two_pi * rint(ang / two_pi)), &sn, &cs);
+        const float v0 = u0 * cs - u1 * sn;
+        const float v1 = u1 * cs + u0 * sn;
+        u0 = v0;
+        u1 = v1;
+    }
+    if (hd < a.nq) {
+        float* q = a.q + (size_t)bb * a.n_q + row0;
+        q[0] = u0;
+        q[half] = u1;
+    } else {
+        const int kvrow = row0 - a.n_q;                  // in [0, 2 nkv D)
+        const int is_v = kvrow >= a.nkv * D;
+        const int col = is_v ? kvrow - a.nkv * D : kvrow;
+        float* kn = a.kv_new + ((size_t)bb * 2 + is_v) * a.nkv * D + col;
+        kn[0] = u0;
+        kn[half] = u1;
+        if (ok) {
+            T* dst = static_cast<T*>(is_v ? a.v_cache : a.k_cache) + ((size_t)bb * a.cap + p) * a.nkv * D + col;
+            dst[0] = from_f32<T>(u0);
+            dst[half] = from_f32<T>(u1);
+        }
+    }
+}
+
+// O panel `panel` (RW rows per wave) for batch rows [bgi * NB, +NB).
+// xs: NB x n_q floats of LDS.
+template <typename T, int RW, int NB, bool EXACT>
+__device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int K = a.n_q, H = a.H;
+    const int row0 = (panel * 4 + wave) * RW;
+    const T* W = static_cast<const T*>(a.w_o);
+    const T* rows[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) rows[r] = W + (size_t)(row0 + r) * K;
+    const int b0 = bgi * NB;
+    // sequences of this group with an attention output (valid position)
+    uint32_t valid = 0;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        int p;
+        if (b0 + j < a.B && pos_valid(a, b0 + j, &p)) valid |= 1u << j;
+    }
+
+    // 1. this thread's first attention-output vectors, then the weight stream
+    constexpr int SA = 2 * kStageAhead;               // fp32 vectors: 4 floats each
+    f32x4 xr[SA][NB];
+#pragma unroll
+    for (int i = 0; i < SA; ++i) {
+        const int k = (i * 256 + t) * 4;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            xr[i][j] = (k < K && ((valid >> j) & 1u)) ? *reinterpret_cast<const f32x4*>(a.a + (size_t)(b0 + j) * K + k)
+                                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    PanelDot<T, RW, NB, EXACT> dot;
+    dot.issue(rows, 0, K, lane);
+    DAB_TRACE_POINT(a, 1);
+
+    // 2. attention outputs into LDS (zeros for sequences without one)
+#pragma unroll
+    for (int i = 0; i < SA; ++i) {
+        const int k = (i * 256 + t) * 4;
+        if (k < K) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) *reinterpret_cast<f32x4*>(xs + (size_t)j * K + k) = xr[i][j];
+        }
+    }
+    for (int k = (SA * 256 + t) * 4; k < K; k += 1024) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            *reinterpret_cast<f32x4*>(xs + (size_t)j * K + k) =
+                ((valid >> j) & 1u) ? *reinterpret_cast<const f32x4*>(a.a + (size_t)(b0 + j) * K + k)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+    DAB_TRACE_POINT(a, 2);
+
+    // 3. the rows against every staged sequence
+    dot.run(rows, xs, K, lane);
+
+    // 4. lane j finishes sequence b0 + j: residual, rounding to storage
+    float y[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) y[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+        if (lane == j) {
+#pragma unroll
+            for (int r = 0; r < RW; ++r) y[r] = dot.acc[r][j];
+        }
+    if (lane >= NB || !((valid >> lane) & 1u)) return;
+    const int bb = b0 + lane;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const size_t i = (size_t)bb * H + row0 + r;
+        const float x = to_f32(static_cast<const T*>(a.hidden)[i]);
+        static_cast<T*>(a.out)[i] = from_f32<T>(x + y[r]);
+        if (a.dbg_y) a.dbg_y[i] = y[r];
+    }
+}
+
+}  // namespace dev
+}  // namespace dab

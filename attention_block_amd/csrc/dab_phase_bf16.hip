@@ -1,0 +1,8 @@
+// bf16 storage instantiation of the phase kernels.
+#include "dab_phase.h"
+
+namespace dab {
+hipError_t launch_phase_bf16(const StepArgs& a, const Plan& p, int phase, hipStream_t s) {
+    return dev::launch_phase_t<uint16_t>(a, p, phase, s);
+}
+}  // namespace dab

@@ -1,0 +1,8 @@
+// fp32 storage instantiation of the phase kernels.
+#include "dab_phase.h"
+
+namespace dab {
+hipError_t launch_phase_f32(const StepArgs& a, const Plan& p, int phase, hipStream_t s) {
+    return dev::launch_phase_t<float>(a, p, phase, s);
+}
+}  // namespace dab

@@ -10,24 +10,26 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Split a [K, N] GEMV over `batch` input rows into workgroup tiles: slabs of
-// kSlab columns, `rows` rows of W each (128 where K allows: 64 KB bf16 tiles,
-// and half the partials of 64-row tiles to sum at the end), `bg` batch rows
-// per workgroup.
-void plan_gemv(int K, int N, int batch, bool fused, GemvPlan* g) {
+// Plan a row-panel GEMV over `batch` input rows: W [N, K], `rpw` rows per
+// wave.  Batch rows go four (or two, or one) to a workgroup, as many as the
+// LDS budget for their fp32 copies allows.  With several batch groups the
+// panels are padded to a multiple of 8 so that the groups sharing one panel
+// of W land on one XCD and read it through its L2 (see panel_decode).
+bool plan_panel(int K, int N, int batch, int rpw, PanelPlan* g) {
     g->K = K;
     g->N = N;
-    g->slabs = ceil_div(N, kSlab);
-    g->bg = batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
-    g->nbg = ceil_div(batch, g->bg);
-    (void)fused;
-    g->rows = K % 128 == 0 ? 128 : 64;
-    g->ksplit = K / g->rows;
-    g->tiles = g->slabs * g->ksplit;
-    // With several batch groups the tiles are padded to a multiple of 8 so
-    // that the groups sharing one weight tile land on one XCD (see
-    // gemv_decode).
-    g->grid = g->nbg == 1 ? g->tiles : (int)align_up((size_t)g->tiles, 8) * g->nbg;
+    g->rows_per_wave = rpw;
+    g->rows = 4 * rpw;
+    if (N % g->rows != 0) return false;
+    g->panels = N / g->rows;
+    int nb = batch <= 1 ? 1 : batch == 2 ? 2 : 4;
+    while (nb > 1 && (size_t)nb * K * sizeof(float) > (size_t)kPanelLds) nb >>= 1;
+    if ((size_t)nb * K * sizeof(float) > (size_t)kPanelLds) return false;
+    g->nb = nb;
+    g->nbg = ceil_div(batch, nb);
+    g->grid = g->nbg == 1 ? g->panels : (int)align_up((size_t)g->panels, 8) * g->nbg;
+    g->lds = (size_t)nb * K * sizeof(float);
+    return true;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -39,11 +41,6 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
-
-// The schedule AUTO resolves to, from measurements on MI355X: one kernel per
-// phase beats both fused layouts on every configuration timed so far (the
-// fused hand-offs cost more than the kernel boundaries they remove).
-int auto_schedule(bool /*fused_ok*/) { return DAB_SCHEDULE_PHASED; }
 
 dab_status make_plan(const dab_config* cfg, Plan* p) {
     if (!cfg || !p) return DAB_ERR_INVALID_ARG;
@@ -58,6 +55,10 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     if (c.n_q_heads % c.n_kv_heads != 0) return DAB_ERR_INVALID_ARG;
     if (c.head_dim != 64 && c.head_dim != 128) return DAB_ERR_UNSUPPORTED;
     if (c.hidden % 64 != 0) return DAB_ERR_UNSUPPORTED;
+    // every GEMV workgroup keeps one batch row of its input in LDS as fp32
+    if ((size_t)c.hidden * sizeof(float) > (size_t)kPanelLds ||
+        (size_t)c.n_q_heads * c.head_dim * sizeof(float) > (size_t)kPanelLds)
+        return DAB_ERR_UNSUPPORTED;
     if (c.n_q_heads / c.n_kv_heads > kMaxGroup) return DAB_ERR_UNSUPPORTED;
     if (c.kv_chunk != 0 && (c.kv_chunk < 32 || c.kv_chunk > 4096 || c.kv_chunk % 16 != 0))
         return DAB_ERR_INVALID_ARG;
@@ -83,32 +84,23 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
 
     const int B = p->B > 0 ? p->B : 1;  // plan a batch-0 call as batch 1; nothing is launched
 
-    // schedule: fused only where its fixed chunk and group sizes apply
-    const int fchunk = fused_chunk(p->D);
-    const bool fused_ok = (p->G == 1 || p->G == 2 || p->G == 4 || p->G == 8) &&
-                          (c.kv_chunk == 0 || c.kv_chunk == fchunk) &&
-                          (p->cap - 1 + fchunk - 1) / fchunk <= kMaxChunks;
-    if (c.schedule < DAB_SCHEDULE_AUTO || c.schedule > DAB_SCHEDULE_TWO_STAGE) return DAB_ERR_INVALID_ARG;
-    if ((c.schedule == DAB_SCHEDULE_FUSED || c.schedule == DAB_SCHEDULE_TWO_STAGE) && !fused_ok)
-        return DAB_ERR_UNSUPPORTED;
-    // AUTO: the schedule that measures fastest on MI355X where it applies
-    p->schedule = c.schedule != DAB_SCHEDULE_AUTO ? c.schedule : auto_schedule(fused_ok);
-    p->fused = p->schedule != DAB_SCHEDULE_PHASED;
+    if (c.schedule != DAB_SCHEDULE_AUTO && c.schedule != DAB_SCHEDULE_PHASED) return DAB_ERR_INVALID_ARG;
+    p->schedule = DAB_SCHEDULE_PHASED;
 
-    plan_gemv(p->H, p->n_qkv, B, p->fused, &p->qkv);
-    plan_gemv(p->n_q, p->H, B, p->fused, &p->oproj);
+    // QKV: one RoPE pair (rows e and e + D/2 of a head) per wave; output
+    // projection: one row per wave (twice the workgroups for a quarter of
+    // the stream)
+    if (!plan_panel(p->H, p->n_qkv, B, 2, &p->qkv) || !plan_panel(p->n_q, p->H, B, 1, &p->oproj))
+        return DAB_ERR_UNSUPPORTED;
 
     // split-KV chunk over the cached tokens (at most cap - 1; the new token
-    // rides with the last chunk).  Fused: one batch of loads per item.
-    // Phased: about 1024 items per pass over the batch and KV heads (one
+    // rides with the last chunk): about 1024 items per pass over the batch and KV heads (one
     // wave of resident workgroups, four per CU), chunks of 32..256 tokens in
     // steps of 16; a chunk count just above a wave boundary would leave a
     // nearly empty second wave.
     const int hist = p->cap - 1 > 0 ? p->cap - 1 : 1;
     int T = c.kv_chunk;
-    if (p->fused) {
-        T = fchunk;
-    } else if (T == 0) {
+    if (T == 0) {
         const int want = (1024 + B * p->nkv - 1) / (B * p->nkv);     // chunks per sequence and kv head
         T = (ceil_div(hist, want) + 15) / 16 * 16;
         if (T < 32) T = 32;
@@ -122,24 +114,6 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     if (attn_grid + p->qkv.grid + p->oproj.grid > (1LL << 30)) return DAB_ERR_UNSUPPORTED;
     p->attn_grid = (int)attn_grid;
 
-    // fused unit order.  A unit is the kv heads of one 256-column key slab
-    // (256/D heads); it needs the query block and both kv blocks to start on
-    // slab boundaries and the output row blocks to hold whole units.
-    // Unit order measured 2.3x slower than phase order on MI355X (units wait
-    // on long hand-off chains while holding their slots), so it is off.
-    constexpr bool kUnitOrder = false;
-    const int kvu = 256 / p->D;
-    const bool unitise = kUnitOrder && p->fused && p->n_q % 256 == 0 && p->nkv % kvu == 0 && p->nkv > kvu &&
-                         (kvu * p->G * p->D) % p->oproj.rows == 0;
-    p->units = unitise ? p->nkv / kvu : 1;
-    p->unit_kv = p->nkv / p->units;
-    p->unit_slabs = unitise ? p->G + 2 : p->qkv.slabs;
-    p->unit_oks = p->oproj.ksplit / p->units;
-    auto items = [&](int tiles) { return p->qkv.nbg == 1 ? tiles : (tiles + 7) / 8 * 8 * p->qkv.nbg; };
-    p->unit_items = items(p->unit_slabs * p->qkv.ksplit) + B * p->unit_kv * p->max_chunks +
-                    items(p->unit_oks * p->oproj.slabs);
-    p->total_items = p->units * p->unit_items;
-
     // workspace layout
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -148,20 +122,12 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
         return at;
     };
     p->off_flags = take(256);
-    p->off_done = take(256 * 16);
-    p->off_qkv_cnt = take(sizeof(int32_t) * p->qkv.slabs * p->qkv.nbg);
     p->off_attn_cnt = take(sizeof(int32_t) * B * p->nkv);
-    p->off_oproj_cnt = take(sizeof(int32_t) * p->oproj.slabs * p->oproj.nbg);
-    // published buffers: 8 bytes per element (tagged words in the fused schedule)
-    const size_t w = 8;
-    p->off_qkv_part = take(w * (size_t)p->qkv.ksplit * B * p->n_qkv);
-    p->off_ssq = take(w * (size_t)p->qkv.slabs * p->qkv.ksplit * B);
-    p->off_q = take(w * (size_t)B * p->n_q);
-    p->off_kv_new = take(w * (size_t)B * 2 * p->nkv * p->D);
-    p->off_attn_o = take(w * (size_t)B * p->nq * p->max_chunks * p->D);
-    p->off_attn_ml = take(w * (size_t)B * p->nq * p->max_chunks * 2);
-    p->off_a = take(w * (size_t)B * p->n_q);
-    p->off_oproj_part = take(w * (size_t)p->oproj.ksplit * B * p->H);
+    p->off_q = take(sizeof(float) * (size_t)B * p->n_q);
+    p->off_kv_new = take(sizeof(float) * (size_t)B * 2 * p->nkv * p->D);
+    p->off_attn_o = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * p->D);
+    p->off_attn_ml = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * 2);
+    p->off_a = take(sizeof(float) * (size_t)B * p->n_q);
     p->ws_bytes = off;
 
     const size_t e = (size_t)p->elem;

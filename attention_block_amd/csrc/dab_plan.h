@@ -10,27 +10,28 @@
 
 namespace dab {
 
-// Columns of one GEMV slab: 32 lanes x 8 columns (one 16-byte bf16 load each).
-constexpr int kSlab = 256;
-// Threads per workgroup of every kernel.
+// Threads per workgroup of every kernel (four waves).
 constexpr int kThreads = 256;
 // Largest number of split-KV chunks per sequence the merge step stages.
 constexpr int kMaxChunks = 1024;
 // Largest query-head group per KV head the attention kernel keeps in registers.
 constexpr int kMaxGroup = 8;
-// Tokens per attention chunk in the fused schedule: one batch of loads,
-// 256 / (D/8) row slots x 8 tokens.
-inline int fused_chunk(int head_dim) { return 8 * 256 / (head_dim / 8); }
+// LDS a GEMV workgroup may give its fp32 input rows (nb x K floats).
+constexpr int kPanelLds = 64 * 1024;
 
-struct GemvPlan {
-    int K = 0, N = 0;     // reduction length, output columns
-    int slabs = 0;        // ceil(N / kSlab)
-    int rows = 0;         // rows of W per workgroup (KR), 64 or 128
-    int ksplit = 0;       // K / rows
-    int bg = 0;           // batch rows per workgroup (1, 2, 4 or 8)
-    int nbg = 0;          // ceil(B / bg)
-    int tiles = 0;        // slabs * ksplit
-    int grid = 0;         // work indices: tiles, padded per batch group
+// A row-panel GEMV y[b, n] = sum_k W[n, k] x[b, k] with W stored [N, K]
+// (every output's K weights contiguous).  A workgroup owns `rows` = 4 waves
+// x rows_per_wave outputs and all K for `nb` batch rows, so no partial sums
+// cross workgroups.
+struct PanelPlan {
+    int K = 0, N = 0;
+    int rows_per_wave = 0;  // 1 or 2 (the QKV panel: one RoPE pair per wave)
+    int rows = 0;           // 4 * rows_per_wave
+    int panels = 0;         // N / rows
+    int nb = 0;             // batch rows per workgroup: 1, 2 or 4
+    int nbg = 0;            // ceil(B / nb)
+    int grid = 0;           // workgroups: panels, padded to a multiple of 8 per batch group
+    size_t lds = 0;         // dynamic LDS bytes: nb * K floats
 };
 
 struct Plan {
@@ -39,21 +40,14 @@ struct Plan {
     float theta = 0.f, eps = 0.f;
     int elem = 0;                // bytes per stored element
 
-    int schedule = DAB_SCHEDULE_PHASED;   // resolved: FUSED, TWO_STAGE or PHASED
-    bool fused = false;          // FUSED or TWO_STAGE: tagged hand-offs, fused device code
-    GemvPlan qkv, oproj;
+    int schedule = DAB_SCHEDULE_PHASED;   // resolved schedule
+    PanelPlan qkv, oproj;
     int kv_chunk = 0, max_chunks = 0, attn_grid = 0;
-    int total_items = 0;         // fused: qkv.grid + attn_grid + oproj.grid (+ unit padding)
-    // fused unit order: units of unit_kv kv heads, each with unit_slabs QKV
-    // slabs, its attention chunks and unit_oks output row blocks
-    int units = 1, unit_items = 0, unit_slabs = 0, unit_kv = 0, unit_oks = 0;
 
-    // workspace layout, byte offsets (each 256-byte aligned).  The flags
-    // word is at offset 0, the finished-shard count at 4, the call epoch at
-    // 8; the 16 finish sub-counters follow, one per 256 bytes.
-    size_t off_flags = 0, off_done = 0, off_qkv_cnt = 0, off_attn_cnt = 0, off_oproj_cnt = 0;
-    size_t off_qkv_part = 0, off_ssq = 0, off_q = 0, off_kv_new = 0;
-    size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0, off_oproj_part = 0;
+    // workspace layout, byte offsets (each 256-byte aligned); the flags
+    // word is at offset 0
+    size_t off_flags = 0, off_attn_cnt = 0, off_q = 0, off_kv_new = 0;
+    size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0;
     size_t ws_bytes = 0;
 
     // byte extents of the caller's tensors (for alias checks)

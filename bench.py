@@ -47,8 +47,7 @@ def phase_bytes(cfg: BlockConfig, pos) -> dict:
     attn = s * 2 * nkv * D * tot
     # the hidden row is counted once, with the QKV kernel; the O-projection writes out
     oproj = s * nq * D * H + s * B * H
-    return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj,
-            "attention_oproj_fused": attn + oproj, "decode_block_fused": qkv + attn + oproj}
+    return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj}
 
 
 def make_layer_set(cfg: BlockConfig, pos, cap: int, gen, device):
@@ -63,8 +62,8 @@ def make_layer_set(cfg: BlockConfig, pos, cap: int, gen, device):
     ls = {
         "hidden": randn(B, H),
         "norm_w": randn(H, scale=0.1, shift=1.0),
-        "w_qkv": randn(H, cfg.n_qkv, scale=std),
-        "w_o": randn(nq * D, H, scale=std),
+        "w_qkv": randn(cfg.n_qkv, H, scale=std),     # one output feature per row
+        "w_o": randn(H, nq * D, scale=std),
         "k_cache": torch.zeros(B, cap, nkv, D, dtype=dt, device=device),
         "v_cache": torch.zeros(B, cap, nkv, D, dtype=dt, device=device),
         "pos": torch.tensor(np.asarray(pos, dtype=np.int32), device=device),
@@ -122,7 +121,7 @@ def main() -> int:
     ap.add_argument("--config", default=HEADLINE, choices=sorted(CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kv-chunk", type=int, default=0)
-    ap.add_argument("--schedule", default="auto", choices=["auto", "fused", "two_stage", "phased"])
+    ap.add_argument("--schedule", default="auto", choices=["auto", "phased"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true")

@@ -8,15 +8,22 @@
  * section 1; the fused dataflow of the ClusterFusion page, section 3.2):
  *
  *   r      = (mean_i x_i^2 + eps)^(-1/2),  xh = x * r * norm_w        RMSNorm
- *   u      = xh @ W_qkv          (packed columns [Q | K | V])           QKV GEMV
+ *   u      = xh @ W_qkv^T        (packed outputs [Q | K | V])           QKV GEMV
  *   q, k   = RoPE(q, pos_b), RoPE(k, pos_b)   (rotate-half pairing)     RoPE
  *   cache  : K[b, pos_b] = k, V[b, pos_b] = v                           KV append
  *   a_h    = softmax(q_h . K[b, 0..pos_b, g(h)] / sqrt(D)) @ V[...]     attention
- *   out    = x + a @ W_o                                                O-proj + residual
+ *   out    = x + a @ W_o^T                                              O-proj + residual
  *
  * with g(h) = h / (n_q_heads / n_kv_heads) (grouped-query mapping of the
  * operator-fusion page, section 3).  RoPE angle for pair (j, j + D/2) is
  * pos_b * theta^(-2j/D).
+ *
+ * Weights are taken in the [out_features, in_features] layout (the layout of
+ * a torch.nn.Linear weight): the transpose of the [in, out] matrices the
+ * pages multiply by.  Each output's weights are then one contiguous row, so
+ * at decode batch sizes one workgroup computes whole outputs and no partial
+ * sums cross workgroups.  Weights are static; transposing the pages' layout
+ * once at load time gives this one.
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise,
@@ -61,10 +68,10 @@ typedef enum { DAB_F32 = 0, DAB_BF16 = 1 } dab_dtype;
 /* Shape and numerics of one decode-block call. */
 typedef struct {
     int32_t batch;           /* B >= 0 sequences (0: nothing to do)                     */
-    int32_t hidden;          /* H, multiple of 64                                       */
+    int32_t hidden;          /* H, multiple of 64, at most 16384                        */
     int32_t n_q_heads;       /* nq >= 1                                                 */
     int32_t n_kv_heads;      /* nkv >= 1, divides nq, nq / nkv <= 8                     */
-    int32_t head_dim;        /* D: 64 or 128                                            */
+    int32_t head_dim;        /* D: 64 or 128; nq * D at most 16384                      */
     int32_t cache_capacity;  /* cap: token rows per sequence in each cache              */
     int32_t dtype;           /* dab_dtype                                               */
     float rope_theta;        /* RoPE base, > 0                                          */
@@ -75,30 +82,21 @@ typedef struct {
 } dab_config;
 
 /*
- * DAB_SCHEDULE_FUSED runs the whole step as one persistent launch: workgroups
- * take work items in dependency order (QKV tiles, attention chunks, output
- * tiles), issue their HBM loads first and then wait on device-side counters,
- * so the three weight/cache streams overlap.  It needs n_q_heads / n_kv_heads
- * in {1, 2, 4, 8} and kv_chunk 0 (the chunk is 128 tokens for D = 128, 256
- * for D = 64).  DAB_SCHEDULE_TWO_STAGE runs the QKV tiles as a kernel of
- * their own, then the rest of the fused launch (same requirements).
- * DAB_SCHEDULE_PHASED runs one kernel per phase.  AUTO picks the schedule
- * measured fastest on MI355X among those that apply (at present PHASED).
- * FUSED and TWO_STAGE share their device code and give identical bits; PHASED
- * splits its sums differently, so it agrees with them to fp32 rounding, not
- * bit for bit.  Each schedule is deterministic.
+ * DAB_SCHEDULE_PHASED runs one kernel per phase: QKV (RMSNorm, projection,
+ * RoPE, append), split-KV attention (each (sequence, kv head) merged by its
+ * last chunk), output projection with the residual.  AUTO picks the schedule
+ * measured fastest on MI355X among those that apply (at present the only
+ * one).  Results are deterministic: every sum has a fixed order.
  */
 typedef enum {
     DAB_SCHEDULE_AUTO = 0,
-    DAB_SCHEDULE_FUSED = 1,
-    DAB_SCHEDULE_PHASED = 2,
-    DAB_SCHEDULE_TWO_STAGE = 3
+    DAB_SCHEDULE_PHASED = 1
 } dab_schedule;
 
 /*
  * Bytes of device workspace one call with this configuration needs (0 when
- * the configuration is invalid).  The workspace holds split partial sums,
- * arrival counters and the device error flag.  It must be initialised once
+ * the configuration is invalid).  The workspace holds q, the new k and v,
+ * the split-KV partials, arrival counters and the device error flag.  It must be initialised once
  * with dab_workspace_init; every call leaves its counters at zero again, so
  * it can be reused by later calls (on one stream at a time) without
  * re-initialising.
@@ -116,9 +114,11 @@ dab_status dab_workspace_init(void* workspace, size_t bytes, void* stream);
  *
  *   hidden   [B, H]              input hidden state x (read only)
  *   norm_w   [H]                 RMSNorm weight (read only)
- *   w_qkv    [H, (nq+2nkv)*D]    row-major; column blocks Q (nq*D), K (nkv*D),
- *                                V (nkv*D), head-major inside each block
- *   w_o      [nq*D, H]           row-major; row h*D + d belongs to query head h
+ *   w_qkv    [(nq+2nkv)*D, H]    row-major, one output feature per row; row
+ *                                blocks Q (nq*D), K (nkv*D), V (nkv*D), head-major
+ *                                inside each block (row h*D + d: head h, dim d)
+ *   w_o      [H, nq*D]           row-major, one output feature per row; column
+ *                                h*D + d belongs to query head h
  *   k_cache, v_cache [B, cap, nkv, D]  token-major per sequence.  Rows
  *                                t < pos[b] are read; row pos[b] is written with
  *                                the new token's rotated k (resp. v), rounded to
@@ -143,8 +143,7 @@ dab_status dab_decode_attn_block(const dab_config* cfg,
 /*
  * Same as dab_decode_attn_block, and also records `n_events` hipEvent_t
  * (passed as void*) on `stream`: events[0] before the first kernel and
- * events[i] after kernel i-1.  n_events must equal dab_phase_count(cfg) + 1
- * (2 for the fused schedule, 3 for the two-stage one, 4 for the phased one).
+ * events[i] after kernel i-1.  n_events must equal dab_phase_count(cfg) + 1.
  * Used to time the phases of the step on the stream they run on.
  */
 dab_status dab_decode_attn_block_timed(const dab_config* cfg,
@@ -164,8 +163,6 @@ const char* dab_phase_name(const dab_config* cfg, int i);
 /*
  * Copy the workspace's sticky device error flag to *flag (host pointer) and
  * clear it.  Synchronises `stream`.  Bit 0: some pos[b] was outside [0, cap).
- * Bit 1: a workgroup of the fused schedule gave up waiting for a dependency
- * (a bounded wait that cannot expire in a correct run; results are invalid).
  */
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag);
 

@@ -25,7 +25,9 @@ def to_device(inp: dict, device="cuda"):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
-    return dict(hidden=t(inp["hidden"]), norm_w=t(inp["norm_w"]), w_qkv=t(inp["w_qkv"]), w_o=t(inp["w_o"]),
+    # the library takes weights one output feature per row: the transpose
+    # of the [in, out] matrices the generator (and the oracle) use
+    return dict(hidden=t(inp["hidden"]), norm_w=t(inp["norm_w"]), w_qkv=t(inp["w_qkv"].T), w_o=t(inp["w_o"].T),
                 k_cache=t(inp["k_cache"]), v_cache=t(inp["v_cache"]),
                 pos=torch.from_numpy(inp["pos"].astype(np.int32)).to(device))
 

@@ -71,33 +71,31 @@ def test_workspace_size_valid(lib):
     big = cfg(batch=32, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, cache_capacity=8193,
               dtype=_lib.DAB_BF16, rope_theta=5e5)
     assert lib.dab_workspace_size(ctypes.byref(big)) > n
-    fu = cfg(schedule=1)
-    assert lib.dab_phase_count(ctypes.byref(fu)) == 1
-    assert lib.dab_phase_name(ctypes.byref(fu), 0) == b"decode_block_fused"
-    ts = cfg(schedule=3)
-    assert [lib.dab_phase_name(ctypes.byref(ts), i) for i in range(3)] == [
-        b"qkv_rmsnorm_rope_append", b"attention_oproj_fused", None]
-    ph = cfg(schedule=2)
+    ph = cfg(schedule=1)
     assert lib.dab_phase_count(ctypes.byref(ph)) == 3
     assert [lib.dab_phase_name(ctypes.byref(ph), i) for i in range(4)] == [
         b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual", None]
 
 
 def test_schedule_selection(lib):
-    # a group of 3 query heads per kv head runs phased under auto, and cannot run fused
-    g3 = cfg(n_q_heads=6, n_kv_heads=2)
-    assert lib.dab_phase_count(ctypes.byref(g3)) == 3
-    assert call(lib, cfg(n_q_heads=6, n_kv_heads=2, schedule=1)) == _lib.DAB_ERR_UNSUPPORTED
-    # the fused chunk is 256 tokens for D = 64: another explicit chunk needs the phased schedule
-    assert call(lib, cfg(kv_chunk=64, schedule=1)) == _lib.DAB_ERR_UNSUPPORTED
-    assert lib.dab_phase_count(ctypes.byref(cfg(kv_chunk=64))) == 3
-    assert lib.dab_workspace_size(ctypes.byref(cfg(schedule=7))) == 0
-    assert call(lib, cfg(n_q_heads=6, n_kv_heads=2, schedule=3)) == _lib.DAB_ERR_UNSUPPORTED
-    # auto resolves to one kernel per phase, the layout measured fastest
+    # auto and phased both resolve to one kernel per phase; other values are rejected
+    for sched in (0, 1):
+        c = cfg(n_q_heads=6, n_kv_heads=2, schedule=sched)
+        assert [lib.dab_phase_name(ctypes.byref(c), i) for i in range(3)] == [
+            b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual"]
+    for bad in (-1, 2, 3, 7):
+        assert lib.dab_workspace_size(ctypes.byref(cfg(schedule=bad))) == 0
+        assert call(lib, cfg(schedule=bad)) == _lib.DAB_ERR_INVALID_ARG
     head = cfg(batch=1, hidden=4096, n_q_heads=32, n_kv_heads=32, head_dim=128, cache_capacity=4097,
                dtype=_lib.DAB_BF16)
-    assert [lib.dab_phase_name(ctypes.byref(head), i) for i in range(3)] == [
-        b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual"]
+    assert lib.dab_phase_count(ctypes.byref(head)) == 3
+
+
+def test_gemv_width_limits(lib):
+    # every GEMV workgroup keeps one fp32 input row in 64 KB of LDS
+    assert lib.dab_workspace_size(ctypes.byref(cfg(hidden=16384, n_q_heads=256, n_kv_heads=32))) > 0
+    assert call(lib, cfg(hidden=16384 + 64)) == _lib.DAB_ERR_UNSUPPORTED
+    assert call(lib, cfg(n_q_heads=264, n_kv_heads=33)) == _lib.DAB_ERR_UNSUPPORTED
 
 
 class FakePtrs:

@@ -42,11 +42,10 @@ def parity_case(cfg: BlockConfig, seed: int, *, cap=None, pos=None, kv_chunk=0, 
 # the workload configurations, full size
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
 @pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("name", list(CONFIGS))
-def test_config_parity(name, seed, schedule):
-    parity_case(CONFIGS[name], seed, schedule=schedule)
+def test_config_parity(name, seed):
+    parity_case(CONFIGS[name], seed)
 
 
 # ---------------------------------------------------------------------------
@@ -70,43 +69,38 @@ EDGE = [
 
 @pytest.mark.parametrize("label,cfg,cap,pos,kv_chunk", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_parity(label, cfg, cap, pos, kv_chunk):
-    parity_case(cfg, 7, cap=cap, pos=pos, kv_chunk=kv_chunk, label=label, schedule="phased")
-    if cfg.group in (1, 2, 4, 8):
-        parity_case(cfg, 7, cap=cap, pos=pos, label=label, schedule="fused")
-        parity_case(cfg, 7, cap=cap, pos=pos, label=label, schedule="two_stage")
+    parity_case(cfg, 7, cap=cap, pos=pos, kv_chunk=kv_chunk, label=label)
 
 
-FUSED_VS_PHASED = [
-    small_cfg("fp1", 1, 256, 4, 4, 64, "f32"),
-    small_cfg("fp2", 3, 512, 8, 2, 128, "bf16", 5e5),
-    small_cfg("fp3", 9, 320, 4, 1, 64, "bf16", 5e5),
+BATCH_INVARIANCE = [
+    small_cfg("bi1", 5, 512, 8, 2, 128, "bf16", 5e5),    # batch groups of 4: one full, one padded
+    small_cfg("bi2", 3, 256, 4, 4, 64, "f32"),
+    small_cfg("bi3", 2, 4096, 32, 8, 128, "bf16", 5e5),  # full-width rows (whole K-blocks)
 ]
 
 
-@pytest.mark.parametrize("cfg", FUSED_VS_PHASED, ids=[c.name for c in FUSED_VS_PHASED])
-def test_fused_and_phased_agree(cfg):
-    """Both schedules agree to fp32 rounding (they split the sums differently) and append identical rows
-    up to one storage ulp."""
+@pytest.mark.parametrize("cfg", BATCH_INVARIANCE, ids=[c.name for c in BATCH_INVARIANCE])
+def test_sequence_alone_matches_its_batch(cfg):
+    """Every sum of a sequence runs in one fixed order whatever batch group it lands in, so (at a fixed
+    KV chunk) a sequence run alone gives the same bits as inside its batch: out, y and the appended rows."""
     import torch
     pos = [(37 * b + 300) % 700 for b in range(cfg.batch)]
     inp = make_inputs(cfg, 13, cap=701, pos=pos)
-    say(f"[fused vs phased] {cfg.name}")
-    res = {}
-    for sched in ("fused", "two_stage", "phased"):
-        dev = to_device(inp)
-        out, dbg = run_gpu(dev, cfg, schedule=sched)
-        res[sched] = (dbg.double(), dev["k_cache"].double(), dev["v_cache"].double())
-    # the fused and two-stage schedules run the same work items in the same order
-    for i in range(3):   # raw bits: the caches hold NaN sentinels
-        assert torch.equal(res["fused"][i].view(torch.int64), res["two_stage"][i].view(torch.int64)), i
-    f, p = res["fused"], res["phased"]
-    assert torch.linalg.norm(f[0] - p[0]) / torch.linalg.norm(p[0]) < 1e-5
-    rows = (torch.arange(cfg.batch), torch.tensor(pos))
-    tol = 1e-2 if cfg.dtype == "bf16" else 1e-5
-    for i in (1, 2):
-        # every other cache element is untouched by both (checked bit-exactly by the parity tests)
-        fr, pr = f[i][rows], p[i][rows]
-        assert torch.linalg.norm(fr - pr) / torch.linalg.norm(pr) < tol
+    say(f"[batch invariance] {cfg.name}")
+    dev = to_device(inp)
+    out, dbg = run_gpu(dev, cfg, kv_chunk=64)
+    for b in range(cfg.batch):
+        one = BlockConfig(cfg.name + "_1", 1, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype,
+                          cfg.rope_theta)
+        sub = {**inp, "hidden": inp["hidden"][b:b + 1], "k_cache": inp["k_cache"][b:b + 1],
+               "v_cache": inp["v_cache"][b:b + 1], "pos": inp["pos"][b:b + 1], "cfg": one}
+        d1 = to_device(sub)
+        o1, y1 = run_gpu(d1, one, kv_chunk=64)
+        assert torch.equal(o1[0], out[b]) and torch.equal(y1[0], dbg[b]), b
+        p = pos[b]
+        for k in ("k_cache", "v_cache"):   # raw bits: the caches hold NaN sentinels
+            assert torch.equal(d1[k][0, p].view(torch.int16 if cfg.dtype == "bf16" else torch.int32),
+                               dev[k][b, p].view(torch.int16 if cfg.dtype == "bf16" else torch.int32)), (b, k)
 
 
 def test_tiny_fp32_tolerance_is_met_tightly():
@@ -133,7 +127,7 @@ def test_split_count_invariance():
         assert np.linalg.norm(o - outs[0]) / np.linalg.norm(outs[0]) < 1e-6
 
 
-@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
+@pytest.mark.parametrize("schedule", ["auto", "phased"])
 def test_repeat_calls_are_bit_identical(schedule):
     """Deterministic merges, and counters back at zero after each call."""
     import torch
@@ -149,31 +143,25 @@ def test_repeat_calls_are_bit_identical(schedule):
         assert torch.equal(o, res[0][0]) and torch.equal(d, res[0][1])
 
 
-@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
-def test_workspace_counters_return_to_zero(schedule):
+def test_workspace_counters_return_to_zero():
     import torch
     import attention_block_amd as ab
     cfg = small_cfg("ws", 3, 512, 8, 2, 128, "bf16", 5e5)
     inp = make_inputs(cfg, 2, cap=300, pos=[299, 10, 150])
     dev = to_device(inp)
     c = ab.make_config(batch=3, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, cache_capacity=300,
-                       dtype="bf16", rope_theta=5e5, schedule=schedule)
+                       dtype="bf16", rope_theta=5e5)
     ws = ab.Workspace(ab.workspace_size(c), dev["hidden"].device)
-    say(f"[counters] {schedule}: call then inspect workspace counters")
-    run_gpu(dev, cfg, workspace=ws, schedule=schedule)
+    say("[counters] call then inspect workspace counters")
+    run_gpu(dev, cfg, workspace=ws)
     torch.cuda.synchronize()
-    raw = ws._buf[ws.ptr - ws._buf.data_ptr():][: 256 + 4096 + 3 * 256].cpu().numpy().view(np.int32).copy()
-    # the workspace starts with the flags words (256 bytes), the 16 finish
-    # sub-counters (256 bytes each), then the arrival counters of the three
-    # phases (each fits in 256 bytes at this shape).  Word 2 is the call
-    # epoch, which the fused schedule advances once per call.
-    assert raw[2] == (0 if schedule == "phased" else 1)
-    raw[2] = 0
+    raw = ws._buf[ws.ptr - ws._buf.data_ptr():][: 256 + 256].cpu().numpy().view(np.int32).copy()
+    # the workspace starts with the flags words (256 bytes), then the
+    # attention arrival counters (B * nkv = 6 of them at this shape)
     assert np.all(raw == 0)
 
 
-@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
-def test_bad_position_sets_flag_and_skips_sequence(schedule):
+def test_bad_position_sets_flag_and_skips_sequence():
     import torch
     import attention_block_amd as ab
     cfg = small_cfg("badpos", 3, 256, 4, 2, 64, "f32")
@@ -185,7 +173,7 @@ def test_bad_position_sets_flag_and_skips_sequence(schedule):
     say("[bad pos] sequence 1 at pos == cap")
     ab.read_device_error()                             # clear any earlier flag
     ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"], dev["v_cache"],
-                         dev["pos"], cfg.rope_theta, cfg.eps, out=out, schedule=schedule)
+                         dev["pos"], cfg.rope_theta, cfg.eps, out=out)
     flag = ab.read_device_error()
     assert flag == 1
     assert torch.all(out[1] == 12345.0)               # its output row was left unwritten
@@ -199,34 +187,31 @@ def test_bad_position_sets_flag_and_skips_sequence(schedule):
     assert ab.read_device_error() == 0                 # reading cleared it
 
 
-@pytest.mark.parametrize("schedule", ["fused", "two_stage", "phased"])
-def test_graph_replay_matches_eager(schedule):
+def test_graph_replay_matches_eager():
     import torch
     import attention_block_amd as ab
     cfg = small_cfg("graph", 2, 512, 8, 2, 128, "bf16", 5e5)
     inp = make_inputs(cfg, 9, cap=700, pos=[699, 333])
     dev = to_device(inp)
-    say(f"[graph] {schedule}: eager, capture, 4 replays")
-    eager, _ = run_gpu(dev, cfg, schedule=schedule)
+    say("[graph] eager, capture, 4 replays")
+    eager, _ = run_gpu(dev, cfg)
     eager = eager.clone()
     out = torch.empty_like(dev["hidden"])
     c = ab.make_config(batch=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, cache_capacity=700,
-                       dtype="bf16", rope_theta=5e5, schedule=schedule)
+                       dtype="bf16", rope_theta=5e5)
     ws = ab.Workspace(ab.workspace_size(c), dev["hidden"].device)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):  # warm-up call outside capture
         ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
-                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws,
-                             schedule=schedule)
+                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
-                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws,
-                             schedule=schedule)
+                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws)
     for i in range(4):
         out.zero_()
         torch.cuda.synchronize()
