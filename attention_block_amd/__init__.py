@@ -40,7 +40,7 @@ def lib_version() -> str:
 def make_config(*, batch: int, hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                 cache_capacity: int, dtype: str, rope_theta: float, eps: float = 1e-6,
                 kv_chunk: int = 0, schedule: str = "auto") -> DabConfig:
-    """Build the C config struct.  dtype is "bf16" or "f32"; schedule "auto" or "phased"."""
+    """Build the C config struct.  dtype is "bf16" or "f32"; schedule one of _lib.SCHEDULES."""
     if dtype not in ("bf16", "f32"):
         raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
     if schedule not in _lib.SCHEDULES:
@@ -65,9 +65,11 @@ def phase_names(cfg: DabConfig) -> list:
 class Workspace:
     """Device scratch for the library (partials, counters, error flag).
 
-    Allocated once with torch, zeroed once by dab_workspace_init; every call
-    leaves its counters at zero, so one workspace serves any number of
-    calls on one stream at a time.
+    Allocated once with torch and zeroed once by dab_workspace_init.  Every
+    call re-arms the counters it uses, so one workspace serves any number of
+    calls with ONE configuration on one stream at a time.  Where the
+    counters sit depends on the configuration: a workspace used with another
+    configuration must be zeroed again first (reset()).
     """
 
     def __init__(self, nbytes: int, device):
@@ -77,20 +79,32 @@ class Workspace:
         base = self._buf.data_ptr()
         self.ptr = (base + 255) // 256 * 256
         self.device = self._buf.device
+        self.reset()
+
+    def reset(self) -> None:
+        """Zero the workspace (on the current stream), as before its first call."""
         _check(_lib.load().dab_workspace_init(ctypes.c_void_p(self.ptr), self.nbytes, _stream_ptr(self.device)),
                "dab_workspace_init")
 
 
+# Default workspaces, one per device and configuration (the counters of a
+# workspace sit where its configuration puts them); the most recent few are kept.
 _default_ws = {}
+_DEFAULT_WS_KEEP = 8
+
+
+def _config_key(cfg: DabConfig) -> tuple:
+    return tuple(getattr(cfg, name) for name, _ in DabConfig._fields_)
 
 
 def _workspace_for(cfg: DabConfig, device) -> Workspace:
-    need = workspace_size(cfg)
-    key = (device.type, device.index)
-    ws = _default_ws.get(key)
-    if ws is None or ws.nbytes < need:
-        ws = Workspace(max(need, 1 << 20), device)
-        _default_ws[key] = ws
+    key = (device.type, device.index, _config_key(cfg))
+    ws = _default_ws.pop(key, None)
+    if ws is None:
+        ws = Workspace(workspace_size(cfg), device)
+        while len(_default_ws) >= _DEFAULT_WS_KEEP:
+            _default_ws.pop(next(iter(_default_ws)))
+    _default_ws[key] = ws          # most recently used last
     return ws
 
 
@@ -155,8 +169,9 @@ def decode_attn_block(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_th
     k_cache, v_cache [B, cap, nkv, D] (row pos[b] is written); pos int32 [B];
     all but pos in one dtype (bfloat16 or float32) on one GPU.  dbg_y
     (optional, float32 [B, H]) receives the pre-residual a @ W_o^T.
-    schedule: "phased" (one kernel per phase) or "auto" (the fastest that
-    applies).
+    schedule: "phased" (one kernel per phase), "attn_oproj" (attention and
+    the output projection in one launch), "qkv_attn" (QKV and attention in
+    one launch) or "auto" (the fastest that applies).
     """
     cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
                         schedule)
@@ -229,14 +244,20 @@ def decode_attn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_qkv, w
 
 
 def read_device_error(workspace: Optional[Workspace] = None, device=None) -> int:
-    """Read and clear the sticky device error flag (synchronises the stream)."""
+    """Read and clear the sticky device error flag (synchronises the stream).
+
+    Without `workspace`: the flags of every default workspace of the device,
+    OR-ed together (each is cleared)."""
     import torch
-    if workspace is None:
+    if workspace is not None:
+        spaces = [workspace]
+    else:
         dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
-        workspace = _default_ws.get((dev.type, dev.index))
-        if workspace is None:
-            return 0
-    flag = ctypes.c_int32()
-    _check(_lib.load().dab_read_device_error(ctypes.c_void_p(workspace.ptr), _stream_ptr(workspace.device),
-                                             ctypes.byref(flag)), "dab_read_device_error")
-    return flag.value
+        spaces = [ws for key, ws in _default_ws.items() if key[:2] == (dev.type, dev.index)]
+    flags = 0
+    for ws in spaces:
+        flag = ctypes.c_int32()
+        _check(_lib.load().dab_read_device_error(ctypes.c_void_p(ws.ptr), _stream_ptr(ws.device),
+                                                 ctypes.byref(flag)), "dab_read_device_error")
+        flags |= flag.value
+    return flags

@@ -10,7 +10,7 @@ LIB_PATH = os.environ.get("DAB_LIBRARY") or os.path.join(HERE, "libdab.so")
 
 DAB_OK, DAB_ERR_INVALID_ARG, DAB_ERR_UNSUPPORTED, DAB_ERR_WORKSPACE, DAB_ERR_HIP = range(5)
 DAB_F32, DAB_BF16 = 0, 1
-SCHEDULES = {"auto": 0, "phased": 1}
+SCHEDULES = {"auto": 0, "phased": 1, "attn_oproj": 2, "qkv_attn": 3}
 
 # every symbol include/dab.h declares
 EXPORTS = (

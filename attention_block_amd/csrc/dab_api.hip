@@ -19,6 +19,8 @@ unsigned long long* g_trace = nullptr;
 #endif
 
 const char* const kPhasedNames[3] = {"qkv_rmsnorm_rope_append", "attention_split_kv", "oproj_residual"};
+const char* const kAttnOprojNames[2] = {"qkv_rmsnorm_rope_append", "attention_oproj_residual"};
+const char* const kQkvAttnNames[2] = {"qkv_attention_split_kv", "oproj_residual"};
 
 thread_local char g_last_error[256] = "no error";
 
@@ -28,7 +30,7 @@ dab_status hip_status(hipError_t e) {
     return DAB_ERR_HIP;
 }
 
-int phase_count(const Plan&) { return 3; }
+int phase_count(const Plan& p) { return p.schedule == DAB_SCHEDULE_PHASED ? 3 : 2; }
 
 dab_status record(void* const* events, int i, hipStream_t s) {
     if (!events) return DAB_OK;
@@ -61,6 +63,9 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.dbg_y = dbg_y;
     a.flags = n(p.off_flags);
     a.attn_cnt = n(p.off_attn_cnt);
+    a.seq_cnt = n(p.off_seq_cnt);
+    a.seq_ready = n(p.off_seq_ready);
+    a.head_cnt = n(p.off_head_cnt);
     a.q = f(p.off_q);
     a.kv_new = f(p.off_kv_new);
     a.attn_o = f(p.off_attn_o);
@@ -93,7 +98,7 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
 dab_status enqueue(const Plan& p, const dab::StepArgs& a, hipStream_t s, void* const* events) {
     dab_status st = record(events, 0, s);
     if (st != DAB_OK) return st;
-    for (int phase = 0; phase < 3; ++phase) {
+    for (int phase = 0; phase < phase_count(p); ++phase) {
         if ((st = hip_status(dab::launch_phase(a, p, phase, s))) != DAB_OK) return st;
         if ((st = record(events, phase + 1, s)) != DAB_OK) return st;
     }
@@ -143,7 +148,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s) {
 #ifdef DAB_TRACE
     StepArgs t = a;   // phases trace at consecutive item numbers: QKV, attention, output
-    t.trace_base = phase == 0 ? 0 : phase == 1 ? p.qkv.grid : p.qkv.grid + p.attn_grid;
+    // consecutive item numbers: QKV, attention, output projection
+    const bool oproj_only = phase == 2 || (phase == 1 && p.schedule == DAB_SCHEDULE_QKV_ATTN);
+    t.trace_base = phase == 0 ? 0 : oproj_only ? p.qkv.grid + p.attn_grid : p.qkv.grid;
     return p.dtype == DAB_BF16 ? launch_phase_bf16(t, p, phase, s) : launch_phase_f32(t, p, phase, s);
 #else
     return p.dtype == DAB_BF16 ? launch_phase_bf16(a, p, phase, s) : launch_phase_f32(a, p, phase, s);
@@ -194,7 +201,8 @@ int dab_phase_count(const dab_config* cfg) {
 const char* dab_phase_name(const dab_config* cfg, int i) {
     Plan p;
     if (dab::make_plan(cfg, &p) != DAB_OK || i < 0 || i >= phase_count(p)) return nullptr;
-    return kPhasedNames[i];
+    return p.schedule == DAB_SCHEDULE_ATTN_OPROJ ? kAttnOprojNames[i]
+         : p.schedule == DAB_SCHEDULE_QKV_ATTN ? kQkvAttnNames[i] : kPhasedNames[i];
 }
 
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag) {

@@ -162,6 +162,14 @@ __device__ inline float fetch(const float* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Two consecutive published floats (8-byte aligned) in one device-coherent load.
+__device__ inline void fetch2(const float* p, float* out) {
+    const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    out[0] = __uint_as_float((uint32_t)w);
+    out[1] = __uint_as_float((uint32_t)(w >> 32));
+}
+
 __device__ inline int load_counter(const int* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -179,6 +187,19 @@ __device__ inline void drain_and_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // keeps the compiler from sinking stores
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+}
+
+// Thread-level bounded wait until *p >= target, SLEEP x 64 cycles between
+// polls.  The bound (at least 0.2 s) cannot be reached in a correct run; if it is, bit 1 of the error flags is
+// raised and the caller carries on, so every wave still exits.
+constexpr int kSpinLimit = 1 << 21;
+template <int SLEEP = 4>
+__device__ inline void wait_at_least(const int* p, int target, int* flags) {
+    for (int it = 0; it < kSpinLimit; ++it) {
+        if (load_counter(p) >= target) return;
+        __builtin_amdgcn_s_sleep(SLEEP);
+    }
+    __hip_atomic_fetch_or(flags, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Arrival at a counter shared by `expected` workgroups; true in exactly one
@@ -232,16 +253,29 @@ struct AttnGeom {
     static constexpr int BATCH = NSLOT * U;   // tokens per batch of loads (128 for D=128)
 };
 
-// 8 consecutive fp32 values of the workspace (32-byte aligned), plain loads:
-// the kernel boundary before this kernel orders them after their writer.
+// 8 consecutive fp32 values of the workspace (32-byte aligned).  COHERENT:
+// written in this launch by another workgroup, so read past the L2; else
+// plain loads (the kernel boundary orders them after their writer).
+template <bool COHERENT>
 __device__ inline void load8(const float* p, float* f) {
-    const f32x4 lo = reinterpret_cast<const f32x4*>(p)[0];
-    const f32x4 hi = reinterpret_cast<const f32x4*>(p)[1];
+    if constexpr (COHERENT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
+        for (int i = 0; i < 4; ++i) fetch2(p + 2 * i, f + 2 * i);
+    } else {
+        const f32x4 lo = reinterpret_cast<const f32x4*>(p)[0];
+        const f32x4 hi = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
+    }
 }
 
-template <typename T, int D, int G>
+// PUBLISH: the output projection runs in the same launch, so the merged
+// output is stored device-coherently and, once every head of the group is
+// stored and acknowledged, the sequence's merge counter is bumped.
+// WAITQ: the QKV projection runs in the same launch; after the K/V loads are
+// issued, wait until every panel of the group's q heads and of its k and v
+// heads is done, then read q and the new k, v device-coherently.
+template <typename T, int D, int G, bool PUBLISH, bool WAITQ>
 __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, G>& sm, int* s_flag) {
     using Geo = AttnGeom<D>;
     constexpr int LPR = Geo::LPR, NSLOT = Geo::NSLOT, U = Geo::U;
@@ -281,10 +315,20 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     DAB_TRACE_POINT(a, 1);
 
     // 2. q of this group's heads, in log2 units
+    if constexpr (WAITQ) {
+        if (t == 0) {
+            const int nheads = a.nq + 2 * nkv, panels = D / 8;      // panels per head: 4 RoPE pairs each
+            const int* cnt = a.head_cnt + (b / a.qkv.nb) * nheads;
+            for (int j = 0; j < G; ++j) wait_at_least<2>(cnt + g * G + j, panels, a.flags);
+            wait_at_least<2>(cnt + a.nq + g, panels, a.flags);
+            wait_at_least<2>(cnt + a.nq + nkv + g, panels, a.flags);
+        }
+        __syncthreads();
+    }
     float qv[G][8];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-        load8(a.q + (size_t)b * a.n_q + (size_t)(g * G + j) * D + l * 8, qv[j]);
+        load8<WAITQ>(a.q + (size_t)b * a.n_q + (size_t)(g * G + j) * D + l * 8, qv[j]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[j][e] *= a.qscale;
     }
@@ -357,8 +401,8 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
         const size_t kn = ((size_t)b * 2 * nkv + g) * D + l * 8;
         const size_t vn = kn + (size_t)nkv * D;
         float kf[8], vf[8];
-        load8(a.kv_new + kn, kf);
-        load8(a.kv_new + vn, vf);
+        load8<WAITQ>(a.kv_new + kn, kf);
+        load8<WAITQ>(a.kv_new + vn, vf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             kf[e] = to_f32(from_f32<T>(kf[e]));
@@ -433,7 +477,7 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     if (!arrive_last(cnt, nchunk, s_flag)) return;
     DAB_TRACE_POINT(a, 4);
     constexpr int PARTS = 256 / D;       // threads per output element
-    constexpr int OB = 8;                // chunks per thread in the first request
+    constexpr int OB = 16;               // chunks per thread in the first request (32 at D = 128)
     const int d = t % D, part = t / D;
     for (int j = 0; j < G; ++j) {
         const int h = g * G + j;
@@ -501,9 +545,19 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
             float tot = 0.f;
 #pragma unroll
             for (int q = 0; q < PARTS; ++q) tot += sm.acc[q * D + t];
-            a.a[(size_t)b * a.n_q + (size_t)h * D + t] = tot / L;
+            if constexpr (PUBLISH) publish(a.a + (size_t)b * a.n_q + (size_t)h * D + t, tot / L);
+            else a.a[(size_t)b * a.n_q + (size_t)h * D + t] = tot / L;
         }
         __syncthreads();
+    }
+    if constexpr (PUBLISH) {
+        // one more kv group of sequence b merged; the last one raises the
+        // sequence's ready flags (every other group's output was stored and
+        // acknowledged before its bump)
+        drain_and_sync();
+        if (t == 0) *s_flag = bump(&a.seq_cnt[b]) == nkv - 1;
+        __syncthreads();
+        if (*s_flag && t < kReadyCopies) set_counter(&a.seq_ready[(b * kReadyCopies + t) * kReadyStride], 1);
     }
     DAB_TRACE_POINT(a, 6);
 }

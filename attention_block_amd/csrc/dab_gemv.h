@@ -155,8 +155,65 @@ struct QkvShared {
     float ss[NB][4];
 };
 
+// Lane work of a QKV panel for sequence bb: RMS scale, RoPE, q and the new
+// k, v out, the cache append.  ss: the four waves' sums of x^2.
+template <typename T, bool SIGNAL>
+__device__ void qkv_finish(const StepArgs& a, int panel, int wave, int bb, int hd, int e, int row0, float u0,
+                           float u1, const float* ss) {
+    const int H = a.H, D = a.D, half = D >> 1;
+    // re-arm the merge counter and ready flags of this sequence for the
+    // attention kernel that follows (it runs after this kernel completes)
+    if (panel == 0 && wave == 0) {
+        set_counter(&a.seq_cnt[bb], 0);
+        for (int i = 0; i < kReadyCopies; ++i) set_counter(&a.seq_ready[(bb * kReadyCopies + i) * kReadyStride], 0);
+    }
+    const float sum_sq = ss[0] + ss[1] + ss[2] + ss[3];
+    const float r = 1.0f / sqrtf(sum_sq / (float)H + a.eps);
+    u0 *= r;
+    u1 *= r;
+    int p;
+    const bool ok = pos_valid(a, bb, &p);
+    if (!ok && panel == 0 && wave == 0) __hip_atomic_fetch_or(a.flags, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (hd < a.nq + a.nkv) {
+        // q and k rows rotate: angle pos * theta^(-2e/D) in fp64, reduced to
+        // [-pi, pi] (fp32 would lose ~1e-3 rad at pos 16K), sin/cos in fp32
+        const double ang = (double)p * exp2(-(2.0 * e / D) * a.log2_theta);
+        const double two_pi = 6.283185307179586;
+        float sn, cs;
+        sincosf((float)(ang - two_pi * rint(ang / two_pi)), &sn, &cs);
+        const float v0 = u0 * cs - u1 * sn;
+        const float v1 = u1 * cs + u0 * sn;
+        u0 = v0;
+        u1 = v1;
+    }
+    auto out = [&](float* dst, float v) {
+        if constexpr (SIGNAL) publish(dst, v);
+        else *dst = v;
+    };
+    if (hd < a.nq) {
+        float* q = a.q + (size_t)bb * a.n_q + row0;
+        out(q, u0);
+        out(q + half, u1);
+    } else {
+        const int kvrow = row0 - a.n_q;                  // in [0, 2 nkv D)
+        const int is_v = kvrow >= a.nkv * D;
+        const int col = is_v ? kvrow - a.nkv * D : kvrow;
+        float* kn = a.kv_new + ((size_t)bb * 2 + is_v) * a.nkv * D + col;
+        out(kn, u0);
+        out(kn + half, u1);
+        if (ok) {
+            T* dst = static_cast<T*>(is_v ? a.v_cache : a.k_cache) + ((size_t)bb * a.cap + p) * a.nkv * D + col;
+            dst[0] = from_f32<T>(u0);
+            dst[half] = from_f32<T>(u1);
+        }
+    }
+}
+
 // QKV panel `panel` for batch rows [bgi * NB, +NB).  xs: NB x H floats of LDS.
-template <typename T, int NB, bool EXACT>
+// SIGNAL: attention runs in the same launch; q and the new k, v are stored
+// device-coherently and, once the whole panel's stores are acknowledged,
+// the counter of its (batch group, head) is bumped.
+template <typename T, int NB, bool EXACT, bool SIGNAL>
 __device__ void qkv_panel(const StepArgs& a, int panel, int bgi, float* xs, QkvShared<T, NB>& sm) {
     constexpr int N = W16<T>::N;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -245,48 +302,19 @@ __device__ void qkv_panel(const StepArgs& a, int panel, int bgi, float* xs, QkvS
             u1 = dot.acc[1][j];
         }
     const int bb = b0 + lane;
-    if (lane >= NB || bb >= a.B) return;
-    const float sum_sq = sm.ss[lane][0] + sm.ss[lane][1] + sm.ss[lane][2] + sm.ss[lane][3];
-    const float r = 1.0f / sqrtf(sum_sq / (float)H + a.eps);
-    u0 *= r;
-    u1 *= r;
-    int p;
-    const bool ok = pos_valid(a, bb, &p);
-    if (!ok && panel == 0 && wave == 0) __hip_atomic_fetch_or(a.flags, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (hd < a.nq + a.nkv) {
-        // q and k rows rotate: angle pos * theta^(-2e/D) in fp64, reduced to
-        // [-pi, pi] (fp32 would lose ~1e-3 rad at pos 16K), sin/cos in fp32
-        const double ang = (double)p * exp2(-(2.0 * e / D) * a.log2_theta);
-        const double two_pi = 6.283185307179586;
-        float sn, cs;
-        sincosf((float)(ang - two_pi * rint(ang / two_pi)), &sn, &cs);
-        const float v0 = u0 * cs - u1 * sn;
-        const float v1 = u1 * cs + u0 * sn;
-        u0 = v0;
-        u1 = v1;
-    }
-    if (hd < a.nq) {
-        float* q = a.q + (size_t)bb * a.n_q + row0;
-        q[0] = u0;
-        q[half] = u1;
-    } else {
-        const int kvrow = row0 - a.n_q;                  // in [0, 2 nkv D)
-        const int is_v = kvrow >= a.nkv * D;
-        const int col = is_v ? kvrow - a.nkv * D : kvrow;
-        float* kn = a.kv_new + ((size_t)bb * 2 + is_v) * a.nkv * D + col;
-        kn[0] = u0;
-        kn[half] = u1;
-        if (ok) {
-            T* dst = static_cast<T*>(is_v ? a.v_cache : a.k_cache) + ((size_t)bb * a.cap + p) * a.nkv * D + col;
-            dst[0] = from_f32<T>(u0);
-            dst[half] = from_f32<T>(u1);
-        }
+    if (lane < NB && bb < a.B) qkv_finish<T, SIGNAL>(a, panel, wave, bb, hd, e, row0, u0, u1, sm.ss[lane]);
+    if constexpr (SIGNAL) {
+        drain_and_sync();
+        if (t == 0) bump(&a.head_cnt[bgi * (a.nq + 2 * a.nkv) + hd]);
     }
 }
 
 // O panel `panel` (RW rows per wave) for batch rows [bgi * NB, +NB).
-// xs: NB x n_q floats of LDS.
-template <typename T, int RW, int NB, bool EXACT>
+// xs: NB x n_q floats of LDS.  WAIT: the attention output is produced in the
+// same launch; the weight stream goes out first, then the workgroup waits
+// until every kv group of its sequences is merged and reads the attention
+// output device-coherently.
+template <typename T, int RW, int NB, bool EXACT, bool WAIT>
 __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int K = a.n_q, H = a.H;
@@ -303,37 +331,87 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
         int p;
         if (b0 + j < a.B && pos_valid(a, b0 + j, &p)) valid |= 1u << j;
     }
+    // lane j's residual inputs, requested first so they are in by the end
+    const bool mine = lane < NB && ((valid >> lane) & 1u);
+    float xres[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+        xres[r] = mine ? to_f32(static_cast<const T*>(a.hidden)[(size_t)(b0 + lane) * H + row0 + r]) : 0.f;
 
-    // 1. this thread's first attention-output vectors, then the weight stream
-    constexpr int SA = 2 * kStageAhead;               // fp32 vectors: 4 floats each
-    f32x4 xr[SA][NB];
-#pragma unroll
-    for (int i = 0; i < SA; ++i) {
-        const int k = (i * 256 + t) * 4;
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-            xr[i][j] = (k < K && ((valid >> j) & 1u)) ? *reinterpret_cast<const f32x4*>(a.a + (size_t)(b0 + j) * K + k)
-                                                     : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     PanelDot<T, RW, NB, EXACT> dot;
-    dot.issue(rows, 0, K, lane);
-    DAB_TRACE_POINT(a, 1);
-
-    // 2. attention outputs into LDS (zeros for sequences without one)
+    if constexpr (WAIT) {
+        // 1. the weight stream, then the wait for the attention output
+        dot.issue(rows, 0, K, lane);
+        DAB_TRACE_POINT(a, 1);
+        if (t == 0) {
+            const int copy = blockIdx.x % kReadyCopies;
 #pragma unroll
-    for (int i = 0; i < SA; ++i) {
-        const int k = (i * 256 + t) * 4;
-        if (k < K) {
-#pragma unroll
-            for (int j = 0; j < NB; ++j) *reinterpret_cast<f32x4*>(xs + (size_t)j * K + k) = xr[i][j];
+            for (int j = 0; j < NB; ++j)
+                if ((valid >> j) & 1u)
+                    wait_at_least<8>(&a.seq_ready[((b0 + j) * kReadyCopies + copy) * kReadyStride], 1, a.flags);
         }
-    }
-    for (int k = (SA * 256 + t) * 4; k < K; k += 1024) {
+        __syncthreads();
+        // 2. attention outputs into LDS (zeros for sequences without one):
+        // every load of a round issued before any is used, so the round
+        // costs one trip to the memory-side cache
+        constexpr int PR = 8;                         // 8-byte loads per thread and round
+        for (int k0 = 0; k0 < K; k0 += 2 * 256 * PR) {
+            float v[NB][PR][2];
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-            *reinterpret_cast<f32x4*>(xs + (size_t)j * K + k) =
-                ((valid >> j) & 1u) ? *reinterpret_cast<const f32x4*>(a.a + (size_t)(b0 + j) * K + k)
-                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < PR; ++i) {
+                    const int k = k0 + 2 * (i * 256 + t);
+                    if (k < K && ((valid >> j) & 1u)) {
+                        fetch2(a.a + (size_t)(b0 + j) * K + k, v[j][i]);
+                    } else {
+                        v[j][i][0] = 0.f;
+                        v[j][i][1] = 0.f;
+                    }
+                }
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < PR; ++i) {
+                    const int k = k0 + 2 * (i * 256 + t);
+                    if (k < K) {
+                        xs[(size_t)j * K + k] = v[j][i][0];
+                        xs[(size_t)j * K + k + 1] = v[j][i][1];
+                    }
+                }
+        }
+    } else {
+        // 1. this thread's first attention-output vectors, then the weight stream
+        constexpr int SA = 2 * kStageAhead;           // fp32 vectors: 4 floats each
+        f32x4 xr[SA][NB];
+#pragma unroll
+        for (int i = 0; i < SA; ++i) {
+            const int k = (i * 256 + t) * 4;
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                xr[i][j] = (k < K && ((valid >> j) & 1u))
+                               ? *reinterpret_cast<const f32x4*>(a.a + (size_t)(b0 + j) * K + k)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        dot.issue(rows, 0, K, lane);
+        DAB_TRACE_POINT(a, 1);
+
+        // 2. attention outputs into LDS (zeros for sequences without one)
+#pragma unroll
+        for (int i = 0; i < SA; ++i) {
+            const int k = (i * 256 + t) * 4;
+            if (k < K) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) *reinterpret_cast<f32x4*>(xs + (size_t)j * K + k) = xr[i][j];
+            }
+        }
+        for (int k = (SA * 256 + t) * 4; k < K; k += 1024) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                *reinterpret_cast<f32x4*>(xs + (size_t)j * K + k) =
+                    ((valid >> j) & 1u) ? *reinterpret_cast<const f32x4*>(a.a + (size_t)(b0 + j) * K + k)
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     __syncthreads();
     DAB_TRACE_POINT(a, 2);
@@ -351,13 +429,12 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
 #pragma unroll
             for (int r = 0; r < RW; ++r) y[r] = dot.acc[r][j];
         }
-    if (lane >= NB || !((valid >> lane) & 1u)) return;
+    if (!mine) return;
     const int bb = b0 + lane;
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
         const size_t i = (size_t)bb * H + row0 + r;
-        const float x = to_f32(static_cast<const T*>(a.hidden)[i]);
-        static_cast<T*>(a.out)[i] = from_f32<T>(x + y[r]);
+        static_cast<T*>(a.out)[i] = from_f32<T>(xres[r] + y[r]);
         if (a.dbg_y) a.dbg_y[i] = y[r];
     }
 }

@@ -32,6 +32,10 @@ struct StepArgs {
     // workspace
     int* flags;             // error bits
     int* attn_cnt;          // [B * nkv] chunk arrivals (re-armed by the merging workgroup)
+    int* seq_cnt;           // [B] kv groups merged (one-launch attention + projection; re-armed by the QKV kernel)
+    int* seq_ready;         // [B, kReadyCopies] x kReadyStride: 1 once every group of the sequence is merged
+    int* head_cnt;          // [qkv.nbg, nq + 2 nkv] QKV panels done per (batch group, head) (one-launch
+                            // QKV + attention; re-armed by the output projection kernel)
     float* q;               // [B, n_q] rotated q
     float* kv_new;          // [B, 2, nkv, D] the new token's rotated k and v
     float* attn_o;          // [B, nq, maxc, D] chunk partial outputs
@@ -51,6 +55,7 @@ struct StepArgs {
 };
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Kernel `phase` of the plan's schedule (0 .. phase_count - 1).
 hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s);
 
 // per-dtype instantiations (separate translation units)

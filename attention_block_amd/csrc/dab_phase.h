@@ -1,23 +1,25 @@
-// The three kernels of the phased schedule (QKV, attention, output
-// projection) and their launchers, templated on the storage type; each
-// storage type is instantiated in a translation unit of its own.
+// The kernels of the step and their launchers, templated on the storage
+// type; each storage type is instantiated in a translation unit of its own.
+//   phased schedule    QKV, attention, output projection: three kernels.
+//   attn_oproj         QKV, then attention and output projection in one
+//                      launch: the projection's workgroups follow every
+//                      attention chunk in the grid, stream their rows of W_o
+//                      while the last chunks and merges finish, and wait on
+//                      per-sequence ready flags.
+//   qkv_attn           QKV and attention in one launch: the attention chunks
+//                      follow every QKV panel in the grid, load their K/V
+//                      rows while the projection finishes, and wait on
+//                      per-(batch group, head) panel counters; then the
+//                      output projection.
+// In a one-launch kernel a workgroup only waits on lower-numbered ones that
+// never wait themselves, and each XCD dispatches its workgroups in index
+// order, so every wait ends.
 #pragma once
 
 #include "dab_gemv.h"
 
 namespace dab {
 namespace dev {
-
-template <typename T, int NB, bool EXACT>
-__global__ __launch_bounds__(256) void qkv_kernel(StepArgs a) {
-    extern __shared__ f32x4 xs_raw[];
-    __shared__ QkvShared<T, NB> sm;
-    DAB_TRACE_POINT(a, 0);
-    int panel, bgi;
-    if (panel_decode(a.qkv.nbg, a.qkv.panels, blockIdx.x, &panel, &bgi))
-        qkv_panel<T, NB, EXACT>(a, panel, bgi, reinterpret_cast<float*>(xs_raw), sm);
-    DAB_TRACE_POINT(a, 3);
-}
 
 // Attention work index -> (sequence, kv head, chunk); kv head fastest, so
 // concurrent items read neighbouring rows of one token range.
@@ -28,6 +30,36 @@ __device__ inline void attn_decode(const StepArgs& a, int i, int* b, int* g, int
     *b = rest / a.maxc;
 }
 
+template <typename T, int NB, bool EXACT>
+__global__ __launch_bounds__(256) void qkv_kernel(StepArgs a) {
+    extern __shared__ f32x4 xs_raw[];
+    __shared__ QkvShared<T, NB> sm;
+    DAB_TRACE_POINT(a, 0);
+    int panel, bgi;
+    if (panel_decode(a.qkv.nbg, a.qkv.panels, blockIdx.x, &panel, &bgi))
+        qkv_panel<T, NB, EXACT, false>(a, panel, bgi, reinterpret_cast<float*>(xs_raw), sm);
+    DAB_TRACE_POINT(a, 3);
+}
+
+template <typename T, int NB, int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && G == 1 && NB == 1 ? 4 : 1)))
+void qkv_attn_kernel(StepArgs a) {
+    extern __shared__ f32x4 lds_raw[];   // the QKV panel's staged inputs, or attention scratch
+    __shared__ QkvShared<T, NB> qsm;
+    __shared__ int s_flag;
+    DAB_TRACE_POINT(a, 0);
+    if ((int)blockIdx.x < a.qkv.items) {
+        int panel, bgi;
+        if (panel_decode(a.qkv.nbg, a.qkv.panels, blockIdx.x, &panel, &bgi))
+            qkv_panel<T, NB, true, true>(a, panel, bgi, reinterpret_cast<float*>(lds_raw), qsm);
+    } else {
+        int b, g, c;
+        attn_decode(a, blockIdx.x - a.qkv.items, &b, &g, &c);
+        attn_item<T, D, G, false, true>(a, b, g, c, *reinterpret_cast<AttnShared<D, G>*>(lds_raw), &s_flag);
+    }
+    DAB_TRACE_POINT(a, 3);
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_kernel(StepArgs a) {
     __shared__ AttnShared<D, G> sm;
@@ -35,7 +67,26 @@ __global__ __launch_bounds__(256) void attn_kernel(StepArgs a) {
     int b, g, c;
     DAB_TRACE_POINT(a, 0);
     attn_decode(a, blockIdx.x, &b, &g, &c);
-    attn_item<T, D, G>(a, b, g, c, sm, &s_flag);
+    attn_item<T, D, G, false, false>(a, b, g, c, sm, &s_flag);
+    DAB_TRACE_POINT(a, 3);
+}
+
+// Four waves per SIMD, as the attention kernel alone gets: all 1024 chunks of
+// a 7B-sized step resident at once.
+template <typename T, int D, int G, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && G == 1 && NB != 2 ? 4 : 1))) void attn_oproj_kernel(StepArgs a) {
+    extern __shared__ f32x4 lds_raw[];   // attention scratch, or the projection's staged inputs
+    __shared__ int s_flag;
+    DAB_TRACE_POINT(a, 0);
+    if ((int)blockIdx.x < a.attn_items) {
+        int b, g, c;
+        attn_decode(a, blockIdx.x, &b, &g, &c);
+        attn_item<T, D, G, true, false>(a, b, g, c, *reinterpret_cast<AttnShared<D, G>*>(lds_raw), &s_flag);
+    } else {
+        int panel, bgi;
+        if (panel_decode(a.oproj.nbg, a.oproj.panels, blockIdx.x - a.attn_items, &panel, &bgi))
+            oproj_panel<T, 1, NB, true, true>(a, panel, bgi, reinterpret_cast<float*>(lds_raw));
+    }
     DAB_TRACE_POINT(a, 3);
 }
 
@@ -43,9 +94,12 @@ template <typename T, int RW, int NB, bool EXACT>
 __global__ __launch_bounds__(256) void oproj_kernel(StepArgs a) {
     extern __shared__ f32x4 xs_raw[];
     DAB_TRACE_POINT(a, 0);
+    // re-arm the panel counters of a one-launch QKV + attention that ran before
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < a.qkv.nbg * (a.nq + 2 * a.nkv); i += 256) set_counter(&a.head_cnt[i], 0);
     int panel, bgi;
     if (panel_decode(a.oproj.nbg, a.oproj.panels, blockIdx.x, &panel, &bgi))
-        oproj_panel<T, RW, NB, EXACT>(a, panel, bgi, reinterpret_cast<float*>(xs_raw));
+        oproj_panel<T, RW, NB, EXACT, false>(a, panel, bgi, reinterpret_cast<float*>(xs_raw));
     DAB_TRACE_POINT(a, 3);
 }
 
@@ -110,13 +164,80 @@ hipError_t launch_attn_d(const StepArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <typename T, int D, int G>
+hipError_t launch_attn_oproj_g(const StepArgs& a, const Plan& p, hipStream_t s) {
+    const dim3 grid(p.attn_grid + p.oproj.grid), block(kThreads);
+    const size_t lds = p.oproj.lds > sizeof(AttnShared<D, G>) ? p.oproj.lds : sizeof(AttnShared<D, G>);
+    switch (p.oproj.nb) {
+        case 1: hipLaunchKernelGGL((attn_oproj_kernel<T, D, G, 1>), grid, block, lds, s, a); break;
+        case 2: hipLaunchKernelGGL((attn_oproj_kernel<T, D, G, 2>), grid, block, lds, s, a); break;
+        case 4: hipLaunchKernelGGL((attn_oproj_kernel<T, D, G, 4>), grid, block, lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Shapes the one-launch attention + projection is instantiated for: whole
+// K-blocks in the projection, one row per wave, groups of 1, 2, 4 or 8.
+template <typename T>
+inline bool attn_oproj_supported(const Plan& p) {
+    return exact_blocks<T>(p.n_q) && p.oproj.rows_per_wave == 1 && (p.G == 1 || p.G == 2 || p.G == 4 || p.G == 8);
+}
+
+template <typename T, int D>
+hipError_t launch_attn_oproj_d(const StepArgs& a, const Plan& p, hipStream_t s) {
+    switch (p.G) {
+        case 1: return launch_attn_oproj_g<T, D, 1>(a, p, s);
+        case 2: return launch_attn_oproj_g<T, D, 2>(a, p, s);
+        case 4: return launch_attn_oproj_g<T, D, 4>(a, p, s);
+        case 8: return launch_attn_oproj_g<T, D, 8>(a, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int NB, int D>
+hipError_t launch_qkv_attn_nd(const StepArgs& a, const Plan& p, hipStream_t s) {
+    const dim3 grid(p.qkv.grid + p.attn_grid), block(kThreads);
+    size_t lds = p.qkv.lds;
+    switch (p.G) {
+#define DAB_G(NG)                                                                                           \
+        case NG:                                                                                            \
+            if (sizeof(AttnShared<D, NG>) > lds) lds = sizeof(AttnShared<D, NG>);                             \
+            hipLaunchKernelGGL((qkv_attn_kernel<T, NB, D, NG>), grid, block, lds, s, a);                    \
+            break;
+        DAB_G(1) DAB_G(2) DAB_G(4) DAB_G(8)
+#undef DAB_G
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int NB>
+hipError_t launch_qkv_attn_n(const StepArgs& a, const Plan& p, hipStream_t s) {
+    return a.D == 128 ? launch_qkv_attn_nd<T, NB, 128>(a, p, s) : launch_qkv_attn_nd<T, NB, 64>(a, p, s);
+}
+
+template <typename T>
+hipError_t launch_qkv_attn(const StepArgs& a, const Plan& p, hipStream_t s) {
+    if (!exact_blocks<T>(a.H)) return hipErrorInvalidValue;
+    switch (p.qkv.nb) {
+        case 1: return launch_qkv_attn_n<T, 1>(a, p, s);
+        case 2: return launch_qkv_attn_n<T, 2>(a, p, s);
+        case 4: return launch_qkv_attn_n<T, 4>(a, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T>
 hipError_t launch_phase_t(const StepArgs& a, const Plan& p, int phase, hipStream_t s) {
-    switch (phase) {
-        case 0: return launch_qkv<T>(a, p, s);
-        case 1: return a.D == 128 ? launch_attn_d<T, 128>(a, s) : launch_attn_d<T, 64>(a, s);
-        default: return launch_oproj<T>(a, p, s);
+    if (p.schedule == DAB_SCHEDULE_QKV_ATTN) return phase == 0 ? launch_qkv_attn<T>(a, p, s) : launch_oproj<T>(a, p, s);
+    if (phase == 0) return launch_qkv<T>(a, p, s);
+    if (p.schedule == DAB_SCHEDULE_ATTN_OPROJ) {
+        if (!attn_oproj_supported<T>(p)) return hipErrorInvalidValue;
+        return a.D == 128 ? launch_attn_oproj_d<T, 128>(a, p, s) : launch_attn_oproj_d<T, 64>(a, p, s);
     }
+    if (phase == 1) return a.D == 128 ? launch_attn_d<T, 128>(a, s) : launch_attn_d<T, 64>(a, s);
+    return launch_oproj<T>(a, p, s);
 }
 
 }  // namespace dev

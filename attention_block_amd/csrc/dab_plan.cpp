@@ -84,14 +84,36 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
 
     const int B = p->B > 0 ? p->B : 1;  // plan a batch-0 call as batch 1; nothing is launched
 
-    if (c.schedule != DAB_SCHEDULE_AUTO && c.schedule != DAB_SCHEDULE_PHASED) return DAB_ERR_INVALID_ARG;
-    p->schedule = DAB_SCHEDULE_PHASED;
+    if (c.schedule < DAB_SCHEDULE_AUTO || c.schedule > DAB_SCHEDULE_QKV_ATTN) return DAB_ERR_INVALID_ARG;
 
     // QKV: one RoPE pair (rows e and e + D/2 of a head) per wave; output
     // projection: one row per wave (twice the workgroups for a quarter of
     // the stream)
     if (!plan_panel(p->H, p->n_qkv, B, 2, &p->qkv) || !plan_panel(p->n_q, p->H, B, 1, &p->oproj))
         return DAB_ERR_UNSUPPORTED;
+
+    // the one-launch kernels are instantiated for groups 1, 2, 4, 8 and for
+    // projections of whole K-blocks (4096 bf16 or 2048 fp32 values): the
+    // output projection's K (nq D) for attention + projection, the QKV
+    // projection's K (H) for QKV + attention
+    const int kblock = 64 * 8 * (16 / p->elem);
+    const bool group_ok = p->G == 1 || p->G == 2 || p->G == 4 || p->G == 8;
+    p->attn_oproj_ok = group_ok && p->n_q % kblock == 0;
+    p->qkv_attn_ok = group_ok && p->H % kblock == 0;
+    if ((c.schedule == DAB_SCHEDULE_ATTN_OPROJ && !p->attn_oproj_ok) ||
+        (c.schedule == DAB_SCHEDULE_QKV_ATTN && !p->qkv_attn_ok))
+        return DAB_ERR_UNSUPPORTED;
+    // AUTO: the schedule measured fastest on MI355X.  Attention + projection
+    // in one launch wins for one query head per kv head at small batch (7B
+    // layer, batch 1: 42.7 against 43.7 us at 4K tokens, 38.6 against 39.6
+    // at 1K); with grouped heads the attention chunks run two to a CU and
+    // the waiting projection workgroups cost them slots (8B GQA layer: 267
+    // against 169 us at batch 16, 71.9 against 69.8 at batch 1 and 16K
+    // tokens).  QKV + attention in one launch never won: the early K/V loads
+    // delay the QKV weight stream that every chunk waits for.
+    const bool auto_attn_oproj = p->attn_oproj_ok && p->G == 1 && B <= 4;
+    p->schedule = c.schedule != DAB_SCHEDULE_AUTO ? c.schedule
+                : auto_attn_oproj ? DAB_SCHEDULE_ATTN_OPROJ : DAB_SCHEDULE_PHASED;
 
     // split-KV chunk over the cached tokens (at most cap - 1; the new token
     // rides with the last chunk): about 1024 items per pass over the batch and KV heads (one
@@ -123,6 +145,9 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     };
     p->off_flags = take(256);
     p->off_attn_cnt = take(sizeof(int32_t) * B * p->nkv);
+    p->off_seq_cnt = take(sizeof(int32_t) * B);
+    p->off_seq_ready = take(sizeof(int32_t) * B * kReadyCopies * kReadyStride);
+    p->off_head_cnt = take(sizeof(int32_t) * p->qkv.nbg * (p->nq + 2 * p->nkv));
     p->off_q = take(sizeof(float) * (size_t)B * p->n_q);
     p->off_kv_new = take(sizeof(float) * (size_t)B * 2 * p->nkv * p->D);
     p->off_attn_o = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * p->D);

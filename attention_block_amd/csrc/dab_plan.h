@@ -18,6 +18,12 @@ constexpr int kMaxChunks = 1024;
 constexpr int kMaxGroup = 8;
 // LDS a GEMV workgroup may give its fp32 input rows (nb x K floats).
 constexpr int kPanelLds = 64 * 1024;
+// Ready flags of a sequence's attention output (one-launch attention +
+// projection): copies on separate 128-byte lines, so that the projection's
+// workgroups, which poll them, spread over kReadyCopies addresses instead of
+// queueing on one.
+constexpr int kReadyCopies = 16;
+constexpr int kReadyStride = 32;     // ints
 
 // A row-panel GEMV y[b, n] = sum_k W[n, k] x[b, k] with W stored [N, K]
 // (every output's K weights contiguous).  A workgroup owns `rows` = 4 waves
@@ -40,13 +46,16 @@ struct Plan {
     float theta = 0.f, eps = 0.f;
     int elem = 0;                // bytes per stored element
 
-    int schedule = DAB_SCHEDULE_PHASED;   // resolved schedule
+    int schedule = DAB_SCHEDULE_PHASED;   // resolved schedule (never AUTO)
+    bool attn_oproj_ok = false;           // the one-launch attention + projection is built for this shape
+    bool qkv_attn_ok = false;             // the one-launch QKV + attention is built for this shape
     PanelPlan qkv, oproj;
     int kv_chunk = 0, max_chunks = 0, attn_grid = 0;
 
     // workspace layout, byte offsets (each 256-byte aligned); the flags
     // word is at offset 0
-    size_t off_flags = 0, off_attn_cnt = 0, off_q = 0, off_kv_new = 0;
+    size_t off_flags = 0, off_attn_cnt = 0, off_seq_cnt = 0, off_seq_ready = 0, off_head_cnt = 0;
+    size_t off_q = 0, off_kv_new = 0;
     size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0;
     size_t ws_bytes = 0;
 

@@ -47,7 +47,8 @@ def phase_bytes(cfg: BlockConfig, pos) -> dict:
     attn = s * 2 * nkv * D * tot
     # the hidden row is counted once, with the QKV kernel; the O-projection writes out
     oproj = s * nq * D * H + s * B * H
-    return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj}
+    return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj,
+            "attention_oproj_residual": attn + oproj, "qkv_attention_split_kv": qkv + attn}
 
 
 def make_layer_set(cfg: BlockConfig, pos, cap: int, gen, device):
@@ -121,7 +122,7 @@ def main() -> int:
     ap.add_argument("--config", default=HEADLINE, choices=sorted(CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kv-chunk", type=int, default=0)
-    ap.add_argument("--schedule", default="auto", choices=["auto", "phased"])
+    ap.add_argument("--schedule", default="auto", choices=["auto", "phased", "attn_oproj", "qkv_attn"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true")

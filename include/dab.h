@@ -84,22 +84,36 @@ typedef struct {
 /*
  * DAB_SCHEDULE_PHASED runs one kernel per phase: QKV (RMSNorm, projection,
  * RoPE, append), split-KV attention (each (sequence, kv head) merged by its
- * last chunk), output projection with the residual.  AUTO picks the schedule
- * measured fastest on MI355X among those that apply (at present the only
- * one).  Results are deterministic: every sum has a fixed order.
+ * last chunk), output projection with the residual.
+ * DAB_SCHEDULE_ATTN_OPROJ runs the QKV kernel, then attention and the output
+ * projection as one launch whose projection workgroups stream their weights
+ * while the last attention chunks finish.  It needs n_q_heads / n_kv_heads
+ * in {1, 2, 4, 8} and nq * D a multiple of 4096 (bf16) or 2048 (fp32).
+ * DAB_SCHEDULE_QKV_ATTN runs QKV and attention as one launch whose attention
+ * workgroups load their K/V rows while the QKV projection finishes, then
+ * the output projection.  It needs n_q_heads / n_kv_heads in {1, 2, 4, 8}
+ * and H a multiple of 4096 (bf16) or 2048 (fp32).
+ * AUTO picks the schedule measured fastest on MI355X: ATTN_OPROJ where it
+ * applies with n_q_heads == n_kv_heads and batch <= 4, PHASED otherwise.
+ * All schedules give identical bits, and every call is deterministic: every
+ * sum has a fixed order.
  */
 typedef enum {
     DAB_SCHEDULE_AUTO = 0,
-    DAB_SCHEDULE_PHASED = 1
+    DAB_SCHEDULE_PHASED = 1,
+    DAB_SCHEDULE_ATTN_OPROJ = 2,
+    DAB_SCHEDULE_QKV_ATTN = 3
 } dab_schedule;
 
 /*
  * Bytes of device workspace one call with this configuration needs (0 when
  * the configuration is invalid).  The workspace holds q, the new k and v,
- * the split-KV partials, arrival counters and the device error flag.  It must be initialised once
- * with dab_workspace_init; every call leaves its counters at zero again, so
- * it can be reused by later calls (on one stream at a time) without
- * re-initialising.
+ * the split-KV partials, arrival counters and the device error flag.  It must
+ * be initialised with dab_workspace_init before its first call; every call
+ * re-arms the counters it uses, so later calls with the SAME configuration
+ * (on one stream at a time) reuse it as is.  The layout depends on the
+ * configuration: before a call with another configuration, initialise it
+ * again.
  */
 size_t dab_workspace_size(const dab_config* cfg);
 
@@ -130,7 +144,8 @@ dab_status dab_workspace_init(void* workspace, size_t bytes, void* stream);
  *                                not overlap any other argument
  *   dbg_y    [B, H] fp32 or NULL the pre-residual a @ W_o in fp32 (a test tap)
  *   workspace, workspace_bytes   device scratch of at least dab_workspace_size
- *                                bytes, initialised once by dab_workspace_init
+ *                                bytes, initialised by dab_workspace_init for
+ *                                this configuration (see dab_workspace_size)
  */
 dab_status dab_decode_attn_block(const dab_config* cfg,
                                  const void* hidden, const void* norm_w,
@@ -163,6 +178,9 @@ const char* dab_phase_name(const dab_config* cfg, int i);
 /*
  * Copy the workspace's sticky device error flag to *flag (host pointer) and
  * clear it.  Synchronises `stream`.  Bit 0: some pos[b] was outside [0, cap).
+ * Bit 1: a workgroup of a one-launch schedule gave up waiting for its
+ * inputs (a bounded wait that cannot expire in a correct run; results are
+ * invalid).
  */
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag);
 

@@ -77,18 +77,45 @@ def test_workspace_size_valid(lib):
         b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual", None]
 
 
+PHASED = [b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual"]
+ATTN_OPROJ = [b"qkv_rmsnorm_rope_append", b"attention_oproj_residual"]
+QKV_ATTN = [b"qkv_attention_split_kv", b"oproj_residual"]
+
+
+def names(lib, c):
+    return [lib.dab_phase_name(ctypes.byref(c), i) for i in range(lib.dab_phase_count(ctypes.byref(c)))]
+
+
 def test_schedule_selection(lib):
-    # auto and phased both resolve to one kernel per phase; other values are rejected
-    for sched in (0, 1):
-        c = cfg(n_q_heads=6, n_kv_heads=2, schedule=sched)
-        assert [lib.dab_phase_name(ctypes.byref(c), i) for i in range(3)] == [
-            b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual"]
-    for bad in (-1, 2, 3, 7):
+    # a group of 3, or projections that are not whole K-blocks: auto is phased, one-launch schedules unsupported
+    for c in (cfg(n_q_heads=6, n_kv_heads=2), cfg()):
+        assert names(lib, c) == PHASED
+        for sched in (2, 3):
+            c.schedule = sched
+            assert call(lib, c) == _lib.DAB_ERR_UNSUPPORTED
+            assert lib.dab_phase_count(ctypes.byref(c)) == 0
+    for bad in (-1, 4, 7):
         assert lib.dab_workspace_size(ctypes.byref(cfg(schedule=bad))) == 0
         assert call(lib, cfg(schedule=bad)) == _lib.DAB_ERR_INVALID_ARG
-    head = cfg(batch=1, hidden=4096, n_q_heads=32, n_kv_heads=32, head_dim=128, cache_capacity=4097,
-               dtype=_lib.DAB_BF16)
-    assert lib.dab_phase_count(ctypes.byref(head)) == 3
+    # the 7B layer: auto takes attention + projection in one launch; every schedule is available
+    head = dict(batch=1, hidden=4096, n_q_heads=32, n_kv_heads=32, head_dim=128, cache_capacity=4097,
+                dtype=_lib.DAB_BF16)
+    assert names(lib, cfg(**head)) == ATTN_OPROJ
+    assert names(lib, cfg(**head, schedule=1)) == PHASED
+    assert names(lib, cfg(**head, schedule=2)) == ATTN_OPROJ
+    assert names(lib, cfg(**head, schedule=3)) == QKV_ATTN
+    assert lib.dab_phase_name(ctypes.byref(cfg(**head)), 2) is None
+    # grouped heads, or batch above 4: auto stays phased
+    assert names(lib, cfg(**{**head, "n_kv_heads": 8})) == PHASED
+    assert names(lib, cfg(**{**head, "batch": 5})) == PHASED
+    assert names(lib, cfg(**{**head, "batch": 4})) == ATTN_OPROJ
+    # fp32: K a multiple of 2048 -- nq * D for attention + projection, H for QKV + attention
+    assert names(lib, cfg(n_q_heads=16, n_kv_heads=16, head_dim=128)) == ATTN_OPROJ
+    assert names(lib, cfg(n_q_heads=16, n_kv_heads=4, head_dim=128)) == PHASED
+    assert names(lib, cfg(n_q_heads=16, n_kv_heads=4, head_dim=128, schedule=2)) == ATTN_OPROJ
+    assert call(lib, cfg(n_q_heads=16, n_kv_heads=4, head_dim=128, schedule=3)) == _lib.DAB_ERR_UNSUPPORTED
+    assert names(lib, cfg(hidden=2048, schedule=3)) == QKV_ATTN
+    assert call(lib, cfg(hidden=2048, schedule=2)) == _lib.DAB_ERR_UNSUPPORTED
 
 
 def test_gemv_width_limits(lib):

@@ -42,10 +42,38 @@ def parity_case(cfg: BlockConfig, seed: int, *, cap=None, pos=None, kv_chunk=0, 
 # the workload configurations, full size
 # ---------------------------------------------------------------------------
 
+SCHEDULES = ["phased", "attn_oproj", "qkv_attn"]
+
+
+def applies(cfg: BlockConfig, schedule: str) -> bool:
+    """The one-launch kernels are built for groups 1, 2, 4, 8 and a projection of whole K-blocks (a
+    multiple of 4096 bf16 / 2048 fp32 values): the output projection's K = nq * D for attn_oproj, the
+    QKV projection's K = H for qkv_attn."""
+    if schedule in ("auto", "phased"):
+        return True
+    kblock = 4096 if cfg.dtype == "bf16" else 2048
+    k = cfg.n_q_heads * cfg.head_dim if schedule == "attn_oproj" else cfg.hidden
+    return cfg.group in (1, 2, 4, 8) and k % kblock == 0
+
+
+@pytest.mark.parametrize("schedule", ["auto"] + SCHEDULES)
 @pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("name", list(CONFIGS))
-def test_config_parity(name, seed):
-    parity_case(CONFIGS[name], seed)
+def test_config_parity(name, seed, schedule):
+    if not applies(CONFIGS[name], schedule):
+        pytest.skip(f"{schedule} is not built for this shape")
+    parity_case(CONFIGS[name], seed, schedule=schedule)
+
+
+def test_auto_takes_attn_oproj_for_mha_at_small_batch():
+    import attention_block_amd as ab
+    for name, cfg in CONFIGS.items():
+        c = ab.make_config(batch=cfg.batch, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                           head_dim=cfg.head_dim, cache_capacity=8193, dtype=cfg.dtype, rope_theta=cfg.rope_theta)
+        fused = applies(cfg, "attn_oproj") and cfg.group == 1 and cfg.batch <= 4
+        want = ["qkv_rmsnorm_rope_append", "attention_oproj_residual"] if fused else \
+            ["qkv_rmsnorm_rope_append", "attention_split_kv", "oproj_residual"]
+        assert ab.phase_names(c) == want, name
 
 
 # ---------------------------------------------------------------------------
@@ -70,6 +98,62 @@ EDGE = [
 @pytest.mark.parametrize("label,cfg,cap,pos,kv_chunk", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_parity(label, cfg, cap, pos, kv_chunk):
     parity_case(cfg, 7, cap=cap, pos=pos, kv_chunk=kv_chunk, label=label)
+
+
+# shapes the one-launch kernels are built for, at small sizes
+EDGE_ONE_LAUNCH = [
+    ("mha f32", small_cfg("o1", 1, 256, 16, 16, 128, "f32"), 300, [299], 0),
+    ("gqa f32 empty history", small_cfg("o2", 3, 512, 32, 8, 64, "f32", 5e5), 130, [0, 129, 64], 64),
+    ("bf16 group 2 ragged", small_cfg("o3", 5, 512, 32, 16, 128, "bf16", 5e5), 700, [699, 1, 350, 64, 500], 0),
+    ("bf16 group 8 batch 9", small_cfg("o4", 9, 1024, 64, 8, 64, "bf16"), 200, list(range(3, 200, 22)), 32),
+    ("f32 H 2048 gqa ragged", small_cfg("o5", 3, 2048, 16, 4, 128, "f32", 5e5), 300, [299, 0, 150], 0),
+    ("bf16 H 4096 batch 6", small_cfg("o6", 6, 4096, 32, 8, 128, "bf16", 5e5), 260, [259, 3, 128, 0, 200, 64], 0),
+    ("f32 H 2048 d64 group 1", small_cfg("o7", 2, 2048, 32, 32, 64, "f32"), 90, [89, 17], 32),
+]
+ONE_LAUNCH_CASES = [(sched, *e) for e in EDGE_ONE_LAUNCH for sched in ("attn_oproj", "qkv_attn")
+                    if applies(e[1], sched)]
+
+
+@pytest.mark.parametrize("schedule,label,cfg,cap,pos,kv_chunk", ONE_LAUNCH_CASES,
+                         ids=[f"{c[0]}: {c[1]}" for c in ONE_LAUNCH_CASES])
+def test_edge_parity_one_launch(schedule, label, cfg, cap, pos, kv_chunk):
+    parity_case(cfg, 7, cap=cap, pos=pos, kv_chunk=kv_chunk, label=label, schedule=schedule)
+
+
+def test_one_launch_edge_cases_cover_both_schedules():
+    assert {c[0] for c in ONE_LAUNCH_CASES} == {"attn_oproj", "qkv_attn"}
+    assert sum(c[0] == "qkv_attn" for c in ONE_LAUNCH_CASES) >= 3
+
+
+def test_default_workspaces_follow_the_configuration():
+    """Counters sit where the configuration puts them: a call with a second configuration must not see
+    the counters a first one left (here the first one's merge counters lie where the second one's
+    chunk-arrival counters for its last sequence go)."""
+    first, second = EDGE_ONE_LAUNCH[1], EDGE_ONE_LAUNCH[2]
+    for label, cfg, cap, pos, kv_chunk in (first, second, first, second):
+        parity_case(cfg, 3, cap=cap, pos=pos, kv_chunk=kv_chunk, label="workspace reuse: " + label,
+                    schedule="attn_oproj")
+
+
+SAME_BITS = EDGE_ONE_LAUNCH[1:] + [("7B 4K", CONFIGS["llama2_7b_bs1_4k"], None, None, 0)]
+
+
+@pytest.mark.parametrize("label,cfg,cap,pos,kv_chunk", SAME_BITS, ids=[e[0] for e in SAME_BITS])
+def test_schedules_give_identical_bits(label, cfg, cap, pos, kv_chunk):
+    """Every schedule runs the same arithmetic in the same order: identical out, y and caches."""
+    import torch
+    inp = make_inputs(cfg, 21, cap=cap, pos=pos)
+    scheds = [s for s in SCHEDULES if applies(cfg, s)]
+    say(f"[schedules] {label}: {scheds}")
+    res = {}
+    bits = torch.int16 if cfg.dtype == "bf16" else torch.int32
+    for sched in scheds:
+        dev = to_device(inp)
+        out, dbg = run_gpu(dev, cfg, kv_chunk=kv_chunk, schedule=sched)
+        res[sched] = (out.view(bits), dbg, dev["k_cache"].view(bits), dev["v_cache"].view(bits))
+    for sched in scheds[1:]:
+        for i in range(4):
+            assert torch.equal(res[sched][i], res["phased"][i]), (sched, i)
 
 
 BATCH_INVARIANCE = [
@@ -161,10 +245,11 @@ def test_workspace_counters_return_to_zero():
     assert np.all(raw == 0)
 
 
-def test_bad_position_sets_flag_and_skips_sequence():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_bad_position_sets_flag_and_skips_sequence(schedule):
     import torch
     import attention_block_amd as ab
-    cfg = small_cfg("badpos", 3, 256, 4, 2, 64, "f32")
+    cfg = small_cfg("badpos", 3, 2048, 16, 4, 128, "f32")     # H = nq * D = 2048: every schedule applies
     inp = make_inputs(cfg, 4, cap=40, pos=[10, 20, 30])
     dev = to_device(inp)
     dev["pos"][1] = 40                                 # == cap: out of range, seen only on the device
@@ -173,7 +258,7 @@ def test_bad_position_sets_flag_and_skips_sequence():
     say("[bad pos] sequence 1 at pos == cap")
     ab.read_device_error()                             # clear any earlier flag
     ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"], dev["v_cache"],
-                         dev["pos"], cfg.rope_theta, cfg.eps, out=out)
+                         dev["pos"], cfg.rope_theta, cfg.eps, out=out, schedule=schedule)
     flag = ab.read_device_error()
     assert flag == 1
     assert torch.all(out[1] == 12345.0)               # its output row was left unwritten
@@ -187,31 +272,34 @@ def test_bad_position_sets_flag_and_skips_sequence():
     assert ab.read_device_error() == 0                 # reading cleared it
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_graph_replay_matches_eager(schedule):
     import torch
     import attention_block_amd as ab
-    cfg = small_cfg("graph", 2, 512, 8, 2, 128, "bf16", 5e5)
+    cfg = small_cfg("graph", 2, 4096, 32, 8, 128, "bf16", 5e5)   # H = nq * D = 4096: every schedule applies
     inp = make_inputs(cfg, 9, cap=700, pos=[699, 333])
     dev = to_device(inp)
-    say("[graph] eager, capture, 4 replays")
-    eager, _ = run_gpu(dev, cfg)
+    say(f"[graph] {schedule}: eager, capture, 4 replays")
+    eager, _ = run_gpu(dev, cfg, schedule=schedule)
     eager = eager.clone()
     out = torch.empty_like(dev["hidden"])
-    c = ab.make_config(batch=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, cache_capacity=700,
-                       dtype="bf16", rope_theta=5e5)
+    c = ab.make_config(batch=2, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, cache_capacity=700,
+                       dtype="bf16", rope_theta=5e5, schedule=schedule)
     ws = ab.Workspace(ab.workspace_size(c), dev["hidden"].device)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):  # warm-up call outside capture
         ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
-                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws)
+                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws,
+                             schedule=schedule)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
-                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws)
+                             dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws,
+                             schedule=schedule)
     for i in range(4):
         out.zero_()
         torch.cuda.synchronize()
