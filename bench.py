@@ -19,9 +19,11 @@ baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -36,6 +38,36 @@ from attention_block_amd.inputs import (CONFIGS, HEADLINE, BlockConfig, algorith
 METRIC = "µs per decode block step and achieved HBM GB/s (% of peak), 7B layer bs1 4K"
 PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 1024 * 1024
+PROFILES = os.path.join(HERE, "profiles")
+
+
+def source_digest() -> str:
+    """Digest of the library's kernel sources; a counter summary is only used for the sources it was taken on."""
+    csrc = os.path.join(HERE, "attention_block_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE summary, or None when
+    there is none or it was taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"pmc_traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^- (\w+): `?([^`\s]+)`?$", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("source_digest") != source_digest():
+        return None
+    return int(fields["hbm_bytes_per_launch"])
 
 
 def phase_bytes(cfg: BlockConfig, pos) -> dict:
@@ -114,6 +146,95 @@ def cpu_baseline(cfg: BlockConfig, seed: int, budget_s: float) -> dict:
                       f"bf16->fp64 upcast outside the timing"}
 
 
+# kernel function names (as rocprofv3 reports them) -> phase names of the C ABI
+KERNEL_PHASES = [("qkv_attn_kernel", "qkv_attention_split_kv"), ("attn_oproj_kernel", "attention_oproj_residual"),
+                 ("qkv_kernel", "qkv_rmsnorm_rope_append"), ("attn_kernel", "attention_split_kv"),
+                 ("oproj_kernel", "oproj_residual")]
+
+
+def phase_of(kernel_name: str):
+    fn = kernel_name.split("(")[0].split("<")[0].split("::")[-1]
+    for k, ph in KERNEL_PHASES:
+        if fn == k:
+            return ph
+    return None
+
+
+def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
+                       commands: list) -> list:
+    """Write the rocprofv3 summaries under profiles/: the kernel-trace statistics of the library's kernels,
+    and per kernel the HBM bytes of one launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the counter reads for the copy probe (copy_mib MiB read and written)."""
+    import csv
+    cfg = CONFIGS[workload]
+    pos = positions(cfg, 0)
+    pb = phase_bytes(cfg, pos)
+    digest = source_digest()
+    written = []
+
+    stats = [r for r in csv.DictReader(open(os.path.join(kt_dir, "run_kernel_stats.csv"))) if phase_of(r["Name"])]
+    lines = [f"# rocprofv3 kernel trace: {workload}", "",
+             "Commands (from /tmp with TMPDIR=/tmp; R = the repository root):", ""]
+    lines += [f"    {c}" for c in commands if "--kernel-trace" in c or "--summarize-profiles" in c]
+    lines += ["", "| phase | kernel | calls | average us | min us | max us | algorithmic bytes | GB/s at average |",
+              "|---|---|---|---|---|---|---|---|"]
+    for r in stats:
+        ph = phase_of(r["Name"])
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"| {ph} | `{r['Name'].split('(')[0]}` | {r['Calls']} | {avg:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {pb[ph]} | "
+                     f"{pb[ph] / (avg * 1e-6) / 1e9:.1f} |")
+    lines += ["", "bench.py times each kernel between HIP events recorded on its stream, back to back in an eager "
+              "queue; that interval also holds the dispatch gap before the kernel, so it reads a few "
+              "microseconds above the kernel's own duration here.", "",
+              f"- source_digest: `{digest}`"]
+    path = os.path.join(PROFILES, f"kernel_trace_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    written.append(path)
+
+    def counters(d, counter):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        rows = [r for r in rows if r["Counter_Name"] == counter]
+        probe = [r for r in rows if "neg_kernel" in r["Kernel_Name"]]
+        assert len(probe) == 1, f"expected one copy probe dispatch in {d}"
+        per = {}
+        for r in rows:
+            ph = phase_of(r["Kernel_Name"])
+            if ph:
+                per.setdefault(ph, []).append(float(r["Counter_Value"]))
+        return per, float(probe[0]["Counter_Value"])
+
+    fetch, fetch_probe = counters(fetch_dir, "FETCH_SIZE")
+    write, write_probe = counters(write_dir, "WRITE_SIZE")
+    probe_kib = copy_mib * 1024.0
+    f_scale, w_scale = probe_kib / fetch_probe, probe_kib / write_probe
+    for ph in fetch:
+        fk, wk = float(np.mean(fetch[ph])), float(np.mean(write[ph]))
+        fb, wb = fk * f_scale * 1024, wk * w_scale * 1024
+        total = int(round(fb + wb))
+        lines = [f"# HBM traffic of {ph}: {workload}", "",
+                 "Counter runs (each its own rocprofv3 pass; from /tmp with TMPDIR=/tmp; R = the repository root):",
+                 ""]
+        lines += [f"    {c}" for c in commands if "--pmc" in c or "--summarize-profiles" in c]
+        lines += ["",
+                  f"Copy probe: one elementwise copy of {copy_mib} MiB ({probe_kib:.0f} KiB read, {probe_kib:.0f} KiB "
+                  f"written) reads FETCH_SIZE {fetch_probe:.1f} KiB and WRITE_SIZE {write_probe:.1f} KiB, so the "
+                  f"counters are scaled by {f_scale:.5f} (fetch) and {w_scale:.5f} (write).", "",
+                  "| counter | dispatches | KiB per dispatch (mean) | scale | bytes per launch |", "|---|---|---|---|---|",
+                  f"| FETCH_SIZE | {len(fetch[ph])} | {fk:.2f} | {f_scale:.5f} | {fb:.0f} |",
+                  f"| WRITE_SIZE | {len(write[ph])} | {wk:.2f} | {w_scale:.5f} | {wb:.0f} |", "",
+                  f"Measured HBM traffic per launch is {total / pb[ph]:.4f} x the algorithmic bytes.", "",
+                  f"- hbm_bytes_per_launch: `{total}`",
+                  f"- algorithmic_bytes_per_launch: `{pb[ph]}`",
+                  f"- source_digest: `{digest}`"]
+        path = os.path.join(PROFILES, f"pmc_traffic_{ph}_{workload}.md")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        written.append(path)
+    return written
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,7 +247,22 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="turn rocprofv3 csv output (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass of a "
+                         "--copy-probe-mb run) into the summaries under profiles/; no GPU needed")
+    ap.add_argument("--commands", default="", help="with --summarize-profiles: the commands that made the "
+                                                     "output, separated by ';', recorded in the summaries")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run one elementwise copy of this many MiB (fp32 in, fp32 out): the "
+                         "reference kernel of known size for the FETCH_SIZE / WRITE_SIZE counter runs")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        kt, fd, wd = args.summarize_profiles
+        cmds = [c.strip() for c in args.commands.split(";") if c.strip()]
+        for p in summarize_profiles(kt, fd, wd, args.config, args.copy_probe_mb or 256, cmds):
+            print("wrote", os.path.relpath(p, HERE))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode block runs on a single MI355X here "
@@ -241,10 +377,19 @@ def main() -> int:
         k = phases.index(dom)
         ach = pb[dom] / (phase_us[k] * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_GBPS, 4), "traffic": None, "kernel": dom,
+                    "frac": round(ach / PEAK_GBPS, 4), "traffic": measured_traffic(dom, cfg.name), "kernel": dom,
                     "bytes_per_launch": pb[dom], "avg_launch_us": round(phase_us[k], 3)}
         phase_report = {n: {"us": round(phase_us[i], 3), "bytes": pb[n],
                             "gbps": round(pb[n] / (phase_us[i] * 1e-6) / 1e9, 1)} for i, n in enumerate(phases)}
+
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"copy probe: {n * 4} bytes read, {n * 4} bytes written", file=sys.stderr)
 
     cpu = None
     if not args.no_cpu_baseline:
