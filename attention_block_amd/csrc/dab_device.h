@@ -229,28 +229,39 @@ __device__ inline bool pos_valid(const StepArgs& a, int b, int* p_out) {
 // ---------------------------------------------------------------------------
 //
 // LPR = D/8 lanes hold one token row (8 elements each); the workgroup's
-// 256/LPR row slots take tokens slot, slot + NSLOT, ...; U tokens per slot
-// are loaded per batch (16 loads of 16 bytes in flight per lane).  Scores
-// are kept in log2 units (q is pre-scaled by log2(e)/sqrt(D)), so every
-// exponential is an exp2.  The new token never comes from the cache: its
-// k and v are taken from the fp32 workspace copy the QKV kernel wrote,
-// rounded to the storage type exactly as the appended row.
+// NSLOT = 256/LPR row slots each take U tokens of a buffer of HB = NSLOT * U
+// tokens.  With grouped heads two half-batch buffers are in flight, the next
+// requested before the current one is used, so a chunk of many half-batches
+// streams without a round trip between them (see AttnGeom).  Scores are kept in log2 units (q is
+// pre-scaled by log2(e)/sqrt(D)), so every exponential is an exp2.  The new
+// token never comes from the cache: its k and v are taken from the fp32
+// workspace copy the QKV kernel wrote, rounded to the storage type exactly
+// as the appended row.
 
 template <int D, int G>
 struct AttnShared {
     float m[4][G], l[4][G];
     float o[4][G][D];
-    float cm[kMaxChunks], cw[kMaxChunks];
-    float red[8];
-    float acc[256];
+    float w[G][kMaxChunks];      // merge: chunk maxima, then their weights exp2(m - M)
+    float cl[G][kMaxChunks];     // merge: chunk sums
+    float red[4][G];
+    float L[G];
+    float acc[256 / D][G * D];   // merge: per-part weighted sums
 };
 
-template <int D>
+template <int D, int G>
 struct AttnGeom {
     static constexpr int LPR = D / 8;
     static constexpr int NSLOT = 256 / LPR;
-    static constexpr int U = 8;
-    static constexpr int BATCH = NSLOT * U;   // tokens per batch of loads (128 for D=128)
+    // One query head per kv head: one buffer of 8 tokens per slot, loaded,
+    // used, then the next loaded (a 7B-sized step's chunks are one such
+    // batch, and the single copy of the loop body measured faster there).
+    // Grouped heads: two half-batch buffers of 4 tokens per slot (2 with
+    // four or more heads, whose scores and accumulators take the
+    // registers), the next requested before the current one is used.
+    static constexpr bool PIPE = G > 1;
+    static constexpr int U = G == 1 ? 8 : G >= 4 ? 2 : 4;
+    static constexpr int HB = NSLOT * U;      // tokens per buffer (128 for D = 128, G = 1)
 };
 
 // 8 consecutive fp32 values of the workspace (32-byte aligned).  COHERENT:
@@ -277,8 +288,8 @@ __device__ inline void load8(const float* p, float* f) {
 // heads is done, then read q and the new k, v device-coherently.
 template <typename T, int D, int G, bool PUBLISH, bool WAITQ>
 __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, G>& sm, int* s_flag) {
-    using Geo = AttnGeom<D>;
-    constexpr int LPR = Geo::LPR, NSLOT = Geo::NSLOT, U = Geo::U;
+    using Geo = AttnGeom<D, G>;
+    constexpr int LPR = Geo::LPR, NSLOT = Geo::NSLOT, U = Geo::U, HB = Geo::HB;
     const int nkv = a.nkv;
     int p;
     if (!pos_valid(a, b, &p)) return;
@@ -288,6 +299,7 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     const int t0 = c * a.T;
     const int t1 = min(t0 + a.T, p);
     const bool has_new = c == nchunk - 1;
+    const int nhb = (t1 - t0 + HB - 1) / HB;          // buffers of HB tokens (0 when there is no history)
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int slot = t / LPR, l = t % LPR;
@@ -296,12 +308,12 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     const T* Kp = static_cast<const T*>(a.k_cache) + base;
     const T* Vp = static_cast<const T*>(a.v_cache) + base;
 
-    // 1. first batch of history rows in flight
-    Vec8<T> kr[U], vr[U];
-    auto issue = [&](int tb) {
+    // 1. the first buffer(s) of history rows in flight
+    Vec8<T> kA[U], vA[U], kB[U], vB[U];
+    auto issue = [&](Vec8<T> (&kr)[U], Vec8<T> (&vr)[U], int hb0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int tok = tb + NSLOT * u;
+            const int tok = hb0 + slot + NSLOT * u;
             if (tok < t1) {
                 kr[u].load(Kp + (size_t)tok * row);
                 vr[u].load(Vp + (size_t)tok * row);
@@ -311,7 +323,8 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
             }
         }
     };
-    issue(t0 + slot);
+    issue(kA, vA, t0);
+    if constexpr (Geo::PIPE) issue(kB, vB, t0 + HB);
     DAB_TRACE_POINT(a, 1);
 
     // 2. q of this group's heads, in log2 units
@@ -342,7 +355,8 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
         for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
     }
 
-    // online-softmax update of this slot's state with n scores / value rows
+    // online-softmax update of this slot's state with its first nvalid
+    // scores / value rows (nvalid >= 1)
     auto absorb = [&](float (&s)[G][U], Vec8<T> (&vv)[U], int nvalid) {
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -374,8 +388,10 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
         }
     };
 
-    for (int tb = t0 + slot; tb < t1; tb += NSLOT * U) {
-        if (tb != t0 + slot) issue(tb);
+    // scores of one buffer starting at token hb0, then the update; every
+    // lane of the workgroup runs it (the trip count is uniform), the lanes of
+    // a slot agree on how many of its tokens are valid
+    auto process = [&](Vec8<T> (&kr)[U], Vec8<T> (&vr)[U], int hb0) {
         float s[G][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -389,9 +405,25 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
                 s[j][u] = group_sum<LPR>(d);
             }
         }
-        // tokens tb + NSLOT*u < t1 are valid, u = 0 always
-        const int nvalid = min(U, (t1 - tb + NSLOT - 1) / NSLOT);
-        absorb(s, vr, nvalid);
+        const int left = t1 - hb0 - slot;                  // this slot's tokens hb0 + slot + NSLOT*u < t1
+        const int nvalid = left <= 0 ? 0 : min(U, (left + NSLOT - 1) / NSLOT);
+        if (nvalid > 0) absorb(s, vr, nvalid);
+    };
+
+    if constexpr (Geo::PIPE) {
+        for (int k = 0; k < nhb; k += 2) {
+            process(kA, vA, t0 + k * HB);
+            if (k + 2 < nhb) issue(kA, vA, t0 + (k + 2) * HB);
+            if (k + 1 < nhb) {
+                process(kB, vB, t0 + (k + 1) * HB);
+                if (k + 3 < nhb) issue(kB, vB, t0 + (k + 3) * HB);
+            }
+        }
+    } else {
+        for (int k = 0; k < nhb; ++k) {
+            if (k > 0) issue(kA, vA, t0 + k * HB);
+            process(kA, vA, t0 + k * HB);
+        }
     }
 
     // the new token, in slot 0 of the last chunk: its k and v come from the
@@ -470,85 +502,109 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
         }
     }
 
-    // 4. the last chunk of (b, g) merges all chunks.  Each head's chunk
-    // statistics (m, l) and the first OB weighted outputs of every thread
-    // are requested together, so short merges cost one round trip.
+    // 4. the last chunk of (b, g) merges all chunks of all G heads:
+    // statistics first (one request per chunk and head), then the weighted
+    // outputs, every load of a round requested before any is used
     int* cnt = &a.attn_cnt[b * nkv + g];
     if (!arrive_last(cnt, nchunk, s_flag)) return;
     DAB_TRACE_POINT(a, 4);
-    constexpr int PARTS = 256 / D;       // threads per output element
-    constexpr int OB = 16;               // chunks per thread in the first request (32 at D = 128)
+    const size_t pbase = ((size_t)b * a.nq + g * G) * a.maxc;   // head j, chunk cc: pbase + j * maxc + cc
+    // thread (part, d) sums chunks part, part + PARTS, ... of every head, QB
+    // chunks of each head per round (32 loads in flight); the first round is
+    // requested together with the statistics
+    constexpr int PARTS = 256 / D;
+    constexpr int QB = G >= 8 ? 4 : 32 / G;
     const int d = t % D, part = t / D;
+    auto request = [&](int q0, float (&v)[G][QB]) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const int cc = part + (q0 + q) * PARTS;
+                v[j][q] = cc < nchunk ? fetch(a.attn_o + (pbase + (size_t)j * a.maxc + cc) * D + d) : 0.f;
+            }
+    };
+    float ml0[2] = {kNegInf, 0.f};
+    if (t < G * nchunk) {
+        const int j = t / nchunk, cc = t - j * nchunk;
+        fetch2(a.attn_ml + (pbase + (size_t)j * a.maxc + cc) * 2, ml0);
+    }
+    float v0[G][QB];
+    request(0, v0);
+    if (t < G * nchunk) {
+        const int j = t / nchunk, cc = t - j * nchunk;
+        sm.w[j][cc] = ml0[0];
+        sm.cl[j][cc] = ml0[1];
+    }
+    for (int idx = t + 256; idx < G * nchunk; idx += 256) {
+        const int j = idx / nchunk, cc = idx - j * nchunk;
+        float ml[2];
+        fetch2(a.attn_ml + (pbase + (size_t)j * a.maxc + cc) * 2, ml);
+        sm.w[j][cc] = ml[0];
+        sm.cl[j][cc] = ml[1];
+    }
+    __syncthreads();
+    DAB_TRACE_POINT(a, 5);
+    // per head: M = max of the chunk maxima, weights exp2(m - M), L = sum w l
+    float mx[G];
+#pragma unroll
     for (int j = 0; j < G; ++j) {
-        const int h = g * G + j;
-        const size_t pbase = ((size_t)b * a.nq + h) * a.maxc;
-        float m0 = kNegInf, l0 = 0.f;
-        if (t < nchunk) {
-            m0 = fetch(a.attn_ml + (pbase + t) * 2);
-            l0 = fetch(a.attn_ml + (pbase + t) * 2 + 1);
-        }
-        // this thread's chunks part, part + PARTS, ... below nchunk
-        float ov[OB];
+        float v = kNegInf;
+        for (int cc = t; cc < nchunk; cc += 256) v = fmaxf(v, sm.w[j][cc]);
+        mx[j] = wave_max(v);
+        if (lane == 0) sm.red[wave][j] = mx[j];
+    }
+    __syncthreads();
+    float lsum[G];
 #pragma unroll
-        for (int q = 0; q < OB; ++q) {
-            const int cc = part + q * PARTS;
-            ov[q] = cc < nchunk ? fetch(a.attn_o + (pbase + cc) * D + d) : 0.f;
-        }
-        DAB_TRACE_POINT(a, 5);
-        float mloc = m0;
-        if (t < nchunk) {
-            sm.cm[t] = m0;
-            sm.cw[t] = l0;               // l for now, weight below
-        }
-        for (int cc = t + 256; cc < nchunk; cc += 256) {
-            const float mc = fetch(a.attn_ml + (pbase + cc) * 2);
-            sm.cm[cc] = mc;
-            sm.cw[cc] = fetch(a.attn_ml + (pbase + cc) * 2 + 1);
-            mloc = fmaxf(mloc, mc);
-        }
-        mloc = wave_max(mloc);
-        if (lane == 0) sm.red[wave] = mloc;
-        __syncthreads();
-        const float M = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
-        float lloc = 0.f;
+    for (int j = 0; j < G; ++j) {
+        const float M = fmaxf(fmaxf(sm.red[0][j], sm.red[1][j]), fmaxf(sm.red[2][j], sm.red[3][j]));
+        float v = 0.f;
         for (int cc = t; cc < nchunk; cc += 256) {
-            const float w = __builtin_amdgcn_exp2f(sm.cm[cc] - M);
-            lloc += w * sm.cw[cc];
-            sm.cw[cc] = w;
+            const float w = __builtin_amdgcn_exp2f(sm.w[j][cc] - M);   // every chunk has a token: m finite
+            v += w * sm.cl[j][cc];
+            sm.w[j][cc] = w;
         }
-        lloc = wave_sum(lloc);
-        __syncthreads();                 // weights visible; sm.red[0..3] read by everyone
-        if (lane == 0) sm.red[4 + wave] = lloc;
-        float acc = 0.f;
+        lsum[j] = wave_sum(v);
+    }
+    __syncthreads();                     // weights visible, sm.red read by everyone
 #pragma unroll
-        for (int q = 0; q < OB; ++q) {
-            const int cc = part + q * PARTS;
-            if (cc < nchunk) acc += sm.cw[cc] * ov[q];
+    for (int j = 0; j < G; ++j)
+        if (lane == 0) sm.red[wave][j] = lsum[j];
+    // outputs, in fixed chunk order
+    float acc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc[j] = 0.f;
+    for (int q0 = 0; part + q0 * PARTS < nchunk; q0 += QB) {
+        float v[G][QB];
+        if (q0 == 0) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int q = 0; q < QB; ++q) v[j][q] = v0[j][q];
+        } else {
+            request(q0, v);
         }
-        for (int c0 = part + OB * PARTS; c0 < nchunk; c0 += 8 * PARTS) {
-            float v[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int cc = c0 + q * PARTS;
-                v[q] = cc < nchunk ? fetch(a.attn_o + (pbase + cc) * D + d) : 0.f;
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const int cc = part + (q0 + q) * PARTS;
+                if (cc < nchunk) acc[j] += sm.w[j][cc] * v[j][q];
             }
+    }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int cc = c0 + q * PARTS;
-                if (cc < nchunk) acc += sm.cw[cc] * v[q];
-            }
-        }
-        sm.acc[t] = acc;
-        __syncthreads();
-        const float L = sm.red[4] + sm.red[5] + sm.red[6] + sm.red[7];
-        if (t < D) {
-            float tot = 0.f;
+    for (int j = 0; j < G; ++j) sm.acc[part][j * D + d] = acc[j];
+    __syncthreads();
+    for (int idx = t; idx < G * D; idx += 256) {
+        const int j = idx / D;
+        const float L = sm.red[0][j] + sm.red[1][j] + sm.red[2][j] + sm.red[3][j];
+        float tot = 0.f;
 #pragma unroll
-            for (int q = 0; q < PARTS; ++q) tot += sm.acc[q * D + t];
-            if constexpr (PUBLISH) publish(a.a + (size_t)b * a.n_q + (size_t)h * D + t, tot / L);
-            else a.a[(size_t)b * a.n_q + (size_t)h * D + t] = tot / L;
-        }
-        __syncthreads();
+        for (int q = 0; q < PARTS; ++q) tot += sm.acc[q][idx];
+        const size_t ai = (size_t)b * a.n_q + (size_t)g * G * D + idx;   // head g*G + j, dim idx % D
+        if constexpr (PUBLISH) publish(a.a + ai, tot / L);
+        else a.a[ai] = tot / L;
     }
     if constexpr (PUBLISH) {
         // one more kv group of sequence b merged; the last one raises the

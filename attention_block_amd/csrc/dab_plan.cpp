@@ -116,18 +116,24 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
                 : auto_attn_oproj ? DAB_SCHEDULE_ATTN_OPROJ : DAB_SCHEDULE_PHASED;
 
     // split-KV chunk over the cached tokens (at most cap - 1; the new token
-    // rides with the last chunk): about 1024 items per pass over the batch and KV heads (one
-    // wave of resident workgroups, four per CU), chunks of 32..256 tokens in
-    // steps of 16; a chunk count just above a wave boundary would leave a
-    // nearly empty second wave.
+    // rides with the last chunk): about 512 chunks per pass over the batch
+    // and kv heads (two per CU: measured faster than 1024 at 1K and 4K
+    // tokens on the 7B layer, and it leaves slots for the projection in the
+    // one-launch schedule), at most 64 per (sequence, kv head) so that the
+    // merge stays short, in steps of 16 tokens, at least one buffer of loads
+    // (256 / (D/8) row slots x 4 tokens) and at most 512 tokens, which keeps
+    // ragged batches balanced; longer only where the context would need more
+    // than kMaxChunks chunks.
     const int hist = p->cap - 1 > 0 ? p->cap - 1 : 1;
     int T = c.kv_chunk;
     if (T == 0) {
-        const int want = (1024 + B * p->nkv - 1) / (B * p->nkv);     // chunks per sequence and kv head
+        const int half_batch = 256 / (p->D / 8) * 4;
+        int want = ceil_div(512, (long long)B * p->nkv);              // chunks per sequence and kv head
+        if (want > 64) want = 64;
         T = (ceil_div(hist, want) + 15) / 16 * 16;
-        if (T < 32) T = 32;
-        if (T > 256) T = 256;
-        while (ceil_div(hist, T) > kMaxChunks) T += 256;
+        if (T < half_batch) T = half_batch;
+        if (T > 512) T = 512;
+        while (ceil_div(hist, T) > kMaxChunks) T += 512;
     }
     p->kv_chunk = T;
     p->max_chunks = ceil_div(hist, T);

@@ -12,8 +12,9 @@ namespace dab {
 
 // Threads per workgroup of every kernel (four waves).
 constexpr int kThreads = 256;
-// Largest number of split-KV chunks per sequence the merge step stages.
-constexpr int kMaxChunks = 1024;
+// Largest number of split-KV chunks per (sequence, kv head) the merge step
+// stages (the chunk length grows with the context to stay below it).
+constexpr int kMaxChunks = 256;
 // Largest query-head group per KV head the attention kernel keeps in registers.
 constexpr int kMaxGroup = 8;
 // LDS a GEMV workgroup may give its fp32 input rows (nb x K floats).
