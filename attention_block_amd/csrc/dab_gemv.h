@@ -439,5 +439,145 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA panels (bf16, batch >= 8)
+// ---------------------------------------------------------------------------
+//
+// A panel is 16 output rows for 16 sequences, all of K: one
+// v_mfma_f32_16x16x32_bf16 per 32 values of K.  The weight operand comes
+// straight from 16-byte global loads (lane i: row i % 16, K values
+// 8 (i / 16) .. +8 of the step, contiguous in the [N, K] layout); the batch
+// operand is x .* norm_w (QKV) or the attention output (O projection) for
+// sequence i % 16, rounded to bf16; C lane i holds rows 4 (i / 16) + j of
+// sequence i % 16.  The workgroup's kMfmaWaves waves split K; each requests
+// up to kMfmaSteps steps of operands at once (64 KB of weights per
+// workgroup in flight), and the partial tiles are summed through LDS in
+// fixed wave order.  For QKV the 16 rows are 8 RoPE pairs of one head (rows
+// e and e + D/2 at tile rows r and r + 8), so each rotation stays in the
+// tile; the lane work after the sum is the one of the VALU panel.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMfmaWaves = 8;            // waves per workgroup (512 threads)
+constexpr int kMfmaSteps = 8;            // K-steps of 32 requested at once per wave
+
+struct MfmaShared {
+    float c[kMfmaWaves][16][17];   // per-wave partial tiles [row][sequence] (padded)
+    float ss[16][kMfmaWaves];      // QKV: per-sequence sums of x^2, one per wave
+};
+
+template <bool QKV>
+__device__ void mfma_panel(const StepArgs& a, int panel, int bgi, MfmaShared& sm) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int K = QKV ? a.H : a.n_q;
+    const int m = lane & 15, kg = lane >> 4;
+    const int D = a.D, half = D >> 1;
+    // this lane's weight row (tile row m)
+    int hd = 0, e0 = 0, row;
+    if constexpr (QKV) {
+        const int pr0 = panel * 8;                     // first RoPE pair of the tile
+        hd = pr0 / half;
+        e0 = pr0 - hd * half;
+        row = hd * D + e0 + (m & 7) + (m >= 8 ? half : 0);
+    } else {
+        row = panel * 16 + m;
+    }
+    const uint16_t* W = static_cast<const uint16_t*>(QKV ? a.w_qkv : a.w_o) + (size_t)row * K + kg * 8;
+    // this lane's sequence (tile column m)
+    const int b = bgi * 16 + m;
+    int p;
+    const bool live = b < a.B && (QKV || pos_valid(a, b, &p));
+    const uint16_t* X = static_cast<const uint16_t*>(a.hidden) + (size_t)(live ? b : 0) * K + kg * 8;
+    const uint16_t* NW = static_cast<const uint16_t*>(a.norm_w) + kg * 8;
+    const float* AO = a.a + (size_t)(live ? b : 0) * K + kg * 8;
+
+    // this wave's steps: K / (32 kMfmaWaves) of them, in groups of kMfmaSteps
+    const int nsteps = K / (32 * kMfmaWaves), k_begin = wave * nsteps * 32;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float ssq = 0.f;
+    for (int s0 = 0; s0 < nsteps; s0 += kMfmaSteps) {
+        u32x4 w[kMfmaSteps], x[kMfmaSteps], y[kMfmaSteps];   // weights; QKV: x, norm_w; O: a (8 floats)
+#pragma unroll
+        for (int s = 0; s < kMfmaSteps; ++s) {
+            const int k = k_begin + (s0 + s) * 32;
+            const bool in = s0 + s < nsteps;
+            w[s] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + k)) : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (QKV) {
+                x[s] = in && live ? *reinterpret_cast<const u32x4*>(X + k) : u32x4{0u, 0u, 0u, 0u};
+                y[s] = in ? *reinterpret_cast<const u32x4*>(NW + k) : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                x[s] = in && live ? *reinterpret_cast<const u32x4*>(AO + k) : u32x4{0u, 0u, 0u, 0u};
+                y[s] = in && live ? *reinterpret_cast<const u32x4*>(AO + k + 4) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        if (s0 == 0) DAB_TRACE_POINT(a, 1);
+#pragma unroll
+        for (int s = 0; s < kMfmaSteps; ++s) {
+            if (s0 + s >= nsteps) break;
+            bf16x8 av, bv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[2 * i] = __builtin_bit_cast(__bf16, (uint16_t)(w[s][i] & 0xffffu));
+                av[2 * i + 1] = __builtin_bit_cast(__bf16, (uint16_t)(w[s][i] >> 16));
+            }
+            if constexpr (QKV) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = __uint_as_float(x[s][i] << 16), x1 = __uint_as_float(x[s][i] & 0xffff0000u);
+                    const float w0 = __uint_as_float(y[s][i] << 16), w1 = __uint_as_float(y[s][i] & 0xffff0000u);
+                    ssq = fmaf(x0, x0, ssq);
+                    ssq = fmaf(x1, x1, ssq);
+                    bv[2 * i] = (__bf16)(x0 * w0);
+                    bv[2 * i + 1] = (__bf16)(x1 * w1);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bv[i] = (__bf16)__uint_as_float(x[s][i]);
+                    bv[4 + i] = (__bf16)__uint_as_float(y[s][i]);
+                }
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+        }
+    }
+
+    // partial tiles (and sums of x^2) to LDS, summed in wave order
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm.c[wave][4 * kg + j][m] = acc[j];
+    if constexpr (QKV) {
+        ssq += __shfl_xor(ssq, 16);
+        ssq += __shfl_xor(ssq, 32);
+        if (kg == 0) sm.ss[m][wave] = ssq;
+    }
+    __syncthreads();
+    DAB_TRACE_POINT(a, 2);
+    if (t >= 256) return;                        // 16 rows x 16 sequences: the first four waves
+    const int r = t >> 4, n = t & 15;            // tile row, sequence
+    const int bb = bgi * 16 + n;
+    if constexpr (QKV) {
+        // threads of the first 8 rows finish pair (r, r + 8) of sequence n
+        if (r < 8 && bb < a.B) {
+            float u0 = 0.f, u1 = 0.f, ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kMfmaWaves; ++w) {
+                u0 += sm.c[w][r][n];
+                u1 += sm.c[w][r + 8][n];
+                ss[w % 4] += sm.ss[n][w];
+            }
+            qkv_finish<uint16_t, false>(a, panel, r, bb, hd, e0 + r, hd * D + e0 + r, u0, u1, ss);
+        }
+    } else {
+        int pp;
+        if (bb < a.B && pos_valid(a, bb, &pp)) {
+            float y = 0.f;
+#pragma unroll
+            for (int w = 0; w < kMfmaWaves; ++w) y += sm.c[w][r][n];
+            const size_t i = (size_t)bb * a.H + panel * 16 + r;
+            static_cast<uint16_t*>(a.out)[i] = from_f32<uint16_t>(to_f32(static_cast<const uint16_t*>(a.hidden)[i]) + y);
+            if (a.dbg_y) a.dbg_y[i] = y;
+        }
+    }
+}
+
 }  // namespace dev
 }  // namespace dab

@@ -103,6 +103,33 @@ __global__ __launch_bounds__(256) void oproj_kernel(StepArgs a) {
     DAB_TRACE_POINT(a, 3);
 }
 
+// MFMA panels of the phased schedule (bf16, batch >= 8)
+template <bool QKV>
+__global__ __launch_bounds__(64 * kMfmaWaves) void mfma_panel_kernel(StepArgs a) {
+    __shared__ MfmaShared sm;
+    DAB_TRACE_POINT(a, 0);
+    if constexpr (!QKV) {
+        // re-arm the panel counters of a one-launch QKV + attention that ran before
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < a.qkv.nbg * (a.nq + 2 * a.nkv); i += 64 * kMfmaWaves)
+                set_counter(&a.head_cnt[i], 0);
+    }
+    const PanelPlanDev& g = QKV ? a.qkv : a.oproj;
+    int panel, bgi;
+    if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi)) mfma_panel<QKV>(a, panel, bgi, sm);
+    DAB_TRACE_POINT(a, 3);
+}
+
+template <typename T, bool QKV>
+hipError_t launch_mfma(const StepArgs& a, const Plan& p, hipStream_t s) {
+    if constexpr (sizeof(T) != 2) {
+        return hipErrorInvalidValue;               // planned for bf16 only
+    } else {
+        hipLaunchKernelGGL((mfma_panel_kernel<QKV>), dim3((QKV ? p.qkv : p.oproj).grid), dim3(64 * kMfmaWaves), 0, s, a);
+        return hipGetLastError();
+    }
+}
+
 // K is a whole number of PanelDot K-blocks (4096 bf16 or 2048 fp32 values)
 template <typename T>
 inline bool exact_blocks(int K) { return K % PanelDot<T, 1, 1, true>::KB == 0; }
@@ -122,6 +149,7 @@ hipError_t launch_qkv_e(const StepArgs& a, const Plan& p, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_qkv(const StepArgs& a, const Plan& p, hipStream_t s) {
+    if (p.qkv.mfma) return launch_mfma<T, true>(a, p, s);
     return exact_blocks<T>(a.H) ? launch_qkv_e<T, true>(a, p, s) : launch_qkv_e<T, false>(a, p, s);
 }
 
@@ -145,6 +173,7 @@ hipError_t launch_oproj_rw(const StepArgs& a, const Plan& p, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_oproj(const StepArgs& a, const Plan& p, hipStream_t s) {
+    if (p.oproj.mfma) return launch_mfma<T, false>(a, p, s);
     switch (p.oproj.rows_per_wave) {
         case 1: return launch_oproj_rw<T, 1>(a, p, s);
         case 2: return launch_oproj_rw<T, 2>(a, p, s);

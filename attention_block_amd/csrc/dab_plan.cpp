@@ -18,6 +18,7 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 bool plan_panel(int K, int N, int batch, int rpw, PanelPlan* g) {
     g->K = K;
     g->N = N;
+    g->mfma = false;
     g->rows_per_wave = rpw;
     g->rows = 4 * rpw;
     if (N % g->rows != 0) return false;
@@ -29,6 +30,23 @@ bool plan_panel(int K, int N, int batch, int rpw, PanelPlan* g) {
     g->nbg = ceil_div(batch, nb);
     g->grid = g->nbg == 1 ? g->panels : (int)align_up((size_t)g->panels, 8) * g->nbg;
     g->lds = (size_t)nb * K * sizeof(float);
+    return true;
+}
+
+// An MFMA panel: 16 rows x all K for 16 sequences (bf16, K a multiple of
+// 256: eight waves x steps of 32).
+bool plan_mfma_panel(int K, int N, int batch, PanelPlan* g) {
+    if (K % 256 != 0 || N % 16 != 0) return false;
+    g->K = K;
+    g->N = N;
+    g->mfma = true;
+    g->rows_per_wave = 0;
+    g->rows = 16;
+    g->panels = N / 16;
+    g->nb = 16;
+    g->nbg = ceil_div(batch, 16);
+    g->grid = g->nbg == 1 ? g->panels : (int)align_up((size_t)g->panels, 8) * g->nbg;
+    g->lds = 0;
     return true;
 }
 
@@ -86,12 +104,6 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
 
     if (c.schedule < DAB_SCHEDULE_AUTO || c.schedule > DAB_SCHEDULE_QKV_ATTN) return DAB_ERR_INVALID_ARG;
 
-    // QKV: one RoPE pair (rows e and e + D/2 of a head) per wave; output
-    // projection: one row per wave (twice the workgroups for a quarter of
-    // the stream)
-    if (!plan_panel(p->H, p->n_qkv, B, 2, &p->qkv) || !plan_panel(p->n_q, p->H, B, 1, &p->oproj))
-        return DAB_ERR_UNSUPPORTED;
-
     // the one-launch kernels are instantiated for groups 1, 2, 4, 8 and for
     // projections of whole K-blocks (4096 bf16 or 2048 fp32 values): the
     // output projection's K (nq D) for attention + projection, the QKV
@@ -114,6 +126,18 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     const bool auto_attn_oproj = p->attn_oproj_ok && p->G == 1 && B <= 4;
     p->schedule = c.schedule != DAB_SCHEDULE_AUTO ? c.schedule
                 : auto_attn_oproj ? DAB_SCHEDULE_ATTN_OPROJ : DAB_SCHEDULE_PHASED;
+
+    // projections.  VALU panels: QKV with one RoPE pair (rows e and e + D/2
+    // of a head) per wave, the output projection with one row per wave
+    // (twice the workgroups for a quarter of the stream).  In the phased
+    // schedule, bf16 batches of 8 or more take MFMA panels instead (16
+    // sequences per workgroup: the VALU panel holds 4 and would read each
+    // panel of weights once per group of 4).
+    const bool mfma = p->schedule == DAB_SCHEDULE_PHASED && p->dtype == DAB_BF16 && B >= 8;
+    if (!(mfma && plan_mfma_panel(p->H, p->n_qkv, B, &p->qkv)) && !plan_panel(p->H, p->n_qkv, B, 2, &p->qkv))
+        return DAB_ERR_UNSUPPORTED;
+    if (!(mfma && plan_mfma_panel(p->n_q, p->H, B, &p->oproj)) && !plan_panel(p->n_q, p->H, B, 1, &p->oproj))
+        return DAB_ERR_UNSUPPORTED;
 
     // split-KV chunk over the cached tokens (at most cap - 1; the new token
     // rides with the last chunk): about 512 chunks per pass over the batch

@@ -32,6 +32,7 @@ constexpr int kReadyStride = 32;     // ints
 // cross workgroups.
 struct PanelPlan {
     int K = 0, N = 0;
+    bool mfma = false;      // MFMA panels: 16 rows x 16 sequences per workgroup (bf16, batch >= 8)
     int rows_per_wave = 0;  // 1 or 2 (the QKV panel: one RoPE pair per wave)
     int rows = 0;           // 4 * rows_per_wave
     int panels = 0;         // N / rows

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from attention_block_amd.inputs import CONFIGS, BlockConfig, make_inputs
-from gpu_util import check_errs, compare, run_gpu, small_cfg, storage_bits, to_device
+from gpu_util import check_errs, compare, run_gpu, small_cfg, storage_bits, storage_values, tol_for, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +92,11 @@ EDGE = [
     ("batch 9 groups", small_cfg("e8", 9, 512, 4, 4, 128, "bf16"), 130, list(range(0, 129, 16)), 64),
     ("fp32 d128 gqa", small_cfg("e9", 3, 512, 8, 2, 128, "f32", 5e5), 1100, [1099, 512, 3], 0),
     ("many chunks", small_cfg("e10", 1, 256, 2, 1, 128, "bf16"), 4097 * 2, [8000], 64),
+    # bf16 batches of 8 or more with K a multiple of 1024 take the MFMA panels
+    ("mfma batch 9, one padded tile", small_cfg("m1", 9, 1024, 8, 2, 128, "bf16", 5e5), 300,
+     [299, 0, 17, 256, 1, 128, 64, 200, 33], 0),
+    ("mfma batch 20, two tiles", small_cfg("m2", 20, 2048, 16, 4, 128, "bf16"), 130, list(range(3, 130, 6))[:20], 0),
+    ("mfma d64 group 8", small_cfg("m3", 8, 1024, 16, 2, 64, "bf16", 5e5), 90, [89, 0, 5, 64, 33, 80, 12, 1], 32),
 ]
 
 
@@ -140,10 +145,14 @@ SAME_BITS = EDGE_ONE_LAUNCH[1:] + [("7B 4K", CONFIGS["llama2_7b_bs1_4k"], None, 
 
 @pytest.mark.parametrize("label,cfg,cap,pos,kv_chunk", SAME_BITS, ids=[e[0] for e in SAME_BITS])
 def test_schedules_give_identical_bits(label, cfg, cap, pos, kv_chunk):
-    """Every schedule runs the same arithmetic in the same order: identical out, y and caches."""
+    """Every schedule runs the same arithmetic in the same order: identical out, y and caches.  (Except
+    that bf16 batches of 8 or more take MFMA panels in the phased schedule, which round the projection
+    inputs to bf16; there only the one-launch schedules are compared with each other.)"""
     import torch
     inp = make_inputs(cfg, 21, cap=cap, pos=pos)
     scheds = [s for s in SCHEDULES if applies(cfg, s)]
+    if cfg.dtype == "bf16" and cfg.batch >= 8:
+        scheds.remove("phased")
     say(f"[schedules] {label}: {scheds}")
     res = {}
     bits = torch.int16 if cfg.dtype == "bf16" else torch.int32
@@ -153,7 +162,7 @@ def test_schedules_give_identical_bits(label, cfg, cap, pos, kv_chunk):
         res[sched] = (out.view(bits), dbg, dev["k_cache"].view(bits), dev["v_cache"].view(bits))
     for sched in scheds[1:]:
         for i in range(4):
-            assert torch.equal(res[sched][i], res["phased"][i]), (sched, i)
+            assert torch.equal(res[sched][i], res[scheds[0]][i]), (sched, scheds[0], i)
 
 
 BATCH_INVARIANCE = [
@@ -166,7 +175,9 @@ BATCH_INVARIANCE = [
 @pytest.mark.parametrize("cfg", BATCH_INVARIANCE, ids=[c.name for c in BATCH_INVARIANCE])
 def test_sequence_alone_matches_its_batch(cfg):
     """Every sum of a sequence runs in one fixed order whatever batch group it lands in, so (at a fixed
-    KV chunk) a sequence run alone gives the same bits as inside its batch: out, y and the appended rows."""
+    KV chunk) a sequence run alone gives the same bits as inside its batch: out, y and the appended rows.
+    (Batches below 8, where both calls take the VALU panels; bf16 batches of 8 or more take MFMA panels,
+    which round their inputs to bf16.)"""
     import torch
     pos = [(37 * b + 300) % 700 for b in range(cfg.batch)]
     inp = make_inputs(cfg, 13, cap=701, pos=pos)
@@ -245,12 +256,15 @@ def test_workspace_counters_return_to_zero():
     assert np.all(raw == 0)
 
 
-@pytest.mark.parametrize("schedule", SCHEDULES)
-def test_bad_position_sets_flag_and_skips_sequence(schedule):
+BAD_POS = [(sched, small_cfg("badpos", 3, 2048, 16, 4, 128, "f32")) for sched in SCHEDULES] + [
+    ("phased", small_cfg("badpos_mfma", 8, 1024, 8, 2, 128, "bf16"))]       # MFMA panels
+
+
+@pytest.mark.parametrize("schedule,cfg", BAD_POS, ids=[f"{s}-{c.name}" for s, c in BAD_POS])
+def test_bad_position_sets_flag_and_skips_sequence(schedule, cfg):
     import torch
     import attention_block_amd as ab
-    cfg = small_cfg("badpos", 3, 2048, 16, 4, 128, "f32")     # H = nq * D = 2048: every schedule applies
-    inp = make_inputs(cfg, 4, cap=40, pos=[10, 20, 30])
+    inp = make_inputs(cfg, 4, cap=40, pos=[10 + 3 * b for b in range(cfg.batch)])
     dev = to_device(inp)
     dev["pos"][1] = 40                                 # == cap: out of range, seen only on the device
     before = (storage_bits(dev["k_cache"]), storage_bits(dev["v_cache"]))
@@ -265,10 +279,11 @@ def test_bad_position_sets_flag_and_skips_sequence(schedule):
     kb, vb = storage_bits(dev["k_cache"]), storage_bits(dev["v_cache"])
     assert np.array_equal(kb[1], before[0][1]) and np.array_equal(vb[1], before[1][1])
     # the other sequences are still right
-    ref = oracle.decode_step_from_inputs({**inp, "pos": np.array([10, 20, 30])})
-    got = out.cpu().numpy().astype(np.float64)
-    for b in (0, 2):
-        assert np.linalg.norm(got[b] - ref["out"][b]) / np.linalg.norm(ref["out"][b]) < 1e-5
+    ref = oracle.decode_step_from_inputs(inp)
+    got = storage_values(out)
+    for b in range(cfg.batch):
+        if b != 1:
+            assert np.linalg.norm(got[b] - ref["out"][b]) / np.linalg.norm(ref["out"][b]) < tol_for(cfg.dtype), b
     assert ab.read_device_error() == 0                 # reading cleared it
 
 
