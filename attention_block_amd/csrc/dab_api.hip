@@ -71,6 +71,7 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.attn_o = f(p.off_attn_o);
     a.attn_ml = f(p.off_attn_ml);
     a.a = f(p.off_a);
+    a.a16 = reinterpret_cast<uint16_t*>(ws + p.off_a16);
     a.B = p.B;
     a.H = p.H;
     a.nq = p.nq;

@@ -603,8 +603,12 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
 #pragma unroll
         for (int q = 0; q < PARTS; ++q) tot += sm.acc[q][idx];
         const size_t ai = (size_t)b * a.n_q + (size_t)g * G * D + idx;   // head g*G + j, dim idx % D
-        if constexpr (PUBLISH) publish(a.a + ai, tot / L);
-        else a.a[ai] = tot / L;
+        if constexpr (PUBLISH) {
+            publish(a.a + ai, tot / L);
+        } else {
+            a.a[ai] = tot / L;
+            if constexpr (sizeof(T) == 2) a.a16[ai] = from_f32<uint16_t>(tot / L);   // input of the MFMA projection
+        }
     }
     if constexpr (PUBLISH) {
         // one more kv group of sequence b merged; the last one raises the

@@ -443,18 +443,19 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
 // MFMA panels (bf16, batch >= 8)
 // ---------------------------------------------------------------------------
 //
-// A panel is 16 output rows for 16 sequences, all of K: one
-// v_mfma_f32_16x16x32_bf16 per 32 values of K.  The weight operand comes
-// straight from 16-byte global loads (lane i: row i % 16, K values
-// 8 (i / 16) .. +8 of the step, contiguous in the [N, K] layout); the batch
-// operand is x .* norm_w (QKV) or the attention output (O projection) for
-// sequence i % 16, rounded to bf16; C lane i holds rows 4 (i / 16) + j of
-// sequence i % 16.  The workgroup's kMfmaWaves waves split K; each requests
-// up to kMfmaSteps steps of operands at once (64 KB of weights per
+// A panel is TILES x 16 output rows (one or two tiles of 16) for 16
+// sequences, all of K: per 32 values of K, one v_mfma_f32_16x16x32_bf16 per
+// tile, the tiles sharing the batch operand.  The weight operand comes straight from 16-byte global loads
+// (lane i: row i % 16 of the tile, K values 8 (i / 16) .. +8 of the step,
+// contiguous in the [N, K] layout); the batch operand is x .* norm_w (QKV;
+// norm_w staged in LDS) or the bf16 copy of the attention output the merge
+// wrote (O projection) for sequence i % 16; C lane i holds rows 4 (i / 16) + j
+// of sequence i % 16.  The workgroup's kMfmaWaves waves split K; each
+// requests kMfmaSteps steps of operands at once (128 KB of weights per
 // workgroup in flight), and the partial tiles are summed through LDS in
-// fixed wave order.  For QKV the 16 rows are 8 RoPE pairs of one head (rows
-// e and e + D/2 at tile rows r and r + 8), so each rotation stays in the
-// tile; the lane work after the sum is the one of the VALU panel.
+// fixed wave order.  For QKV each tile is 8 RoPE pairs of one head (rows e
+// and e + D/2 at tile rows r and r + 8), so each rotation stays in a tile;
+// the lane work after the sum is the one of the VALU panel.
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -462,88 +463,94 @@ constexpr int kMfmaWaves = 8;            // waves per workgroup (512 threads)
 constexpr int kMfmaSteps = 8;            // K-steps of 32 requested at once per wave
 
 struct MfmaShared {
-    float c[kMfmaWaves][16][17];   // per-wave partial tiles [row][sequence] (padded)
-    float ss[16][kMfmaWaves];      // QKV: per-sequence sums of x^2, one per wave
+    float c[kMfmaWaves][2][16][17];   // per-wave partial tiles [tile][row][sequence] (padded)
+    float ss[16][kMfmaWaves];         // QKV: per-sequence sums of x^2, one per wave
 };
 
-template <bool QKV>
-__device__ void mfma_panel(const StepArgs& a, int panel, int bgi, MfmaShared& sm) {
+__device__ inline bf16x8 as_bf16x8(const u32x4& v) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = __builtin_bit_cast(__bf16, (uint16_t)(v[i] & 0xffffu));
+        r[2 * i + 1] = __builtin_bit_cast(__bf16, (uint16_t)(v[i] >> 16));
+    }
+    return r;
+}
+
+// nw_lds: QKV only, H bf16 values of norm_w (staged by the caller).
+template <bool QKV, int TILES>
+__device__ void mfma_panel(const StepArgs& a, int panel, int bgi, MfmaShared& sm, const uint16_t* nw_lds) {
+    constexpr int ROWS = 16 * TILES;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int K = QKV ? a.H : a.n_q;
     const int m = lane & 15, kg = lane >> 4;
     const int D = a.D, half = D >> 1;
-    // this lane's weight row (tile row m)
-    int hd = 0, e0 = 0, row;
+    // this lane's weight rows (row m of each tile)
+    int hd = 0, e0 = 0, row0, row1;
     if constexpr (QKV) {
-        const int pr0 = panel * 8;                     // first RoPE pair of the tile
+        const int pr0 = panel * 8 * TILES;             // first RoPE pair of the panel
         hd = pr0 / half;
         e0 = pr0 - hd * half;
-        row = hd * D + e0 + (m & 7) + (m >= 8 ? half : 0);
+        row0 = hd * D + e0 + (m & 7) + (m >= 8 ? half : 0);
+        row1 = row0 + 8;
     } else {
-        row = panel * 16 + m;
+        row0 = panel * ROWS + m;
+        row1 = row0 + 16;
     }
-    const uint16_t* W = static_cast<const uint16_t*>(QKV ? a.w_qkv : a.w_o) + (size_t)row * K + kg * 8;
+    const uint16_t* Wbase = static_cast<const uint16_t*>(QKV ? a.w_qkv : a.w_o);
+    const uint16_t* W0 = Wbase + (size_t)row0 * K + kg * 8;
+    const uint16_t* W1 = Wbase + (size_t)row1 * K + kg * 8;
     // this lane's sequence (tile column m)
     const int b = bgi * 16 + m;
     int p;
     const bool live = b < a.B && (QKV || pos_valid(a, b, &p));
-    const uint16_t* X = static_cast<const uint16_t*>(a.hidden) + (size_t)(live ? b : 0) * K + kg * 8;
-    const uint16_t* NW = static_cast<const uint16_t*>(a.norm_w) + kg * 8;
-    const float* AO = a.a + (size_t)(live ? b : 0) * K + kg * 8;
+    const uint16_t* X = (QKV ? static_cast<const uint16_t*>(a.hidden) : a.a16) + (size_t)(live ? b : 0) * K + kg * 8;
 
     // this wave's steps: K / (32 kMfmaWaves) of them, in groups of kMfmaSteps
     const int nsteps = K / (32 * kMfmaWaves), k_begin = wave * nsteps * 32;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
     float ssq = 0.f;
     for (int s0 = 0; s0 < nsteps; s0 += kMfmaSteps) {
-        u32x4 w[kMfmaSteps], x[kMfmaSteps], y[kMfmaSteps];   // weights; QKV: x, norm_w; O: a (8 floats)
+        u32x4 w0[kMfmaSteps], w1[kMfmaSteps], x[kMfmaSteps];
 #pragma unroll
         for (int s = 0; s < kMfmaSteps; ++s) {
             const int k = k_begin + (s0 + s) * 32;
             const bool in = s0 + s < nsteps;
-            w[s] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + k)) : u32x4{0u, 0u, 0u, 0u};
-            if constexpr (QKV) {
-                x[s] = in && live ? *reinterpret_cast<const u32x4*>(X + k) : u32x4{0u, 0u, 0u, 0u};
-                y[s] = in ? *reinterpret_cast<const u32x4*>(NW + k) : u32x4{0u, 0u, 0u, 0u};
-            } else {
-                x[s] = in && live ? *reinterpret_cast<const u32x4*>(AO + k) : u32x4{0u, 0u, 0u, 0u};
-                y[s] = in && live ? *reinterpret_cast<const u32x4*>(AO + k + 4) : u32x4{0u, 0u, 0u, 0u};
-            }
+            w0[s] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W0 + k)) : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (TILES == 2)
+                w1[s] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W1 + k)) : u32x4{0u, 0u, 0u, 0u};
+            x[s] = in && live ? *reinterpret_cast<const u32x4*>(X + k) : u32x4{0u, 0u, 0u, 0u};
         }
         if (s0 == 0) DAB_TRACE_POINT(a, 1);
 #pragma unroll
         for (int s = 0; s < kMfmaSteps; ++s) {
             if (s0 + s >= nsteps) break;
-            bf16x8 av, bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                av[2 * i] = __builtin_bit_cast(__bf16, (uint16_t)(w[s][i] & 0xffffu));
-                av[2 * i + 1] = __builtin_bit_cast(__bf16, (uint16_t)(w[s][i] >> 16));
-            }
+            bf16x8 bv;
             if constexpr (QKV) {
+                const int k = k_begin + (s0 + s) * 32 + kg * 8;
+                const u32x4 nw = *reinterpret_cast<const u32x4*>(nw_lds + k);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float x0 = __uint_as_float(x[s][i] << 16), x1 = __uint_as_float(x[s][i] & 0xffff0000u);
-                    const float w0 = __uint_as_float(y[s][i] << 16), w1 = __uint_as_float(y[s][i] & 0xffff0000u);
                     ssq = fmaf(x0, x0, ssq);
                     ssq = fmaf(x1, x1, ssq);
-                    bv[2 * i] = (__bf16)(x0 * w0);
-                    bv[2 * i + 1] = (__bf16)(x1 * w1);
+                    bv[2 * i] = (__bf16)(x0 * __uint_as_float(nw[i] << 16));
+                    bv[2 * i + 1] = (__bf16)(x1 * __uint_as_float(nw[i] & 0xffff0000u));
                 }
             } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bv[i] = (__bf16)__uint_as_float(x[s][i]);
-                    bv[4 + i] = (__bf16)__uint_as_float(y[s][i]);
-                }
+                bv = as_bf16x8(x[s]);
             }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0[s]), bv, acc0, 0, 0, 0);
+            if constexpr (TILES == 2) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1[s]), bv, acc1, 0, 0, 0);
         }
     }
 
     // partial tiles (and sums of x^2) to LDS, summed in wave order
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.c[wave][4 * kg + j][m] = acc[j];
+    for (int j = 0; j < 4; ++j) {
+        sm.c[wave][0][4 * kg + j][m] = acc0[j];
+        if constexpr (TILES == 2) sm.c[wave][1][4 * kg + j][m] = acc1[j];
+    }
     if constexpr (QKV) {
         ssq += __shfl_xor(ssq, 16);
         ssq += __shfl_xor(ssq, 32);
@@ -551,28 +558,29 @@ __device__ void mfma_panel(const StepArgs& a, int panel, int bgi, MfmaShared& sm
     }
     __syncthreads();
     DAB_TRACE_POINT(a, 2);
-    if (t >= 256) return;                        // 16 rows x 16 sequences: the first four waves
-    const int r = t >> 4, n = t & 15;            // tile row, sequence
+    if (t >= 256 * TILES) return;                                // tiles x 16 rows x 16 sequences
+    const int tile = t >> 8, r = (t >> 4) & 15, n = t & 15;
     const int bb = bgi * 16 + n;
     if constexpr (QKV) {
-        // threads of the first 8 rows finish pair (r, r + 8) of sequence n
+        // threads of the first 8 rows of a tile finish pair (r, r + 8) of sequence n
         if (r < 8 && bb < a.B) {
             float u0 = 0.f, u1 = 0.f, ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < kMfmaWaves; ++w) {
-                u0 += sm.c[w][r][n];
-                u1 += sm.c[w][r + 8][n];
+                u0 += sm.c[w][tile][r][n];
+                u1 += sm.c[w][tile][r + 8][n];
                 ss[w % 4] += sm.ss[n][w];
             }
-            qkv_finish<uint16_t, false>(a, panel, r, bb, hd, e0 + r, hd * D + e0 + r, u0, u1, ss);
+            const int e = e0 + tile * 8 + r;
+            qkv_finish<uint16_t, false>(a, panel, tile * 8 + r, bb, hd, e, hd * D + e, u0, u1, ss);
         }
     } else {
         int pp;
         if (bb < a.B && pos_valid(a, bb, &pp)) {
             float y = 0.f;
 #pragma unroll
-            for (int w = 0; w < kMfmaWaves; ++w) y += sm.c[w][r][n];
-            const size_t i = (size_t)bb * a.H + panel * 16 + r;
+            for (int w = 0; w < kMfmaWaves; ++w) y += sm.c[w][tile][r][n];
+            const size_t i = (size_t)bb * a.H + panel * ROWS + tile * 16 + r;
             static_cast<uint16_t*>(a.out)[i] = from_f32<uint16_t>(to_f32(static_cast<const uint16_t*>(a.hidden)[i]) + y);
             if (a.dbg_y) a.dbg_y[i] = y;
         }

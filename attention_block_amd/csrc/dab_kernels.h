@@ -41,6 +41,7 @@ struct StepArgs {
     float* attn_o;          // [B, nq, maxc, D] chunk partial outputs
     float* attn_ml;         // [B, nq, maxc, 2] chunk (max, sum)
     float* a;               // [B, n_q] attention output
+    uint16_t* a16;          // [B, n_q] the same rounded to bf16 (bf16 storage, phased schedule: MFMA input)
     // shapes and numerics
     int B, H, nq, nkv, D, G, cap, n_qkv, n_q;
     float eps, qscale;      // qscale = log2(e) / sqrt(D)

@@ -104,10 +104,16 @@ __global__ __launch_bounds__(256) void oproj_kernel(StepArgs a) {
 }
 
 // MFMA panels of the phased schedule (bf16, batch >= 8)
-template <bool QKV>
+template <bool QKV, int TILES>
 __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_panel_kernel(StepArgs a) {
     __shared__ MfmaShared sm;
+    extern __shared__ u32x4 nw_raw[];    // QKV: norm_w, H bf16 values
     DAB_TRACE_POINT(a, 0);
+    if constexpr (QKV) {
+        for (int k = threadIdx.x * 8; k < a.H; k += 64 * kMfmaWaves * 8)
+            nw_raw[k / 8] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.norm_w) + k);
+        __syncthreads();
+    }
     if constexpr (!QKV) {
         // re-arm the panel counters of a one-launch QKV + attention that ran before
         if (blockIdx.x == 0)
@@ -116,7 +122,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_panel_kernel(StepArgs a)
     }
     const PanelPlanDev& g = QKV ? a.qkv : a.oproj;
     int panel, bgi;
-    if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi)) mfma_panel<QKV>(a, panel, bgi, sm);
+    if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi))
+        mfma_panel<QKV, TILES>(a, panel, bgi, sm, reinterpret_cast<const uint16_t*>(nw_raw));
     DAB_TRACE_POINT(a, 3);
 }
 
@@ -125,7 +132,12 @@ hipError_t launch_mfma(const StepArgs& a, const Plan& p, hipStream_t s) {
     if constexpr (sizeof(T) != 2) {
         return hipErrorInvalidValue;               // planned for bf16 only
     } else {
-        hipLaunchKernelGGL((mfma_panel_kernel<QKV>), dim3((QKV ? p.qkv : p.oproj).grid), dim3(64 * kMfmaWaves), 0, s, a);
+        const PanelPlan& g = QKV ? p.qkv : p.oproj;
+        const size_t lds = QKV ? (size_t)p.H * 2 : 0;
+        if (g.rows == 32)
+            hipLaunchKernelGGL((mfma_panel_kernel<QKV, 2>), dim3(g.grid), dim3(64 * kMfmaWaves), lds, s, a);
+        else
+            hipLaunchKernelGGL((mfma_panel_kernel<QKV, 1>), dim3(g.grid), dim3(64 * kMfmaWaves), lds, s, a);
         return hipGetLastError();
     }
 }

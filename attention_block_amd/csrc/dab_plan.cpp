@@ -33,16 +33,22 @@ bool plan_panel(int K, int N, int batch, int rpw, PanelPlan* g) {
     return true;
 }
 
-// An MFMA panel: 16 rows x all K for 16 sequences (bf16, K a multiple of
-// 256: eight waves x steps of 32).
-bool plan_mfma_panel(int K, int N, int batch, PanelPlan* g) {
-    if (K % 256 != 0 || N % 16 != 0) return false;
+// An MFMA panel: 16 or 32 rows x all K for 16 sequences (bf16, K a multiple
+// of 256: eight waves x steps of 32; for QKV, 8 or 16 RoPE pairs of one
+// head).  Two tiles share each load of the batch operand; they are used
+// where the panels still number 192 or more (at 128, half the CUs idled:
+// the 4096-row output projection at batch 16 measured 20.1 us with two
+// tiles, 17.6 with one).
+bool plan_mfma_panel(int K, int N, int batch, bool qkv, int half, PanelPlan* g) {
+    if (K % 256 != 0 || N % 16 != 0 || (qkv && half % 8 != 0)) return false;
+    const int nbg = ceil_div(batch, 16);
+    const bool two = N % 32 == 0 && (!qkv || half % 16 == 0) && (long long)(N / 32) * nbg >= 192;
     g->K = K;
     g->N = N;
     g->mfma = true;
     g->rows_per_wave = 0;
-    g->rows = 16;
-    g->panels = N / 16;
+    g->rows = two ? 32 : 16;
+    g->panels = N / g->rows;
     g->nb = 16;
     g->nbg = ceil_div(batch, 16);
     g->grid = g->nbg == 1 ? g->panels : (int)align_up((size_t)g->panels, 8) * g->nbg;
@@ -134,9 +140,11 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     // sequences per workgroup: the VALU panel holds 4 and would read each
     // panel of weights once per group of 4).
     const bool mfma = p->schedule == DAB_SCHEDULE_PHASED && p->dtype == DAB_BF16 && B >= 8;
-    if (!(mfma && plan_mfma_panel(p->H, p->n_qkv, B, &p->qkv)) && !plan_panel(p->H, p->n_qkv, B, 2, &p->qkv))
+    const int half = p->D / 2;
+    if (!(mfma && plan_mfma_panel(p->H, p->n_qkv, B, true, half, &p->qkv)) && !plan_panel(p->H, p->n_qkv, B, 2, &p->qkv))
         return DAB_ERR_UNSUPPORTED;
-    if (!(mfma && plan_mfma_panel(p->n_q, p->H, B, &p->oproj)) && !plan_panel(p->n_q, p->H, B, 1, &p->oproj))
+    if (!(mfma && plan_mfma_panel(p->n_q, p->H, B, false, half, &p->oproj)) &&
+        !plan_panel(p->n_q, p->H, B, 1, &p->oproj))
         return DAB_ERR_UNSUPPORTED;
 
     // split-KV chunk over the cached tokens (at most cap - 1; the new token
@@ -183,6 +191,7 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     p->off_attn_o = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * p->D);
     p->off_attn_ml = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * 2);
     p->off_a = take(sizeof(float) * (size_t)B * p->n_q);
+    p->off_a16 = take(sizeof(uint16_t) * (size_t)B * p->n_q);
     p->ws_bytes = off;
 
     const size_t e = (size_t)p->elem;

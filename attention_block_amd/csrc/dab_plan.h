@@ -32,7 +32,7 @@ constexpr int kReadyStride = 32;     // ints
 // cross workgroups.
 struct PanelPlan {
     int K = 0, N = 0;
-    bool mfma = false;      // MFMA panels: 16 rows x 16 sequences per workgroup (bf16, batch >= 8)
+    bool mfma = false;      // MFMA panels: 32 rows x 16 sequences per workgroup (bf16, batch >= 8)
     int rows_per_wave = 0;  // 1 or 2 (the QKV panel: one RoPE pair per wave)
     int rows = 0;           // 4 * rows_per_wave
     int panels = 0;         // N / rows
@@ -58,7 +58,7 @@ struct Plan {
     // word is at offset 0
     size_t off_flags = 0, off_attn_cnt = 0, off_seq_cnt = 0, off_seq_ready = 0, off_head_cnt = 0;
     size_t off_q = 0, off_kv_new = 0;
-    size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0;
+    size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0, off_a16 = 0;
     size_t ws_bytes = 0;
 
     // byte extents of the caller's tensors (for alias checks)
