@@ -154,6 +154,8 @@ KERNEL_PHASES = [("qkv_attn_kernel", "qkv_attention_split_kv"), ("attn_oproj_ker
 
 def phase_of(kernel_name: str):
     fn = kernel_name.split("(")[0].split("<")[0].split("::")[-1]
+    if fn == "mfma_panel_kernel":            # template argument QKV: true or false
+        return "qkv_rmsnorm_rope_append" if "<true" in kernel_name else "oproj_residual"
     for k, ph in KERNEL_PHASES:
         if fn == k:
             return ph
@@ -205,6 +207,8 @@ def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: st
                 per.setdefault(ph, []).append(float(r["Counter_Value"]))
         return per, float(probe[0]["Counter_Value"])
 
+    if fetch_dir == "-" or write_dir == "-":
+        return written
     fetch, fetch_probe = counters(fetch_dir, "FETCH_SIZE")
     write, write_probe = counters(write_dir, "WRITE_SIZE")
     probe_kib = copy_mib * 1024.0
@@ -249,7 +253,8 @@ def main() -> int:
     ap.add_argument("--no-phase-timing", action="store_true")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 csv output (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass of a "
-                         "--copy-probe-mb run) into the summaries under profiles/; no GPU needed")
+                         "--copy-probe-mb run; '-' for no counter passes) into the summaries under profiles/ "
+                         "for --config; no GPU needed")
     ap.add_argument("--commands", default="", help="with --summarize-profiles: the commands that made the "
                                                      "output, separated by ';', recorded in the summaries")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
