@@ -231,7 +231,8 @@ class HipEvent:
 def decode_attn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos,
                             rope_theta: float, eps: float = 1e-6, out=None, dbg_y=None,
                             workspace: Optional[Workspace] = None, kv_chunk: int = 0, schedule: str = "auto"):
-    """decode_attn_block that also records events[0] before the first kernel and events[i] after kernel i-1."""
+    """decode_attn_block that also records events[2i], events[2i + 1] at the start and end of kernel i
+    (2 * len(phase_names) events; taken by each kernel's own dispatch)."""
     cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
                         schedule)
     ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)

@@ -32,11 +32,6 @@ dab_status hip_status(hipError_t e) {
 
 int phase_count(const Plan& p) { return p.schedule == DAB_SCHEDULE_PHASED ? 3 : 2; }
 
-dab_status record(void* const* events, int i, hipStream_t s) {
-    if (!events) return DAB_OK;
-    return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
-}
-
 dab::PanelPlanDev panel_dev(const dab::PanelPlan& g) {
     dab::PanelPlanDev d;
     d.panels = g.panels;
@@ -97,11 +92,14 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
 }
 
 dab_status enqueue(const Plan& p, const dab::StepArgs& a, hipStream_t s, void* const* events) {
-    dab_status st = record(events, 0, s);
-    if (st != DAB_OK) return st;
     for (int phase = 0; phase < phase_count(p); ++phase) {
-        if ((st = hip_status(dab::launch_phase(a, p, phase, s))) != DAB_OK) return st;
-        if ((st = record(events, phase + 1, s)) != DAB_OK) return st;
+        dab::LaunchEvents ev;
+        if (events) {
+            ev.start = static_cast<hipEvent_t>(events[2 * phase]);
+            ev.stop = static_cast<hipEvent_t>(events[2 * phase + 1]);
+        }
+        const dab_status st = hip_status(dab::launch_phase(a, p, phase, s, ev));
+        if (st != DAB_OK) return st;
     }
     return DAB_OK;
 }
@@ -116,7 +114,7 @@ dab_status call(const dab_config* cfg, const void* hidden, const void* norm_w, c
                          workspace_bytes);
     if (st != DAB_OK) return st;
     if (events) {
-        if (n_events != phase_count(p) + 1) return DAB_ERR_INVALID_ARG;
+        if (n_events != 2 * phase_count(p)) return DAB_ERR_INVALID_ARG;
         for (int i = 0; i < n_events; ++i)
             if (!events[i]) return DAB_ERR_INVALID_ARG;
     }
@@ -146,15 +144,15 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s) {
+hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev) {
 #ifdef DAB_TRACE
     StepArgs t = a;   // phases trace at consecutive item numbers: QKV, attention, output
     // consecutive item numbers: QKV, attention, output projection
     const bool oproj_only = phase == 2 || (phase == 1 && p.schedule == DAB_SCHEDULE_QKV_ATTN);
     t.trace_base = phase == 0 ? 0 : oproj_only ? p.qkv.grid + p.attn_grid : p.qkv.grid;
-    return p.dtype == DAB_BF16 ? launch_phase_bf16(t, p, phase, s) : launch_phase_f32(t, p, phase, s);
+    return p.dtype == DAB_BF16 ? launch_phase_bf16(t, p, phase, s, ev) : launch_phase_f32(t, p, phase, s, ev);
 #else
-    return p.dtype == DAB_BF16 ? launch_phase_bf16(a, p, phase, s) : launch_phase_f32(a, p, phase, s);
+    return p.dtype == DAB_BF16 ? launch_phase_bf16(a, p, phase, s, ev) : launch_phase_f32(a, p, phase, s, ev);
 #endif
 }
 

@@ -55,12 +55,17 @@ struct StepArgs {
 #endif
 };
 
+// Events a timed call records at a kernel's own start and end (null: untimed).
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // Kernel `phase` of the plan's schedule (0 .. phase_count - 1).
-hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s);
+hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev);
 
 // per-dtype instantiations (separate translation units)
-hipError_t launch_phase_bf16(const StepArgs& a, const Plan& p, int phase, hipStream_t s);
-hipError_t launch_phase_f32(const StepArgs& a, const Plan& p, int phase, hipStream_t s);
+hipError_t launch_phase_bf16(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_phase_f32(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev);
 
 }  // namespace dab

@@ -16,10 +16,23 @@
 // order, so every wait ends.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "dab_gemv.h"
 
 namespace dab {
 namespace dev {
+
+// Launch `kernel(a)` on `s`; with events, through hipExtLaunchKernel, which
+// records them at the kernel's own start and end.
+template <typename K>
+inline hipError_t dab_launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const LaunchEvents& ev,
+                             StepArgs a) {
+    void* args[] = {&a};
+    const void* f = reinterpret_cast<const void*>(kernel);
+    if (ev.start || ev.stop) return hipExtLaunchKernel(f, grid, block, args, lds, s, ev.start, ev.stop, 0);
+    return hipLaunchKernel(f, grid, block, args, lds, s);
+}
 
 // Attention work index -> (sequence, kv head, chunk); kv head fastest, so
 // concurrent items read neighbouring rows of one token range.
@@ -74,7 +87,7 @@ __global__ __launch_bounds__(256) void attn_kernel(StepArgs a) {
 // Four waves per SIMD, as the attention kernel alone gets: all 1024 chunks of
 // a 7B-sized step resident at once.
 template <typename T, int D, int G, int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && G == 1 && NB != 2 ? 4 : 1))) void attn_oproj_kernel(StepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && G == 1 && NB == 1 ? 4 : 1))) void attn_oproj_kernel(StepArgs a) {
     extern __shared__ f32x4 lds_raw[];   // attention scratch, or the projection's staged inputs
     __shared__ int s_flag;
     DAB_TRACE_POINT(a, 0);
@@ -85,7 +98,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     } else {
         int panel, bgi;
         if (panel_decode(a.oproj.nbg, a.oproj.panels, blockIdx.x - a.attn_items, &panel, &bgi))
-            oproj_panel<T, 1, NB, true, true>(a, panel, bgi, reinterpret_cast<float*>(lds_raw));
+            oproj_panel<T, 2, NB, true, true>(a, panel, bgi, reinterpret_cast<float*>(lds_raw));
     }
     DAB_TRACE_POINT(a, 3);
 }
@@ -128,16 +141,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_panel_kernel(StepArgs a)
 }
 
 template <typename T, bool QKV>
-hipError_t launch_mfma(const StepArgs& a, const Plan& p, hipStream_t s) {
+hipError_t launch_mfma(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
     if constexpr (sizeof(T) != 2) {
         return hipErrorInvalidValue;               // planned for bf16 only
     } else {
         const PanelPlan& g = QKV ? p.qkv : p.oproj;
         const size_t lds = QKV ? (size_t)p.H * 2 : 0;
         if (g.rows == 32)
-            hipLaunchKernelGGL((mfma_panel_kernel<QKV, 2>), dim3(g.grid), dim3(64 * kMfmaWaves), lds, s, a);
+            dab_launch((mfma_panel_kernel<QKV, 2>), dim3(g.grid), dim3(64 * kMfmaWaves), lds, s, ev, a);
         else
-            hipLaunchKernelGGL((mfma_panel_kernel<QKV, 1>), dim3(g.grid), dim3(64 * kMfmaWaves), lds, s, a);
+            dab_launch((mfma_panel_kernel<QKV, 1>), dim3(g.grid), dim3(64 * kMfmaWaves), lds, s, ev, a);
         return hipGetLastError();
     }
 }
@@ -147,57 +160,57 @@ template <typename T>
 inline bool exact_blocks(int K) { return K % PanelDot<T, 1, 1, true>::KB == 0; }
 
 template <typename T, bool EXACT>
-hipError_t launch_qkv_e(const StepArgs& a, const Plan& p, hipStream_t s) {
+hipError_t launch_qkv_e(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
     const dim3 grid(p.qkv.grid), block(kThreads);
     const size_t lds = p.qkv.lds;
     switch (p.qkv.nb) {
-        case 1: hipLaunchKernelGGL((qkv_kernel<T, 1, EXACT>), grid, block, lds, s, a); break;
-        case 2: hipLaunchKernelGGL((qkv_kernel<T, 2, EXACT>), grid, block, lds, s, a); break;
-        case 4: hipLaunchKernelGGL((qkv_kernel<T, 4, EXACT>), grid, block, lds, s, a); break;
+        case 1: dab_launch((qkv_kernel<T, 1, EXACT>), grid, block, lds, s, ev, a); break;
+        case 2: dab_launch((qkv_kernel<T, 2, EXACT>), grid, block, lds, s, ev, a); break;
+        case 4: dab_launch((qkv_kernel<T, 4, EXACT>), grid, block, lds, s, ev, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_qkv(const StepArgs& a, const Plan& p, hipStream_t s) {
-    if (p.qkv.mfma) return launch_mfma<T, true>(a, p, s);
-    return exact_blocks<T>(a.H) ? launch_qkv_e<T, true>(a, p, s) : launch_qkv_e<T, false>(a, p, s);
+hipError_t launch_qkv(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
+    if (p.qkv.mfma) return launch_mfma<T, true>(a, p, s, ev);
+    return exact_blocks<T>(a.H) ? launch_qkv_e<T, true>(a, p, s, ev) : launch_qkv_e<T, false>(a, p, s, ev);
 }
 
 template <typename T, int RW, bool EXACT>
-hipError_t launch_oproj_e(const StepArgs& a, const Plan& p, hipStream_t s) {
+hipError_t launch_oproj_e(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
     const dim3 grid(p.oproj.grid), block(kThreads);
     const size_t lds = p.oproj.lds;
     switch (p.oproj.nb) {
-        case 1: hipLaunchKernelGGL((oproj_kernel<T, RW, 1, EXACT>), grid, block, lds, s, a); break;
-        case 2: hipLaunchKernelGGL((oproj_kernel<T, RW, 2, EXACT>), grid, block, lds, s, a); break;
-        case 4: hipLaunchKernelGGL((oproj_kernel<T, RW, 4, EXACT>), grid, block, lds, s, a); break;
+        case 1: dab_launch((oproj_kernel<T, RW, 1, EXACT>), grid, block, lds, s, ev, a); break;
+        case 2: dab_launch((oproj_kernel<T, RW, 2, EXACT>), grid, block, lds, s, ev, a); break;
+        case 4: dab_launch((oproj_kernel<T, RW, 4, EXACT>), grid, block, lds, s, ev, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 template <typename T, int RW>
-hipError_t launch_oproj_rw(const StepArgs& a, const Plan& p, hipStream_t s) {
-    return exact_blocks<T>(a.n_q) ? launch_oproj_e<T, RW, true>(a, p, s) : launch_oproj_e<T, RW, false>(a, p, s);
+hipError_t launch_oproj_rw(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
+    return exact_blocks<T>(a.n_q) ? launch_oproj_e<T, RW, true>(a, p, s, ev) : launch_oproj_e<T, RW, false>(a, p, s, ev);
 }
 
 template <typename T>
-hipError_t launch_oproj(const StepArgs& a, const Plan& p, hipStream_t s) {
-    if (p.oproj.mfma) return launch_mfma<T, false>(a, p, s);
+hipError_t launch_oproj(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
+    if (p.oproj.mfma) return launch_mfma<T, false>(a, p, s, ev);
     switch (p.oproj.rows_per_wave) {
-        case 1: return launch_oproj_rw<T, 1>(a, p, s);
-        case 2: return launch_oproj_rw<T, 2>(a, p, s);
+        case 1: return launch_oproj_rw<T, 1>(a, p, s, ev);
+        case 2: return launch_oproj_rw<T, 2>(a, p, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T, int D>
-hipError_t launch_attn_d(const StepArgs& a, hipStream_t s) {
+hipError_t launch_attn_d(const StepArgs& a, hipStream_t s, const LaunchEvents& ev) {
     const dim3 grid(a.attn_items), block(kThreads);
     switch (a.G) {
-#define DAB_G(NG) case NG: hipLaunchKernelGGL((attn_kernel<T, D, NG>), grid, block, 0, s, a); break;
+#define DAB_G(NG) case NG: dab_launch((attn_kernel<T, D, NG>), grid, block, 0, s, ev, a); break;
         DAB_G(1) DAB_G(2) DAB_G(3) DAB_G(4) DAB_G(5) DAB_G(6) DAB_G(7) DAB_G(8)
 #undef DAB_G
         default: return hipErrorInvalidValue;
@@ -206,45 +219,45 @@ hipError_t launch_attn_d(const StepArgs& a, hipStream_t s) {
 }
 
 template <typename T, int D, int G>
-hipError_t launch_attn_oproj_g(const StepArgs& a, const Plan& p, hipStream_t s) {
+hipError_t launch_attn_oproj_g(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
     const dim3 grid(p.attn_grid + p.oproj.grid), block(kThreads);
     const size_t lds = p.oproj.lds > sizeof(AttnShared<D, G>) ? p.oproj.lds : sizeof(AttnShared<D, G>);
     switch (p.oproj.nb) {
-        case 1: hipLaunchKernelGGL((attn_oproj_kernel<T, D, G, 1>), grid, block, lds, s, a); break;
-        case 2: hipLaunchKernelGGL((attn_oproj_kernel<T, D, G, 2>), grid, block, lds, s, a); break;
-        case 4: hipLaunchKernelGGL((attn_oproj_kernel<T, D, G, 4>), grid, block, lds, s, a); break;
+        case 1: dab_launch((attn_oproj_kernel<T, D, G, 1>), grid, block, lds, s, ev, a); break;
+        case 2: dab_launch((attn_oproj_kernel<T, D, G, 2>), grid, block, lds, s, ev, a); break;
+        case 4: dab_launch((attn_oproj_kernel<T, D, G, 4>), grid, block, lds, s, ev, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 // Shapes the one-launch attention + projection is instantiated for: whole
-// K-blocks in the projection, one row per wave, groups of 1, 2, 4 or 8.
+// K-blocks in the projection, two rows per wave, groups of 1, 2, 4 or 8.
 template <typename T>
 inline bool attn_oproj_supported(const Plan& p) {
-    return exact_blocks<T>(p.n_q) && p.oproj.rows_per_wave == 1 && (p.G == 1 || p.G == 2 || p.G == 4 || p.G == 8);
+    return exact_blocks<T>(p.n_q) && p.oproj.rows_per_wave == 2 && (p.G == 1 || p.G == 2 || p.G == 4 || p.G == 8);
 }
 
 template <typename T, int D>
-hipError_t launch_attn_oproj_d(const StepArgs& a, const Plan& p, hipStream_t s) {
+hipError_t launch_attn_oproj_d(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
     switch (p.G) {
-        case 1: return launch_attn_oproj_g<T, D, 1>(a, p, s);
-        case 2: return launch_attn_oproj_g<T, D, 2>(a, p, s);
-        case 4: return launch_attn_oproj_g<T, D, 4>(a, p, s);
-        case 8: return launch_attn_oproj_g<T, D, 8>(a, p, s);
+        case 1: return launch_attn_oproj_g<T, D, 1>(a, p, s, ev);
+        case 2: return launch_attn_oproj_g<T, D, 2>(a, p, s, ev);
+        case 4: return launch_attn_oproj_g<T, D, 4>(a, p, s, ev);
+        case 8: return launch_attn_oproj_g<T, D, 8>(a, p, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T, int NB, int D>
-hipError_t launch_qkv_attn_nd(const StepArgs& a, const Plan& p, hipStream_t s) {
+hipError_t launch_qkv_attn_nd(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
     const dim3 grid(p.qkv.grid + p.attn_grid), block(kThreads);
     size_t lds = p.qkv.lds;
     switch (p.G) {
 #define DAB_G(NG)                                                                                           \
         case NG:                                                                                            \
             if (sizeof(AttnShared<D, NG>) > lds) lds = sizeof(AttnShared<D, NG>);                             \
-            hipLaunchKernelGGL((qkv_attn_kernel<T, NB, D, NG>), grid, block, lds, s, a);                    \
+            dab_launch((qkv_attn_kernel<T, NB, D, NG>), grid, block, lds, s, ev, a);                    \
             break;
         DAB_G(1) DAB_G(2) DAB_G(4) DAB_G(8)
 #undef DAB_G
@@ -254,31 +267,31 @@ hipError_t launch_qkv_attn_nd(const StepArgs& a, const Plan& p, hipStream_t s) {
 }
 
 template <typename T, int NB>
-hipError_t launch_qkv_attn_n(const StepArgs& a, const Plan& p, hipStream_t s) {
-    return a.D == 128 ? launch_qkv_attn_nd<T, NB, 128>(a, p, s) : launch_qkv_attn_nd<T, NB, 64>(a, p, s);
+hipError_t launch_qkv_attn_n(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
+    return a.D == 128 ? launch_qkv_attn_nd<T, NB, 128>(a, p, s, ev) : launch_qkv_attn_nd<T, NB, 64>(a, p, s, ev);
 }
 
 template <typename T>
-hipError_t launch_qkv_attn(const StepArgs& a, const Plan& p, hipStream_t s) {
+hipError_t launch_qkv_attn(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
     if (!exact_blocks<T>(a.H)) return hipErrorInvalidValue;
     switch (p.qkv.nb) {
-        case 1: return launch_qkv_attn_n<T, 1>(a, p, s);
-        case 2: return launch_qkv_attn_n<T, 2>(a, p, s);
-        case 4: return launch_qkv_attn_n<T, 4>(a, p, s);
+        case 1: return launch_qkv_attn_n<T, 1>(a, p, s, ev);
+        case 2: return launch_qkv_attn_n<T, 2>(a, p, s, ev);
+        case 4: return launch_qkv_attn_n<T, 4>(a, p, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-hipError_t launch_phase_t(const StepArgs& a, const Plan& p, int phase, hipStream_t s) {
-    if (p.schedule == DAB_SCHEDULE_QKV_ATTN) return phase == 0 ? launch_qkv_attn<T>(a, p, s) : launch_oproj<T>(a, p, s);
-    if (phase == 0) return launch_qkv<T>(a, p, s);
+hipError_t launch_phase_t(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev) {
+    if (p.schedule == DAB_SCHEDULE_QKV_ATTN) return phase == 0 ? launch_qkv_attn<T>(a, p, s, ev) : launch_oproj<T>(a, p, s, ev);
+    if (phase == 0) return launch_qkv<T>(a, p, s, ev);
     if (p.schedule == DAB_SCHEDULE_ATTN_OPROJ) {
         if (!attn_oproj_supported<T>(p)) return hipErrorInvalidValue;
-        return a.D == 128 ? launch_attn_oproj_d<T, 128>(a, p, s) : launch_attn_oproj_d<T, 64>(a, p, s);
+        return a.D == 128 ? launch_attn_oproj_d<T, 128>(a, p, s, ev) : launch_attn_oproj_d<T, 64>(a, p, s, ev);
     }
-    if (phase == 1) return a.D == 128 ? launch_attn_d<T, 128>(a, s) : launch_attn_d<T, 64>(a, s);
-    return launch_oproj<T>(a, p, s);
+    if (phase == 1) return a.D == 128 ? launch_attn_d<T, 128>(a, s, ev) : launch_attn_d<T, 64>(a, s, ev);
+    return launch_oproj<T>(a, p, s, ev);
 }
 
 }  // namespace dev

@@ -2,7 +2,7 @@
 #include "dab_phase.h"
 
 namespace dab {
-hipError_t launch_phase_bf16(const StepArgs& a, const Plan& p, int phase, hipStream_t s) {
-    return dev::launch_phase_t<uint16_t>(a, p, phase, s);
+hipError_t launch_phase_bf16(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev) {
+    return dev::launch_phase_t<uint16_t>(a, p, phase, s, ev);
 }
 }  // namespace dab

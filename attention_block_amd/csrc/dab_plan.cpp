@@ -143,8 +143,14 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     const int half = p->D / 2;
     if (!(mfma && plan_mfma_panel(p->H, p->n_qkv, B, true, half, &p->qkv)) && !plan_panel(p->H, p->n_qkv, B, 2, &p->qkv))
         return DAB_ERR_UNSUPPORTED;
+    // In the one-launch attention + projection, two rows per wave: half the
+    // projection workgroups, so that with ~512 attention chunks all of them
+    // hold a slot from the start and their weights stream with the cache
+    // (with 1024, the last ones got slots only as chunks finished and their
+    // weight loads ended the step).
+    const int rpw_o = p->schedule == DAB_SCHEDULE_ATTN_OPROJ ? 2 : 1;
     if (!(mfma && plan_mfma_panel(p->n_q, p->H, B, false, half, &p->oproj)) &&
-        !plan_panel(p->n_q, p->H, B, 1, &p->oproj))
+        !plan_panel(p->n_q, p->H, B, rpw_o, &p->oproj))
         return DAB_ERR_UNSUPPORTED;
 
     // split-KV chunk over the cached tokens (at most cap - 1; the new token

@@ -12,8 +12,8 @@ size exceeds twice the 256 MiB Infinity Cache, so no step is served from it.
 
 Prints one JSON line: microseconds per step (the metric), achieved HBM GB/s
 and % of the 8 TB/s peak over the algorithmic bytes, a roofline entry for
-the dominant kernel (its average duration from HIP events recorded on the
-stream it runs on), and the fp64 CPU oracle timed on the host as a
+the dominant kernel (its average duration from HIP events recorded at its
+own start and end on the stream it runs on), and the fp64 CPU oracle timed on the host as a
 baseline.
 """
 from __future__ import annotations
@@ -163,7 +163,7 @@ def phase_of(kernel_name: str):
 
 
 def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
-                       commands: list) -> list:
+                       commands: list, bench_json: str = "") -> list:
     """Write the rocprofv3 summaries under profiles/: the kernel-trace statistics of the library's kernels,
     and per kernel the HBM bytes of one launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
     scaled by what the counter reads for the copy probe (copy_mib MiB read and written)."""
@@ -177,7 +177,7 @@ def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: st
     stats = [r for r in csv.DictReader(open(os.path.join(kt_dir, "run_kernel_stats.csv"))) if phase_of(r["Name"])]
     lines = [f"# rocprofv3 kernel trace: {workload}", "",
              "Commands (from /tmp with TMPDIR=/tmp; R = the repository root):", ""]
-    lines += [f"    {c}" for c in commands if "--kernel-trace" in c or "--summarize-profiles" in c]
+    lines += [f"    {c}" for c in commands if "--pmc" not in c]
     lines += ["", "| phase | kernel | calls | average us | min us | max us | algorithmic bytes | GB/s at average |",
               "|---|---|---|---|---|---|---|---|"]
     for r in stats:
@@ -186,10 +186,20 @@ def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: st
         lines.append(f"| {ph} | `{r['Name'].split('(')[0]}` | {r['Calls']} | {avg:.3f} | "
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {pb[ph]} | "
                      f"{pb[ph] / (avg * 1e-6) / 1e9:.1f} |")
-    lines += ["", "bench.py times each kernel between HIP events recorded on its stream, back to back in an eager "
-              "queue; that interval also holds the dispatch gap before the kernel, so it reads a few "
-              "microseconds above the kernel's own duration here.", "",
-              f"- source_digest: `{digest}`"]
+    lines += ["", "bench.py times each kernel with HIP events that the kernel's own dispatch records at its start "
+              "and end (hipExtLaunchKernel); under the profiler those events are perturbed, so its figures "
+              "are taken from an unprofiled run of the same sources."]
+    if bench_json:
+        with open(bench_json) as f:
+            line = json.loads([ln for ln in f if ln.startswith("{")][-1])
+        lines += ["", f"Unprofiled `bench.py --config {workload}` on the same sources: {line['value']} us per step; "
+                      "per-kernel averages from the dispatch events:", "",
+                  "| phase | event average us | kernel-trace average us |", "|---|---|---|"]
+        kt_avg = {phase_of(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
+        for ph, v in (line.get("phases") or {}).items():
+            kt = kt_avg.get(ph)
+            lines.append(f"| {ph} | {v['us']:.3f} | {kt:.3f} |" if kt is not None else f"| {ph} | {v['us']:.3f} | - |")
+    lines += ["", f"- source_digest: `{digest}`"]
     path = os.path.join(PROFILES, f"kernel_trace_{workload}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -257,6 +267,8 @@ def main() -> int:
                          "for --config; no GPU needed")
     ap.add_argument("--commands", default="", help="with --summarize-profiles: the commands that made the "
                                                      "output, separated by ';', recorded in the summaries")
+    ap.add_argument("--bench-json", default="", help="with --summarize-profiles: output of an unprofiled bench.py "
+                                                      "run of the same sources, whose event timings are quoted")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one elementwise copy of this many MiB (fp32 in, fp32 out): the "
                          "reference kernel of known size for the FETCH_SIZE / WRITE_SIZE counter runs")
@@ -265,7 +277,7 @@ def main() -> int:
     if args.summarize_profiles:
         kt, fd, wd = args.summarize_profiles
         cmds = [c.strip() for c in args.commands.split(";") if c.strip()]
-        for p in summarize_profiles(kt, fd, wd, args.config, args.copy_probe_mb or 256, cmds):
+        for p in summarize_profiles(kt, fd, wd, args.config, args.copy_probe_mb or 256, cmds, args.bench_json):
             print("wrote", os.path.relpath(p, HERE))
         return 0
 
@@ -363,14 +375,14 @@ def main() -> int:
     # enqueued behind a spin kernel so they run back to back on the GPU.
     phase_us = None
     if not args.no_phase_timing:
-        ev = [[ab.HipEvent() for _ in range(len(phases) + 1)] for _ in range(args.steps)]
+        ev = [[ab.HipEvent() for _ in range(2 * len(phases))] for _ in range(args.steps)]
         torch.cuda.synchronize()
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(int(2.4e9 * 1e-4 * args.steps))   # ~100 us of spinning per queued step
         for i in range(args.steps):
             step(i, ev[i])
         torch.cuda.synchronize()
-        phase_us = [float(np.mean([ev[i][k].elapsed_ms(ev[i][k + 1]) * 1e3 for i in range(args.steps)]))
+        phase_us = [float(np.mean([ev[i][2 * k].elapsed_ms(ev[i][2 * k + 1]) * 1e3 for i in range(args.steps)]))
                     for k in range(len(phases))]
 
     gbps = nbytes / (us * 1e-6) / 1e9

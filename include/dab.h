@@ -157,9 +157,11 @@ dab_status dab_decode_attn_block(const dab_config* cfg,
 
 /*
  * Same as dab_decode_attn_block, and also records `n_events` hipEvent_t
- * (passed as void*) on `stream`: events[0] before the first kernel and
- * events[i] after kernel i-1.  n_events must equal dab_phase_count(cfg) + 1.
- * Used to time the phases of the step on the stream they run on.
+ * (passed as void*, created by the caller) for the kernels it enqueues on
+ * `stream`: events[2i] at the start and events[2i + 1] at the end of kernel
+ * i, taken by the kernel's own dispatch (hipExtLaunchKernel), so that
+ * hipEventElapsedTime of the pair is the kernel's duration without the gaps
+ * between kernels.  n_events must equal 2 * dab_phase_count(cfg).
  */
 dab_status dab_decode_attn_block_timed(const dab_config* cfg,
                                        const void* hidden, const void* norm_w,

@@ -189,10 +189,21 @@ def test_batch_zero_is_a_no_op(lib):
 
 
 def test_timed_variant_checks_events(lib):
+    # two events per kernel (its own start and end); every check fails before anything is enqueued
     c = cfg()
     vp = ctypes.c_void_p
-    args = [ctypes.byref(c)] + [vp(1 << 40)] * 9 + [vp(1 << 44), lib.dab_workspace_size(ctypes.byref(c)), None]
+    f = FakePtrs()
+    ptrs = [f.take(1 << 20), f.take(1 << 20), f.take(1 << 24), f.take(1 << 24), f.take(1 << 24), f.take(1 << 24),
+            f.take(64), f.take(1 << 20)]
+    args = [ctypes.byref(c)] + [vp(q) for q in ptrs] + [vp(0), vp(f.take(1 << 26)),
+                                                      lib.dab_workspace_size(ctypes.byref(c)), None]
     assert lib.dab_decode_attn_block_timed(*args, None, 0) == _lib.DAB_ERR_INVALID_ARG
+    n = lib.dab_phase_count(ctypes.byref(c))
+    for count in (n + 1, 2 * n - 1, 2 * n + 1):        # the old one-between-kernels count is rejected too
+        ev = (vp * count)(*[vp(8 * (i + 1)) for i in range(count)])
+        assert lib.dab_decode_attn_block_timed(*args, ev, count) == _lib.DAB_ERR_INVALID_ARG, count
+    ev = (vp * (2 * n))(*[vp(8 * (i + 1)) for i in range(2 * n - 1)] + [vp(0)])
+    assert lib.dab_decode_attn_block_timed(*args, ev, 2 * n) == _lib.DAB_ERR_INVALID_ARG   # a null event
 
 
 def test_status_strings(lib):
