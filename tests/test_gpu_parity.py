@@ -114,6 +114,8 @@ EDGE_ONE_LAUNCH = [
     ("f32 H 2048 gqa ragged", small_cfg("o5", 3, 2048, 16, 4, 128, "f32", 5e5), 300, [299, 0, 150], 0),
     ("bf16 H 4096 batch 6", small_cfg("o6", 6, 4096, 32, 8, 128, "bf16", 5e5), 260, [259, 3, 128, 0, 200, 64], 0),
     ("f32 H 2048 d64 group 1", small_cfg("o7", 2, 2048, 32, 32, 64, "f32"), 90, [89, 17], 32),
+    # 2048 chunks: every attention workgroup of the one-launch attention + projection takes several
+    ("bf16 many chunks per workgroup", small_cfg("o8", 2, 4096, 32, 32, 128, "bf16"), 2000, [1999, 1000], 64),
 ]
 ONE_LAUNCH_CASES = [(sched, *e) for e in EDGE_ONE_LAUNCH for sched in ("attn_oproj", "qkv_attn")
                     if applies(e[1], sched)]
@@ -145,10 +147,12 @@ SAME_BITS = EDGE_ONE_LAUNCH[1:] + [("7B 4K", CONFIGS["llama2_7b_bs1_4k"], None, 
 
 @pytest.mark.parametrize("label,cfg,cap,pos,kv_chunk", SAME_BITS, ids=[e[0] for e in SAME_BITS])
 def test_schedules_give_identical_bits(label, cfg, cap, pos, kv_chunk):
-    """Every schedule runs the same arithmetic in the same order: identical out, y and caches.  (Except
-    that bf16 batches of 8 or more take MFMA panels in the phased schedule, which round the projection
-    inputs to bf16; there only the one-launch schedules are compared with each other.)"""
+    """Every schedule runs the same arithmetic in the same order for one chunk length: identical out, y
+    and caches.  (The default chunk lengths differ between schedules, so the chunk length is fixed
+    here; and bf16 batches of 8 or more take MFMA panels in the phased schedule, which round the
+    projection inputs to bf16; there only the one-launch schedules are compared with each other.)"""
     import torch
+    kv_chunk = kv_chunk or 128
     inp = make_inputs(cfg, 21, cap=cap, pos=pos)
     scheds = [s for s in SCHEDULES if applies(cfg, s)]
     if cfg.dtype == "bf16" and cfg.batch >= 8:
