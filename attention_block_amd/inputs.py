@@ -168,6 +168,61 @@ def make_inputs(cfg: BlockConfig, seed: int, *, cap: Optional[int] = None,
     }
 
 
+# ---------------------------------------------------------------------------
+# the FFN half of the layer
+# ---------------------------------------------------------------------------
+#
+# Draw order: hidden [B, H] ~ N(0, 1); norm_w [H] = 1 + 0.1 N(0, 1);
+# w_gate [H, F] ~ N(0, 1/H); w_up [H, F] ~ N(0, 1/H); w_down [F, H] ~ N(0, 1/F)
+# (variances 1/fan-in, so g, u and y stay of order one).  The intermediate
+# sizes are those of the models the pages benchmark (Llama-2-7B 11008,
+# Llama-3-8B 14336); the pages do not give them.
+
+@dataclasses.dataclass(frozen=True)
+class FfnConfig:
+    """Shape and precision of one FFN workload."""
+    name: str
+    batch: int
+    hidden: int
+    intermediate: int
+    dtype: str
+    eps: float = 1e-6
+
+
+FFN_CONFIGS = {
+    "tiny_ffn_f32": FfnConfig("tiny_ffn_f32", 1, 256, 704, "f32"),
+    "llama2_7b_ffn_bs1": FfnConfig("llama2_7b_ffn_bs1", 1, 4096, 11008, "bf16"),
+    "llama3_8b_ffn_bs16": FfnConfig("llama3_8b_ffn_bs16", 16, 4096, 14336, "bf16"),
+}
+
+FFN_HEADLINE = "llama2_7b_ffn_bs1"
+
+
+def make_ffn_inputs(cfg: FfnConfig, seed: int) -> dict:
+    """Draw one seeded FFN input set (storage form, weights in the [in, out] orientation)."""
+    rng = np.random.default_rng(seed)
+    B, H, F = cfg.batch, cfg.hidden, cfg.intermediate
+    hidden = rng.standard_normal((B, H), dtype=np.float32)
+    norm_w = (1.0 + 0.1 * rng.standard_normal(H, dtype=np.float32)).astype(np.float32)
+    sh, sf = np.float32(1.0 / np.sqrt(H)), np.float32(1.0 / np.sqrt(F))
+    w_gate = (rng.standard_normal((H, F), dtype=np.float32) * sh).astype(np.float32)
+    w_up = (rng.standard_normal((H, F), dtype=np.float32) * sh).astype(np.float32)
+    w_down = (rng.standard_normal((F, H), dtype=np.float32) * sf).astype(np.float32)
+    return {"cfg": cfg, "hidden": _store(hidden, cfg.dtype), "norm_w": _store(norm_w, cfg.dtype),
+            "w_gate": _store(w_gate, cfg.dtype), "w_up": _store(w_up, cfg.dtype),
+            "w_down": _store(w_down, cfg.dtype)}
+
+
+def ffn_algorithmic_bytes(cfg: FfnConfig) -> int:
+    """Three weight matrices once, the norm weight, hidden in and out."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    return s * 3 * cfg.hidden * cfg.intermediate + s * cfg.hidden + 2 * s * cfg.batch * cfg.hidden
+
+
+def ffn_algorithmic_flops(cfg: FfnConfig) -> int:
+    return 2 * cfg.batch * 3 * cfg.hidden * cfg.intermediate
+
+
 def algorithmic_bytes(cfg: BlockConfig, pos: Sequence[int]) -> int:
     """Bytes one decode step must move through HBM at minimum.
 

@@ -1,4 +1,4 @@
-"""50-digit brute-force twin of the decode-block oracle, for tiny shapes.
+"""50-digit brute-force twins of the decode-block and FFN oracles, for tiny shapes.
 
 TEST INFRASTRUCTURE ONLY (imported by the CPU tests, never by the library).
 
@@ -106,3 +106,36 @@ def decode_step_brute(hidden, norm_w, w_qkv, w_o, k_hist, v_hist, pos, *,
             y.append(s)
         out = [x[c] + y[c] for c in range(H)]
         return {"out": out, "y": y, "q": q, "k": k, "v": v, "probs": probs}
+
+
+def ffn_step_brute(hidden, norm_w, w_gate, w_up, w_down, *, eps, digits=50):
+    """The FFN half for one sequence, in explicit loops over mpmath numbers.
+
+    hidden [H], norm_w [H], w_gate [H][F], w_up [H][F], w_down [F][H].
+    Returns dict of lists of mpf: out [H], y [H], m [F].  The gate is
+    written from its definition, z / (1 + e^-z).
+    """
+    with mpmath.workdps(digits):
+        f = mpmath.mpf
+        H, F = len(hidden), len(w_gate[0])
+        h = [f(hidden[i]) for i in range(H)]
+        sq = f(0)
+        for i in range(H):
+            sq += h[i] * h[i]
+        r = 1 / mpmath.sqrt(sq / H + f(eps))
+        hn = [h[i] * r * f(norm_w[i]) for i in range(H)]
+        m = []
+        for c in range(F):
+            g = f(0)
+            u = f(0)
+            for i in range(H):
+                g += hn[i] * f(w_gate[i][c])
+                u += hn[i] * f(w_up[i][c])
+            m.append(g / (1 + mpmath.exp(-g)) * u)
+        y = []
+        for c in range(H):
+            s = f(0)
+            for j in range(F):
+                s += m[j] * f(w_down[j][c])
+            y.append(s)
+        return {"out": [h[c] + y[c] for c in range(H)], "y": y, "m": m}

@@ -16,7 +16,12 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 
-from oracle.brute import decode_step_brute  # noqa: E402
+from oracle.brute import decode_step_brute, ffn_step_brute  # noqa: E402
+
+FFN_CASES = [
+    # H, F
+    (8, 12),
+]
 
 CASES = [
     # H, nq, nkv, D, pos, theta
@@ -55,6 +60,26 @@ def main():
             "expected": expect,
         }
         name = f"brute_h{H}_nq{nq}_nkv{nkv}_d{D}_p{p}.json"
+        with open(os.path.join(HERE, name), "w") as f:
+            json.dump(doc, f, indent=1)
+        print("wrote", name)
+    for (H, F) in FFN_CASES:
+        rng = np.random.default_rng(2000 + H + F)
+        inp = {
+            "hidden": rng.standard_normal(H).round(6).tolist(),
+            "norm_w": (1 + 0.1 * rng.standard_normal(H)).round(6).tolist(),
+            "w_gate": (rng.standard_normal((H, F)) / np.sqrt(H)).round(6).tolist(),
+            "w_up": (rng.standard_normal((H, F)) / np.sqrt(H)).round(6).tolist(),
+            "w_down": (rng.standard_normal((F, H)) / np.sqrt(F)).round(6).tolist(),
+        }
+        res = ffn_step_brute(inp["hidden"], inp["norm_w"], inp["w_gate"], inp["w_up"], inp["w_down"], eps=1e-6)
+        doc = {
+            "source": "oracle/brute.py ffn_step_brute (mpmath, 50 digits); written by tests/golden/make_golden.py",
+            "shape": {"hidden": H, "intermediate": F, "eps": 1e-6},
+            "inputs": inp,
+            "expected": {k: [str(v) for v in res[k]] for k in ("out", "y", "m")},
+        }
+        name = f"ffn_brute_h{H}_f{F}.json"
         with open(os.path.join(HERE, name), "w") as f:
             json.dump(doc, f, indent=1)
         print("wrote", name)
