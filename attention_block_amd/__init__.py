@@ -12,10 +12,11 @@ import ctypes
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import DAB_BF16, DAB_F32, DabConfig
+from ._lib import DAB_BF16, DAB_F32, FFN_PHASES, DabConfig, DabFfnConfig
 
 __all__ = ["DabError", "DabConfig", "make_config", "workspace_size", "Workspace", "decode_attn_block",
-           "decode_attn_block_timed", "read_device_error", "phase_names", "HipEvent", "lib_version"]
+           "decode_attn_block_timed", "read_device_error", "phase_names", "HipEvent", "lib_version",
+           "DabFfnConfig", "FFN_PHASES", "ffn_workspace_size", "decode_ffn_block", "decode_ffn_block_timed"]
 
 
 class DabError(RuntimeError):
@@ -241,6 +242,79 @@ def decode_attn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_qkv, w
         ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache), _ptr(v_cache),
         _ptr(pos), _ptr(out), _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device),
         arr, len(events)), "dab_decode_attn_block_timed")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the FFN half of the layer
+# ---------------------------------------------------------------------------
+
+def ffn_workspace_size(cfg: DabFfnConfig) -> int:
+    n = _lib.load().dab_ffn_workspace_size(ctypes.byref(cfg))
+    if n == 0:
+        raise DabError(_lib.DAB_ERR_INVALID_ARG, "dab_ffn_workspace_size")
+    return n
+
+
+_ffn_ws = {}
+
+
+def _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspace):
+    import torch
+    if hidden.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("hidden must be bfloat16 or float32")
+    dt, dev = hidden.dtype, hidden.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for name, t in dict(hidden=hidden, norm_w=norm_w, w_gate=w_gate, w_up=w_up, w_down=w_down).items():
+        if t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+    if hidden.dim() != 2 or w_gate.dim() != 2:
+        raise ValueError("hidden must be [B, H] and w_gate [F, H]")
+    B, H = hidden.shape
+    F = w_gate.shape[0]
+    if norm_w.shape != (H,) or w_gate.shape != (F, H) or w_up.shape != (F, H) or w_down.shape != (H, F):
+        raise ValueError("need norm_w [H], w_gate and w_up [F, H], w_down [H, F] (one output feature per row)")
+    if out is None:
+        out = torch.empty_like(hidden)
+    elif out.shape != hidden.shape or out.dtype != dt or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must match hidden")
+    if dbg_y is not None and (dbg_y.shape != hidden.shape or dbg_y.dtype != torch.float32
+                              or dbg_y.device != dev or not dbg_y.is_contiguous()):
+        raise ValueError("dbg_y must be a contiguous float32 [B, H] tensor")
+    cfg = DabFfnConfig(B, H, F, DAB_BF16 if dt == torch.bfloat16 else DAB_F32, eps)
+    if workspace is None:
+        key = (dev.type, dev.index, B, F)
+        workspace = _ffn_ws.get(key)
+        if workspace is None:
+            workspace = _ffn_ws[key] = Workspace(ffn_workspace_size(cfg), dev)
+    return cfg, out, workspace
+
+
+def decode_ffn_block(hidden, norm_w, w_gate, w_up, w_down, eps: float = 1e-6, out=None, dbg_y=None,
+                     workspace: Optional[Workspace] = None):
+    """The FFN half of the layer on the current stream; returns `out` = h + silu(g) * u @ W_down^T.
+
+    Shapes: hidden [B, H]; norm_w [H]; w_gate and w_up [F, H]; w_down [H, F]
+    (one output feature per row); one dtype (bfloat16 or float32) on one GPU.
+    dbg_y (optional, float32 [B, H]) receives the pre-residual projection.
+    """
+    cfg, out, ws = _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspace)
+    _check(_lib.load().dab_decode_ffn_block(
+        ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
+        _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device)), "dab_decode_ffn_block")
+    return out
+
+
+def decode_ffn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_gate, w_up, w_down, eps: float = 1e-6,
+                           out=None, dbg_y=None, workspace: Optional[Workspace] = None):
+    """decode_ffn_block that records events[0..3] at the start and end of its two kernels."""
+    cfg, out, ws = _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspace)
+    arr = (ctypes.c_void_p * len(events))(*[e.handle.value for e in events])
+    _check(_lib.load().dab_decode_ffn_block_timed(
+        ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
+        _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device), arr, len(events)),
+        "dab_decode_ffn_block_timed")
     return out
 
 

@@ -16,8 +16,10 @@ SCHEDULES = {"auto": 0, "phased": 1, "attn_oproj": 2, "qkv_attn": 3}
 EXPORTS = (
     "dab_workspace_size", "dab_workspace_init", "dab_decode_attn_block", "dab_decode_attn_block_timed",
     "dab_phase_count", "dab_phase_name", "dab_read_device_error", "dab_status_string", "dab_version",
-    "dab_last_hip_error",
+    "dab_last_hip_error", "dab_ffn_workspace_size", "dab_decode_ffn_block", "dab_decode_ffn_block_timed",
 )
+# names of the two FFN kernels, in launch order
+FFN_PHASES = ("ffn_rmsnorm_gate_up_silu", "ffn_down_residual")
 
 
 class DabConfig(ctypes.Structure):
@@ -33,6 +35,16 @@ class DabConfig(ctypes.Structure):
         ("eps", ctypes.c_float),
         ("kv_chunk", ctypes.c_int32),
         ("schedule", ctypes.c_int32),
+    ]
+
+
+class DabFfnConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("intermediate", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("eps", ctypes.c_float),
     ]
 
 
@@ -72,5 +84,13 @@ def load() -> ctypes.CDLL:
     lib.dab_version.restype = ctypes.c_char_p
     lib.dab_last_hip_error.argtypes = []
     lib.dab_last_hip_error.restype = ctypes.c_char_p
+    ffnp = ctypes.POINTER(DabFfnConfig)
+    lib.dab_ffn_workspace_size.argtypes = [ffnp]
+    lib.dab_ffn_workspace_size.restype = sz
+    ffn_call = [ffnp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dab_decode_ffn_block.argtypes = ffn_call
+    lib.dab_decode_ffn_block.restype = i32
+    lib.dab_decode_ffn_block_timed.argtypes = ffn_call + [ctypes.POINTER(vp), i32]
+    lib.dab_decode_ffn_block_timed.restype = i32
     _lib = lib
     return lib

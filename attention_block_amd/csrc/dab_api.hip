@@ -123,6 +123,55 @@ dab_status call(const dab_config* cfg, const void* hidden, const void* norm_w, c
     return enqueue(p, a, static_cast<hipStream_t>(stream), events);
 }
 
+dab_status ffn_call(const dab_ffn_config* cfg, const void* hidden, const void* norm_w, const void* w_gate,
+                    const void* w_up, const void* w_down, void* out, float* dbg_y, void* workspace,
+                    size_t workspace_bytes, void* stream, void* const* events, int n_events) {
+    dab::FfnPlan p;
+    dab_status st = dab::make_ffn_plan(cfg, &p);
+    if (st != DAB_OK) return st;
+    st = dab::check_ffn_call(p, hidden, norm_w, w_gate, w_up, w_down, out, dbg_y, workspace, workspace_bytes);
+    if (st != DAB_OK) return st;
+    if (events) {
+        if (n_events != 4) return DAB_ERR_INVALID_ARG;
+        for (int i = 0; i < n_events; ++i)
+            if (!events[i]) return DAB_ERR_INVALID_ARG;
+    }
+    if (p.B == 0) return DAB_OK;
+    dab::FfnArgs a{};
+    a.hidden = hidden;
+    a.norm_w = norm_w;
+    a.w_gate = w_gate;
+    a.w_up = w_up;
+    a.w_down = w_down;
+    a.out = out;
+    a.dbg_y = dbg_y;
+    a.m = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_m);
+    a.m16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + p.off_m16);
+    a.mfma = p.mfma ? 1 : 0;
+    a.down_tiles = p.down.rows == 32 ? 2 : 1;
+    a.B = p.B;
+    a.H = p.H;
+    a.F = p.F;
+    a.eps = p.eps;
+    a.gu = panel_dev(p.gu);
+    a.down = panel_dev(p.down);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int phase = 0; phase < 2; ++phase) {
+        dab::LaunchEvents ev;
+        if (events) {
+            ev.start = static_cast<hipEvent_t>(events[2 * phase]);
+            ev.stop = static_cast<hipEvent_t>(events[2 * phase + 1]);
+        }
+#ifdef DAB_TRACE
+        a.trace = g_trace;
+        a.trace_base = phase == 0 ? 0 : p.gu.grid;
+#endif
+        st = hip_status(dab::launch_ffn_phase(a, p.dtype, phase, s, ev));
+        if (st != DAB_OK) return st;
+    }
+    return DAB_OK;
+}
+
 }  // namespace
 
 namespace dab {
@@ -220,9 +269,9 @@ const char* dab_status_string(dab_status status) {
     switch (status) {
         case DAB_OK: return "ok";
         case DAB_ERR_INVALID_ARG: return "invalid argument (null, misaligned or overlapping pointer, bad size)";
-        case DAB_ERR_UNSUPPORTED: return "unsupported shape (head_dim not 64/128, hidden not a multiple of 64, "
-                                         "hidden or n_q_heads * head_dim above 16384, group > 8, "
-                                         "or too many KV chunks)";
+        case DAB_ERR_UNSUPPORTED: return "unsupported shape (head_dim not 64/128, hidden or intermediate not a "
+                                         "multiple of 64, hidden, intermediate or n_q_heads * head_dim above "
+                                         "16384, group > 8, or too many KV chunks)";
         case DAB_ERR_WORKSPACE: return "workspace missing or too small";
         case DAB_ERR_HIP: return "HIP runtime error";
     }
@@ -230,6 +279,28 @@ const char* dab_status_string(dab_status status) {
 }
 
 const char* dab_last_hip_error(void) { return g_last_error; }
+
+size_t dab_ffn_workspace_size(const dab_ffn_config* cfg) {
+    dab::FfnPlan p;
+    if (dab::make_ffn_plan(cfg, &p) != DAB_OK) return 0;
+    return p.ws_bytes;
+}
+
+dab_status dab_decode_ffn_block(const dab_ffn_config* cfg, const void* hidden, const void* norm_w, const void* w_gate,
+                                const void* w_up, const void* w_down, void* out, float* dbg_y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return ffn_call(cfg, hidden, norm_w, w_gate, w_up, w_down, out, dbg_y, workspace, workspace_bytes, stream,
+                    nullptr, 0);
+}
+
+dab_status dab_decode_ffn_block_timed(const dab_ffn_config* cfg, const void* hidden, const void* norm_w,
+                                      const void* w_gate, const void* w_up, const void* w_down, void* out,
+                                      float* dbg_y, void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* events, int n_events) {
+    if (!events) return DAB_ERR_INVALID_ARG;
+    return ffn_call(cfg, hidden, norm_w, w_gate, w_up, w_down, out, dbg_y, workspace, workspace_bytes, stream,
+                    events, n_events);
+}
 
 const char* dab_version(void) { return "dab 0.1.0 (gfx950)"; }
 

@@ -1,0 +1,109 @@
+// Kernels and launchers of the FFN half of the layer (bf16 and fp32 storage).
+#include <hip/hip_runtime.h>
+
+#include "dab_ffn.h"
+#include "dab_phase.h"
+
+namespace dab {
+namespace dev {
+namespace {
+
+template <typename T, int NB, bool EXACT>
+__global__ __launch_bounds__(256) void ffn_gate_up_kernel(FfnArgs a) {
+    extern __shared__ f32x4 xs_raw[];
+    __shared__ FfnShared<NB> sm;
+    DAB_TRACE_POINT(a, 0);
+    int panel, bgi;
+    if (panel_decode(a.gu.nbg, a.gu.panels, blockIdx.x, &panel, &bgi))
+        ffn_gate_up_panel<T, NB, EXACT>(a, panel, bgi, reinterpret_cast<float*>(xs_raw), sm);
+    DAB_TRACE_POINT(a, 3);
+}
+
+template <typename T, int NB, bool EXACT>
+__global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
+    extern __shared__ f32x4 xs_raw[];
+    DAB_TRACE_POINT(a, 0);
+    int panel, bgi;
+    if (panel_decode(a.down.nbg, a.down.panels, blockIdx.x, &panel, &bgi))
+        ffn_down_panel<T, NB, EXACT>(a, panel, bgi, reinterpret_cast<float*>(xs_raw));
+    DAB_TRACE_POINT(a, 3);
+}
+
+template <bool GATE_UP, int TILES>
+__global__ __launch_bounds__(64 * kMfmaWaves) void ffn_mfma_kernel(FfnArgs a) {
+    __shared__ MfmaShared sm;
+    extern __shared__ u32x4 nw_raw[];    // gate/up: norm_w, H bf16 values
+    DAB_TRACE_POINT(a, 0);
+    if constexpr (GATE_UP) {
+        for (int k = threadIdx.x * 8; k < a.H; k += 64 * kMfmaWaves * 8)
+            nw_raw[k / 8] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.norm_w) + k);
+        __syncthreads();
+    }
+    const PanelPlanDev& g = GATE_UP ? a.gu : a.down;
+    int panel, bgi;
+    if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi))
+        ffn_mfma_panel<GATE_UP, TILES>(a, panel, bgi, sm, reinterpret_cast<const uint16_t*>(nw_raw));
+    DAB_TRACE_POINT(a, 3);
+}
+
+template <typename T, bool GATE_UP>
+hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
+    if constexpr (sizeof(T) != 2) {
+        return hipErrorInvalidValue;               // planned for bf16 only
+    } else {
+        const dim3 block(64 * kMfmaWaves);
+        if constexpr (GATE_UP) {
+            dab_launch((ffn_mfma_kernel<true, 2>), dim3(a.gu.items), block, (size_t)a.H * 2, s, ev, a);
+        } else if (a.down_tiles == 2) {
+            dab_launch((ffn_mfma_kernel<false, 2>), dim3(a.down.items), block, 0, s, ev, a);
+        } else {
+            dab_launch((ffn_mfma_kernel<false, 1>), dim3(a.down.items), block, 0, s, ev, a);
+        }
+        return hipGetLastError();
+    }
+}
+
+template <typename T, bool EXACT>
+hipError_t launch_gate_up_e(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
+    const dim3 grid(a.gu.items), block(kThreads);
+    const size_t lds = (size_t)a.gu.nb * a.H * sizeof(float);
+    switch (a.gu.nb) {
+        case 1: dab_launch((ffn_gate_up_kernel<T, 1, EXACT>), grid, block, lds, s, ev, a); break;
+        case 2: dab_launch((ffn_gate_up_kernel<T, 2, EXACT>), grid, block, lds, s, ev, a); break;
+        case 4: dab_launch((ffn_gate_up_kernel<T, 4, EXACT>), grid, block, lds, s, ev, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, bool EXACT>
+hipError_t launch_down_e(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
+    const dim3 grid(a.down.items), block(kThreads);
+    const size_t lds = (size_t)a.down.nb * a.F * sizeof(float);
+    switch (a.down.nb) {
+        case 1: dab_launch((ffn_down_kernel<T, 1, EXACT>), grid, block, lds, s, ev, a); break;
+        case 2: dab_launch((ffn_down_kernel<T, 2, EXACT>), grid, block, lds, s, ev, a); break;
+        case 4: dab_launch((ffn_down_kernel<T, 4, EXACT>), grid, block, lds, s, ev, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_ffn_t(const FfnArgs& a, int phase, hipStream_t s, const LaunchEvents& ev) {
+    if (a.mfma) return phase == 0 ? launch_ffn_mfma<T, true>(a, s, ev) : launch_ffn_mfma<T, false>(a, s, ev);
+    if (phase == 0)
+        return exact_blocks<T>(a.H) ? launch_gate_up_e<T, true>(a, s, ev) : launch_gate_up_e<T, false>(a, s, ev);
+    if (phase == 1)
+        return exact_blocks<T>(a.F) ? launch_down_e<T, true>(a, s, ev) : launch_down_e<T, false>(a, s, ev);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace dev
+
+hipError_t launch_ffn_phase(const FfnArgs& a, int dtype, int phase, hipStream_t s, const LaunchEvents& ev) {
+    return dtype == DAB_BF16 ? dev::launch_ffn_t<uint16_t>(a, phase, s, ev) : dev::launch_ffn_t<float>(a, phase, s, ev);
+}
+
+}  // namespace dab

@@ -60,7 +60,31 @@ struct LaunchEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 
+// The FFN half of the layer, for both of its kernels.
+struct FfnArgs {
+    const void* hidden;     // [B, H] h
+    const void* norm_w;     // [H]
+    const void* w_gate;     // [F, H]
+    const void* w_up;       // [F, H]
+    const void* w_down;     // [H, F]
+    void* out;              // [B, H]
+    float* dbg_y;           // [B, H] or null
+    float* m;               // [B, F] silu(g) * u (workspace; VALU panels)
+    uint16_t* m16;          // [B, F] the same rounded to bf16 (workspace; MFMA panels)
+    int B, H, F;
+    float eps;
+    int mfma;               // MFMA panels (bf16, batch >= 8): 16 sequences per workgroup
+    int down_tiles;         // MFMA down panel: 1 or 2 tiles of 16 rows
+    PanelPlanDev gu, down;
+#ifdef DAB_TRACE
+    unsigned long long* trace;
+    int trace_base;
+#endif
+};
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// FFN kernel `phase` (0: RMSNorm + gate/up + silu, 1: down + residual).
+hipError_t launch_ffn_phase(const FfnArgs& a, int dtype, int phase, hipStream_t s, const LaunchEvents& ev);
 // Kernel `phase` of the plan's schedule (0 .. phase_count - 1).
 hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev);
 

@@ -212,6 +212,84 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     return DAB_OK;
 }
 
+dab_status make_ffn_plan(const dab_ffn_config* cfg, FfnPlan* p) {
+    if (!cfg || !p) return DAB_ERR_INVALID_ARG;
+    *p = FfnPlan();
+    const dab_ffn_config& c = *cfg;
+    if (c.batch < 0 || c.hidden <= 0 || c.intermediate <= 0) return DAB_ERR_INVALID_ARG;
+    if (c.dtype != DAB_F32 && c.dtype != DAB_BF16) return DAB_ERR_INVALID_ARG;
+    if (!(c.eps >= 0.f) || !isfinite(c.eps)) return DAB_ERR_INVALID_ARG;
+    if (c.hidden % 64 != 0 || c.intermediate % 64 != 0) return DAB_ERR_UNSUPPORTED;
+    // each GEMV workgroup keeps one batch row of its input (H, or F for the
+    // down projection) in LDS as fp32
+    if ((size_t)c.hidden * sizeof(float) > (size_t)kPanelLds ||
+        (size_t)c.intermediate * sizeof(float) > (size_t)kPanelLds || c.batch > 4096)
+        return DAB_ERR_UNSUPPORTED;
+    p->B = c.batch;
+    p->H = c.hidden;
+    p->F = c.intermediate;
+    p->dtype = c.dtype;
+    p->elem = c.dtype == DAB_BF16 ? 2 : 4;
+    p->eps = c.eps;
+    const int B = p->B > 0 ? p->B : 1;
+    // bf16 batches of 8 or more: MFMA panels, 16 sequences per workgroup (the
+    // VALU panel holds at most 4 and is bound by its arithmetic there).  The
+    // gate/up panel is 16 rows of W_gate and the same 16 rows of W_up, one
+    // MFMA tile each, so both sums of an output meet in one workgroup.
+    p->mfma = p->dtype == DAB_BF16 && B >= 8 && p->H % 256 == 0 && p->F % 256 == 0;
+    if (p->mfma) {
+        PanelPlan& g = p->gu;
+        g.K = p->H;
+        g.N = 2 * p->F;
+        g.mfma = true;
+        g.rows = 16;
+        g.panels = p->F / 16;
+        g.nb = 16;
+        g.nbg = ceil_div(B, 16);
+        g.grid = g.nbg == 1 ? g.panels : (int)align_up((size_t)g.panels, 8) * g.nbg;
+        if (!plan_mfma_panel(p->F, p->H, B, false, 0, &p->down)) return DAB_ERR_UNSUPPORTED;
+    } else if (!plan_panel(p->H, 2 * p->F, B, 2, &p->gu) || !plan_panel(p->F, p->H, B, 1, &p->down)) {
+        return DAB_ERR_UNSUPPORTED;
+    }
+    p->off_m = 0;
+    p->off_m16 = align_up(sizeof(float) * (size_t)B * p->F, 256);
+    p->ws_bytes = p->off_m16 + align_up(sizeof(uint16_t) * (size_t)B * p->F, 256);
+    const size_t e = (size_t)p->elem;
+    p->bytes_hidden = e * p->B * p->H;
+    p->bytes_norm = e * p->H;
+    p->bytes_wgu = e * (size_t)p->F * p->H;
+    p->bytes_wdown = e * (size_t)p->H * p->F;
+    p->bytes_out = e * p->B * p->H;
+    p->bytes_dbg = sizeof(float) * p->B * p->H;
+    return DAB_OK;
+}
+
+dab_status check_ffn_call(const FfnPlan& p, const void* hidden, const void* norm_w, const void* w_gate,
+                          const void* w_up, const void* w_down, const void* out, const float* dbg_y,
+                          const void* workspace, size_t ws_bytes) {
+    if (!workspace) return DAB_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DAB_ERR_INVALID_ARG;
+    if (ws_bytes < p.ws_bytes) return DAB_ERR_WORKSPACE;
+    if (p.B == 0) return DAB_OK;  // nothing is read or written
+    const void* req[] = {hidden, norm_w, w_gate, w_up, w_down, out};
+    for (const void* q : req)
+        if (!q || !aligned(q, 16)) return DAB_ERR_INVALID_ARG;
+    if (dbg_y && !aligned(dbg_y, 16)) return DAB_ERR_INVALID_ARG;
+    struct Span { const void* p; size_t n; bool written; };
+    const Span spans[] = {
+        {hidden, p.bytes_hidden, false}, {norm_w, p.bytes_norm, false}, {w_gate, p.bytes_wgu, false},
+        {w_up, p.bytes_wgu, false},      {w_down, p.bytes_wdown, false}, {out, p.bytes_out, true},
+        {dbg_y, p.bytes_dbg, true},      {workspace, p.ws_bytes, true},
+    };
+    const int n = (int)(sizeof(spans) / sizeof(spans[0]));
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if ((spans[i].written || spans[j].written) &&
+                overlaps(spans[i].p, spans[i].n, spans[j].p, spans[j].n))
+                return DAB_ERR_INVALID_ARG;
+    return DAB_OK;
+}
+
 dab_status check_call(const Plan& p, const void* hidden, const void* norm_w, const void* w_qkv,
                       const void* w_o, const void* k_cache, const void* v_cache, const int32_t* pos,
                       const void* out, const float* dbg_y, const void* workspace, size_t ws_bytes) {

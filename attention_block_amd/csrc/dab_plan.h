@@ -66,6 +66,24 @@ struct Plan {
     size_t bytes_pos = 0, bytes_out = 0, bytes_dbg = 0;
 };
 
+// The FFN half of the layer: two row-panel GEMVs.  gu: W_gate and W_up
+// (wave w of panel i takes row 4i + w of both, K = H, N = 2F counted as
+// rows of the pair); down: W_down, one row per wave, K = F.
+struct FfnPlan {
+    int B = 0, H = 0, F = 0, dtype = 0, elem = 0;
+    float eps = 0.f;
+    bool mfma = false;        // bf16, batch >= 8, H and F multiples of 256: MFMA panels for both GEMVs
+    PanelPlan gu, down;
+    size_t off_m = 0, off_m16 = 0, ws_bytes = 0;
+    size_t bytes_hidden = 0, bytes_norm = 0, bytes_wgu = 0, bytes_wdown = 0, bytes_out = 0, bytes_dbg = 0;
+};
+
+dab_status make_ffn_plan(const dab_ffn_config* cfg, FfnPlan* plan);
+
+dab_status check_ffn_call(const FfnPlan& p, const void* hidden, const void* norm_w, const void* w_gate,
+                          const void* w_up, const void* w_down, const void* out, const float* dbg_y,
+                          const void* workspace, size_t ws_bytes);
+
 // Validate `cfg` and fill `plan`.  Returns DAB_OK, DAB_ERR_INVALID_ARG or
 // DAB_ERR_UNSUPPORTED.  Makes no HIP calls.
 dab_status make_plan(const dab_config* cfg, Plan* plan);

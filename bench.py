@@ -32,10 +32,12 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
-from attention_block_amd.inputs import (CONFIGS, HEADLINE, BlockConfig, algorithmic_bytes,  # noqa: E402
-                                        algorithmic_flops, positions)
+from attention_block_amd.inputs import (CONFIGS, FFN_CONFIGS, HEADLINE, BlockConfig, FfnConfig,  # noqa: E402
+                                        algorithmic_bytes, algorithmic_flops, ffn_algorithmic_bytes,
+                                        ffn_algorithmic_flops, positions)
 
 METRIC = "µs per decode block step and achieved HBM GB/s (% of peak), 7B layer bs1 4K"
+FFN_METRIC = "µs per FFN half-layer decode step and achieved HBM GB/s (% of peak)"
 PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 1024 * 1024
 PROFILES = os.path.join(HERE, "profiles")
@@ -149,7 +151,17 @@ def cpu_baseline(cfg: BlockConfig, seed: int, budget_s: float) -> dict:
 # kernel function names (as rocprofv3 reports them) -> phase names of the C ABI
 KERNEL_PHASES = [("qkv_attn_kernel", "qkv_attention_split_kv"), ("attn_oproj_kernel", "attention_oproj_residual"),
                  ("qkv_kernel", "qkv_rmsnorm_rope_append"), ("attn_kernel", "attention_split_kv"),
-                 ("oproj_kernel", "oproj_residual")]
+                 ("oproj_kernel", "oproj_residual"), ("ffn_gate_up_kernel", "ffn_rmsnorm_gate_up_silu"),
+                 ("ffn_down_kernel", "ffn_down_residual")]
+
+
+def ffn_phase_bytes(cfg: FfnConfig) -> dict:
+    """Algorithmic bytes of the two FFN kernels; they add up to ffn_algorithmic_bytes()."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    B, H, F = cfg.batch, cfg.hidden, cfg.intermediate
+    # hidden is counted with the first kernel, out with the second
+    return {"ffn_rmsnorm_gate_up_silu": s * 2 * H * F + s * H + s * B * H,
+            "ffn_down_residual": s * H * F + s * B * H}
 
 
 def phase_of(kernel_name: str):
@@ -168,9 +180,10 @@ def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: st
     and per kernel the HBM bytes of one launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
     scaled by what the counter reads for the copy probe (copy_mib MiB read and written)."""
     import csv
-    cfg = CONFIGS[workload]
-    pos = positions(cfg, 0)
-    pb = phase_bytes(cfg, pos)
+    if workload in FFN_CONFIGS:
+        pb = ffn_phase_bytes(FFN_CONFIGS[workload])
+    else:
+        pb = phase_bytes(CONFIGS[workload], positions(CONFIGS[workload], 0))
     digest = source_digest()
     written = []
 
@@ -249,12 +262,178 @@ def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: st
     return written
 
 
+def graph_time(step, steps: int, R: int) -> float:
+    """Microseconds per step over exactly `steps` steps replayed from HIP graphs.
+
+    One captured launch sequence per step, over all layer-sets, so host-side
+    marshalling never starves the GPU: a graph of L steps replayed steps // L
+    times plus a remainder graph."""
+    import torch
+    import attention_block_amd as ab
+    L = min(steps, R * max(1, math.ceil(64 / R)))
+
+    def capture(nsteps, first):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(first)                     # warm call on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(nsteps):
+                step(first + i)
+        torch.cuda.synchronize()
+        return g
+
+    g_main = capture(L, 0)
+    n_main, rem = divmod(steps, L)
+    g_rem = capture(rem, 0) if rem else None
+    g_main.replay()
+    torch.cuda.synchronize()
+
+    start, end = ab.HipEvent(), ab.HipEvent()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    start.record(stream.cuda_stream)
+    for _ in range(n_main):
+        g_main.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    end.record(stream.cuda_stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_ms(end) * 1e3 / steps
+
+
+def event_phase_times(step, nphases: int, steps: int) -> list:
+    """Average duration of each kernel over `steps` eager steps, from the events its own dispatch records
+    (step(i, events) records events[2k] / events[2k + 1] at the start / end of kernel k); the steps are
+    enqueued behind a spin kernel so that they run back to back on the GPU."""
+    import torch
+    import attention_block_amd as ab
+    ev = [[ab.HipEvent() for _ in range(2 * nphases)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2.4e9 * 1e-4 * steps))   # ~100 us of spinning per queued step
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    return [float(np.mean([ev[i][2 * k].elapsed_ms(ev[i][2 * k + 1]) * 1e3 for i in range(steps)]))
+            for k in range(nphases)]
+
+
+def make_ffn_set(cfg: FfnConfig, gen, device):
+    import torch
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    B, H, F = cfg.batch, cfg.hidden, cfg.intermediate
+
+    def randn(*shape, scale=1.0, shift=0.0):
+        return (torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * scale + shift).to(dt)
+
+    ls = {"hidden": randn(B, H), "norm_w": randn(H, scale=0.1, shift=1.0),
+          "w_gate": randn(F, H, scale=1 / math.sqrt(H)), "w_up": randn(F, H, scale=1 / math.sqrt(H)),
+          "w_down": randn(H, F, scale=1 / math.sqrt(F))}      # one output feature per row
+    ls["out"] = torch.empty_like(ls["hidden"])
+    return ls
+
+
+def ffn_cpu_baseline(cfg: FfnConfig, seed: int, budget_s: float) -> dict:
+    """The fp64 FFN oracle on the host, on the full step of this workload."""
+    import oracle
+    from attention_block_amd.inputs import make_ffn_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    inp = make_ffn_inputs(cfg, seed)
+    st = cfg.dtype
+    args = [oracle.to_f64(inp[k], st) for k in ("hidden", "norm_w", "w_gate", "w_up", "w_down")]
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.ffn_step_fp64(*args, eps=cfg.eps, storage=st)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 200:
+            break
+    med = float(np.median(times))
+    return {"value": med * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} full {cfg.name} steps (seed {seed}) of the fp64 numpy FFN oracle, median; "
+                      f"bf16->fp64 upcast outside the timing"}
+
+
+def bench_ffn(args, dev) -> int:
+    """The FFN half of the layer: RMSNorm + gate/up + silu, then down + residual, one JSON line."""
+    import torch
+    import attention_block_amd as ab
+    cfg = FFN_CONFIGS[args.config]
+    nbytes = ffn_algorithmic_bytes(cfg)
+    R = max(3, math.ceil(2 * MALL_BYTES / nbytes) + 1)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4321 + args.seed)
+    sets = [make_ffn_set(cfg, gen, dev) for _ in range(R)]
+    c = ab.DabFfnConfig(cfg.batch, cfg.hidden, cfg.intermediate, ab.DAB_BF16 if cfg.dtype == "bf16" else ab.DAB_F32,
+                        cfg.eps)
+    ws = ab.Workspace(ab.ffn_workspace_size(c), dev)
+    phases = list(ab.FFN_PHASES)
+
+    def step(i, events=None):
+        s = sets[i % R]
+        w = (s["hidden"], s["norm_w"], s["w_gate"], s["w_up"], s["w_down"], cfg.eps)
+        if events is None:
+            ab.decode_ffn_block(*w, out=s["out"], workspace=ws)
+        else:
+            ab.decode_ffn_block_timed(events, *w, out=s["out"], workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    us = graph_time(step, args.steps, R)
+    phase_us = None if args.no_phase_timing else event_phase_times(step, len(phases), args.steps)
+    pb = ffn_phase_bytes(cfg)
+    roofline = phase_report = None
+    if phase_us is not None:
+        dom = max(phases, key=lambda n: pb[n])
+        k = phases.index(dom)
+        ach = pb[dom] / (phase_us[k] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_GBPS, 4), "traffic": measured_traffic(dom, cfg.name), "kernel": dom,
+                    "bytes_per_launch": pb[dom], "avg_launch_us": round(phase_us[k], 3)}
+        phase_report = {n: {"us": round(phase_us[i], 3), "bytes": pb[n],
+                            "gbps": round(pb[n] / (phase_us[i] * 1e-6) / 1e9, 1)} for i, n in enumerate(phases)}
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+    cpu = None if args.no_cpu_baseline else ffn_cpu_baseline(cfg, args.seed, args.cpu_budget)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    line = {
+        "metric": FFN_METRIC, "value": round(us, 3), "unit": "us/step", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "hidden": cfg.hidden,
+                   "intermediate": cfg.intermediate, "layer_sets": R, "parallelism": "single GPU",
+                   "schedule": "+".join(phases)},
+        "hbm_gbps": round(gbps, 1), "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "algorithmic_bytes": nbytes, "algorithmic_flops": ffn_algorithmic_flops(cfg),
+        "roofline": roofline, "phases": phase_report, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default=HEADLINE, choices=sorted(CONFIGS))
+    ap.add_argument("--config", default=HEADLINE, choices=sorted(CONFIGS) + sorted(FFN_CONFIGS),
+                    help="a decode attention block workload, or an FFN half-layer workload (*_ffn_*)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--schedule", default="auto", choices=["auto", "phased", "attn_oproj", "qkv_attn"])
@@ -295,6 +474,8 @@ def main() -> int:
         return 1
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.config in FFN_CONFIGS:
+        return bench_ffn(args, dev)
     cfg = CONFIGS[args.config]
     pos = positions(cfg, args.seed)
     cap = int(pos.max()) + 1
@@ -329,61 +510,12 @@ def main() -> int:
         print("device error flag raised during warm-up", file=sys.stderr)
         return 1
 
-    # The timed steps replay HIP graphs (one captured launch sequence per
-    # step, over all layer-sets), so host-side marshalling never starves the
-    # GPU: graph of L steps replayed K // L times plus a remainder graph,
-    # exactly K steps in all.
-    L = min(args.steps, R * max(1, math.ceil(64 / R)))
-
-    def capture(nsteps, first):
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step(first)                     # warm call on the capture stream
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for i in range(nsteps):
-                step(first + i)
-        torch.cuda.synchronize()
-        return g
-
-    g_main = capture(L, 0)
-    n_main, rem = divmod(args.steps, L)
-    g_rem = capture(rem, 0) if rem else None
-    g_main.replay()
-    torch.cuda.synchronize()
-
-    start, end = ab.HipEvent(), ab.HipEvent()
-    stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    start.record(stream.cuda_stream)
-    for _ in range(n_main):
-        g_main.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    end.record(stream.cuda_stream)
-    end.synchronize()
-    torch.cuda.synchronize()
-    us = start.elapsed_ms(end) * 1e3 / args.steps
+    us = graph_time(step, args.steps, R)
     if ab.read_device_error(ws) != 0:
         print("device error flag raised during timing", file=sys.stderr)
         return 1
 
-    # Per-kernel durations: K eager steps with events between the kernels,
-    # enqueued behind a spin kernel so they run back to back on the GPU.
-    phase_us = None
-    if not args.no_phase_timing:
-        ev = [[ab.HipEvent() for _ in range(2 * len(phases))] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(int(2.4e9 * 1e-4 * args.steps))   # ~100 us of spinning per queued step
-        for i in range(args.steps):
-            step(i, ev[i])
-        torch.cuda.synchronize()
-        phase_us = [float(np.mean([ev[i][2 * k].elapsed_ms(ev[i][2 * k + 1]) * 1e3 for i in range(args.steps)]))
-                    for k in range(len(phases))]
+    phase_us = None if args.no_phase_timing else event_phase_times(step, len(phases), args.steps)
 
     gbps = nbytes / (us * 1e-6) / 1e9
     pb = phase_bytes(cfg, pos)

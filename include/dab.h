@@ -199,6 +199,72 @@ const char* dab_last_hip_error(void);
 /* Library version string. */
 const char* dab_version(void);
 
+/*
+ * The feed-forward half of the decoder layer, the step after the attention
+ * block: the operator-fusion article ("LayerNorm + Attention" CUDA kernel
+ * page, section 1) lists a second RMS norm and the FFN after the O
+ * projection and residual of each LLaMA-style block.  The pages do not
+ * spell the FFN out; this is the LLaMA one (gated, SiLU):
+ *
+ *   r    = (mean_i h_i^2 + eps)^(-1/2),  hh = h * r * norm_w      RMSNorm
+ *   g    = hh @ W_gate^T,  u = hh @ W_up^T                        [F] each
+ *   m    = silu(g) * u,    silu(z) = z / (1 + exp(-z))
+ *   out  = h + m @ W_down^T                                       down + residual
+ *
+ * Same conventions as the attention block (device pointers, 16-byte
+ * alignment, [out_features, in_features] weights, bf16 or fp32 storage with
+ * fp32 arithmetic, asynchronous on `stream`, kernel launches only).
+ */
+typedef struct {
+    int32_t batch;         /* B >= 0 sequences (0: nothing to do)            */
+    int32_t hidden;        /* H, multiple of 64, at most 16384               */
+    int32_t intermediate;  /* F, multiple of 64, at most 16384               */
+    int32_t dtype;         /* dab_dtype                                      */
+    float eps;             /* RMSNorm epsilon, >= 0                          */
+} dab_ffn_config;
+
+/*
+ * Bytes of device workspace one FFN call needs (0 when the configuration is
+ * invalid): m [B, F] in fp32.  Every call writes it before reading it, so it
+ * needs no initialisation; calls that share one workspace must not overlap.
+ */
+size_t dab_ffn_workspace_size(const dab_ffn_config* cfg);
+
+/*
+ * One FFN step for every sequence of the batch, two kernels: RMSNorm + gate
+ * and up GEMVs + silu(g) * u, then the down GEMV + residual.
+ *
+ *   hidden   [B, H]     input h (read only)
+ *   norm_w   [H]        RMSNorm weight (read only)
+ *   w_gate   [F, H]     row-major, one output feature per row
+ *   w_up     [F, H]     row-major, one output feature per row
+ *   w_down   [H, F]     row-major, one output feature per row
+ *   out      [B, H]     h + m @ W_down^T rounded to the storage dtype; must
+ *                       not overlap any other argument
+ *   dbg_y    [B, H] fp32 or NULL  the pre-residual m @ W_down^T (a test tap)
+ *   workspace, workspace_bytes    at least dab_ffn_workspace_size bytes
+ *
+ * Returns DAB_ERR_INVALID_ARG / DAB_ERR_UNSUPPORTED / DAB_ERR_WORKSPACE
+ * before anything is enqueued, DAB_ERR_HIP if a launch fails.
+ */
+dab_status dab_decode_ffn_block(const dab_ffn_config* cfg,
+                                const void* hidden, const void* norm_w,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                void* out, float* dbg_y,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Same, recording events[0] / events[1] at the start / end of the first
+ * kernel and events[2] / events[3] at those of the second (as in
+ * dab_decode_attn_block_timed); n_events must be 4.
+ */
+dab_status dab_decode_ffn_block_timed(const dab_ffn_config* cfg,
+                                      const void* hidden, const void* norm_w,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      void* out, float* dbg_y,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* events, int n_events);
+
 #ifdef __cplusplus
 }
 #endif
