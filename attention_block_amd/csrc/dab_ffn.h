@@ -5,8 +5,14 @@
 //                  QKV panel), against x .* norm_w staged in LDS; RMSNorm is
 //                  applied as a scale after the sums, r = (mean x^2 + eps)^-1/2,
 //                  then m[n] = silu(r g) * (r u) goes to the workspace.
-//   down panel     one row of W_down per wave against m staged in LDS;
+//   down panel     two rows of W_down per wave against m staged in LDS;
 //                  out = h + m . W_down[n], rounded to the storage type.
+//                  (Two rows: with m in fp32 a workgroup takes 4 bytes of
+//                  LDS per intermediate feature, 44 KB at F = 11008, so
+//                  three fit on a CU, and 512 workgroups of 8 rows all hold
+//                  a slot from the start where 1024 of 4 rows needed a
+//                  second, partial round: 19.5 against 21.8 us for the 7B
+//                  layer's 90 MB.)
 //
 // The operator-fusion page, section 1, places a second RMS norm and the FFN
 // after the attention block's residual; the gated SiLU form is the one of
@@ -121,18 +127,23 @@ __device__ void ffn_gate_up_panel(const FfnArgs& a, int panel, int bgi, float* x
     }
 }
 
-// Down panel `panel` (one row per wave) for batch rows [bgi * NB, +NB).
+// Down panel `panel` (RW rows per wave) for batch rows [bgi * NB, +NB).
 // xs: NB x F floats of LDS.
-template <typename T, int NB, bool EXACT>
+template <typename T, int RW, int NB, bool EXACT>
 __device__ void ffn_down_panel(const FfnArgs& a, int panel, int bgi, float* xs) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int K = a.F, H = a.H;
-    const int row = panel * 4 + wave;
-    const T* const rows[1] = {static_cast<const T*>(a.w_down) + (size_t)row * K};
+    const int row0 = (panel * 4 + wave) * RW;
+    const T* rows[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) rows[r] = static_cast<const T*>(a.w_down) + (size_t)(row0 + r) * K;
     const int b0 = bgi * NB;
-    // lane j's residual input, requested first so it is in by the end
+    // lane j's residual inputs, requested first so they are in by the end
     const bool mine = lane < NB && b0 + lane < a.B;
-    const float xres = mine ? to_f32(static_cast<const T*>(a.hidden)[(size_t)(b0 + lane) * H + row]) : 0.f;
+    float xres[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+        xres[r] = mine ? to_f32(static_cast<const T*>(a.hidden)[(size_t)(b0 + lane) * H + row0 + r]) : 0.f;
 
     // 1. this thread's first m vectors, then the weight stream
     constexpr int SA = 2 * kStageAhead;               // fp32 vectors: 4 floats each
@@ -145,7 +156,7 @@ __device__ void ffn_down_panel(const FfnArgs& a, int panel, int bgi, float* xs) 
             xr[i][j] = k < K && b0 + j < a.B ? *reinterpret_cast<const f32x4*>(a.m + (size_t)(b0 + j) * K + k)
                                              : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    PanelDot<T, 1, NB, EXACT> dot;
+    PanelDot<T, RW, NB, EXACT> dot;
     dot.issue(rows, 0, K, lane);
     DAB_TRACE_POINT(a, 1);
 
@@ -168,18 +179,26 @@ __device__ void ffn_down_panel(const FfnArgs& a, int panel, int bgi, float* xs) 
     __syncthreads();
     DAB_TRACE_POINT(a, 2);
 
-    // 3. the row against every staged sequence
+    // 3. the rows against every staged sequence
     dot.run(rows, xs, K, lane);
 
     // 4. lane j finishes sequence b0 + j: residual, rounding to storage
-    float y = 0.f;
+    float y[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) y[r] = 0.f;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-        if (lane == j) y = dot.acc[0][j];
+        if (lane == j) {
+#pragma unroll
+            for (int r = 0; r < RW; ++r) y[r] = dot.acc[r][j];
+        }
     if (!mine) return;
-    const size_t i = (size_t)(b0 + lane) * H + row;
-    static_cast<T*>(a.out)[i] = from_f32<T>(xres + y);
-    if (a.dbg_y) a.dbg_y[i] = y;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const size_t i = (size_t)(b0 + lane) * H + row0 + r;
+        static_cast<T*>(a.out)[i] = from_f32<T>(xres[r] + y[r]);
+        if (a.dbg_y) a.dbg_y[i] = y[r];
+    }
 }
 
 // MFMA panels (bf16, batch >= 8): 16 sequences per workgroup, kMfmaWaves

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
     DAB_TRACE_POINT(a, 0);
     int panel, bgi;
     if (panel_decode(a.down.nbg, a.down.panels, blockIdx.x, &panel, &bgi))
-        ffn_down_panel<T, NB, EXACT>(a, panel, bgi, reinterpret_cast<float*>(xs_raw));
+        ffn_down_panel<T, 2, NB, EXACT>(a, panel, bgi, reinterpret_cast<float*>(xs_raw));
     DAB_TRACE_POINT(a, 3);
 }
 

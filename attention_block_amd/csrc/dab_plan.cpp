@@ -248,7 +248,7 @@ dab_status make_ffn_plan(const dab_ffn_config* cfg, FfnPlan* p) {
         g.nbg = ceil_div(B, 16);
         g.grid = g.nbg == 1 ? g.panels : (int)align_up((size_t)g.panels, 8) * g.nbg;
         if (!plan_mfma_panel(p->F, p->H, B, false, 0, &p->down)) return DAB_ERR_UNSUPPORTED;
-    } else if (!plan_panel(p->H, 2 * p->F, B, 2, &p->gu) || !plan_panel(p->F, p->H, B, 1, &p->down)) {
+    } else if (!plan_panel(p->H, 2 * p->F, B, 2, &p->gu) || !plan_panel(p->F, p->H, B, 2, &p->down)) {
         return DAB_ERR_UNSUPPORTED;
     }
     p->off_m = 0;

@@ -68,7 +68,7 @@ struct Plan {
 
 // The FFN half of the layer: two row-panel GEMVs.  gu: W_gate and W_up
 // (wave w of panel i takes row 4i + w of both, K = H, N = 2F counted as
-// rows of the pair); down: W_down, one row per wave, K = F.
+// rows of the pair); down: W_down, two rows per wave, K = F.
 struct FfnPlan {
     int B = 0, H = 0, F = 0, dtype = 0, elem = 0;
     float eps = 0.f;

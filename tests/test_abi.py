@@ -210,3 +210,72 @@ def test_status_strings(lib):
     for s in range(5):
         assert lib.dab_status_string(s)
     assert lib.dab_version().startswith(b"dab")
+
+
+# ---------------------------------------------------------------------------
+# the FFN entry points
+# ---------------------------------------------------------------------------
+
+def ffn_cfg(**kw):
+    base = dict(batch=1, hidden=256, intermediate=512, dtype=_lib.DAB_BF16, eps=1e-6)
+    base.update(kw)
+    return _lib.DabFfnConfig(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=0), dict(intermediate=0), dict(hidden=100), dict(intermediate=96 + 8), dict(dtype=7),
+    dict(eps=float("nan")), dict(eps=-1.0), dict(batch=-1), dict(hidden=16384 + 64), dict(intermediate=16384 + 64),
+])
+def test_ffn_invalid_configs_have_no_workspace(lib, bad):
+    assert lib.dab_ffn_workspace_size(ctypes.byref(ffn_cfg(**bad))) == 0
+
+
+def test_ffn_workspace_size(lib):
+    n = lib.dab_ffn_workspace_size(ctypes.byref(ffn_cfg()))
+    assert n > 0 and n % 256 == 0
+    # m in fp32 and in bf16, per sequence
+    assert lib.dab_ffn_workspace_size(ctypes.byref(ffn_cfg(batch=16, hidden=4096, intermediate=14336))) >= \
+        16 * 14336 * 6
+
+
+def ffn_call(lib, c, timed=None, **over):
+    f = FakePtrs()
+    ptrs = dict(hidden=f.take(1 << 20), norm_w=f.take(1 << 20), w_gate=f.take(1 << 24), w_up=f.take(1 << 24),
+                w_down=f.take(1 << 24), out=f.take(1 << 20), dbg_y=0, ws=f.take(1 << 26))
+    ws_bytes = lib.dab_ffn_workspace_size(ctypes.byref(c))
+    ws_bytes = over.pop("ws_bytes", ws_bytes)
+    ptrs.update(over)
+    vp = ctypes.c_void_p
+    args = [ctypes.byref(c)] + [vp(ptrs[k]) for k in ("hidden", "norm_w", "w_gate", "w_up", "w_down", "out",
+                                                         "dbg_y", "ws")] + [ws_bytes, None]
+    if timed is None:
+        return lib.dab_decode_ffn_block(*args)
+    events, n = timed
+    return lib.dab_decode_ffn_block_timed(*args, events, n)
+
+
+def test_ffn_host_checks(lib):
+    c = ffn_cfg()
+    for name in ("hidden", "norm_w", "w_gate", "w_up", "w_down", "out"):
+        assert ffn_call(lib, c, **{name: 0}) == _lib.DAB_ERR_INVALID_ARG, name
+        assert ffn_call(lib, c, **{name: (1 << 44) + 8}) == _lib.DAB_ERR_INVALID_ARG, name
+    assert ffn_call(lib, c, dbg_y=(1 << 45) + 4) == _lib.DAB_ERR_INVALID_ARG
+    assert ffn_call(lib, c, ws=0) == _lib.DAB_ERR_WORKSPACE
+    assert ffn_call(lib, c, ws_bytes=lib.dab_ffn_workspace_size(ctypes.byref(c)) - 256) == _lib.DAB_ERR_WORKSPACE
+    shared = FakePtrs().take(1 << 20)
+    assert ffn_call(lib, c, hidden=shared, out=shared) == _lib.DAB_ERR_INVALID_ARG
+    assert ffn_call(lib, c, w_gate=shared, out=shared + 256) == _lib.DAB_ERR_INVALID_ARG
+    assert ffn_call(lib, ffn_cfg(hidden=96)) == _lib.DAB_ERR_UNSUPPORTED
+    # nothing is enqueued for an empty batch, so this is safe without a device
+    assert ffn_call(lib, ffn_cfg(batch=0)) == _lib.DAB_OK
+
+
+def test_ffn_timed_variant_checks_events(lib):
+    vp = ctypes.c_void_p
+    c = ffn_cfg()
+    assert ffn_call(lib, c, timed=(None, 0)) == _lib.DAB_ERR_INVALID_ARG
+    for count in (2, 3, 5):
+        ev = (vp * count)(*[vp(8 * (i + 1)) for i in range(count)])
+        assert ffn_call(lib, c, timed=(ev, count)) == _lib.DAB_ERR_INVALID_ARG, count
+    ev = (vp * 4)(vp(8), vp(16), vp(0), vp(32))
+    assert ffn_call(lib, c, timed=(ev, 4)) == _lib.DAB_ERR_INVALID_ARG
