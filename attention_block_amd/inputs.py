@@ -198,6 +198,18 @@ FFN_CONFIGS = {
 FFN_HEADLINE = "llama2_7b_ffn_bs1"
 
 
+def layer_ffn(cfg: BlockConfig) -> FfnConfig:
+    """The FFN that follows `cfg`'s attention block in a full decoder layer (multi-layer chains).
+
+    Intermediate size: Llama-3-8B's 14336 for its GQA shape (32 q / 8 kv heads at H 4096), else
+    Llama-2's rule, 8H/3 rounded up to a multiple of 256 (11008 at H 4096)."""
+    if (cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads) == (4096, 32, 8):
+        F = 14336
+    else:
+        F = 256 * -(-8 * cfg.hidden // 768)          # ceil(8H / 3 / 256) * 256
+    return FfnConfig(cfg.name + "_ffn", cfg.batch, cfg.hidden, F, cfg.dtype, cfg.eps)
+
+
 def make_ffn_inputs(cfg: FfnConfig, seed: int) -> dict:
     """Draw one seeded FFN input set (storage form, weights in the [in, out] orientation)."""
     rng = np.random.default_rng(seed)

@@ -34,10 +34,11 @@ sys.path.insert(0, HERE)
 
 from attention_block_amd.inputs import (CONFIGS, FFN_CONFIGS, HEADLINE, BlockConfig, FfnConfig,  # noqa: E402
                                         algorithmic_bytes, algorithmic_flops, ffn_algorithmic_bytes,
-                                        ffn_algorithmic_flops, positions)
+                                        ffn_algorithmic_flops, layer_ffn, positions)
 
 METRIC = "µs per decode block step and achieved HBM GB/s (% of peak), 7B layer bs1 4K"
 FFN_METRIC = "µs per FFN half-layer decode step and achieved HBM GB/s (% of peak)"
+CHAIN_METRIC = "µs per token through a chain of synthetic decoder layers (attention block + FFN each)"
 PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 1024 * 1024
 PROFILES = os.path.join(HERE, "profiles")
@@ -427,6 +428,81 @@ def bench_ffn(args, dev) -> int:
     return 0
 
 
+def bench_chain(args, dev) -> int:
+    """--layers N: one token through N decoder layers, each the attention block of --config followed by
+    its FFN (distinct weights and caches per layer; layer l's output is layer l + 1's input), all N
+    layers captured as one HIP graph; reports µs per token (a synthetic time per output token, without
+    embedding, final norm and LM head)."""
+    import torch
+    import attention_block_amd as ab
+    cfg = CONFIGS[args.config]
+    fcfg = layer_ffn(cfg)
+    N = args.layers
+    pos = positions(cfg, args.seed)
+    cap = int(pos.max()) + 1
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(777 + args.seed)
+    layers = []
+    for _ in range(N):
+        attn = make_layer_set(cfg, pos, cap, gen, dev)
+        ffn = make_ffn_set(fcfg, gen, dev)
+        layers.append((attn, ffn))
+    x0 = layers[0][0]["hidden"]
+    acfg = ab.make_config(batch=cfg.batch, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                          head_dim=cfg.head_dim, cache_capacity=cap, dtype=cfg.dtype, rope_theta=cfg.rope_theta,
+                          eps=cfg.eps, kv_chunk=args.kv_chunk, schedule=args.schedule)
+    ws = ab.Workspace(ab.workspace_size(acfg), dev)
+    fws = ab.Workspace(ab.ffn_workspace_size(ab.DabFfnConfig(
+        fcfg.batch, fcfg.hidden, fcfg.intermediate, ab.DAB_BF16 if fcfg.dtype == "bf16" else ab.DAB_F32,
+        fcfg.eps)), dev)
+
+    def token(_i=0):
+        x = x0
+        for attn, ffn in layers:
+            h = ab.decode_attn_block(x, attn["norm_w"], attn["w_qkv"], attn["w_o"], attn["k_cache"],
+                                     attn["v_cache"], attn["pos"], cfg.rope_theta, cfg.eps, out=attn["out"],
+                                     workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule)
+            x = ab.decode_ffn_block(h, ffn["norm_w"], ffn["w_gate"], ffn["w_up"], ffn["w_down"], fcfg.eps,
+                                    out=ffn["out"], workspace=fws)
+
+    for i in range(max(1, args.warmup // 10)):
+        token(i)
+    torch.cuda.synchronize()
+    if ab.read_device_error(ws) != 0:
+        print("device error flag raised during warm-up", file=sys.stderr)
+        return 1
+    steps = max(1, args.steps // 10)
+    us = graph_time(token, steps, 1)
+    if ab.read_device_error(ws) != 0:
+        print("device error flag raised during timing", file=sys.stderr)
+        return 1
+    per_layer = algorithmic_bytes(cfg, pos) + ffn_algorithmic_bytes(fcfg)
+    nbytes = N * per_layer
+    gbps = nbytes / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        a = cpu_baseline(cfg, args.seed, args.cpu_budget / 2)
+        f = ffn_cpu_baseline(fcfg, args.seed, args.cpu_budget / 2)
+        cpu = {"value": N * (a["value"] + f["value"]), "unit": "us/token", "cores": max(a["cores"], f["cores"]),
+               "kind": "oracle", "sample": f"one layer: {a['sample']}; {f['sample']}; times {N} layers"}
+    line = {
+        "metric": CHAIN_METRIC, "value": round(us, 3), "unit": "us/token", "n_gpus": 1, "steps": steps,
+        "warmup": max(1, args.warmup // 10), "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name} x {N} layers", "layers": N, "batch": cfg.batch, "hidden": cfg.hidden,
+                   "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
+                   "intermediate": fcfg.intermediate, "kv_tokens": int(pos[0]) if cfg.ragged is None else
+                   f"ragged sum {int(np.sum(pos))}", "parallelism": "single GPU",
+                   "schedule": "+".join(ab.phase_names(acfg)) + " | " + "+".join(ab.FFN_PHASES)},
+        "hbm_gbps": round(gbps, 1), "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "algorithmic_bytes": nbytes, "us_per_layer": round(us / N, 3),
+        "algorithmic_flops": N * (algorithmic_flops(cfg, pos) + ffn_algorithmic_flops(fcfg)),
+        "roofline": None, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,6 +511,9 @@ def main() -> int:
     ap.add_argument("--config", default=HEADLINE, choices=sorted(CONFIGS) + sorted(FFN_CONFIGS),
                     help="a decode attention block workload, or an FFN half-layer workload (*_ffn_*)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="time one token through this many decoder layers (attention block of --config + its "
+                         "FFN), one HIP graph; 0: the single attention block step")
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--schedule", default="auto", choices=["auto", "phased", "attn_oproj", "qkv_attn"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
@@ -476,6 +555,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.config in FFN_CONFIGS:
         return bench_ffn(args, dev)
+    if args.layers > 0:
+        return bench_chain(args, dev)
     cfg = CONFIGS[args.config]
     pos = positions(cfg, args.seed)
     cap = int(pos.max()) + 1
