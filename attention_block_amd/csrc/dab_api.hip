@@ -19,6 +19,8 @@ unsigned long long* g_trace = nullptr;
 #endif
 
 const char* const kPhasedNames[3] = {"qkv_rmsnorm_rope_append", "attention_split_kv", "oproj_residual"};
+const char* const kPhasedSplitNames[4] = {"qkv_rmsnorm_rope_append", "attention_split_kv", "attention_merge",
+                                          "oproj_residual"};
 const char* const kAttnOprojNames[2] = {"qkv_rmsnorm_rope_append", "attention_oproj_residual"};
 const char* const kQkvAttnNames[2] = {"qkv_attention_split_kv", "oproj_residual"};
 
@@ -30,7 +32,9 @@ dab_status hip_status(hipError_t e) {
     return DAB_ERR_HIP;
 }
 
-int phase_count(const Plan& p) { return p.schedule == DAB_SCHEDULE_PHASED ? 3 : 2; }
+int phase_count(const Plan& p) {
+    return p.schedule == DAB_SCHEDULE_PHASED ? (p.split_merge ? 4 : 3) : 2;
+}
 
 dab::PanelPlanDev panel_dev(const dab::PanelPlan& g) {
     dab::PanelPlanDev d;
@@ -84,6 +88,7 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.T = p.kv_chunk;
     a.maxc = p.max_chunks;
     a.attn_items = p.attn_grid;
+    a.split_merge = p.split_merge ? 1 : 0;
 #ifdef DAB_TRACE
     a.trace = g_trace;
     a.trace_base = 0;
@@ -250,7 +255,8 @@ const char* dab_phase_name(const dab_config* cfg, int i) {
     Plan p;
     if (dab::make_plan(cfg, &p) != DAB_OK || i < 0 || i >= phase_count(p)) return nullptr;
     return p.schedule == DAB_SCHEDULE_ATTN_OPROJ ? kAttnOprojNames[i]
-         : p.schedule == DAB_SCHEDULE_QKV_ATTN ? kQkvAttnNames[i] : kPhasedNames[i];
+         : p.schedule == DAB_SCHEDULE_QKV_ATTN ? kQkvAttnNames[i]
+         : p.split_merge ? kPhasedSplitNames[i] : kPhasedNames[i];
 }
 
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag) {

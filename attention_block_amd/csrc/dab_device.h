@@ -505,6 +505,7 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     // 4. the last chunk of (b, g) merges all chunks of all G heads:
     // statistics first (one request per chunk and head), then the weighted
     // outputs, every load of a round requested before any is used
+    if (a.split_merge) return;           // merged by the merge kernel that follows
     int* cnt = &a.attn_cnt[b * nkv + g];
     if (!arrive_last(cnt, nchunk, s_flag)) return;
     DAB_TRACE_POINT(a, 4);
@@ -513,7 +514,7 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     // chunks of each head per round (32 loads in flight); the first round is
     // requested together with the statistics
     constexpr int PARTS = 256 / D;
-    constexpr int QB = G >= 8 ? 4 : 32 / G;
+    constexpr int QB = merge_round(G);
     const int d = t % D, part = t / D;
     auto request = [&](int q0, float (&v)[G][QB]) {
 #pragma unroll

@@ -49,6 +49,7 @@ struct StepArgs {
     // plan
     PanelPlanDev qkv, oproj;
     int T, maxc, attn_items;
+    int split_merge;        // phased: chunk partials are merged by a kernel of their own
 #ifdef DAB_TRACE
     unsigned long long* trace;   // [items, 8] timestamps per workgroup (profiling builds only)
     int trace_base;              // item number of this launch's workgroup 0

@@ -103,6 +103,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     DAB_TRACE_POINT(a, 3);
 }
 
+// Log-sum-exp merge of the chunk partials of one (sequence, q head), after
+// the attention kernel (phased schedule, split merge).  The arithmetic and
+// its order are those of the merge inside the attention kernel (thread
+// (part, d) sums chunks part, part + PARTS, ... in order; maxima and sums by
+// wave reductions, the waves in order), so the bits are the same; only the
+// loads differ: plain loads after the kernel boundary, up to 32
+// chunks per thread requested at once.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
+    constexpr int PARTS = 256 / D, R = 32;
+    __shared__ float w[kMaxChunks], cl[kMaxChunks], red[4], acc[PARTS][D];
+    DAB_TRACE_POINT(a, 0);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int b = blockIdx.x / a.nq, h = blockIdx.x - b * a.nq;
+    int p;
+    if (!pos_valid(a, b, &p)) return;
+    const int nchunk = p > 0 ? (p + a.T - 1) / a.T : 1;
+    const size_t pbase = ((size_t)b * a.nq + h) * a.maxc;     // chunk cc: pbase + cc
+    const int d = t % D, part = t / D;
+    float v0[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int cc = part + q * PARTS;
+        v0[q] = cc < nchunk ? a.attn_o[(pbase + cc) * D + d] : 0.f;
+    }
+    for (int cc = t; cc < nchunk; cc += 256) {
+        w[cc] = a.attn_ml[(pbase + cc) * 2];
+        cl[cc] = a.attn_ml[(pbase + cc) * 2 + 1];
+    }
+    __syncthreads();
+    float v = kNegInf;
+    for (int cc = t; cc < nchunk; cc += 256) v = fmaxf(v, w[cc]);
+    const float mx = wave_max(v);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float ls = 0.f;
+    for (int cc = t; cc < nchunk; cc += 256) {
+        const float wt = __builtin_amdgcn_exp2f(w[cc] - M);       // every chunk has a token: m finite
+        ls += wt * cl[cc];
+        w[cc] = wt;
+    }
+    const float lsum = wave_sum(ls);
+    __syncthreads();                     // weights visible, red read by everyone
+    if (lane == 0) red[wave] = lsum;
+    float s = 0.f;
+    for (int q0 = 0; part + q0 * PARTS < nchunk; q0 += R) {
+        float vq[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int cc = part + (q0 + q) * PARTS;
+            vq[q] = q0 == 0 ? v0[q] : (cc < nchunk ? a.attn_o[(pbase + cc) * D + d] : 0.f);
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int cc = part + (q0 + q) * PARTS;
+            if (cc < nchunk) s += w[cc] * vq[q];
+        }
+    }
+    acc[part][d] = s;
+    __syncthreads();
+    if (t < D) {
+        const float L = red[0] + red[1] + red[2] + red[3];
+        float tot = 0.f;
+#pragma unroll
+        for (int q = 0; q < PARTS; ++q) tot += acc[q][t];
+        const size_t ai = (size_t)b * a.n_q + (size_t)h * D + t;
+        a.a[ai] = tot / L;
+        if constexpr (sizeof(T) == 2) a.a16[ai] = from_f32<uint16_t>(tot / L);   // input of the MFMA projection
+    }
+    DAB_TRACE_POINT(a, 3);
+}
+
 template <typename T, int RW, int NB, bool EXACT>
 __global__ __launch_bounds__(256) void oproj_kernel(StepArgs a) {
     extern __shared__ f32x4 xs_raw[];
@@ -291,6 +364,12 @@ hipError_t launch_phase_t(const StepArgs& a, const Plan& p, int phase, hipStream
         return a.D == 128 ? launch_attn_oproj_d<T, 128>(a, p, s, ev) : launch_attn_oproj_d<T, 64>(a, p, s, ev);
     }
     if (phase == 1) return a.D == 128 ? launch_attn_d<T, 128>(a, s, ev) : launch_attn_d<T, 64>(a, s, ev);
+    if (phase == 2 && p.split_merge) {
+        const dim3 grid(p.B * p.nq), block(kThreads);
+        if (a.D == 128) dab_launch((merge_kernel<T, 128>), grid, block, 0, s, ev, a);
+        else dab_launch((merge_kernel<T, 64>), grid, block, 0, s, ev, a);
+        return hipGetLastError();
+    }
     return launch_oproj<T>(a, p, s, ev);
 }
 

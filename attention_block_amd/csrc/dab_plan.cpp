@@ -179,6 +179,16 @@ dab_status make_plan(const dab_config* cfg, Plan* p) {
     const long long attn_grid = (long long)B * p->nkv * p->max_chunks;
     if (attn_grid + p->qkv.grid + p->oproj.grid > (1LL << 30)) return DAB_ERR_UNSUPPORTED;
     p->attn_grid = (int)attn_grid;
+    // The last chunk of a (sequence, kv group) merges G heads x chunks
+    // partials with device-coherent loads, merge_round(G) chunks per thread
+    // and head at a time; each round costs ~2-3 us on MI355X with the
+    // launch otherwise idle (a GQA layer at 16K tokens, 64 chunks of 4
+    // heads: four rounds, a 10 us tail behind 8 workgroups).  Where one
+    // round does not cover the chunks, the phased schedule merges in a
+    // kernel of its own instead: plain loads after the kernel boundary, one
+    // workgroup per (sequence, q head), every load of a round in flight.
+    p->split_merge = p->schedule == DAB_SCHEDULE_PHASED &&
+                     ceil_div(p->max_chunks, 256 / p->D) > merge_round(p->G);
 
     // workspace layout
     size_t off = 0;

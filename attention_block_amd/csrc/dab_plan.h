@@ -25,6 +25,9 @@ constexpr int kPanelLds = 64 * 1024;
 // queueing on one.
 constexpr int kReadyCopies = 16;
 constexpr int kReadyStride = 32;     // ints
+// Chunks per thread and head that the attention kernel's in-launch merge
+// requests at once (32 loads in flight per thread).
+constexpr int merge_round(int G) { return G >= 8 ? 4 : 32 / G; }
 
 // A row-panel GEMV y[b, n] = sum_k W[n, k] x[b, k] with W stored [N, K]
 // (every output's K weights contiguous).  A workgroup owns `rows` = 4 waves
@@ -53,6 +56,7 @@ struct Plan {
     bool qkv_attn_ok = false;             // the one-launch QKV + attention is built for this shape
     PanelPlan qkv, oproj;
     int kv_chunk = 0, max_chunks = 0, attn_grid = 0;
+    bool split_merge = false;             // phased: the LSE merge runs as a kernel of its own
 
     // workspace layout, byte offsets (each 256-byte aligned); the flags
     // word is at offset 0

@@ -82,8 +82,9 @@ def phase_bytes(cfg: BlockConfig, pos) -> dict:
     attn = s * 2 * nkv * D * tot
     # the hidden row is counted once, with the QKV kernel; the O-projection writes out
     oproj = s * nq * D * H + s * B * H
+    # the separate merge kernel reads and writes workspace only (the chunk partials, the attention output)
     return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj,
-            "attention_oproj_residual": attn + oproj, "qkv_attention_split_kv": qkv + attn}
+            "attention_oproj_residual": attn + oproj, "qkv_attention_split_kv": qkv + attn, "attention_merge": 0}
 
 
 def make_layer_set(cfg: BlockConfig, pos, cap: int, gen, device):
@@ -152,7 +153,8 @@ def cpu_baseline(cfg: BlockConfig, seed: int, budget_s: float) -> dict:
 # kernel function names (as rocprofv3 reports them) -> phase names of the C ABI
 KERNEL_PHASES = [("qkv_attn_kernel", "qkv_attention_split_kv"), ("attn_oproj_kernel", "attention_oproj_residual"),
                  ("qkv_kernel", "qkv_rmsnorm_rope_append"), ("attn_kernel", "attention_split_kv"),
-                 ("oproj_kernel", "oproj_residual"), ("ffn_gate_up_kernel", "ffn_rmsnorm_gate_up_silu"),
+                 ("oproj_kernel", "oproj_residual"), ("merge_kernel", "attention_merge"),
+                 ("ffn_gate_up_kernel", "ffn_rmsnorm_gate_up_silu"),
                  ("ffn_down_kernel", "ffn_down_residual")]
 
 
@@ -238,6 +240,8 @@ def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: st
     probe_kib = copy_mib * 1024.0
     f_scale, w_scale = probe_kib / fetch_probe, probe_kib / write_probe
     for ph in fetch:
+        if not pb.get(ph):
+            continue                     # workspace-only kernels have no algorithmic bytes to compare with
         fk, wk = float(np.mean(fetch[ph])), float(np.mean(write[ph]))
         fb, wb = fk * f_scale * 1024, wk * w_scale * 1024
         total = int(round(fb + wb))

@@ -78,6 +78,7 @@ def test_workspace_size_valid(lib):
 
 
 PHASED = [b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"oproj_residual"]
+PHASED_SPLIT = [b"qkv_rmsnorm_rope_append", b"attention_split_kv", b"attention_merge", b"oproj_residual"]
 ATTN_OPROJ = [b"qkv_rmsnorm_rope_append", b"attention_oproj_residual"]
 QKV_ATTN = [b"qkv_attention_split_kv", b"oproj_residual"]
 
@@ -105,8 +106,11 @@ def test_schedule_selection(lib):
     assert names(lib, cfg(**head, schedule=2)) == ATTN_OPROJ
     assert names(lib, cfg(**head, schedule=3)) == QKV_ATTN
     assert lib.dab_phase_name(ctypes.byref(cfg(**head)), 2) is None
-    # grouped heads, or batch above 4: auto stays phased
-    assert names(lib, cfg(**{**head, "n_kv_heads": 8})) == PHASED
+    # grouped heads, or batch above 4: auto stays phased; a group of 4 at 4K tokens has 64 chunks of 64,
+    # more than one merge round (8 chunks per thread and head) in the attention kernel, so the merge
+    # runs as a kernel of its own; 16 sequences have 8 chunks each and merge in the attention kernel
+    assert names(lib, cfg(**{**head, "n_kv_heads": 8})) == PHASED_SPLIT
+    assert names(lib, cfg(**{**head, "n_kv_heads": 8, "batch": 16})) == PHASED
     assert names(lib, cfg(**{**head, "batch": 5})) == PHASED
     assert names(lib, cfg(**{**head, "batch": 4})) == ATTN_OPROJ
     # fp32: K a multiple of 2048 -- nq * D for attention + projection, H for QKV + attention

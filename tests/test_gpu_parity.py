@@ -73,7 +73,8 @@ def test_auto_takes_attn_oproj_for_mha_at_small_batch():
         fused = applies(cfg, "attn_oproj") and cfg.group == 1 and cfg.batch <= 4
         want = ["qkv_rmsnorm_rope_append", "attention_oproj_residual"] if fused else \
             ["qkv_rmsnorm_rope_append", "attention_split_kv", "oproj_residual"]
-        assert ab.phase_names(c) == want, name
+        # (the phased schedule adds a merge kernel where the chunks need more than one merge round)
+        assert [n for n in ab.phase_names(c) if n != "attention_merge"] == want, name
 
 
 # ---------------------------------------------------------------------------
@@ -142,7 +143,12 @@ def test_default_workspaces_follow_the_configuration():
                     schedule="attn_oproj")
 
 
-SAME_BITS = EDGE_ONE_LAUNCH[1:] + [("7B 4K", CONFIGS["llama2_7b_bs1_4k"], None, None, 0)]
+SAME_BITS = EDGE_ONE_LAUNCH[1:] + [
+    ("7B 4K", CONFIGS["llama2_7b_bs1_4k"], None, None, 0),
+    # 41 chunks of a group of 4: the phased schedule merges in a kernel of its own, the one-launch
+    # schedules inside their attention workgroups, with the same arithmetic
+    ("gqa 41 chunks, merge kernel", small_cfg("sb1", 1, 4096, 32, 8, 128, "bf16", 5e5), 2600, [2599], 64),
+]
 
 
 @pytest.mark.parametrize("label,cfg,cap,pos,kv_chunk", SAME_BITS, ids=[e[0] for e in SAME_BITS])
