@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "dab.h"
 #include "dab_kernels.h"
 #include "dab_plan.h"
@@ -31,6 +33,41 @@ dab_status hip_status(hipError_t e) {
     snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
     return DAB_ERR_HIP;
 }
+
+// Attention workgroups the current device holds at once for cfg's shape
+// (CUs x the phased attention kernel's residency per CU), cached per device,
+// storage type, head dim and group; 0 without a device.  Every planning call
+// goes through it, so the workspace size and the launch agree.
+constexpr int kSlotDevices = 16;
+std::atomic<int> g_slots[kSlotDevices][2][2][dab::kMaxGroup + 1];   // 0: not yet asked; -1: unknown
+
+int attn_slots(const dab_config* cfg) {
+    if (!cfg || cfg->n_kv_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads != 0) return 0;
+    const int G = cfg->n_q_heads / cfg->n_kv_heads;
+    const int di = cfg->head_dim == 128 ? 1 : cfg->head_dim == 64 ? 0 : -1;
+    const int ti = cfg->dtype == DAB_BF16 ? 1 : cfg->dtype == DAB_F32 ? 0 : -1;
+    if (G < 1 || G > dab::kMaxGroup || di < 0 || ti < 0) return 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSlotDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    std::atomic<int>& slot = g_slots[dev][ti][di][G];
+    int v = slot.load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            cus = 0;
+        }
+        const int per_cu = ti ? dab::attn_resident_bf16(cfg->head_dim, G) : dab::attn_resident_f32(cfg->head_dim, G);
+        v = cus > 0 && per_cu > 0 ? cus * per_cu : -1;
+        slot.store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? v : 0;
+}
+
+dab_status plan(const dab_config* cfg, Plan* p) { return dab::make_plan(cfg, p, attn_slots(cfg)); }
 
 int phase_count(const Plan& p) {
     return p.schedule == DAB_SCHEDULE_PHASED ? (p.split_merge ? 4 : 3) : 2;
@@ -62,7 +99,6 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.dbg_y = dbg_y;
     a.flags = n(p.off_flags);
     a.attn_cnt = n(p.off_attn_cnt);
-    a.seq_cnt = n(p.off_seq_cnt);
     a.seq_ready = n(p.off_seq_ready);
     a.head_cnt = n(p.off_head_cnt);
     a.q = f(p.off_q);
@@ -113,7 +149,7 @@ dab_status call(const dab_config* cfg, const void* hidden, const void* norm_w, c
                 void* k_cache, void* v_cache, const int32_t* pos, void* out, float* dbg_y, void* workspace,
                 size_t workspace_bytes, void* stream, void* const* events, int n_events) {
     Plan p;
-    dab_status st = dab::make_plan(cfg, &p);
+    dab_status st = plan(cfg, &p);
     if (st != DAB_OK) return st;
     st = dab::check_call(p, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y, workspace,
                          workspace_bytes);
@@ -221,7 +257,7 @@ void dab_trace_set_buffer(void* p) { g_trace = static_cast<unsigned long long*>(
 
 size_t dab_workspace_size(const dab_config* cfg) {
     Plan p;
-    if (dab::make_plan(cfg, &p) != DAB_OK) return 0;
+    if (plan(cfg, &p) != DAB_OK) return 0;
     return p.ws_bytes;
 }
 
@@ -248,12 +284,12 @@ dab_status dab_decode_attn_block_timed(const dab_config* cfg, const void* hidden
 
 int dab_phase_count(const dab_config* cfg) {
     Plan p;
-    return dab::make_plan(cfg, &p) == DAB_OK ? phase_count(p) : 0;
+    return plan(cfg, &p) == DAB_OK ? phase_count(p) : 0;
 }
 
 const char* dab_phase_name(const dab_config* cfg, int i) {
     Plan p;
-    if (dab::make_plan(cfg, &p) != DAB_OK || i < 0 || i >= phase_count(p)) return nullptr;
+    if (plan(cfg, &p) != DAB_OK || i < 0 || i >= phase_count(p)) return nullptr;
     return p.schedule == DAB_SCHEDULE_ATTN_OPROJ ? kAttnOprojNames[i]
          : p.schedule == DAB_SCHEDULE_QKV_ATTN ? kQkvAttnNames[i]
          : p.split_merge ? kPhasedSplitNames[i] : kPhasedNames[i];

@@ -178,6 +178,11 @@ __device__ inline int bump(int* p) {
     return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// +1 with no reply requested (the result is unused, so no return trip).
+__device__ inline void add_counter(int* p) {
+    (void)__hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ inline void set_counter(int* p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -612,13 +617,11 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
         }
     }
     if constexpr (PUBLISH) {
-        // one more kv group of sequence b merged; the last one raises the
-        // sequence's ready flags (every other group's output was stored and
-        // acknowledged before its bump)
+        // one more kv group of sequence b merged: once its output is stored
+        // and acknowledged, every copy of the sequence's ready count goes up
+        // by one (no reply awaited); the projection waits for nkv
         drain_and_sync();
-        if (t == 0) *s_flag = bump(&a.seq_cnt[b]) == nkv - 1;
-        __syncthreads();
-        if (*s_flag && t < kReadyCopies) set_counter(&a.seq_ready[(b * kReadyCopies + t) * kReadyStride], 1);
+        if (t < kReadyCopies) add_counter(&a.seq_ready[(b * kReadyCopies + t) * kReadyStride]);
     }
     DAB_TRACE_POINT(a, 6);
 }

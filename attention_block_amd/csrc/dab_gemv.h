@@ -161,12 +161,10 @@ template <typename T, bool SIGNAL>
 __device__ void qkv_finish(const StepArgs& a, int panel, int wave, int bb, int hd, int e, int row0, float u0,
                            float u1, const float* ss) {
     const int H = a.H, D = a.D, half = D >> 1;
-    // re-arm the merge counter and ready flags of this sequence for the
-    // attention kernel that follows (it runs after this kernel completes)
-    if (panel == 0 && wave == 0) {
-        set_counter(&a.seq_cnt[bb], 0);
+    // re-arm the ready counts of this sequence for the attention kernel that
+    // follows (it runs after this kernel completes)
+    if (panel == 0 && wave == 0)
         for (int i = 0; i < kReadyCopies; ++i) set_counter(&a.seq_ready[(bb * kReadyCopies + i) * kReadyStride], 0);
-    }
     const float sum_sq = ss[0] + ss[1] + ss[2] + ss[3];
     const float r = 1.0f / sqrtf(sum_sq / (float)H + a.eps);
     u0 *= r;
@@ -348,7 +346,7 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
                 if ((valid >> j) & 1u)
-                    wait_at_least<8>(&a.seq_ready[((b0 + j) * kReadyCopies + copy) * kReadyStride], 1, a.flags);
+                    wait_at_least<8>(&a.seq_ready[((b0 + j) * kReadyCopies + copy) * kReadyStride], a.nkv, a.flags);
         }
         __syncthreads();
         // 2. attention outputs into LDS (zeros for sequences without one):

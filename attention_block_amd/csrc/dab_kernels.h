@@ -32,8 +32,7 @@ struct StepArgs {
     // workspace
     int* flags;             // error bits
     int* attn_cnt;          // [B * nkv] chunk arrivals (re-armed by the merging workgroup)
-    int* seq_cnt;           // [B] kv groups merged (one-launch attention + projection; re-armed by the QKV kernel)
-    int* seq_ready;         // [B, kReadyCopies] x kReadyStride: 1 once every group of the sequence is merged
+    int* seq_ready;         // [B, kReadyCopies] x kReadyStride: kv groups of the sequence merged so far (one-launch attention + projection; re-armed by the QKV kernel)
     int* head_cnt;          // [qkv.nbg, nq + 2 nkv] QKV panels done per (batch group, head) (one-launch
                             // QKV + attention; re-armed by the output projection kernel)
     float* q;               // [B, n_q] rotated q
@@ -92,5 +91,8 @@ hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t
 // per-dtype instantiations (separate translation units)
 hipError_t launch_phase_bf16(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_phase_f32(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev);
+// Workgroups of the phased schedule's attention kernel one CU holds at once (0: unknown).
+int attn_resident_bf16(int D, int G);
+int attn_resident_f32(int D, int G);
 
 }  // namespace dab

@@ -355,6 +355,30 @@ hipError_t launch_qkv_attn(const StepArgs& a, const Plan& p, hipStream_t s, cons
     }
 }
 
+// Workgroups of the phased schedule's attention kernel one CU holds at once
+// (0 if the runtime cannot say).
+template <typename T, int D>
+int attn_resident_d(int G) {
+    const void* f = nullptr;
+    switch (G) {
+#define DAB_G(NG) case NG: f = reinterpret_cast<const void*>(attn_kernel<T, D, NG>); break;
+        DAB_G(1) DAB_G(2) DAB_G(3) DAB_G(4) DAB_G(5) DAB_G(6) DAB_G(7) DAB_G(8)
+#undef DAB_G
+        default: return 0;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kThreads, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return n;
+}
+
+template <typename T>
+int attn_resident(int D, int G) {
+    return D == 128 ? attn_resident_d<T, 128>(G) : D == 64 ? attn_resident_d<T, 64>(G) : 0;
+}
+
 template <typename T>
 hipError_t launch_phase_t(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev) {
     if (p.schedule == DAB_SCHEDULE_QKV_ATTN) return phase == 0 ? launch_qkv_attn<T>(a, p, s, ev) : launch_oproj<T>(a, p, s, ev);

@@ -60,7 +60,7 @@ struct Plan {
 
     // workspace layout, byte offsets (each 256-byte aligned); the flags
     // word is at offset 0
-    size_t off_flags = 0, off_attn_cnt = 0, off_seq_cnt = 0, off_seq_ready = 0, off_head_cnt = 0;
+    size_t off_flags = 0, off_attn_cnt = 0, off_seq_ready = 0, off_head_cnt = 0;
     size_t off_q = 0, off_kv_new = 0;
     size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0, off_a16 = 0;
     size_t ws_bytes = 0;
@@ -90,7 +90,10 @@ dab_status check_ffn_call(const FfnPlan& p, const void* hidden, const void* norm
 
 // Validate `cfg` and fill `plan`.  Returns DAB_OK, DAB_ERR_INVALID_ARG or
 // DAB_ERR_UNSUPPORTED.  Makes no HIP calls.
-dab_status make_plan(const dab_config* cfg, Plan* plan);
+// attn_slots: attention workgroups of the phased schedule's attention kernel
+// the device holds at once for this shape (CUs x resident per CU), 0 if
+// unknown; it only steers the split-KV chunk length.
+dab_status make_plan(const dab_config* cfg, Plan* plan, int attn_slots = 0);
 
 // Validate the pointers of a call against a plan: non-null where required,
 // 16-byte aligned, `out` disjoint from every other argument, workspace large
