@@ -76,7 +76,8 @@ typedef struct {
     int32_t dtype;           /* dab_dtype                                               */
     float rope_theta;        /* RoPE base, > 0                                          */
     float eps;               /* RMSNorm epsilon, >= 0 (1e-6 in the pages' kernels)      */
-    int32_t kv_chunk;        /* cached tokens per split-KV work item: 0 = automatic,    */
+    int32_t kv_chunk;        /* cached tokens per split-KV work item: 0 = automatic     */
+                             /* (sized for the current device: see dab_workspace_size), */
                              /* else a multiple of 16 in [32, 4096]                     */
     int32_t schedule;        /* dab_schedule: how the step is laid out on the GPU        */
 } dab_config;
@@ -113,7 +114,11 @@ typedef enum {
  * re-arms the counters it uses, so later calls with the SAME configuration
  * (on one stream at a time) reuse it as is.  The layout depends on the
  * configuration: before a call with another configuration, initialise it
- * again.
+ * again.  With kv_chunk = 0 the chunk length, and so the size, also depends
+ * on how many attention workgroups the current HIP device holds at once (read
+ * from the runtime on first use, then cached per device): size and call on
+ * the same device.  Without a device the size is the one of a device-free
+ * plan.
  */
 size_t dab_workspace_size(const dab_config* cfg);
 

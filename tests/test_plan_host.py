@@ -1,0 +1,66 @@
+"""The launch planner's split-KV chunk choice, on the CPU.
+
+dab_plan.cpp holds no HIP code; it is built here with g++ (host sanitizers on) together with
+tests/plan_host.cpp, which prints the plan of one configuration for a given number of attention
+workgroups the device holds at once (the library reads that number from the HIP runtime).
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "attention_block_amd", "csrc")
+
+PHASED, ATTN_OPROJ, AUTO = 1, 2, 0
+BF16 = 1
+
+
+@pytest.fixture(scope="module")
+def plan_host(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not found")
+    exe = str(tmp_path_factory.mktemp("plan") / "plan_host")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(ROOT, "tests", "plan_host.cpp"), os.path.join(CSRC, "dab_plan.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True)
+
+    def run(B, H, nq, nkv, D, cap, schedule=AUTO, slots=0, dtype=BF16):
+        out = subprocess.run([exe] + [str(v) for v in (B, H, nq, nkv, D, cap, dtype, schedule, slots)],
+                             check=True, capture_output=True, text=True).stdout.split()
+        st, sched, T, maxc, grid, split = map(int, out)
+        assert st == 0
+        return dict(schedule=sched, T=T, max_chunks=maxc, grid=grid, split_merge=bool(split))
+    return run
+
+
+def test_one_round_of_resident_workgroups(plan_host):
+    # 8B GQA layer, batch 16, 4K tokens: 1024 chunks of 448 tokens would need a partial second round
+    # of 768 resident workgroups (three per CU); one round of 6 chunks per (sequence, kv head) instead
+    p = plan_host(16, 4096, 32, 8, 128, 4097, slots=768)
+    assert p["schedule"] == PHASED and p["T"] == 688 and p["max_chunks"] == 6 and p["grid"] == 768
+    # without the device's figure: the device-free rule
+    p0 = plan_host(16, 4096, 32, 8, 128, 4097, slots=0)
+    assert p0["T"] == 448 and p0["grid"] == 16 * 8 * 10
+
+
+def test_residency_rule_leaves_other_shapes(plan_host):
+    # 7B layer, batch 1: 512 chunks of 256 tokens fit one round; attention + projection in one launch
+    p = plan_host(1, 4096, 32, 32, 128, 4097, slots=1280)
+    assert p["schedule"] == ATTN_OPROJ and p["T"] == 256 and p["grid"] == 512
+    # long context, batch 1: at most 64 chunks per kv head, 512 chunks fit one round
+    p = plan_host(1, 4096, 32, 8, 128, 16385, slots=768)
+    assert p["T"] == 256 and p["max_chunks"] == 64 and p["split_merge"]
+    # ragged batch 32 up to 8192 tokens: one round would need chunks over 1024 tokens; 448-token chunks
+    p = plan_host(32, 4096, 32, 8, 128, 8193, slots=768)
+    assert p["T"] == 448 and p["max_chunks"] == 19 and p["split_merge"]
+
+
+def test_chunks_cover_every_cached_token(plan_host):
+    for B, nkv, cap, slots in ((16, 8, 4097, 768), (3, 2, 1001, 768), (64, 8, 2049, 512), (8, 8, 30001, 768)):
+        p = plan_host(B, 1024, 2 * nkv, nkv, 128, cap, slots=slots)
+        assert p["T"] % 16 == 0 and p["T"] * p["max_chunks"] >= cap - 1 > p["T"] * (p["max_chunks"] - 1)
+        assert p["grid"] == B * nkv * p["max_chunks"]
