@@ -47,6 +47,18 @@ def test_one_round_of_resident_workgroups(plan_host):
     assert p0["T"] == 448 and p0["grid"] == 16 * 8 * 10
 
 
+def test_one_head_per_kv_head_takes_whole_buffers(plan_host):
+    # one query head per kv head: chunks are whole buffers of 128 tokens (D 128) or 256 (D 64)
+    p = plan_host(1, 4096, 32, 32, 128, 1025, slots=1280)
+    assert p["schedule"] == ATTN_OPROJ and p["T"] == 128 and p["grid"] == 256
+    p = plan_host(1, 4096, 64, 64, 64, 1025, slots=1280)
+    assert p["T"] == 256 and p["max_chunks"] == 4
+    # grouped heads keep the plain rule: about 512 chunks, here 16 of 64 tokens per kv head (64 tokens
+    # is the rule's lower limit at D 128)
+    p = plan_host(1, 4096, 32, 8, 128, 1025, slots=768)
+    assert p["T"] == 64 and p["grid"] == 8 * 16
+
+
 def test_residency_rule_leaves_other_shapes(plan_host):
     # 7B layer, batch 1: 512 chunks of 256 tokens fit one round; attention + projection in one launch
     p = plan_host(1, 4096, 32, 32, 128, 4097, slots=1280)
