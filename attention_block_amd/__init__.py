@@ -12,11 +12,11 @@ import ctypes
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import DAB_BF16, DAB_F32, FFN_PHASES, DabConfig, DabFfnConfig
+from ._lib import DAB_BF16, DAB_F32, FFN_PHASES, READ_PROBE_BLOCKS, DabConfig, DabFfnConfig
 
 __all__ = ["DabError", "DabConfig", "make_config", "workspace_size", "Workspace", "decode_attn_block",
            "decode_attn_block_timed", "read_device_error", "phase_names", "HipEvent", "lib_version",
-           "DabFfnConfig", "FFN_PHASES", "ffn_workspace_size", "decode_ffn_block", "decode_ffn_block_timed"]
+           "DabFfnConfig", "FFN_PHASES", "ffn_workspace_size", "decode_ffn_block", "decode_ffn_block_timed", "read_probe", "READ_PROBE_BLOCKS"]
 
 
 class DabError(RuntimeError):
@@ -316,6 +316,21 @@ def decode_ffn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_gate, w
         _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device), arr, len(events)),
         "dab_decode_ffn_block_timed")
     return out
+
+
+def read_probe(buffer, out) -> None:
+    """One plain stream over `buffer` (a contiguous device tensor, 16-byte aligned, a whole number of
+    16-byte vectors) with the step's 16-byte non-temporal loads; `out` (a device tensor of at least
+    READ_PROBE_BLOCKS 32-bit words) receives each workgroup's XOR of the words it read.  Asynchronous
+    on the current stream: time it with events to get the HBM read bandwidth a plain stream attains."""
+    import torch
+    lib = _lib.load()
+    if not (buffer.is_cuda and out.is_cuda and buffer.is_contiguous() and out.is_contiguous()):
+        raise ValueError("read_probe: contiguous device tensors required")
+    nbytes = buffer.numel() * buffer.element_size()
+    st = lib.dab_read_probe(ctypes.c_void_p(buffer.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                            out.numel() * out.element_size(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    _check(st, "dab_read_probe")
 
 
 def read_device_error(workspace: Optional[Workspace] = None, device=None) -> int:

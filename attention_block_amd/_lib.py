@@ -17,7 +17,9 @@ EXPORTS = (
     "dab_workspace_size", "dab_workspace_init", "dab_decode_attn_block", "dab_decode_attn_block_timed",
     "dab_phase_count", "dab_phase_name", "dab_read_device_error", "dab_status_string", "dab_version",
     "dab_last_hip_error", "dab_ffn_workspace_size", "dab_decode_ffn_block", "dab_decode_ffn_block_timed",
+    "dab_read_probe",
 )
+READ_PROBE_BLOCKS = 2048      # DAB_READ_PROBE_BLOCKS
 # names of the two FFN kernels, in launch order
 FFN_PHASES = ("ffn_rmsnorm_gate_up_silu", "ffn_down_residual")
 
@@ -84,6 +86,8 @@ def load() -> ctypes.CDLL:
     lib.dab_version.restype = ctypes.c_char_p
     lib.dab_last_hip_error.argtypes = []
     lib.dab_last_hip_error.restype = ctypes.c_char_p
+    lib.dab_read_probe.argtypes = [vp, sz, vp, sz, vp]
+    lib.dab_read_probe.restype = i32
     ffnp = ctypes.POINTER(DabFfnConfig)
     lib.dab_ffn_workspace_size.argtypes = [ffnp]
     lib.dab_ffn_workspace_size.restype = sz

@@ -223,6 +223,39 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
         p[i] = 0u;
 }
 
+typedef unsigned int probe_u32x4 __attribute__((ext_vector_type(4)));
+
+// A plain stream over n16 16-byte vectors in chunks of 64 KB, as the
+// row panels read their weights: workgroup w takes chunks w, w + G, ...
+// (G workgroups); thread t reads vectors t, t + 256, ..., t + 15 * 256 of a
+// chunk, all sixteen requested before any is used, so one wave-wide load
+// covers 1 KB.  Each workgroup's XOR of its words goes to out.
+__global__ __launch_bounds__(256) void read_probe_kernel(const probe_u32x4* p, size_t n16, uint32_t* out) {
+    constexpr int V = 16;
+    constexpr size_t kChunk = 256 * V;            // vectors per chunk
+    __shared__ uint32_t red[4];
+    uint32_t acc = 0u;
+    for (size_t c = blockIdx.x; c * kChunk < n16; c += gridDim.x) {
+        const size_t base = c * kChunk + threadIdx.x;
+        probe_u32x4 v[V];
+        if ((c + 1) * kChunk <= n16) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) v[k] = __builtin_nontemporal_load(p + base + (size_t)k * 256);
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                v[k] = base + (size_t)k * 256 < n16 ? __builtin_nontemporal_load(p + base + (size_t)k * 256)
+                                                    : probe_u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+    }
+    for (int off = 32; off > 0; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
 }  // namespace
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
@@ -259,6 +292,16 @@ size_t dab_workspace_size(const dab_config* cfg) {
     Plan p;
     if (plan(cfg, &p) != DAB_OK) return 0;
     return p.ws_bytes;
+}
+
+dab_status dab_read_probe(const void* buffer, size_t bytes, void* out, size_t out_bytes, void* stream) {
+    if (!buffer || !out || ((uintptr_t)buffer % 16) != 0 || ((uintptr_t)out % 4) != 0 || bytes % 16 != 0 ||
+        out_bytes < (size_t)DAB_READ_PROBE_BLOCKS * 4)
+        return DAB_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(dab::read_probe_kernel, dim3(DAB_READ_PROBE_BLOCKS), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const dab::probe_u32x4*>(buffer), bytes / 16,
+                       static_cast<uint32_t*>(out));
+    return hip_status(hipGetLastError());
 }
 
 dab_status dab_workspace_init(void* workspace, size_t bytes, void* stream) {

@@ -267,6 +267,40 @@ def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: st
     return written
 
 
+def read_probe(nbytes: int, device, stream_gib: float = 2.0, reps: int = 20) -> dict:
+    """The library's read probe (one plain stream with the step's 16-byte non-temporal loads) as a
+    bandwidth reference: over `stream_gib` GiB, and over exactly `nbytes` (the step's algorithmic bytes),
+    cycling through enough distinct buffers that no launch is served from the Infinity Cache."""
+    import torch
+    import attention_block_amd as ab
+    out = torch.empty(ab.READ_PROBE_BLOCKS, dtype=torch.int32, device=device)
+
+    def timed(bufs, n):
+        for b in bufs[:2]:
+            ab.read_probe(b, out)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(n):
+            ab.read_probe(bufs[i % len(bufs)], out)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) * 1e3 / n          # us per launch
+
+    big = int(stream_gib * (1 << 30)) // 16 * 16
+    buf = torch.ones(big // 4, dtype=torch.int32, device=device)
+    us_big = timed([buf], reps)
+    del buf
+    step = max(16, nbytes // 16 * 16)
+    nbuf = max(3, math.ceil(2 * MALL_BYTES / step) + 1)
+    bufs = [torch.ones(step // 4, dtype=torch.int32, device=device) for _ in range(nbuf)]
+    us_step = timed(bufs, max(reps, 4 * nbuf))
+    del bufs
+    return {"stream_gib": stream_gib, "stream_gbps": round(big / (us_big * 1e-6) / 1e9, 1),
+            "step_bytes": step, "step_bytes_us": round(us_step, 3),
+            "step_bytes_gbps": round(step / (us_step * 1e-6) / 1e9, 1)}
+
+
 def graph_time(step, steps: int, R: int) -> float:
     """Microseconds per step over exactly `steps` steps replayed from HIP graphs.
 
@@ -524,6 +558,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the plain-stream bandwidth reference (the library's read probe)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 csv output (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass of a "
                          "--copy-probe-mb run; '-' for no counter passes) into the summaries under profiles/ "
@@ -627,6 +663,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(f"copy probe: {n * 4} bytes read, {n * 4} bytes written", file=sys.stderr)
 
+    probe = None if args.no_read_probe else read_probe(nbytes, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.seed, args.cpu_budget)
@@ -654,6 +692,7 @@ def main() -> int:
         "algorithmic_flops": flops,
         "roofline": roofline,
         "phases": phase_report,
+        "hbm_read_probe": probe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -205,6 +205,23 @@ const char* dab_last_hip_error(void);
 const char* dab_version(void);
 
 /*
+ * Measurement aid, not part of the step: streams `bytes` of device memory at
+ * `buffer` once with the 16-byte non-temporal loads the step's kernels use,
+ * in 64 KB chunks as the row panels read their weights (DAB_READ_PROBE_BLOCKS
+ * workgroups of 256 threads; workgroup w takes chunks w, w + blocks, ...;
+ * thread t the vectors t, t + 256, ..., t + 15 * 256 of a chunk, sixteen
+ * loads in flight, one wave-wide load covering 1 KB), and writes each
+ * workgroup's XOR of the 32-bit words it read to out[workgroup] (device,
+ * uint32), so that no load can be dropped.  Timed with events around it, it gives the HBM read bandwidth a
+ * plain stream attains, the practical ceiling the step's kernels are set
+ * against.  buffer: 16-byte aligned, bytes a multiple of 16; out: at least
+ * DAB_READ_PROBE_BLOCKS * 4 bytes.  Asynchronous on `stream`; returns
+ * DAB_ERR_INVALID_ARG on a null or misaligned pointer or a bad size.
+ */
+#define DAB_READ_PROBE_BLOCKS 2048
+dab_status dab_read_probe(const void* buffer, size_t bytes, void* out, size_t out_bytes, void* stream);
+
+/*
  * The feed-forward half of the decoder layer, the step after the attention
  * block: the operator-fusion article ("LayerNorm + Attention" CUDA kernel
  * page, section 1) lists a second RMS norm and the FFN after the O

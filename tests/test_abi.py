@@ -165,6 +165,14 @@ def test_null_and_misaligned_pointers(lib):
     assert call(lib, c, dbg_y=(1 << 42) + 4) == _lib.DAB_ERR_INVALID_ARG
 
 
+def test_read_probe_host_checks(lib):
+    # checked on the host before anything is enqueued (the pointers are never touched)
+    buf, out, n = (1 << 40), (1 << 41), 4096
+    for args in ((0, n, out, 8192), (buf, n, 0, 8192), (buf + 8, n, out, 8192), (buf, n + 4, out, 8192),
+                 (buf, n, out + 2, 8192), (buf, n, out, 4 * _lib.READ_PROBE_BLOCKS - 4)):
+        assert lib.dab_read_probe(*args, None) == _lib.DAB_ERR_INVALID_ARG, args
+
+
 def test_workspace_checks(lib):
     c = cfg()
     assert call(lib, c, ws=0) == _lib.DAB_ERR_WORKSPACE
