@@ -34,40 +34,53 @@ dab_status hip_status(hipError_t e) {
     return DAB_ERR_HIP;
 }
 
-// Attention workgroups the current device holds at once for cfg's shape
-// (CUs x the phased attention kernel's residency per CU), cached per device,
-// storage type, head dim and group; 0 without a device.  Every planning call
-// goes through it, so the workspace size and the launch agree.
+// The current device's compute units and how many workgroups of the phased
+// attention kernel for cfg's shape one of them holds at once, cached per
+// device, storage type, head dim and group; zeros without a device.  Every
+// planning call goes through it, so the workspace size and the launch agree.
 constexpr int kSlotDevices = 16;
-std::atomic<int> g_slots[kSlotDevices][2][2][dab::kMaxGroup + 1];   // 0: not yet asked; -1: unknown
+std::atomic<int> g_cus[kSlotDevices];                               // 0: not yet asked; -1: unknown
+std::atomic<int> g_per_cu[kSlotDevices][2][2][dab::kMaxGroup + 1];   // 0: not yet asked; -1: unknown
 
-int attn_slots(const dab_config* cfg) {
-    if (!cfg || cfg->n_kv_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads != 0) return 0;
+void attn_residency(const dab_config* cfg, int* cus_out, int* per_cu_out) {
+    *cus_out = 0;
+    *per_cu_out = 0;
+    if (!cfg || cfg->n_kv_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads != 0) return;
     const int G = cfg->n_q_heads / cfg->n_kv_heads;
     const int di = cfg->head_dim == 128 ? 1 : cfg->head_dim == 64 ? 0 : -1;
     const int ti = cfg->dtype == DAB_BF16 ? 1 : cfg->dtype == DAB_F32 ? 0 : -1;
-    if (G < 1 || G > dab::kMaxGroup || di < 0 || ti < 0) return 0;
+    if (G < 1 || G > dab::kMaxGroup || di < 0 || ti < 0) return;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSlotDevices) {
         (void)hipGetLastError();
-        return 0;
+        return;
     }
-    std::atomic<int>& slot = g_slots[dev][ti][di][G];
-    int v = slot.load(std::memory_order_relaxed);
-    if (v == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    int cus = g_cus[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
             (void)hipGetLastError();
-            cus = 0;
+            cus = -1;
         }
-        const int per_cu = ti ? dab::attn_resident_bf16(cfg->head_dim, G) : dab::attn_resident_f32(cfg->head_dim, G);
-        v = cus > 0 && per_cu > 0 ? cus * per_cu : -1;
-        slot.store(v, std::memory_order_relaxed);
+        g_cus[dev].store(cus, std::memory_order_relaxed);
     }
-    return v > 0 ? v : 0;
+    std::atomic<int>& slot = g_per_cu[dev][ti][di][G];
+    int per_cu = slot.load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+        per_cu = ti ? dab::attn_resident_bf16(cfg->head_dim, G) : dab::attn_resident_f32(cfg->head_dim, G);
+        if (per_cu <= 0) per_cu = -1;
+        slot.store(per_cu, std::memory_order_relaxed);
+    }
+    if (cus > 0 && per_cu > 0) {
+        *cus_out = cus;
+        *per_cu_out = per_cu;
+    }
 }
 
-dab_status plan(const dab_config* cfg, Plan* p) { return dab::make_plan(cfg, p, attn_slots(cfg)); }
+dab_status plan(const dab_config* cfg, Plan* p) {
+    int cus, per_cu;
+    attn_residency(cfg, &cus, &per_cu);
+    return dab::make_plan(cfg, p, cus, per_cu);
+}
 
 int phase_count(const Plan& p) {
     return p.schedule == DAB_SCHEDULE_PHASED ? (p.split_merge ? 4 : 3) : 2;

@@ -97,6 +97,19 @@ template <> struct Vec8<float> {               // fp32: two 16-byte loads
 __device__ inline float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 __device__ inline float to_f32(float v) { return v; }
 
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (nearest-even), lo in the low half.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// a.lo * b.lo + a.hi * b.hi + c over packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
+}
+
 template <typename T> __device__ inline T from_f32(float f);
 template <> __device__ inline float from_f32<float>(float f) { return f; }
 template <> __device__ inline uint16_t from_f32<uint16_t>(float f) {
@@ -353,6 +366,33 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[j][e] *= a.qscale;
     }
+    // Grouped heads over a bf16 cache: scores and values by bf16 pair dot
+    // products (v_dot2c_f32_bf16, fp32 accumulation), K and V used as they
+    // are stored, q rounded to bf16 once per chunk, the weights p rounded to
+    // bf16 for the values (each a relative 2^-9); the vector ALUs bound this
+    // loop, and the unpacking and the separate multiplies were a third of it.
+    constexpr bool DOT2 = sizeof(T) == 2 && G > 1;
+    uint32_t qp[DOT2 ? G : 1][4];
+    if constexpr (DOT2) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qp[j][i] = pack_bf16x2(qv[j][2 * i], qv[j][2 * i + 1]);
+    }
+    // this lane's part of head j's score for a token row
+    auto score = [&](const Vec8<T>& k, int j) {
+        float d = 0.f;
+        if constexpr (DOT2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d = dot2_bf16(k.r[i], qp[j][i], d);
+        } else {
+            float kf[8];
+            k.unpack(kf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d = fmaf(qv[j][e], kf[e], d);
+        }
+        return d;
+    };
     DAB_TRACE_POINT(a, 2);
     float m[G], ls[G], o[G][8];
 #pragma unroll
@@ -423,24 +463,51 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
                 m[j] = mx[j];
             }
         }
+        float pu[G][U];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            float pu[U], psum = 0.f;
+            float psum = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                pu[u] = u < nvalid ? __builtin_amdgcn_exp2f(s[j][u] - m[j]) : 0.f;
-                psum += pu[u];
+                pu[j][u] = u < nvalid ? __builtin_amdgcn_exp2f(s[j][u] - m[j]) : 0.f;
+                psum += pu[j][u];
             }
             ls[j] += psum;
+        }
+        if constexpr (DOT2) {
+            // token pairs (u, u + 1): their dims interleaved once for all heads
+            // (rows past the valid ones are zeros with weight 0)
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (u < nvalid) {
-                    float vf[8];
-                    vv[u].unpack(vf);
+            for (int u = 0; u < U; u += 2) {
+                uint32_t lo[4], hi[4];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) o[j][e] = fmaf(pu[u], vf[e], o[j][e]);
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a0 = vv[u].r[i], a1 = vv[u + 1].r[i];
+                    lo[i] = (a0 & 0xffffu) | (a1 << 16);            // dim 2i of both tokens
+                    hi[i] = (a0 >> 16) | (a1 & 0xffff0000u);        // dim 2i + 1
+                }
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    const uint32_t pp = pack_bf16x2(pu[j][u], pu[j][u + 1]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        o[j][2 * i] = dot2_bf16(pp, lo[i], o[j][2 * i]);
+                        o[j][2 * i + 1] = dot2_bf16(pp, hi[i], o[j][2 * i + 1]);
+                    }
                 }
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (u < nvalid) {
+                        float vf[8];
+                        vv[u].unpack(vf);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) o[j][e] = fmaf(pu[j][u], vf[e], o[j][e]);
+                    }
+                }
         }
     };
 
@@ -450,17 +517,9 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     auto process = [&](Vec8<T> (&kr)[U], Vec8<T> (&vr)[U], int hb0) {
         float s[G][U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float kf[8];
-            kr[u].unpack(kf);
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) d = fmaf(qv[j][e], kf[e], d);
-                s[j][u] = group_sum<LPR>(d);
-            }
-        }
+            for (int j = 0; j < G; ++j) s[j][u] = group_sum<LPR>(score(kr[u], j));
         const int left = t1 - hb0 - slot;                  // this slot's tokens hb0 + slot + NSLOT*u < t1
         const int nvalid = left <= 0 ? 0 : min(U, (left + NSLOT - 1) / NSLOT);
         if (nvalid > 0) absorb(s, vr, nvalid);
@@ -499,14 +558,27 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
         float s[G][U];
         Vec8<T> vv[U];
         vv[0].pack(vf);
+        if constexpr (DOT2) {
+            Vec8<T> kk;
+            kk.pack(kf);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            float d = 0.f;
+            for (int u = 1; u < U; ++u) vv[u].zero();   // weight 0, and no garbage in a pair product
 #pragma unroll
-            for (int e = 0; e < 8; ++e) d = fmaf(qv[j][e], kf[e], d);
-            s[j][0] = group_sum<LPR>(d);
+            for (int j = 0; j < G; ++j) {
+                s[j][0] = group_sum<LPR>(score(kk, j));
 #pragma unroll
-            for (int u = 1; u < U; ++u) s[j][u] = 0.f;
+                for (int u = 1; u < U; ++u) s[j][u] = 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d = fmaf(qv[j][e], kf[e], d);
+                s[j][0] = group_sum<LPR>(d);
+#pragma unroll
+                for (int u = 1; u < U; ++u) s[j][u] = 0.f;
+            }
         }
         absorb(s, vv, 1);
     }

@@ -66,7 +66,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
-dab_status make_plan(const dab_config* cfg, Plan* p, int attn_slots) {
+dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_cu) {
     if (!cfg || !p) return DAB_ERR_INVALID_ARG;
     *p = Plan();
     const dab_config& c = *cfg;
@@ -180,15 +180,18 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_slots) {
         // the 256 tokens of the rule above are two buffers already).
         if (p->G == 1) T = (T + 2 * half_batch - 1) / (2 * half_batch) * (2 * half_batch);
         // Phased schedule: where those chunks need more than one round of the
-        // attention kernel's resident workgroups but one round holds at least
-        // a chunk per (sequence, kv head), take exactly one round, up to 1024
-        // tokens a chunk (8B GQA layer, batch 16, 4K tokens, three chunks per
-        // CU: 1024 chunks of 512 tokens 66.8 us, 768 of 688 tokens 56.2 us on
-        // MI355X).  Longer chunks would unbalance ragged batches.
+        // attention kernel's resident workgroups, take two chunks per CU (all
+        // resident at once) if that still gives every (sequence, kv head) a
+        // chunk, up to 1024 tokens a chunk; longer chunks would unbalance
+        // ragged batches.  (8B GQA layer, batch 16, 4K tokens, four attention
+        // workgroups resident per CU, on MI355X: 512 chunks of 1024 tokens
+        // 86.4 us per step, 768 of 688 86.9, 1024 of 512 89.0, partial rounds
+        // of 640 or 896 chunks 91-94.)
         const long long pairs = (long long)B * p->nkv;
-        if (p->schedule == DAB_SCHEDULE_PHASED && attn_slots > 0 && pairs * ceil_div(hist, T) > attn_slots &&
-            pairs <= attn_slots) {
-            const int T1 = (ceil_div(hist, attn_slots / pairs) + 15) / 16 * 16;
+        const long long two_per_cu = 2LL * attn_cus;
+        if (p->schedule == DAB_SCHEDULE_PHASED && attn_cus > 0 && attn_per_cu >= 2 &&
+            pairs * ceil_div(hist, T) > (long long)attn_cus * attn_per_cu && pairs <= two_per_cu) {
+            const int T1 = (ceil_div(hist, two_per_cu / pairs) + 15) / 16 * 16;
             if (T1 <= 1024 && T1 > T) T = T1;
         }
         while (ceil_div(hist, T) > kMaxChunks) T += 512;

@@ -90,10 +90,10 @@ dab_status check_ffn_call(const FfnPlan& p, const void* hidden, const void* norm
 
 // Validate `cfg` and fill `plan`.  Returns DAB_OK, DAB_ERR_INVALID_ARG or
 // DAB_ERR_UNSUPPORTED.  Makes no HIP calls.
-// attn_slots: attention workgroups of the phased schedule's attention kernel
-// the device holds at once for this shape (CUs x resident per CU), 0 if
-// unknown; it only steers the split-KV chunk length.
-dab_status make_plan(const dab_config* cfg, Plan* plan, int attn_slots = 0);
+// attn_cus, attn_per_cu: the device's compute units and how many workgroups
+// of the phased schedule's attention kernel one of them holds at once for
+// this shape, 0 if unknown; they only steer the split-KV chunk length.
+dab_status make_plan(const dab_config* cfg, Plan* plan, int attn_cus = 0, int attn_per_cu = 0);
 
 // Validate the pointers of a call against a plan: non-null where required,
 // 16-byte aligned, `out` disjoint from every other argument, workspace large

@@ -1,15 +1,15 @@
 // Host driver of the launch planner (dab_plan.cpp is plain C++): prints the
-// split-KV chunk choice of a configuration for a given number of resident
-// attention workgroups.  Built with g++ by tests/test_plan_host.py.
-//   plan_host B H nq nkv D cap dtype schedule slots
+// split-KV chunk choice of a configuration for a given number of compute
+// units and resident attention workgroups per unit.  Built with g++ by tests/test_plan_host.py.
+//   plan_host B H nq nkv D cap dtype schedule cus per_cu
 #include <stdio.h>
 #include <stdlib.h>
 
 #include "dab_plan.h"
 
 int main(int argc, char** argv) {
-    if (argc != 10) {
-        fprintf(stderr, "usage: plan_host B H nq nkv D cap dtype schedule slots\n");
+    if (argc != 11) {
+        fprintf(stderr, "usage: plan_host B H nq nkv D cap dtype schedule cus per_cu\n");
         return 2;
     }
     dab_config c{};
@@ -25,7 +25,7 @@ int main(int argc, char** argv) {
     c.kv_chunk = 0;
     c.schedule = atoi(argv[8]);
     dab::Plan p;
-    const dab_status st = dab::make_plan(&c, &p, atoi(argv[9]));
+    const dab_status st = dab::make_plan(&c, &p, atoi(argv[9]), atoi(argv[10]));
     printf("%d %d %d %d %d %d\n", (int)st, p.schedule, p.kv_chunk, p.max_chunks, p.attn_grid, p.split_merge ? 1 : 0);
     return 0;
 }

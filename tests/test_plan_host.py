@@ -1,8 +1,8 @@
 """The launch planner's split-KV chunk choice, on the CPU.
 
 dab_plan.cpp holds no HIP code; it is built here with g++ (host sanitizers on) together with
-tests/plan_host.cpp, which prints the plan of one configuration for a given number of attention
-workgroups the device holds at once (the library reads that number from the HIP runtime).
+tests/plan_host.cpp, which prints the plan of one configuration for a given number of compute units and
+attention workgroups each holds at once (the library reads both from the HIP runtime).
 """
 import os
 import shutil
@@ -28,8 +28,8 @@ def plan_host(tmp_path_factory):
            os.path.join(ROOT, "tests", "plan_host.cpp"), os.path.join(CSRC, "dab_plan.cpp"), "-o", exe]
     subprocess.run(cmd, check=True, capture_output=True)
 
-    def run(B, H, nq, nkv, D, cap, schedule=AUTO, slots=0, dtype=BF16):
-        out = subprocess.run([exe] + [str(v) for v in (B, H, nq, nkv, D, cap, dtype, schedule, slots)],
+    def run(B, H, nq, nkv, D, cap, schedule=AUTO, cus=0, per_cu=0, dtype=BF16):
+        out = subprocess.run([exe] + [str(v) for v in (B, H, nq, nkv, D, cap, dtype, schedule, cus, per_cu)],
                              check=True, capture_output=True, text=True).stdout.split()
         st, sched, T, maxc, grid, split = map(int, out)
         assert st == 0
@@ -37,42 +37,45 @@ def plan_host(tmp_path_factory):
     return run
 
 
-def test_one_round_of_resident_workgroups(plan_host):
-    # 8B GQA layer, batch 16, 4K tokens: 1024 chunks of 448 tokens would need a partial second round
-    # of 768 resident workgroups (three per CU); one round of 6 chunks per (sequence, kv head) instead
-    p = plan_host(16, 4096, 32, 8, 128, 4097, slots=768)
-    assert p["schedule"] == PHASED and p["T"] == 688 and p["max_chunks"] == 6 and p["grid"] == 768
-    # without the device's figure: the device-free rule
-    p0 = plan_host(16, 4096, 32, 8, 128, 4097, slots=0)
+def test_two_chunks_per_cu_beyond_one_round(plan_host):
+    # 8B GQA layer, batch 16, 4K tokens: 1280 chunks of 448 tokens would need more than one round of
+    # the 1024 resident workgroups (4 per CU x 256 CUs); two chunks per CU instead: 4 of 1024 tokens
+    # per (sequence, kv head)
+    p = plan_host(16, 4096, 32, 8, 128, 4097, cus=256, per_cu=4)
+    assert p["schedule"] == PHASED and p["T"] == 1024 and p["max_chunks"] == 4 and p["grid"] == 512
+    # three per CU: 768 resident, still more than one round; the same two per CU
+    assert plan_host(16, 4096, 32, 8, 128, 4097, cus=256, per_cu=3)["grid"] == 512
+    # without the device's figures: the device-free rule
+    p0 = plan_host(16, 4096, 32, 8, 128, 4097)
     assert p0["T"] == 448 and p0["grid"] == 16 * 8 * 10
 
 
 def test_one_head_per_kv_head_takes_whole_buffers(plan_host):
     # one query head per kv head: chunks are whole buffers of 128 tokens (D 128) or 256 (D 64)
-    p = plan_host(1, 4096, 32, 32, 128, 1025, slots=1280)
+    p = plan_host(1, 4096, 32, 32, 128, 1025, cus=256, per_cu=5)
     assert p["schedule"] == ATTN_OPROJ and p["T"] == 128 and p["grid"] == 256
-    p = plan_host(1, 4096, 64, 64, 64, 1025, slots=1280)
+    p = plan_host(1, 4096, 64, 64, 64, 1025, cus=256, per_cu=5)
     assert p["T"] == 256 and p["max_chunks"] == 4
     # grouped heads keep the plain rule: about 512 chunks, here 16 of 64 tokens per kv head (64 tokens
     # is the rule's lower limit at D 128)
-    p = plan_host(1, 4096, 32, 8, 128, 1025, slots=768)
+    p = plan_host(1, 4096, 32, 8, 128, 1025, cus=256, per_cu=3)
     assert p["T"] == 64 and p["grid"] == 8 * 16
 
 
 def test_residency_rule_leaves_other_shapes(plan_host):
     # 7B layer, batch 1: 512 chunks of 256 tokens fit one round; attention + projection in one launch
-    p = plan_host(1, 4096, 32, 32, 128, 4097, slots=1280)
+    p = plan_host(1, 4096, 32, 32, 128, 4097, cus=256, per_cu=5)
     assert p["schedule"] == ATTN_OPROJ and p["T"] == 256 and p["grid"] == 512
     # long context, batch 1: at most 64 chunks per kv head, 512 chunks fit one round
-    p = plan_host(1, 4096, 32, 8, 128, 16385, slots=768)
+    p = plan_host(1, 4096, 32, 8, 128, 16385, cus=256, per_cu=3)
     assert p["T"] == 256 and p["max_chunks"] == 64 and p["split_merge"]
     # ragged batch 32 up to 8192 tokens: one round would need chunks over 1024 tokens; 448-token chunks
-    p = plan_host(32, 4096, 32, 8, 128, 8193, slots=768)
+    p = plan_host(32, 4096, 32, 8, 128, 8193, cus=256, per_cu=3)
     assert p["T"] == 448 and p["max_chunks"] == 19 and p["split_merge"]
 
 
 def test_chunks_cover_every_cached_token(plan_host):
-    for B, nkv, cap, slots in ((16, 8, 4097, 768), (3, 2, 1001, 768), (64, 8, 2049, 512), (8, 8, 30001, 768)):
-        p = plan_host(B, 1024, 2 * nkv, nkv, 128, cap, slots=slots)
+    for B, nkv, cap, per_cu in ((16, 8, 4097, 3), (3, 2, 1001, 3), (64, 8, 2049, 2), (8, 8, 30001, 4)):
+        p = plan_host(B, 1024, 2 * nkv, nkv, 128, cap, cus=256, per_cu=per_cu)
         assert p["T"] % 16 == 0 and p["T"] * p["max_chunks"] >= cap - 1 > p["T"] * (p["max_chunks"] - 1)
         assert p["grid"] == B * nkv * p["max_chunks"]
