@@ -16,7 +16,15 @@ from ._lib import DAB_BF16, DAB_F32, FFN_PHASES, READ_PROBE_BLOCKS, DabConfig, D
 
 __all__ = ["DabError", "DabConfig", "make_config", "workspace_size", "Workspace", "decode_attn_block",
            "decode_attn_block_timed", "read_device_error", "phase_names", "HipEvent", "lib_version",
-           "DabFfnConfig", "FFN_PHASES", "ffn_workspace_size", "decode_ffn_block", "decode_ffn_block_timed", "read_probe", "READ_PROBE_BLOCKS"]
+           "DabFfnConfig", "FFN_PHASES", "ffn_workspace_size", "decode_ffn_block", "decode_ffn_block_timed",
+           "read_probe", "READ_PROBE_BLOCKS", "pack_weight", "attention_output", "WEIGHT_LAYOUTS"]
+
+# Weight layouts a call may name: "out_in" is the library's own ([out_features, in_features], one
+# output feature per row, as torch.nn.Linear stores its weight); "in_out" is the pages' ([in, out],
+# y = x @ W), converted by the library's pack kernel into temporaries on every call.  The layout is a
+# required argument because a square matrix (W_o of an MHA layer with nq * D == H) has the same shape
+# in both.
+WEIGHT_LAYOUTS = ("out_in", "in_out")
 
 
 class DabError(RuntimeError):
@@ -118,9 +126,35 @@ def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
 
 
-def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
-             schedule):
+def pack_weight(w, out=None):
+    """[in_features, out_features] -> [out_features, in_features] on the device (dab_pack_weight).
+
+    w: a contiguous 2-D bfloat16 or float32 GPU tensor in the pages' layout (y = x @ w).  Returns (or
+    fills `out`, contiguous, same dtype and device) the library's layout, bit for bit; asynchronous on
+    the current stream.  Pack static weights once at load time."""
     import torch
+    if w.dim() != 2 or not w.is_cuda or not w.is_contiguous() or w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("pack_weight: a contiguous 2-D bfloat16 or float32 GPU tensor is required")
+    n_in, n_out = w.shape
+    if out is None:
+        out = torch.empty((n_out, n_in), dtype=w.dtype, device=w.device)
+    elif out.shape != (n_out, n_in) or out.dtype != w.dtype or out.device != w.device or not out.is_contiguous():
+        raise ValueError(f"pack_weight: out must be a contiguous [{n_out}, {n_in}] {w.dtype} tensor on {w.device}")
+    _check(_lib.load().dab_pack_weight(_ptr(w), _ptr(out), n_in, n_out,
+                                       DAB_BF16 if w.dtype == torch.bfloat16 else DAB_F32, _stream_ptr(w.device)),
+           "dab_pack_weight")
+    return out
+
+
+def _layout(weight_layout: str) -> None:
+    if weight_layout not in WEIGHT_LAYOUTS:
+        raise ValueError(f"weight_layout must be one of {WEIGHT_LAYOUTS}, not {weight_layout!r}")
+
+
+def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
+             schedule, weight_layout):
+    import torch
+    _layout(weight_layout)
     if hidden.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("hidden must be bfloat16 or float32")
     dt = hidden.dtype
@@ -141,6 +175,14 @@ def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps,
         raise ValueError("batch or hidden size mismatch")
     if w_qkv.dim() != 2 or w_o.dim() != 2:
         raise ValueError("w_qkv and w_o must be 2-D")
+    if weight_layout == "in_out":
+        n_qkv = w_qkv.shape[1]
+        if w_qkv.shape[0] != H or n_qkv % D or n_qkv // D <= 2 * nkv:
+            raise ValueError("w_qkv must be [H, (nq + 2 nkv) D] (weight_layout='in_out')")
+        nq = n_qkv // D - 2 * nkv
+        if w_o.shape != (nq * D, H):
+            raise ValueError(f"w_o must be [{nq * D}, {H}] (weight_layout='in_out')")
+        w_qkv, w_o = pack_weight(w_qkv), pack_weight(w_o)
     n_qkv = w_qkv.shape[0]
     if w_qkv.shape[1] != H or n_qkv % D or n_qkv // D <= 2 * nkv:
         raise ValueError("w_qkv must be [(nq + 2 nkv) D, H] (one output feature per row)")
@@ -157,31 +199,54 @@ def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps,
     cfg = make_config(batch=B, hidden=H, n_q_heads=nq, n_kv_heads=nkv, head_dim=D, cache_capacity=cap,
                       dtype="bf16" if dt == torch.bfloat16 else "f32", rope_theta=rope_theta, eps=eps,
                       kv_chunk=kv_chunk, schedule=schedule)
-    return cfg, out
+    return cfg, out, w_qkv, w_o
 
 
 def decode_attn_block(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta: float, eps: float = 1e-6,
                       out=None, dbg_y=None, workspace: Optional[Workspace] = None, kv_chunk: int = 0,
-                      schedule: str = "auto"):
+                      schedule: str = "auto", *, weight_layout: str):
     """One decode step on the current stream; returns `out`.
 
-    Shapes: hidden [B, H]; norm_w [H]; w_qkv [(nq+2nkv)D, H] and w_o [H, nq D]
-    (one output feature per row, as torch.nn.Linear stores its weight);
-    k_cache, v_cache [B, cap, nkv, D] (row pos[b] is written); pos int32 [B];
-    all but pos in one dtype (bfloat16 or float32) on one GPU.  dbg_y
-    (optional, float32 [B, H]) receives the pre-residual a @ W_o^T.
+    Shapes: hidden [B, H]; norm_w [H]; k_cache, v_cache [B, cap, nkv, D] (row
+    pos[b] is written); pos int32 [B]; all but pos in one dtype (bfloat16 or
+    float32) on one GPU.  weight_layout (required) names the layout of w_qkv
+    and w_o: "out_in", the library's (w_qkv [(nq+2nkv)D, H], w_o [H, nq D],
+    one output feature per row, as torch.nn.Linear stores its weight), or
+    "in_out", the pages' (w_qkv [H, (nq+2nkv)D], w_o [nq D, H]), packed by the
+    library's kernel into temporaries on every call (pack once with
+    pack_weight for repeated calls).  dbg_y (optional, float32 [B, H])
+    receives the pre-residual attention-output projection.
     schedule: "phased" (one kernel per phase), "attn_oproj" (attention and
     the output projection in one launch), "qkv_attn" (QKV and attention in
     one launch) or "auto" (the fastest that applies).
     """
-    cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
-                        schedule)
+    cfg, out, w_qkv, w_o = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y,
+                                    kv_chunk, schedule, weight_layout)
     ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)
     _check(_lib.load().dab_decode_attn_block(
         ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache), _ptr(v_cache),
         _ptr(pos), _ptr(out), _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device)),
         "dab_decode_attn_block")
     return out
+
+
+def attention_output(cfg: DabConfig, workspace: Workspace, out=None):
+    """The attention output a [B, nq * D] (float32, head-major) that the last call with configuration `cfg`
+    left in `workspace` (dab_attention_output): a test tap, copied on the current stream."""
+    import torch
+    n = cfg.batch * cfg.n_q_heads * cfg.head_dim
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.n_q_heads * cfg.head_dim), dtype=torch.float32, device=workspace.device)
+    elif out.numel() != n or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("attention_output: out must be a contiguous float32 tensor of B * nq * D elements")
+    _check(_lib.load().dab_attention_output(ctypes.byref(cfg), ctypes.c_void_p(workspace.ptr), workspace.nbytes,
+                                            _ptr(out), _stream_ptr(workspace.device)), "dab_attention_output")
+    return out
+
+
+def workspace_of(cfg: DabConfig, device) -> Workspace:
+    """The default workspace calls without a `workspace` argument use for this configuration and device."""
+    return _workspace_for(cfg, device)
 
 
 class HipEvent:
@@ -231,11 +296,12 @@ class HipEvent:
 
 def decode_attn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos,
                             rope_theta: float, eps: float = 1e-6, out=None, dbg_y=None,
-                            workspace: Optional[Workspace] = None, kv_chunk: int = 0, schedule: str = "auto"):
+                            workspace: Optional[Workspace] = None, kv_chunk: int = 0, schedule: str = "auto", *,
+                            weight_layout: str):
     """decode_attn_block that also records events[2i], events[2i + 1] at the start and end of kernel i
     (2 * len(phase_names) events; taken by each kernel's own dispatch)."""
-    cfg, out = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
-                        schedule)
+    cfg, out, w_qkv, w_o = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y,
+                                    kv_chunk, schedule, weight_layout)
     ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)
     arr = (ctypes.c_void_p * len(events))(*[e.handle.value for e in events])
     _check(_lib.load().dab_decode_attn_block_timed(
@@ -259,8 +325,9 @@ def ffn_workspace_size(cfg: DabFfnConfig) -> int:
 _ffn_ws = {}
 
 
-def _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspace):
+def _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspace, weight_layout):
     import torch
+    _layout(weight_layout)
     if hidden.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("hidden must be bfloat16 or float32")
     dt, dev = hidden.dtype, hidden.device
@@ -272,6 +339,11 @@ def _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspac
     if hidden.dim() != 2 or w_gate.dim() != 2:
         raise ValueError("hidden must be [B, H] and w_gate [F, H]")
     B, H = hidden.shape
+    if weight_layout == "in_out":
+        F = w_gate.shape[1]
+        if w_gate.shape != (H, F) or w_up.shape != (H, F) or w_down.shape != (F, H):
+            raise ValueError("need w_gate and w_up [H, F], w_down [F, H] (weight_layout='in_out')")
+        w_gate, w_up, w_down = pack_weight(w_gate), pack_weight(w_up), pack_weight(w_down)
     F = w_gate.shape[0]
     if norm_w.shape != (H,) or w_gate.shape != (F, H) or w_up.shape != (F, H) or w_down.shape != (H, F):
         raise ValueError("need norm_w [H], w_gate and w_up [F, H], w_down [H, F] (one output feature per row)")
@@ -288,18 +360,21 @@ def _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspac
         workspace = _ffn_ws.get(key)
         if workspace is None:
             workspace = _ffn_ws[key] = Workspace(ffn_workspace_size(cfg), dev)
-    return cfg, out, workspace
+    return cfg, out, workspace, w_gate, w_up, w_down
 
 
 def decode_ffn_block(hidden, norm_w, w_gate, w_up, w_down, eps: float = 1e-6, out=None, dbg_y=None,
-                     workspace: Optional[Workspace] = None):
+                     workspace: Optional[Workspace] = None, *, weight_layout: str):
     """The FFN half of the layer on the current stream; returns `out` = h + silu(g) * u @ W_down^T.
 
-    Shapes: hidden [B, H]; norm_w [H]; w_gate and w_up [F, H]; w_down [H, F]
-    (one output feature per row); one dtype (bfloat16 or float32) on one GPU.
-    dbg_y (optional, float32 [B, H]) receives the pre-residual projection.
+    Shapes: hidden [B, H]; norm_w [H]; with weight_layout "out_in" w_gate and
+    w_up [F, H], w_down [H, F] (one output feature per row), with "in_out" (the
+    pages' layout, packed into temporaries on every call) w_gate and w_up
+    [H, F], w_down [F, H]; one dtype (bfloat16 or float32) on one GPU.  dbg_y
+    (optional, float32 [B, H]) receives the pre-residual projection.
     """
-    cfg, out, ws = _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspace)
+    cfg, out, ws, w_gate, w_up, w_down = _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y,
+                                                      workspace, weight_layout)
     _check(_lib.load().dab_decode_ffn_block(
         ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
         _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device)), "dab_decode_ffn_block")
@@ -307,9 +382,10 @@ def decode_ffn_block(hidden, norm_w, w_gate, w_up, w_down, eps: float = 1e-6, ou
 
 
 def decode_ffn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_gate, w_up, w_down, eps: float = 1e-6,
-                           out=None, dbg_y=None, workspace: Optional[Workspace] = None):
+                           out=None, dbg_y=None, workspace: Optional[Workspace] = None, *, weight_layout: str):
     """decode_ffn_block that records events[0..3] at the start and end of its two kernels."""
-    cfg, out, ws = _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y, workspace)
+    cfg, out, ws, w_gate, w_up, w_down = _prepare_ffn(hidden, norm_w, w_gate, w_up, w_down, eps, out, dbg_y,
+                                                      workspace, weight_layout)
     arr = (ctypes.c_void_p * len(events))(*[e.handle.value for e in events])
     _check(_lib.load().dab_decode_ffn_block_timed(
         ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),

@@ -10,14 +10,14 @@ LIB_PATH = os.environ.get("DAB_LIBRARY") or os.path.join(HERE, "libdab.so")
 
 DAB_OK, DAB_ERR_INVALID_ARG, DAB_ERR_UNSUPPORTED, DAB_ERR_WORKSPACE, DAB_ERR_HIP = range(5)
 DAB_F32, DAB_BF16 = 0, 1
-SCHEDULES = {"auto": 0, "phased": 1, "attn_oproj": 2, "qkv_attn": 3}
+SCHEDULES = {"auto": 0, "phased": 1, "attn_oproj": 2, "qkv_attn": 3, "fused": 4}
 
 # every symbol include/dab.h declares
 EXPORTS = (
     "dab_workspace_size", "dab_workspace_init", "dab_decode_attn_block", "dab_decode_attn_block_timed",
     "dab_phase_count", "dab_phase_name", "dab_read_device_error", "dab_status_string", "dab_version",
     "dab_last_hip_error", "dab_ffn_workspace_size", "dab_decode_ffn_block", "dab_decode_ffn_block_timed",
-    "dab_read_probe",
+    "dab_read_probe", "dab_attention_output", "dab_pack_weight",
 )
 READ_PROBE_BLOCKS = 2048      # DAB_READ_PROBE_BLOCKS
 # names of the two FFN kernels, in launch order
@@ -88,6 +88,10 @@ def load() -> ctypes.CDLL:
     lib.dab_last_hip_error.restype = ctypes.c_char_p
     lib.dab_read_probe.argtypes = [vp, sz, vp, sz, vp]
     lib.dab_read_probe.restype = i32
+    lib.dab_attention_output.argtypes = [cfgp, vp, sz, vp, vp]
+    lib.dab_attention_output.restype = i32
+    lib.dab_pack_weight.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, vp]
+    lib.dab_pack_weight.restype = i32
     ffnp = ctypes.POINTER(DabFfnConfig)
     lib.dab_ffn_workspace_size.argtypes = [ffnp]
     lib.dab_ffn_workspace_size.restype = sz

@@ -25,6 +25,7 @@ const char* const kPhasedSplitNames[4] = {"qkv_rmsnorm_rope_append", "attention_
                                           "oproj_residual"};
 const char* const kAttnOprojNames[2] = {"qkv_rmsnorm_rope_append", "attention_oproj_residual"};
 const char* const kQkvAttnNames[2] = {"qkv_attention_split_kv", "oproj_residual"};
+const char* const kFusedNames[1] = {"decode_block_fused"};
 
 thread_local char g_last_error[256] = "no error";
 
@@ -83,7 +84,7 @@ dab_status plan(const dab_config* cfg, Plan* p) {
 }
 
 int phase_count(const Plan& p) {
-    return p.schedule == DAB_SCHEDULE_PHASED ? (p.split_merge ? 4 : 3) : 2;
+    return p.schedule == DAB_SCHEDULE_PHASED ? (p.split_merge ? 4 : 3) : p.schedule == DAB_SCHEDULE_FUSED ? 1 : 2;
 }
 
 dab::PanelPlanDev panel_dev(const dab::PanelPlan& g) {
@@ -113,7 +114,10 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.flags = n(p.off_flags);
     a.attn_cnt = n(p.off_attn_cnt);
     a.seq_ready = n(p.off_seq_ready);
+    a.ready_done = n(p.off_ready_done);
     a.head_cnt = n(p.off_head_cnt);
+    a.head_cnt_per_seq = p.schedule == DAB_SCHEDULE_FUSED ? 1 : 0;
+    a.ready_copies = p.oproj.panels < dab::kReadyCopies ? p.oproj.panels : dab::kReadyCopies;
     a.q = f(p.off_q);
     a.kv_new = f(p.off_kv_new);
     a.attn_o = f(p.off_attn_o);
@@ -236,6 +240,31 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
         p[i] = 0u;
 }
 
+// dst[o, i] = src[i, o]: a row-major [in, out] matrix rewritten as [out, in],
+// through 64 x 64 tiles of LDS so that both the reads and the writes are
+// whole rows of a tile.  Grid: (ceil(out / 64), ceil(in / 64)).
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E* src, E* dst, int64_t in_f, int64_t out_f) {
+    __shared__ E tile[64][65];
+    const int64_t o0 = (int64_t)blockIdx.x * 64, i0 = (int64_t)blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4) {
+        const int64_t i = i0 + r, o = o0 + tx;
+        if (i < in_f && o < out_f) tile[r][tx] = src[i * out_f + o];
+    }
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) {
+        const int64_t o = o0 + r, i = i0 + tx;
+        if (o < out_f && i < in_f) dst[o * in_f + i] = tile[tx][r];
+    }
+}
+
+// n consecutive fp32 values from src to dst (device to device).
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float* src, float* dst, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
 typedef unsigned int probe_u32x4 __attribute__((ext_vector_type(4)));
 
 // A plain stream over n16 16-byte vectors in chunks of 64 KB, as the
@@ -317,6 +346,47 @@ dab_status dab_read_probe(const void* buffer, size_t bytes, void* out, size_t ou
     return hip_status(hipGetLastError());
 }
 
+dab_status dab_pack_weight(const void* src, void* dst, int64_t in_features, int64_t out_features, int32_t dtype,
+                           void* stream) {
+    if (!src || !dst || ((uintptr_t)src % 16) != 0 || ((uintptr_t)dst % 16) != 0) return DAB_ERR_INVALID_ARG;
+    if (dtype != DAB_F32 && dtype != DAB_BF16) return DAB_ERR_INVALID_ARG;
+    if (in_features <= 0 || out_features <= 0 || in_features > 65535LL * 64 || out_features > (1LL << 30))
+        return DAB_ERR_INVALID_ARG;
+    const size_t bytes = (size_t)in_features * (size_t)out_features * (dtype == DAB_BF16 ? 2 : 4);
+    const uintptr_t s = (uintptr_t)src, d = (uintptr_t)dst;
+    if (s < d + bytes && d < s + bytes) return DAB_ERR_INVALID_ARG;
+    const dim3 grid((unsigned)((out_features + 63) / 64), (unsigned)((in_features + 63) / 64));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == DAB_BF16)
+        hipLaunchKernelGGL(dab::transpose_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(src),
+                           static_cast<uint16_t*>(dst), in_features, out_features);
+    else
+        hipLaunchKernelGGL(dab::transpose_kernel<uint32_t>, grid, dim3(256), 0, st, static_cast<const uint32_t*>(src),
+                           static_cast<uint32_t*>(dst), in_features, out_features);
+    return hip_status(hipGetLastError());
+}
+
+dab_status dab_attention_output(const dab_config* cfg, const void* workspace, size_t workspace_bytes, float* dst,
+                                void* stream) {
+    Plan p;
+    dab_status st = plan(cfg, &p);
+    if (st != DAB_OK) return st;
+    if (!workspace || ((uintptr_t)workspace % 256) != 0 || !dst || ((uintptr_t)dst % 16) != 0)
+        return DAB_ERR_INVALID_ARG;
+    if (workspace_bytes < p.ws_bytes) return DAB_ERR_WORKSPACE;
+    const size_t n = (size_t)p.B * p.n_q;
+    if (n == 0) return DAB_OK;
+    const float* a = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + p.off_a);
+    if ((uintptr_t)dst < (uintptr_t)(static_cast<const char*>(workspace) + p.ws_bytes) &&
+        (uintptr_t)workspace < (uintptr_t)(dst + n))
+        return DAB_ERR_INVALID_ARG;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(dab::copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream), a,
+                       dst, n);
+    return hip_status(hipGetLastError());
+}
+
 dab_status dab_workspace_init(void* workspace, size_t bytes, void* stream) {
     if (!workspace || ((uintptr_t)workspace % 256) != 0) return DAB_ERR_INVALID_ARG;
     return hip_status(dab::launch_fill_zero(workspace, bytes, static_cast<hipStream_t>(stream)));
@@ -348,6 +418,7 @@ const char* dab_phase_name(const dab_config* cfg, int i) {
     if (plan(cfg, &p) != DAB_OK || i < 0 || i >= phase_count(p)) return nullptr;
     return p.schedule == DAB_SCHEDULE_ATTN_OPROJ ? kAttnOprojNames[i]
          : p.schedule == DAB_SCHEDULE_QKV_ATTN ? kQkvAttnNames[i]
+         : p.schedule == DAB_SCHEDULE_FUSED ? kFusedNames[i]
          : p.split_merge ? kPhasedSplitNames[i] : kPhasedNames[i];
 }
 

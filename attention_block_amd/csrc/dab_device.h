@@ -301,12 +301,134 @@ __device__ inline void load8(const float* p, float* f) {
     }
 }
 
+// Log-sum-exp merge of the chunk partials of (sequence b, kv group g) for its
+// G query heads, by the chunk that arrived last: statistics first (one
+// request per chunk and head), then the weighted outputs, every load of a
+// round requested before any is used; deterministic (fixed order).
+template <typename T, int D, int G, bool PUBLISH>
+__device__ void merge_group(const StepArgs& a, int b, int g, int nchunk, AttnShared<D, G>& sm) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int nkv = a.nkv;
+    DAB_TRACE_POINT(a, 4);
+    const size_t pbase = ((size_t)b * a.nq + g * G) * a.maxc;   // head j, chunk cc: pbase + j * maxc + cc
+    // thread (part, d) sums chunks part, part + PARTS, ... of every head, QB
+    // chunks of each head per round (32 loads in flight); the first round is
+    // requested together with the statistics
+    constexpr int PARTS = 256 / D;
+    constexpr int QB = merge_round(G);
+    const int d = t % D, part = t / D;
+    auto request = [&](int q0, float (&v)[G][QB]) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const int cc = part + (q0 + q) * PARTS;
+                v[j][q] = cc < nchunk ? fetch(a.attn_o + (pbase + (size_t)j * a.maxc + cc) * D + d) : 0.f;
+            }
+    };
+    float ml0[2] = {kNegInf, 0.f};
+    if (t < G * nchunk) {
+        const int j = t / nchunk, cc = t - j * nchunk;
+        fetch2(a.attn_ml + (pbase + (size_t)j * a.maxc + cc) * 2, ml0);
+    }
+    float v0[G][QB];
+    request(0, v0);
+    if (t < G * nchunk) {
+        const int j = t / nchunk, cc = t - j * nchunk;
+        sm.w[j][cc] = ml0[0];
+        sm.cl[j][cc] = ml0[1];
+    }
+    for (int idx = t + 256; idx < G * nchunk; idx += 256) {
+        const int j = idx / nchunk, cc = idx - j * nchunk;
+        float ml[2];
+        fetch2(a.attn_ml + (pbase + (size_t)j * a.maxc + cc) * 2, ml);
+        sm.w[j][cc] = ml[0];
+        sm.cl[j][cc] = ml[1];
+    }
+    __syncthreads();
+    DAB_TRACE_POINT(a, 5);
+    // per head: M = max of the chunk maxima, weights exp2(m - M), L = sum w l
+    float mx[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        float v = kNegInf;
+        for (int cc = t; cc < nchunk; cc += 256) v = fmaxf(v, sm.w[j][cc]);
+        mx[j] = wave_max(v);
+        if (lane == 0) sm.red[wave][j] = mx[j];
+    }
+    __syncthreads();
+    float lsum[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const float M = fmaxf(fmaxf(sm.red[0][j], sm.red[1][j]), fmaxf(sm.red[2][j], sm.red[3][j]));
+        float v = 0.f;
+        for (int cc = t; cc < nchunk; cc += 256) {
+            const float w = __builtin_amdgcn_exp2f(sm.w[j][cc] - M);   // every chunk has a token: m finite
+            v += w * sm.cl[j][cc];
+            sm.w[j][cc] = w;
+        }
+        lsum[j] = wave_sum(v);
+    }
+    __syncthreads();                     // weights visible, sm.red read by everyone
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        if (lane == 0) sm.red[wave][j] = lsum[j];
+    // outputs, in fixed chunk order
+    float acc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc[j] = 0.f;
+    for (int q0 = 0; part + q0 * PARTS < nchunk; q0 += QB) {
+        float v[G][QB];
+        if (q0 == 0) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int q = 0; q < QB; ++q) v[j][q] = v0[j][q];
+        } else {
+            request(q0, v);
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const int cc = part + (q0 + q) * PARTS;
+                if (cc < nchunk) acc[j] += sm.w[j][cc] * v[j][q];
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) sm.acc[part][j * D + d] = acc[j];
+    __syncthreads();
+    for (int idx = t; idx < G * D; idx += 256) {
+        const int j = idx / D;
+        const float L = sm.red[0][j] + sm.red[1][j] + sm.red[2][j] + sm.red[3][j];
+        float tot = 0.f;
+#pragma unroll
+        for (int q = 0; q < PARTS; ++q) tot += sm.acc[q][idx];
+        const size_t ai = (size_t)b * a.n_q + (size_t)g * G * D + idx;   // head g*G + j, dim idx % D
+        if constexpr (PUBLISH) {
+            publish(a.a + ai, tot / L);
+        } else {
+            a.a[ai] = tot / L;
+            if constexpr (sizeof(T) == 2) a.a16[ai] = from_f32<uint16_t>(tot / L);   // input of the MFMA projection
+        }
+    }
+    if constexpr (PUBLISH) {
+        // one more kv group of sequence b merged: once its output is stored
+        // and acknowledged, every copy of the sequence's ready count goes up
+        // by one (no reply awaited); the projection waits for nkv
+        drain_and_sync();
+        if (t < a.ready_copies) add_counter(&a.seq_ready[(b * kReadyCopies + t) * kReadyStride]);
+    }
+    DAB_TRACE_POINT(a, 6);
+}
+
 // PUBLISH: the output projection runs in the same launch, so the merged
 // output is stored device-coherently and, once every head of the group is
 // stored and acknowledged, the sequence's merge counter is bumped.
-// WAITQ: the QKV projection runs in the same launch; after the K/V loads are
-// issued, wait until every panel of the group's q heads and of its k and v
-// heads is done, then read q and the new k, v device-coherently.
+// WAITQ: the QKV projection runs in the same launch; after the first K/V
+// loads are issued, wait until every panel of the group's q heads is done
+// and read q device-coherently; the chunk that takes the new token waits for
+// the panels of the group's k and v heads only before that token.
 template <typename T, int D, int G, bool PUBLISH, bool WAITQ>
 __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, G>& sm, int* s_flag) {
     using Geo = AttnGeom<D, G>;
@@ -349,14 +471,11 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     DAB_TRACE_POINT(a, 1);
 
     // 2. q of this group's heads, in log2 units
+    // panel counts of this sequence's heads (panels per head: 4 RoPE pairs each)
+    const int* hcnt = a.head_cnt + (a.head_cnt_per_seq ? b : b / a.qkv.nb) * (a.nq + 2 * nkv);
     if constexpr (WAITQ) {
-        if (t == 0) {
-            const int nheads = a.nq + 2 * nkv, panels = D / 8;      // panels per head: 4 RoPE pairs each
-            const int* cnt = a.head_cnt + (b / a.qkv.nb) * nheads;
-            for (int j = 0; j < G; ++j) wait_at_least<2>(cnt + g * G + j, panels, a.flags);
-            wait_at_least<2>(cnt + a.nq + g, panels, a.flags);
-            wait_at_least<2>(cnt + a.nq + nkv + g, panels, a.flags);
-        }
+        if (t == 0)
+            for (int j = 0; j < G; ++j) wait_at_least<2>(hcnt + g * G + j, D / 8, a.flags);
         __syncthreads();
     }
     float qv[G][8];
@@ -544,6 +663,15 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     // the new token, in slot 0 of the last chunk: its k and v come from the
     // workspace copy the QKV kernel wrote, rounded to the storage type
     // exactly as the appended cache row
+    if constexpr (WAITQ) {
+        if (has_new) {
+            if (t == 0) {
+                wait_at_least<2>(hcnt + a.nq + g, D / 8, a.flags);
+                wait_at_least<2>(hcnt + a.nq + nkv + g, D / 8, a.flags);
+            }
+            __syncthreads();
+        }
+    }
     if (has_new && slot == 0) {
         const size_t kn = ((size_t)b * 2 * nkv + g) * D + l * 8;
         const size_t vn = kn + (size_t)nkv * D;
@@ -630,123 +758,10 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
         }
     }
 
-    // 4. the last chunk of (b, g) merges all chunks of all G heads:
-    // statistics first (one request per chunk and head), then the weighted
-    // outputs, every load of a round requested before any is used
+    // 4. the last chunk of (b, g) to arrive merges all chunks of all G heads
     if (a.split_merge) return;           // merged by the merge kernel that follows
-    int* cnt = &a.attn_cnt[b * nkv + g];
-    if (!arrive_last(cnt, nchunk, s_flag)) return;
-    DAB_TRACE_POINT(a, 4);
-    const size_t pbase = ((size_t)b * a.nq + g * G) * a.maxc;   // head j, chunk cc: pbase + j * maxc + cc
-    // thread (part, d) sums chunks part, part + PARTS, ... of every head, QB
-    // chunks of each head per round (32 loads in flight); the first round is
-    // requested together with the statistics
-    constexpr int PARTS = 256 / D;
-    constexpr int QB = merge_round(G);
-    const int d = t % D, part = t / D;
-    auto request = [&](int q0, float (&v)[G][QB]) {
-#pragma unroll
-        for (int j = 0; j < G; ++j)
-#pragma unroll
-            for (int q = 0; q < QB; ++q) {
-                const int cc = part + (q0 + q) * PARTS;
-                v[j][q] = cc < nchunk ? fetch(a.attn_o + (pbase + (size_t)j * a.maxc + cc) * D + d) : 0.f;
-            }
-    };
-    float ml0[2] = {kNegInf, 0.f};
-    if (t < G * nchunk) {
-        const int j = t / nchunk, cc = t - j * nchunk;
-        fetch2(a.attn_ml + (pbase + (size_t)j * a.maxc + cc) * 2, ml0);
-    }
-    float v0[G][QB];
-    request(0, v0);
-    if (t < G * nchunk) {
-        const int j = t / nchunk, cc = t - j * nchunk;
-        sm.w[j][cc] = ml0[0];
-        sm.cl[j][cc] = ml0[1];
-    }
-    for (int idx = t + 256; idx < G * nchunk; idx += 256) {
-        const int j = idx / nchunk, cc = idx - j * nchunk;
-        float ml[2];
-        fetch2(a.attn_ml + (pbase + (size_t)j * a.maxc + cc) * 2, ml);
-        sm.w[j][cc] = ml[0];
-        sm.cl[j][cc] = ml[1];
-    }
-    __syncthreads();
-    DAB_TRACE_POINT(a, 5);
-    // per head: M = max of the chunk maxima, weights exp2(m - M), L = sum w l
-    float mx[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        float v = kNegInf;
-        for (int cc = t; cc < nchunk; cc += 256) v = fmaxf(v, sm.w[j][cc]);
-        mx[j] = wave_max(v);
-        if (lane == 0) sm.red[wave][j] = mx[j];
-    }
-    __syncthreads();
-    float lsum[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const float M = fmaxf(fmaxf(sm.red[0][j], sm.red[1][j]), fmaxf(sm.red[2][j], sm.red[3][j]));
-        float v = 0.f;
-        for (int cc = t; cc < nchunk; cc += 256) {
-            const float w = __builtin_amdgcn_exp2f(sm.w[j][cc] - M);   // every chunk has a token: m finite
-            v += w * sm.cl[j][cc];
-            sm.w[j][cc] = w;
-        }
-        lsum[j] = wave_sum(v);
-    }
-    __syncthreads();                     // weights visible, sm.red read by everyone
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-        if (lane == 0) sm.red[wave][j] = lsum[j];
-    // outputs, in fixed chunk order
-    float acc[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) acc[j] = 0.f;
-    for (int q0 = 0; part + q0 * PARTS < nchunk; q0 += QB) {
-        float v[G][QB];
-        if (q0 == 0) {
-#pragma unroll
-            for (int j = 0; j < G; ++j)
-#pragma unroll
-                for (int q = 0; q < QB; ++q) v[j][q] = v0[j][q];
-        } else {
-            request(q0, v);
-        }
-#pragma unroll
-        for (int j = 0; j < G; ++j)
-#pragma unroll
-            for (int q = 0; q < QB; ++q) {
-                const int cc = part + (q0 + q) * PARTS;
-                if (cc < nchunk) acc[j] += sm.w[j][cc] * v[j][q];
-            }
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) sm.acc[part][j * D + d] = acc[j];
-    __syncthreads();
-    for (int idx = t; idx < G * D; idx += 256) {
-        const int j = idx / D;
-        const float L = sm.red[0][j] + sm.red[1][j] + sm.red[2][j] + sm.red[3][j];
-        float tot = 0.f;
-#pragma unroll
-        for (int q = 0; q < PARTS; ++q) tot += sm.acc[q][idx];
-        const size_t ai = (size_t)b * a.n_q + (size_t)g * G * D + idx;   // head g*G + j, dim idx % D
-        if constexpr (PUBLISH) {
-            publish(a.a + ai, tot / L);
-        } else {
-            a.a[ai] = tot / L;
-            if constexpr (sizeof(T) == 2) a.a16[ai] = from_f32<uint16_t>(tot / L);   // input of the MFMA projection
-        }
-    }
-    if constexpr (PUBLISH) {
-        // one more kv group of sequence b merged: once its output is stored
-        // and acknowledged, every copy of the sequence's ready count goes up
-        // by one (no reply awaited); the projection waits for nkv
-        drain_and_sync();
-        if (t < kReadyCopies) add_counter(&a.seq_ready[(b * kReadyCopies + t) * kReadyStride]);
-    }
-    DAB_TRACE_POINT(a, 6);
+    if (!arrive_last(&a.attn_cnt[b * nkv + g], nchunk, s_flag)) return;
+    merge_group<T, D, G, PUBLISH>(a, b, g, nchunk, sm);
 }
 
 }  // namespace dev

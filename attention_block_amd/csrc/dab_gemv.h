@@ -155,15 +155,26 @@ struct QkvShared {
     float ss[NB][4];
 };
 
+// How a QKV panel hands its results on.
+enum QkvMode {
+    kQkvPlain = 0,     // a kernel of its own: plain stores, and it re-arms the ready counts of the
+                       // attention + projection launch that follows
+    kQkvSignalGroup,   // attention in the same launch: device-coherent stores, then the panel count of its
+                       // (batch group, head) goes up
+    kQkvSignalSeq,     // the whole step in one launch: device-coherent stores, then the panel count of
+                       // (sequence, head) goes up for each of its valid sequences; no re-arming here
+};
+
 // Lane work of a QKV panel for sequence bb: RMS scale, RoPE, q and the new
 // k, v out, the cache append.  ss: the four waves' sums of x^2.
-template <typename T, bool SIGNAL>
+template <typename T, int MODE>
 __device__ void qkv_finish(const StepArgs& a, int panel, int wave, int bb, int hd, int e, int row0, float u0,
                            float u1, const float* ss) {
+    constexpr bool SIGNAL = MODE != kQkvPlain;
     const int H = a.H, D = a.D, half = D >> 1;
     // re-arm the ready counts of this sequence for the attention kernel that
     // follows (it runs after this kernel completes)
-    if (panel == 0 && wave == 0)
+    if (MODE != kQkvSignalSeq && panel == 0 && wave == 0)
         for (int i = 0; i < kReadyCopies; ++i) set_counter(&a.seq_ready[(bb * kReadyCopies + i) * kReadyStride], 0);
     const float sum_sq = ss[0] + ss[1] + ss[2] + ss[3];
     const float r = 1.0f / sqrtf(sum_sq / (float)H + a.eps);
@@ -208,10 +219,10 @@ __device__ void qkv_finish(const StepArgs& a, int panel, int wave, int bb, int h
 }
 
 // QKV panel `panel` for batch rows [bgi * NB, +NB).  xs: NB x H floats of LDS.
-// SIGNAL: attention runs in the same launch; q and the new k, v are stored
-// device-coherently and, once the whole panel's stores are acknowledged,
-// the counter of its (batch group, head) is bumped.
-template <typename T, int NB, bool EXACT, bool SIGNAL>
+// MODE (QkvMode) kQkvSignal*: attention runs in the same launch; q and the
+// new k, v are stored device-coherently and, once the whole panel's stores
+// are acknowledged, the panel counts of its head go up.
+template <typename T, int NB, bool EXACT, int MODE>
 __device__ void qkv_panel(const StepArgs& a, int panel, int bgi, float* xs, QkvShared<T, NB>& sm) {
     constexpr int N = W16<T>::N;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -300,10 +311,17 @@ __device__ void qkv_panel(const StepArgs& a, int panel, int bgi, float* xs, QkvS
             u1 = dot.acc[1][j];
         }
     const int bb = b0 + lane;
-    if (lane < NB && bb < a.B) qkv_finish<T, SIGNAL>(a, panel, wave, bb, hd, e, row0, u0, u1, sm.ss[lane]);
-    if constexpr (SIGNAL) {
+    if (lane < NB && bb < a.B) qkv_finish<T, MODE>(a, panel, wave, bb, hd, e, row0, u0, u1, sm.ss[lane]);
+    if constexpr (MODE == kQkvSignalGroup) {
         drain_and_sync();
         if (t == 0) bump(&a.head_cnt[bgi * (a.nq + 2 * a.nkv) + hd]);
+    } else if constexpr (MODE == kQkvSignalSeq) {
+        // one count per valid sequence (a sequence with a bad position has no
+        // attention, so nothing would re-arm its counts)
+        drain_and_sync();
+        int p;
+        if (t < NB && b0 + t < a.B && pos_valid(a, b0 + t, &p))
+            add_counter(&a.head_cnt[(b0 + t) * (a.nq + 2 * a.nkv) + hd]);
     }
 }
 
@@ -311,8 +329,13 @@ __device__ void qkv_panel(const StepArgs& a, int panel, int bgi, float* xs, QkvS
 // xs: NB x n_q floats of LDS.  WAIT: the attention output is produced in the
 // same launch; the weight stream goes out first, then the workgroup waits
 // until every kv group of its sequences is merged and reads the attention
-// output device-coherently.
-template <typename T, int RW, int NB, bool EXACT, bool WAIT>
+// output device-coherently.  REARM (with WAIT; the whole step in one
+// launch): past its wait, the panel counts itself as a reader of its copy of
+// each sequence's ready count; the last reader of a copy re-arms it, and
+// panel 0 re-arms the sequences' QKV panel counts (every attention chunk of
+// those sequences, the only readers, has finished: the merges they fed are
+// done).
+template <typename T, int RW, int NB, bool EXACT, bool WAIT, bool REARM = false>
 __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int K = a.n_q, H = a.H;
@@ -337,18 +360,36 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
         xres[r] = mine ? to_f32(static_cast<const T*>(a.hidden)[(size_t)(b0 + lane) * H + row0 + r]) : 0.f;
 
     PanelDot<T, RW, NB, EXACT> dot;
+    const int copy = WAIT ? panel % a.ready_copies : 0;   // this panel's copy of the ready counts
+    int readers_before[NB];                               // REARM: readers of the copy before this one
+#pragma unroll
+    for (int j = 0; j < NB; ++j) readers_before[j] = -1;
     if constexpr (WAIT) {
         // 1. the weight stream, then the wait for the attention output
         dot.issue(rows, 0, K, lane);
         DAB_TRACE_POINT(a, 1);
         if (t == 0) {
-            const int copy = blockIdx.x % kReadyCopies;
 #pragma unroll
             for (int j = 0; j < NB; ++j)
                 if ((valid >> j) & 1u)
                     wait_at_least<8>(&a.seq_ready[((b0 + j) * kReadyCopies + copy) * kReadyStride], a.nkv, a.flags);
+            if constexpr (REARM) {
+                // the replies return while the attention output is read below
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    readers_before[j] = ((valid >> j) & 1u)
+                        ? bump(&a.ready_done[((b0 + j) * kReadyCopies + copy) * kReadyStride]) : -1;
+            }
         }
         __syncthreads();
+        if constexpr (REARM) {
+            if (panel == 0) {
+                const int nheads = a.nq + 2 * a.nkv;
+                for (int j = 0; j < NB; ++j)
+                    if ((valid >> j) & 1u)
+                        for (int i = t; i < nheads; i += 256) set_counter(&a.head_cnt[(b0 + j) * nheads + i], 0);
+            }
+        }
         // 2. attention outputs into LDS (zeros for sequences without one):
         // every load of a round issued before any is used, so the round
         // costs one trip to the memory-side cache
@@ -413,6 +454,18 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
     }
     __syncthreads();
     DAB_TRACE_POINT(a, 2);
+    if constexpr (WAIT && REARM) {
+        if (t == 0) {
+            // readers of this copy: the panels p with p % ready_copies == copy
+            const int readers = (a.oproj.panels - copy + a.ready_copies - 1) / a.ready_copies;
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                if (readers_before[j] == readers - 1) {
+                    set_counter(&a.seq_ready[((b0 + j) * kReadyCopies + copy) * kReadyStride], 0);
+                    set_counter(&a.ready_done[((b0 + j) * kReadyCopies + copy) * kReadyStride], 0);
+                }
+        }
+    }
 
     // 3. the rows against every staged sequence
     dot.run(rows, xs, K, lane);
@@ -570,7 +623,7 @@ __device__ void mfma_panel(const StepArgs& a, int panel, int bgi, MfmaShared& sm
                 ss[w % 4] += sm.ss[n][w];
             }
             const int e = e0 + tile * 8 + r;
-            qkv_finish<uint16_t, false>(a, panel, tile * 8 + r, bb, hd, e, hd * D + e, u0, u1, ss);
+            qkv_finish<uint16_t, kQkvPlain>(a, panel, tile * 8 + r, bb, hd, e, hd * D + e, u0, u1, ss);
         }
     } else {
         int pp;

@@ -33,8 +33,13 @@ struct StepArgs {
     int* flags;             // error bits
     int* attn_cnt;          // [B * nkv] chunk arrivals (re-armed by the merging workgroup)
     int* seq_ready;         // [B, kReadyCopies] x kReadyStride: kv groups of the sequence merged so far (one-launch attention + projection; re-armed by the QKV kernel)
-    int* head_cnt;          // [qkv.nbg, nq + 2 nkv] QKV panels done per (batch group, head) (one-launch
-                            // QKV + attention; re-armed by the output projection kernel)
+    int* ready_done;        // [B, kReadyCopies] x kReadyStride: projection workgroups past their wait on each
+                            // copy of seq_ready (whole step in one launch; the last one re-arms both)
+    int* head_cnt;          // QKV panels done per (batch group, head) [qkv.nbg, nq + 2 nkv] (one-launch QKV +
+                            // attention; re-armed by the output projection kernel) or per (sequence, head)
+                            // [B, nq + 2 nkv] (whole step in one launch; re-armed by its projection panels)
+    int head_cnt_per_seq;   // 1: head_cnt is per (sequence, head)
+    int ready_copies;       // copies of seq_ready in use: min(kReadyCopies, output projection panels)
     float* q;               // [B, n_q] rotated q
     float* kv_new;          // [B, 2, nkv, D] the new token's rotated k and v
     float* attn_o;          // [B, nq, maxc, D] chunk partial outputs

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void qkv_kernel(StepArgs a) {
     DAB_TRACE_POINT(a, 0);
     int panel, bgi;
     if (panel_decode(a.qkv.nbg, a.qkv.panels, blockIdx.x, &panel, &bgi))
-        qkv_panel<T, NB, EXACT, false>(a, panel, bgi, reinterpret_cast<float*>(xs_raw), sm);
+        qkv_panel<T, NB, EXACT, kQkvPlain>(a, panel, bgi, reinterpret_cast<float*>(xs_raw), sm);
     DAB_TRACE_POINT(a, 3);
 }
 
@@ -64,7 +64,7 @@ void qkv_attn_kernel(StepArgs a) {
     if ((int)blockIdx.x < a.qkv.items) {
         int panel, bgi;
         if (panel_decode(a.qkv.nbg, a.qkv.panels, blockIdx.x, &panel, &bgi))
-            qkv_panel<T, NB, true, true>(a, panel, bgi, reinterpret_cast<float*>(lds_raw), qsm);
+            qkv_panel<T, NB, true, kQkvSignalGroup>(a, panel, bgi, reinterpret_cast<float*>(lds_raw), qsm);
     } else {
         int b, g, c;
         attn_decode(a, blockIdx.x - a.qkv.items, &b, &g, &c);
@@ -99,6 +99,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
         int panel, bgi;
         if (panel_decode(a.oproj.nbg, a.oproj.panels, blockIdx.x - a.attn_items, &panel, &bgi))
             oproj_panel<T, 2, NB, true, true>(a, panel, bgi, reinterpret_cast<float*>(lds_raw));
+    }
+    DAB_TRACE_POINT(a, 3);
+}
+
+// The whole step in one launch, its workgroups in dependency order: the QKV
+// panels (q heads, then k, then v heads), the attention chunks, the output
+// projection's panels.  A chunk waits for the q panels of its group's query
+// heads, the chunk with the new token also for the group's k and v panels
+// before that token; a projection panel streams its rows of W_o from the
+// moment it has a slot and waits for its sequences' attention output.
+// Every wait is on lower-numbered workgroups, which never wait on higher
+// ones, and each XCD dispatches its workgroups in index order, so every wait
+// ends.  The counters are re-armed inside the launch by their last readers
+// (see oproj_panel), so consecutive calls need no clearing in between.
+template <typename T, int NB, int D, int G, bool EXACT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && G == 1 && NB == 1 ? 4 : 1)))
+void fused_kernel(StepArgs a) {
+    extern __shared__ f32x4 lds_raw[];   // the QKV panel's staged inputs, attention scratch, or the projection's
+    __shared__ QkvShared<T, NB> qsm;
+    __shared__ int s_flag;
+    DAB_TRACE_POINT(a, 0);
+    const int i = blockIdx.x;
+    if (i < a.qkv.items) {
+        qkv_panel<T, NB, EXACT, kQkvSignalSeq>(a, i, 0, reinterpret_cast<float*>(lds_raw), qsm);
+    } else if (i < a.qkv.items + a.attn_items) {
+        int b, g, c;
+        attn_decode(a, i - a.qkv.items, &b, &g, &c);
+        attn_item<T, D, G, true, true>(a, b, g, c, *reinterpret_cast<AttnShared<D, G>*>(lds_raw), &s_flag);
+    } else {
+        int panel, bgi;
+        if (panel_decode(a.oproj.nbg, a.oproj.panels, i - a.qkv.items - a.attn_items, &panel, &bgi))
+            oproj_panel<T, 2, NB, true, true, true>(a, panel, bgi, reinterpret_cast<float*>(lds_raw));
     }
     DAB_TRACE_POINT(a, 3);
 }
@@ -379,8 +411,50 @@ int attn_resident(int D, int G) {
     return D == 128 ? attn_resident_d<T, 128>(G) : D == 64 ? attn_resident_d<T, 64>(G) : 0;
 }
 
+template <typename T, int NB, int D>
+hipError_t launch_fused_nd(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
+    const dim3 grid(p.qkv.grid + p.attn_grid + p.oproj.grid), block(kThreads);
+    size_t lds = p.qkv.lds > p.oproj.lds ? p.qkv.lds : p.oproj.lds;
+    switch (p.G) {
+#define DAB_G(NG)                                                                                           \
+        case NG:                                                                                            \
+            if (sizeof(AttnShared<D, NG>) > lds) lds = sizeof(AttnShared<D, NG>);                             \
+            if (exact_blocks<T>(p.H))                                                                       \
+                dab_launch((fused_kernel<T, NB, D, NG, true>), grid, block, lds, s, ev, a);                 \
+            else                                                                                            \
+                dab_launch((fused_kernel<T, NB, D, NG, false>), grid, block, lds, s, ev, a);                \
+            break;
+        DAB_G(1) DAB_G(2) DAB_G(4) DAB_G(8)
+#undef DAB_G
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int NB>
+hipError_t launch_fused_n(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
+    return a.D == 128 ? launch_fused_nd<T, NB, 128>(a, p, s, ev) : launch_fused_nd<T, NB, 64>(a, p, s, ev);
+}
+
+// The whole step in one launch: built for groups of 1, 2, 4, 8, an output
+// projection of whole K-blocks with two rows per wave, and one batch group
+// of the same size in both projections.
+template <typename T>
+hipError_t launch_fused(const StepArgs& a, const Plan& p, hipStream_t s, const LaunchEvents& ev) {
+    if (!exact_blocks<T>(p.n_q) || p.oproj.rows_per_wave != 2 || p.qkv.mfma || p.oproj.mfma ||
+        p.qkv.nb != p.oproj.nb || p.qkv.nbg != 1)
+        return hipErrorInvalidValue;
+    switch (p.qkv.nb) {
+        case 1: return launch_fused_n<T, 1>(a, p, s, ev);
+        case 2: return launch_fused_n<T, 2>(a, p, s, ev);
+        case 4: return launch_fused_n<T, 4>(a, p, s, ev);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T>
 hipError_t launch_phase_t(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev) {
+    if (p.schedule == DAB_SCHEDULE_FUSED) return launch_fused<T>(a, p, s, ev);
     if (p.schedule == DAB_SCHEDULE_QKV_ATTN) return phase == 0 ? launch_qkv_attn<T>(a, p, s, ev) : launch_oproj<T>(a, p, s, ev);
     if (phase == 0) return launch_qkv<T>(a, p, s, ev);
     if (p.schedule == DAB_SCHEDULE_ATTN_OPROJ) {

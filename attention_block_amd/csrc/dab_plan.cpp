@@ -108,7 +108,7 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
 
     const int B = p->B > 0 ? p->B : 1;  // plan a batch-0 call as batch 1; nothing is launched
 
-    if (c.schedule < DAB_SCHEDULE_AUTO || c.schedule > DAB_SCHEDULE_QKV_ATTN) return DAB_ERR_INVALID_ARG;
+    if (c.schedule < DAB_SCHEDULE_AUTO || c.schedule > DAB_SCHEDULE_FUSED) return DAB_ERR_INVALID_ARG;
 
     // the one-launch kernels are instantiated for groups 1, 2, 4, 8 and for
     // projections of whole K-blocks (4096 bf16 or 2048 fp32 values): the
@@ -118,8 +118,17 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
     const bool group_ok = p->G == 1 || p->G == 2 || p->G == 4 || p->G == 8;
     p->attn_oproj_ok = group_ok && p->n_q % kblock == 0;
     p->qkv_attn_ok = group_ok && p->H % kblock == 0;
+    // the whole step in one launch: the output projection's panels as in the
+    // one-launch attention + projection, the QKV panels of any width, batches
+    // of up to 4 held by one workgroup in both projections (their fp32 input
+    // rows within the LDS budget)
+    const int nb_all = B <= 1 ? 1 : B == 2 ? 2 : 4;
+    const int kmax = p->H > p->n_q ? p->H : p->n_q;
+    p->fused_ok = group_ok && p->n_q % kblock == 0 && B <= 4 &&
+                  (size_t)nb_all * kmax * sizeof(float) <= (size_t)kPanelLds;
     if ((c.schedule == DAB_SCHEDULE_ATTN_OPROJ && !p->attn_oproj_ok) ||
-        (c.schedule == DAB_SCHEDULE_QKV_ATTN && !p->qkv_attn_ok))
+        (c.schedule == DAB_SCHEDULE_QKV_ATTN && !p->qkv_attn_ok) ||
+        (c.schedule == DAB_SCHEDULE_FUSED && !p->fused_ok))
         return DAB_ERR_UNSUPPORTED;
     // AUTO: the schedule measured fastest on MI355X.  Attention + projection
     // in one launch wins for one query head per kv head at small batch (7B
@@ -128,7 +137,13 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
     // the waiting projection workgroups cost them slots (8B GQA layer: 267
     // against 169 us at batch 16, 71.9 against 69.8 at batch 1 and 16K
     // tokens).  QKV + attention in one launch never won: the early K/V loads
-    // delay the QKV weight stream that every chunk waits for.
+    // delay the QKV weight stream that every chunk waits for.  The whole step
+    // in one launch measured 43.5 against 42.0 us (7B layer, batch 1, 4K
+    // tokens): its attention chunks get slots only as QKV panels finish, so
+    // they start over 8 us instead of together, and the last of them ends
+    // later; with the chunks placed before the k and v panels (so that they
+    // start at once) the 512 chunks waiting for q held half the slots and the
+    // step took 76 us.
     const bool auto_attn_oproj = p->attn_oproj_ok && p->G == 1 && B <= 4;
     p->schedule = c.schedule != DAB_SCHEDULE_AUTO ? c.schedule
                 : auto_attn_oproj ? DAB_SCHEDULE_ATTN_OPROJ : DAB_SCHEDULE_PHASED;
@@ -148,7 +163,7 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
     // hold a slot from the start and their weights stream with the cache
     // (with 1024, the last ones got slots only as chunks finished and their
     // weight loads ended the step).
-    const int rpw_o = p->schedule == DAB_SCHEDULE_ATTN_OPROJ ? 2 : 1;
+    const int rpw_o = p->schedule == DAB_SCHEDULE_ATTN_OPROJ || p->schedule == DAB_SCHEDULE_FUSED ? 2 : 1;
     if (!(mfma && plan_mfma_panel(p->n_q, p->H, B, false, half, &p->oproj)) &&
         !plan_panel(p->n_q, p->H, B, rpw_o, &p->oproj))
         return DAB_ERR_UNSUPPORTED;
@@ -223,7 +238,9 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
     p->off_flags = take(256);
     p->off_attn_cnt = take(sizeof(int32_t) * B * p->nkv);
     p->off_seq_ready = take(sizeof(int32_t) * B * kReadyCopies * kReadyStride);
-    p->off_head_cnt = take(sizeof(int32_t) * p->qkv.nbg * (p->nq + 2 * p->nkv));
+    p->off_ready_done = take(sizeof(int32_t) * B * kReadyCopies * kReadyStride);
+    // panel counts per (batch group, head) (QKV + attention) or per (sequence, head) (whole step)
+    p->off_head_cnt = take(sizeof(int32_t) * B * (p->nq + 2 * p->nkv));
     p->off_q = take(sizeof(float) * (size_t)B * p->n_q);
     p->off_kv_new = take(sizeof(float) * (size_t)B * 2 * p->nkv * p->D);
     p->off_attn_o = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * p->D);

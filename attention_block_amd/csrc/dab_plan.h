@@ -54,13 +54,14 @@ struct Plan {
     int schedule = DAB_SCHEDULE_PHASED;   // resolved schedule (never AUTO)
     bool attn_oproj_ok = false;           // the one-launch attention + projection is built for this shape
     bool qkv_attn_ok = false;             // the one-launch QKV + attention is built for this shape
+    bool fused_ok = false;                // the one-launch whole step is built for this shape
     PanelPlan qkv, oproj;
     int kv_chunk = 0, max_chunks = 0, attn_grid = 0;
     bool split_merge = false;             // phased: the LSE merge runs as a kernel of its own
 
     // workspace layout, byte offsets (each 256-byte aligned); the flags
     // word is at offset 0
-    size_t off_flags = 0, off_attn_cnt = 0, off_seq_ready = 0, off_head_cnt = 0;
+    size_t off_flags = 0, off_attn_cnt = 0, off_seq_ready = 0, off_ready_done = 0, off_head_cnt = 0;
     size_t off_q = 0, off_kv_new = 0;
     size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0, off_a16 = 0;
     size_t ws_bytes = 0;

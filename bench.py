@@ -84,7 +84,8 @@ def phase_bytes(cfg: BlockConfig, pos) -> dict:
     oproj = s * nq * D * H + s * B * H
     # the separate merge kernel reads and writes workspace only (the chunk partials, the attention output)
     return {"qkv_rmsnorm_rope_append": qkv, "attention_split_kv": attn, "oproj_residual": oproj,
-            "attention_oproj_residual": attn + oproj, "qkv_attention_split_kv": qkv + attn, "attention_merge": 0}
+            "attention_oproj_residual": attn + oproj, "qkv_attention_split_kv": qkv + attn, "attention_merge": 0,
+            "decode_block_fused": qkv + attn + oproj}
 
 
 def make_layer_set(cfg: BlockConfig, pos, cap: int, gen, device):
@@ -113,15 +114,47 @@ def make_layer_set(cfg: BlockConfig, pos, cap: int, gen, device):
     return ls
 
 
+
+def host_cpu() -> dict:
+    """The host cores this process may run on (its affinity mask) and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cores": cores, "model": model}
+
+
+class blas_threads:
+    """Limit the BLAS thread pools numpy uses to `n` threads inside the block."""
+
+    def __init__(self, n: int):
+        self.n = n
+        self._ctl = None
+
+    def __enter__(self):
+        try:
+            from threadpoolctl import threadpool_limits
+            self._ctl = threadpool_limits(limits=self.n)
+        except Exception:
+            self._ctl = None
+        return self
+
+    def __exit__(self, *exc):
+        if self._ctl is not None:
+            self._ctl.unregister()
+        return False
+
+
 def cpu_baseline(cfg: BlockConfig, seed: int, budget_s: float) -> dict:
     """The fp64 oracle on the host, on the full step of this workload."""
     import oracle
     from attention_block_amd.inputs import make_inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     inp = make_inputs(cfg, seed)
     st = cfg.dtype
     pos = inp["pos"]
@@ -136,22 +169,26 @@ def cpu_baseline(cfg: BlockConfig, seed: int, budget_s: float) -> dict:
             oracle.to_f64(inp["w_o"], st), kc, vc, pos)
     kw = dict(n_q_heads=cfg.n_q_heads, n_kv_heads=nkv, head_dim=D, rope_theta=cfg.rope_theta, eps=cfg.eps,
               storage=st)
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        oracle.decode_step_fp64(*args, **kw)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 200:
-            break
+    host = host_cpu()
+    with blas_threads(host["cores"]):
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            oracle.decode_step_fp64(*args, **kw)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > budget_s or len(times) >= 200:
+                break
     med = float(np.median(times))
-    return {"value": med * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
+    return {"value": med * 1e6, "unit": "us/step", "cores": host["cores"], "cpu_model": host["model"],
+            "kind": "oracle",
             "sample": f"{len(times)} full {cfg.name} steps (seed {seed}) of the fp64 numpy oracle, median; "
-                      f"bf16->fp64 upcast outside the timing"}
+                      f"bf16->fp64 upcast outside the timing; BLAS threads = cores"}
 
 
 # kernel function names (as rocprofv3 reports them) -> phase names of the C ABI
-KERNEL_PHASES = [("qkv_attn_kernel", "qkv_attention_split_kv"), ("attn_oproj_kernel", "attention_oproj_residual"),
+KERNEL_PHASES = [("fused_kernel", "decode_block_fused"),
+                 ("qkv_attn_kernel", "qkv_attention_split_kv"), ("attn_oproj_kernel", "attention_oproj_residual"),
                  ("qkv_kernel", "qkv_rmsnorm_rope_append"), ("attn_kernel", "attention_split_kv"),
                  ("oproj_kernel", "oproj_residual"), ("merge_kernel", "attention_merge"),
                  ("ffn_gate_up_kernel", "ffn_rmsnorm_gate_up_silu"),
@@ -334,6 +371,10 @@ def graph_time(step, steps: int, R: int) -> float:
     start, end = ab.HipEvent(), ab.HipEvent()
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    # ~1 ms of spinning ahead of the start event: the graphs are submitted while the GPU spins, so the
+    # interval between the events is the GPU time of the K steps, not the host's graph submission
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2.4e6))
     start.record(stream.cuda_stream)
     for _ in range(n_main):
         g_main.replay()
@@ -381,26 +422,24 @@ def ffn_cpu_baseline(cfg: FfnConfig, seed: int, budget_s: float) -> dict:
     """The fp64 FFN oracle on the host, on the full step of this workload."""
     import oracle
     from attention_block_amd.inputs import make_ffn_inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     inp = make_ffn_inputs(cfg, seed)
     st = cfg.dtype
     args = [oracle.to_f64(inp[k], st) for k in ("hidden", "norm_w", "w_gate", "w_up", "w_down")]
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        oracle.ffn_step_fp64(*args, eps=cfg.eps, storage=st)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 200:
-            break
+    host = host_cpu()
+    with blas_threads(host["cores"]):
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            oracle.ffn_step_fp64(*args, eps=cfg.eps, storage=st)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > budget_s or len(times) >= 200:
+                break
     med = float(np.median(times))
-    return {"value": med * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
+    return {"value": med * 1e6, "unit": "us/step", "cores": host["cores"], "cpu_model": host["model"],
+            "kind": "oracle",
             "sample": f"{len(times)} full {cfg.name} steps (seed {seed}) of the fp64 numpy FFN oracle, median; "
-                      f"bf16->fp64 upcast outside the timing"}
+                      f"bf16->fp64 upcast outside the timing; BLAS threads = cores"}
 
 
 def bench_ffn(args, dev) -> int:
@@ -422,9 +461,9 @@ def bench_ffn(args, dev) -> int:
         s = sets[i % R]
         w = (s["hidden"], s["norm_w"], s["w_gate"], s["w_up"], s["w_down"], cfg.eps)
         if events is None:
-            ab.decode_ffn_block(*w, out=s["out"], workspace=ws)
+            ab.decode_ffn_block(*w, out=s["out"], workspace=ws, weight_layout="out_in")
         else:
-            ab.decode_ffn_block_timed(events, *w, out=s["out"], workspace=ws)
+            ab.decode_ffn_block_timed(events, *w, out=s["out"], workspace=ws, weight_layout="out_in")
 
     for i in range(args.warmup):
         step(i)
@@ -500,9 +539,10 @@ def bench_chain(args, dev) -> int:
         for attn, ffn in layers:
             h = ab.decode_attn_block(x, attn["norm_w"], attn["w_qkv"], attn["w_o"], attn["k_cache"],
                                      attn["v_cache"], attn["pos"], cfg.rope_theta, cfg.eps, out=attn["out"],
-                                     workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule)
+                                     workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule,
+                                     weight_layout="out_in")
             x = ab.decode_ffn_block(h, ffn["norm_w"], ffn["w_gate"], ffn["w_up"], ffn["w_down"], fcfg.eps,
-                                    out=ffn["out"], workspace=fws)
+                                    out=ffn["out"], workspace=fws, weight_layout="out_in")
 
     for i in range(max(1, args.warmup // 10)):
         token(i)
@@ -554,7 +594,9 @@ def main() -> int:
                     help="time one token through this many decoder layers (attention block of --config + its "
                          "FFN), one HIP graph; 0: the single attention block step")
     ap.add_argument("--kv-chunk", type=int, default=0)
-    ap.add_argument("--schedule", default="auto", choices=["auto", "phased", "attn_oproj", "qkv_attn"])
+    ap.add_argument("--cap", type=int, default=0,
+                    help="cache capacity per sequence (token rows); 0: the largest position + 1")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "phased", "attn_oproj", "qkv_attn", "fused"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true")
@@ -601,6 +643,11 @@ def main() -> int:
     cfg = CONFIGS[args.config]
     pos = positions(cfg, args.seed)
     cap = int(pos.max()) + 1
+    if args.cap:
+        if args.cap < cap:
+            print(f"--cap {args.cap} is below the largest position + 1 ({cap})", file=sys.stderr)
+            return 2
+        cap = args.cap
     nbytes = algorithmic_bytes(cfg, pos)
     flops = algorithmic_flops(cfg, pos)
     R = max(3, math.ceil(2 * MALL_BYTES / nbytes) + 1)
@@ -619,11 +666,12 @@ def main() -> int:
         if events is None:
             ab.decode_attn_block(s["hidden"], s["norm_w"], s["w_qkv"], s["w_o"], s["k_cache"], s["v_cache"],
                                  s["pos"], cfg.rope_theta, cfg.eps, out=s["out"], workspace=ws,
-                                 kv_chunk=args.kv_chunk, schedule=args.schedule)
+                                 kv_chunk=args.kv_chunk, schedule=args.schedule, weight_layout="out_in")
         else:
             ab.decode_attn_block_timed(events, s["hidden"], s["norm_w"], s["w_qkv"], s["w_o"], s["k_cache"],
                                        s["v_cache"], s["pos"], cfg.rope_theta, cfg.eps, out=s["out"],
-                                       workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule)
+                                       workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule,
+                                     weight_layout="out_in")
 
     for i in range(args.warmup):
         step(i)
@@ -685,7 +733,8 @@ def main() -> int:
         "config": {"workload": cfg.name, "batch": cfg.batch, "hidden": cfg.hidden,
                    "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "kv_tokens": int(pos[0]) if cfg.ragged is None else f"ragged sum {int(np.sum(pos))}",
-                   "layer_sets": R, "parallelism": "single GPU", "schedule": "+".join(phases)},
+                   "cache_capacity": cap, "layer_sets": R, "parallelism": "single GPU",
+                   "schedule": "+".join(phases)},
         "hbm_gbps": round(gbps, 1),
         "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         "algorithmic_bytes": nbytes,

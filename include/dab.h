@@ -20,10 +20,14 @@
  *
  * Weights are taken in the [out_features, in_features] layout (the layout of
  * a torch.nn.Linear weight): the transpose of the [in, out] matrices the
- * pages multiply by.  Each output's weights are then one contiguous row, so
+ * pages multiply by (the ClusterFusion page, section 1.1, multiplies the
+ * hidden state by W_qkv and the attention output by W_out; the
+ * operator-fusion page, section 3, indexes q_weight as [hidden_dim,
+ * heads * head_dim]).  Each output's weights are then one contiguous row, so
  * at decode batch sizes one workgroup computes whole outputs and no partial
- * sums cross workgroups.  Weights are static; transposing the pages' layout
- * once at load time gives this one.
+ * sums cross workgroups.  Weights are static: dab_pack_weight turns a matrix
+ * in the pages' [in, out] layout into this one on the device, once, at load
+ * time.
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise,
@@ -35,8 +39,15 @@
  *     device except dab_read_device_error.  The enqueue sequence contains
  *     only kernel launches, so it may be captured into a HIP graph.
  *   - Storage dtype DAB_BF16: hidden, norm_w, W_qkv, W_o, both caches and out
- *     hold bf16; every intermediate is fp32 and accumulation is fp32.
- *     DAB_F32: every tensor is fp32.
+ *     hold bf16 and every sum accumulates in fp32.  Intermediates are fp32
+ *     except where a matrix-core or pair-dot-product operand is rounded to
+ *     bf16 (nearest-even, a relative 2^-9 each): with grouped heads
+ *     (n_q_heads > n_kv_heads) attention rounds the pre-scaled q and the
+ *     softmax weights to bf16 for v_dot2 products against the stored K and
+ *     V; with a batch of 8 or more the phased schedule's matrix-core panels
+ *     round x * norm_w and the attention output to bf16; the new token's k
+ *     and v enter attention rounded to bf16, exactly as appended.
+ *     DAB_F32: every tensor and every intermediate is fp32.
  *   - Errors a host can see (bad shapes, null or misaligned pointers,
  *     overlapping output, short workspace) return a status before anything
  *     is enqueued, and no buffer is touched.  A launch failure returns
@@ -94,16 +105,28 @@ typedef struct {
  * workgroups load their K/V rows while the QKV projection finishes, then
  * the output projection.  It needs n_q_heads / n_kv_heads in {1, 2, 4, 8}
  * and H a multiple of 4096 (bf16) or 2048 (fp32).
+ * DAB_SCHEDULE_FUSED runs the whole step as one launch, its workgroups in
+ * dependency order: the QKV projection's row panels (q, then k, then v
+ * heads), the attention chunks, then the output projection's panels.  A
+ * chunk waits only for the q panels of its kv group's query heads; the
+ * chunk that also takes the new token waits for that group's k and v
+ * panels before it; the output projection streams its weights as soon as
+ * it has a slot and waits for its sequences' attention output.  It needs
+ * n_q_heads / n_kv_heads in {1, 2, 4, 8}, nq * D a multiple of 4096 (bf16)
+ * or 2048 (fp32), and batch <= 4.
  * AUTO picks the schedule measured fastest on MI355X: ATTN_OPROJ where it
  * applies with n_q_heads == n_kv_heads and batch <= 4, PHASED otherwise.
- * All schedules give identical bits, and every call is deterministic: every
- * sum has a fixed order.
+ * Every call is deterministic: every sum has a fixed order.  At one chunk
+ * length (kv_chunk) the schedules give identical bits, except that the
+ * phased schedule's matrix-core panels (bf16, batch of 8 or more) round
+ * their operands to bf16 where the other schedules keep fp32.
  */
 typedef enum {
     DAB_SCHEDULE_AUTO = 0,
     DAB_SCHEDULE_PHASED = 1,
     DAB_SCHEDULE_ATTN_OPROJ = 2,
-    DAB_SCHEDULE_QKV_ATTN = 3
+    DAB_SCHEDULE_QKV_ATTN = 3,
+    DAB_SCHEDULE_FUSED = 4
 } dab_schedule;
 
 /*
@@ -190,6 +213,40 @@ const char* dab_phase_name(const dab_config* cfg, int i);
  * invalid).
  */
 dab_status dab_read_device_error(void* workspace, void* stream, int32_t* flag);
+
+/*
+ * Test tap, not part of the step: copies the attention output a [B, nq*D]
+ * (fp32, head-major: element b * nq*D + h*D + d is dim d of query head h)
+ * that the last call with this configuration left in `workspace` to `dst`
+ * (device, fp32, 16-byte aligned, must not overlap the workspace), with a
+ * kernel on `stream` ordered after that call.  Every schedule keeps a in
+ * the workspace.  Returns DAB_ERR_INVALID_ARG / DAB_ERR_UNSUPPORTED for a
+ * bad configuration or pointer, DAB_ERR_WORKSPACE for a short workspace.
+ */
+dab_status dab_attention_output(const dab_config* cfg, const void* workspace, size_t workspace_bytes, float* dst,
+                                void* stream);
+
+/*
+ * Weight layout conversion for callers that hold a matrix in the pages'
+ * [in_features, out_features] layout (y = x @ W: the ClusterFusion page,
+ * section 1.1, torch.mm(hidden_states, W_qkv) and torch.mm(attn_out,
+ * W_out); the operator-fusion page, section 3, q_weight [hidden_dim,
+ * num_heads * head_dim]).  Writes dst[o, i] = src[i, o], the
+ * [out_features, in_features] layout every entry point here takes:
+ *
+ *   W_qkv [H, (nq+2nkv)*D]  -> [(nq+2nkv)*D, H]     (in = H)
+ *   W_o   [nq*D, H]         -> [H, nq*D]            (in = nq*D)
+ *   W_gate, W_up [H, F]     -> [F, H];  W_down [F, H] -> [H, F]
+ *
+ * src, dst: device, 16-byte aligned, in_features * out_features elements of
+ * `dtype` each, caller-owned, not overlapping.  in_features at most
+ * 65535 * 64, out_features at most 2^30.  One kernel on `stream`, no
+ * allocation, no synchronisation; the bits are copied unchanged.  Returns
+ * DAB_ERR_INVALID_ARG for a null, misaligned or overlapping pointer, a bad
+ * size or dtype, DAB_ERR_HIP if the launch fails.
+ */
+dab_status dab_pack_weight(const void* src, void* dst, int64_t in_features, int64_t out_features, int32_t dtype,
+                           void* stream);
 
 /* Static, human-readable description of a status code. */
 const char* dab_status_string(dab_status status);

@@ -95,7 +95,7 @@ def test_schedule_selection(lib):
             c.schedule = sched
             assert call(lib, c) == _lib.DAB_ERR_UNSUPPORTED
             assert lib.dab_phase_count(ctypes.byref(c)) == 0
-    for bad in (-1, 4, 7):
+    for bad in (-1, 5, 7):
         assert lib.dab_workspace_size(ctypes.byref(cfg(schedule=bad))) == 0
         assert call(lib, cfg(schedule=bad)) == _lib.DAB_ERR_INVALID_ARG
     # the 7B layer: auto takes attention + projection in one launch; every schedule is available
@@ -105,7 +105,15 @@ def test_schedule_selection(lib):
     assert names(lib, cfg(**head, schedule=1)) == PHASED
     assert names(lib, cfg(**head, schedule=2)) == ATTN_OPROJ
     assert names(lib, cfg(**head, schedule=3)) == QKV_ATTN
+    assert names(lib, cfg(**head, schedule=4)) == [b"decode_block_fused"]
     assert lib.dab_phase_name(ctypes.byref(cfg(**head)), 2) is None
+    # the whole step in one launch: batches of up to 4, whole K-blocks in the output projection
+    assert call(lib, cfg(**{**head, "batch": 5}, schedule=4)) == _lib.DAB_ERR_UNSUPPORTED
+    assert names(lib, cfg(**{**head, "batch": 4, "n_kv_heads": 8}, schedule=4)) == [b"decode_block_fused"]
+    assert call(lib, cfg(n_q_heads=6, n_kv_heads=2, schedule=4)) == _lib.DAB_ERR_UNSUPPORTED
+    # four fp32 rows of H = 8192 do not fit the 64 KB of staged inputs
+    assert call(lib, cfg(batch=4, hidden=8192, n_q_heads=16, n_kv_heads=16, head_dim=128, schedule=4)) == \
+        _lib.DAB_ERR_UNSUPPORTED
     # grouped heads, or batch above 4: auto stays phased; a group of 4 at 4K tokens has 64 chunks of 64,
     # more than one merge round (8 chunks per thread and head) in the attention kernel, so the merge
     # runs as a kernel of its own; 16 sequences have 8 chunks each and merge in the attention kernel
@@ -291,3 +299,45 @@ def test_ffn_timed_variant_checks_events(lib):
         assert ffn_call(lib, c, timed=(ev, count)) == _lib.DAB_ERR_INVALID_ARG, count
     ev = (vp * 4)(vp(8), vp(16), vp(0), vp(32))
     assert ffn_call(lib, c, timed=(ev, 4)) == _lib.DAB_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# the weight-layout conversion and the attention-output tap: host checks
+# ---------------------------------------------------------------------------
+
+def test_pack_weight_host_checks(lib):
+    src, dst = (1 << 40), (1 << 42)
+    ok = dict(src=src, dst=dst, n_in=4096, n_out=12288, dtype=_lib.DAB_BF16)
+    bad = [dict(src=0), dict(dst=0), dict(src=src + 8), dict(dst=dst + 2), dict(n_in=0), dict(n_out=-1),
+           dict(n_in=65535 * 64 + 1), dict(dtype=5),
+           dict(dst=src + 4096 * 2 * 100),            # dst starts inside src
+           dict(src=dst + 16, dst=dst)]               # src starts inside dst
+    for over in bad:
+        a = {**ok, **over}
+        st = lib.dab_pack_weight(ctypes.c_void_p(a["src"]), ctypes.c_void_p(a["dst"]), a["n_in"], a["n_out"],
+                                 a["dtype"], None)
+        assert st == _lib.DAB_ERR_INVALID_ARG, over
+
+
+def test_attention_output_host_checks(lib):
+    c = cfg()
+    n = lib.dab_workspace_size(ctypes.byref(c))
+    ws, dst = (1 << 40), (1 << 42)
+    vp = ctypes.c_void_p
+    assert lib.dab_attention_output(ctypes.byref(cfg(head_dim=96)), vp(ws), n, vp(dst), None) == \
+        _lib.DAB_ERR_UNSUPPORTED
+    assert lib.dab_attention_output(ctypes.byref(c), vp(0), n, vp(dst), None) == _lib.DAB_ERR_INVALID_ARG
+    assert lib.dab_attention_output(ctypes.byref(c), vp(ws + 128), n, vp(dst), None) == _lib.DAB_ERR_INVALID_ARG
+    assert lib.dab_attention_output(ctypes.byref(c), vp(ws), n, vp(0), None) == _lib.DAB_ERR_INVALID_ARG
+    assert lib.dab_attention_output(ctypes.byref(c), vp(ws), n - 256, vp(dst), None) == _lib.DAB_ERR_WORKSPACE
+    assert lib.dab_attention_output(ctypes.byref(c), vp(ws), n, vp(ws + 512), None) == _lib.DAB_ERR_INVALID_ARG
+    # batch 0: nothing to copy, nothing enqueued
+    assert lib.dab_attention_output(ctypes.byref(cfg(batch=0)), vp(ws), n, vp(dst), None) == _lib.DAB_OK
+
+
+def test_python_wrapper_requires_a_weight_layout():
+    import inspect
+    import attention_block_amd as ab
+    for f in (ab.decode_attn_block, ab.decode_attn_block_timed, ab.decode_ffn_block, ab.decode_ffn_block_timed):
+        p = inspect.signature(f).parameters["weight_layout"]
+        assert p.kind is inspect.Parameter.KEYWORD_ONLY and p.default is inspect.Parameter.empty, f.__name__

@@ -43,8 +43,9 @@ def test_layer_chain_parity(label, cfg, pos, n_layers):
         fdev = ffn_to_device(finp)
         x = dev["hidden"] if gpu_x is None else gpu_x
         h = ab.decode_attn_block(x, dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"], dev["v_cache"],
-                                 dev["pos"], cfg.rope_theta, cfg.eps)
-        gpu_x = ab.decode_ffn_block(h, fdev["norm_w"], fdev["w_gate"], fdev["w_up"], fdev["w_down"], fcfg.eps)
+                                 dev["pos"], cfg.rope_theta, cfg.eps, weight_layout="out_in")
+        gpu_x = ab.decode_ffn_block(h, fdev["norm_w"], fdev["w_gate"], fdev["w_up"], fdev["w_down"], fcfg.eps,
+                                    weight_layout="out_in")
         torch.cuda.synchronize()
         err = rel_l2(storage_values(gpu_x), ref_f["out"])
         print(f"[chain] {label}: layer {layer}: rel-L2(out) = {err:.2e}", flush=True)

@@ -32,9 +32,10 @@ def ffn_to_device(inp: dict, device="cuda"):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
-    # one output feature per row: the transposes of the oracle's [in, out] matrices
-    return dict(hidden=t(inp["hidden"]), norm_w=t(inp["norm_w"]), w_gate=t(inp["w_gate"].T),
-                w_up=t(inp["w_up"].T), w_down=t(inp["w_down"].T))
+    # the oracle's [in, out] matrices, packed by the library into its [out, in] layout
+    import attention_block_amd as ab
+    return dict(hidden=t(inp["hidden"]), norm_w=t(inp["norm_w"]), w_gate=ab.pack_weight(t(inp["w_gate"])),
+                w_up=ab.pack_weight(t(inp["w_up"])), w_down=ab.pack_weight(t(inp["w_down"])))
 
 
 def run_ffn(dev: dict, cfg: FfnConfig, workspace=None):
@@ -42,7 +43,7 @@ def run_ffn(dev: dict, cfg: FfnConfig, workspace=None):
     import attention_block_amd as ab
     dbg = torch.empty(dev["hidden"].shape, dtype=torch.float32, device=dev["hidden"].device)
     out = ab.decode_ffn_block(dev["hidden"], dev["norm_w"], dev["w_gate"], dev["w_up"], dev["w_down"], cfg.eps,
-                              dbg_y=dbg, workspace=workspace)
+                              dbg_y=dbg, workspace=workspace, weight_layout="out_in")
     torch.cuda.synchronize()
     return out, dbg
 
@@ -102,7 +103,7 @@ def test_ffn_batch_zero_touches_nothing():
     dev = ffn_to_device(inp)
     hidden = dev["hidden"][:0]
     out = torch.full((0, 256), 7.0, dtype=torch.bfloat16, device="cuda")
-    ab.decode_ffn_block(hidden, dev["norm_w"], dev["w_gate"], dev["w_up"], dev["w_down"], cfg.eps, out=out)
+    ab.decode_ffn_block(hidden, dev["norm_w"], dev["w_gate"], dev["w_up"], dev["w_down"], cfg.eps, out=out, weight_layout="out_in")
     torch.cuda.synchronize()
     assert out.shape == (0, 256)
 
@@ -139,13 +140,13 @@ def test_ffn_graph_replay_matches_eager():
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         ab.decode_ffn_block(dev["hidden"], dev["norm_w"], dev["w_gate"], dev["w_up"], dev["w_down"], cfg.eps,
-                            out=out, workspace=ws)
+                            out=out, workspace=ws, weight_layout="out_in")
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         ab.decode_ffn_block(dev["hidden"], dev["norm_w"], dev["w_gate"], dev["w_up"], dev["w_down"], cfg.eps,
-                            out=out, workspace=ws)
+                            out=out, workspace=ws, weight_layout="out_in")
     for rep in range(3):
         out.fill_(0)
         torch.cuda.synchronize()

@@ -1,10 +1,12 @@
 """HIP path versus the fp64 oracle, element by element, on seeded inputs.
 
-Gates (per tensor, relative L2 over the whole tensor): out, the fp32
-pre-residual tap y, the appended K rows and V rows; <= 1e-2 with bf16
-storage and fp32 accumulation, <= 1e-5 in fp32 mode.  Every cache element
-other than the appended rows must keep its exact bits, including the NaN
-sentinel tail beyond each sequence's position.
+Gates (relative L2 per sequence, the worst sequence counting): out, the
+fp32 pre-residual tap y, the appended K rows and V rows; and per sequence
+and query head the attention output a (read from the workspace through
+the library's test tap); <= 1e-2 with bf16 storage and fp32 accumulation,
+<= 1e-5 in fp32 mode.  Every cache element other than the appended rows
+must keep its exact bits, including the NaN sentinel tail beyond each
+sequence's position.
 """
 import sys
 
@@ -30,8 +32,8 @@ def parity_case(cfg: BlockConfig, seed: int, *, cap=None, pos=None, kv_chunk=0, 
     ref = oracle.decode_step_from_inputs(inp)
     dev = to_device(inp)
     before = (storage_bits(dev["k_cache"]), storage_bits(dev["v_cache"]))
-    out, dbg = run_gpu(dev, cfg, kv_chunk=kv_chunk, schedule=schedule)
-    errs = compare(inp, ref, dev, out, dbg, before)
+    out, dbg, a = run_gpu(dev, cfg, kv_chunk=kv_chunk, schedule=schedule, want_a=True)
+    errs = compare(inp, ref, dev, out, dbg, before, a=a)
     say(f"[parity] {label}: " + ", ".join(f"{k}={v:.2e}" if isinstance(v, float) else f"{k}={v}"
                                           for k, v in errs.items()))
     check_errs(errs, cfg.dtype, label)
@@ -42,18 +44,23 @@ def parity_case(cfg: BlockConfig, seed: int, *, cap=None, pos=None, kv_chunk=0, 
 # the workload configurations, full size
 # ---------------------------------------------------------------------------
 
-SCHEDULES = ["phased", "attn_oproj", "qkv_attn"]
+SCHEDULES = ["phased", "attn_oproj", "qkv_attn", "fused"]
 
 
 def applies(cfg: BlockConfig, schedule: str) -> bool:
     """The one-launch kernels are built for groups 1, 2, 4, 8 and a projection of whole K-blocks (a
-    multiple of 4096 bf16 / 2048 fp32 values): the output projection's K = nq * D for attn_oproj, the
-    QKV projection's K = H for qkv_attn."""
+    multiple of 4096 bf16 / 2048 fp32 values): the output projection's K = nq * D for attn_oproj and
+    fused, the QKV projection's K = H for qkv_attn; fused also for batches of up to 4 whose fp32 input
+    rows fit one workgroup's 64 KB of LDS in both projections."""
     if schedule in ("auto", "phased"):
         return True
     kblock = 4096 if cfg.dtype == "bf16" else 2048
-    k = cfg.n_q_heads * cfg.head_dim if schedule == "attn_oproj" else cfg.hidden
-    return cfg.group in (1, 2, 4, 8) and k % kblock == 0
+    k = cfg.hidden if schedule == "qkv_attn" else cfg.n_q_heads * cfg.head_dim
+    ok = cfg.group in (1, 2, 4, 8) and k % kblock == 0
+    if schedule == "fused":
+        nb = 1 if cfg.batch <= 1 else 2 if cfg.batch == 2 else 4
+        ok = ok and cfg.batch <= 4 and nb * max(cfg.hidden, cfg.n_q_heads * cfg.head_dim) * 4 <= 65536
+    return ok
 
 
 @pytest.mark.parametrize("schedule", ["auto"] + SCHEDULES)
@@ -98,6 +105,14 @@ EDGE = [
      [299, 0, 17, 256, 1, 128, 64, 200, 33], 0),
     ("mfma batch 20, two tiles", small_cfg("m2", 20, 2048, 16, 4, 128, "bf16"), 130, list(range(3, 130, 6))[:20], 0),
     ("mfma d64 group 8", small_cfg("m3", 8, 1024, 16, 2, 64, "bf16", 5e5), 90, [89, 0, 5, 64, 33, 80, 12, 1], 32),
+    # groups of 5, 6 and 7 (merge rounds of 6, 5 and 4 chunks per thread), in bf16 (pair dot products)
+    # and fp32, with the merge inside the attention kernel and in a kernel of its own (63 chunks)
+    ("group 5 bf16", small_cfg("g5b", 2, 640, 10, 2, 64, "bf16", 5e5), 300, [299, 150], 32),
+    ("group 5 f32", small_cfg("g5f", 2, 640, 10, 2, 64, "f32", 5e5), 300, [299, 150], 32),
+    ("group 6 bf16 merge kernel", small_cfg("g6b", 1, 768, 12, 2, 128, "bf16", 5e5), 2100, [2000], 32),
+    ("group 6 f32", small_cfg("g6f", 2, 768, 12, 2, 128, "f32"), 300, [299, 1], 64),
+    ("group 7 bf16", small_cfg("g7b", 2, 896, 14, 2, 64, "bf16"), 300, [299, 0], 32),
+    ("group 7 f32 merge kernel", small_cfg("g7f", 1, 896, 14, 2, 64, "f32", 5e5), 2100, [2000], 32),
 ]
 
 
@@ -118,7 +133,12 @@ EDGE_ONE_LAUNCH = [
     # 2048 chunks: every attention workgroup of the one-launch attention + projection takes several
     ("bf16 many chunks per workgroup", small_cfg("o8", 2, 4096, 32, 32, 128, "bf16"), 2000, [1999, 1000], 64),
 ]
-ONE_LAUNCH_CASES = [(sched, *e) for e in EDGE_ONE_LAUNCH for sched in ("attn_oproj", "qkv_attn")
+EDGE_ONE_LAUNCH += [
+    ("bf16 fused batch 3 ragged", small_cfg("o9", 3, 1024, 32, 8, 128, "bf16", 5e5), 900, [899, 0, 450], 64),
+    ("f32 fused d64 group 2 batch 2", small_cfg("o10", 2, 2048, 32, 16, 64, "f32"), 260, [259, 100], 32),
+    ("bf16 fused group 8 H 8192", small_cfg("o11", 1, 8192, 64, 8, 64, "bf16"), 520, [519], 0),
+]
+ONE_LAUNCH_CASES = [(sched, *e) for e in EDGE_ONE_LAUNCH for sched in ("attn_oproj", "qkv_attn", "fused")
                     if applies(e[1], sched)]
 
 
@@ -128,9 +148,10 @@ def test_edge_parity_one_launch(schedule, label, cfg, cap, pos, kv_chunk):
     parity_case(cfg, 7, cap=cap, pos=pos, kv_chunk=kv_chunk, label=label, schedule=schedule)
 
 
-def test_one_launch_edge_cases_cover_both_schedules():
-    assert {c[0] for c in ONE_LAUNCH_CASES} == {"attn_oproj", "qkv_attn"}
+def test_one_launch_edge_cases_cover_every_schedule():
+    assert {c[0] for c in ONE_LAUNCH_CASES} == {"attn_oproj", "qkv_attn", "fused"}
     assert sum(c[0] == "qkv_attn" for c in ONE_LAUNCH_CASES) >= 3
+    assert sum(c[0] == "fused" for c in ONE_LAUNCH_CASES) >= 6
 
 
 def test_default_workspaces_follow_the_configuration():
@@ -232,7 +253,33 @@ def test_split_count_invariance():
         assert np.linalg.norm(o - outs[0]) / np.linalg.norm(outs[0]) < 1e-6
 
 
-@pytest.mark.parametrize("schedule", ["auto", "phased"])
+def test_fused_counters_return_to_zero():
+    """The whole step in one launch re-arms its counters itself (the last readers zero them): after a
+    call, every word in front of the workspace's data (flags, chunk arrivals, ready counts and their
+    reader counts, QKV panel counts) is zero again."""
+    import torch
+    import attention_block_amd as ab
+    cfg = small_cfg("wsf", 3, 1024, 32, 8, 128, "bf16", 5e5)
+    inp = make_inputs(cfg, 2, cap=300, pos=[299, 10, 150])
+    dev = to_device(inp)
+    c = ab.make_config(batch=3, hidden=1024, n_q_heads=32, n_kv_heads=8, head_dim=128, cache_capacity=300,
+                       dtype="bf16", rope_theta=5e5, schedule="fused")
+    ws = ab.Workspace(ab.workspace_size(c), dev["hidden"].device)
+    say("[counters] fused: three calls, then inspect the counters")
+    for _ in range(3):
+        run_gpu(dev, cfg, workspace=ws, schedule="fused")
+    torch.cuda.synchronize()
+
+    def a256(n):
+        return (n + 255) // 256 * 256
+    B, nkv, nq = 3, 8, 32
+    # the layout of the counter words (flags, arrivals, ready counts, their readers, panel counts)
+    prefix = 256 + a256(4 * B * nkv) + 2 * a256(4 * B * 16 * 32) + a256(4 * B * (nq + 2 * nkv))
+    raw = ws._buf[ws.ptr - ws._buf.data_ptr():][:prefix].cpu().numpy().view(np.int32)
+    assert np.all(raw == 0), np.nonzero(raw)[0][:10]
+
+
+@pytest.mark.parametrize("schedule", ["auto", "phased", "fused"])
 def test_repeat_calls_are_bit_identical(schedule):
     """Deterministic merges, and counters back at zero after each call."""
     import torch
@@ -282,7 +329,7 @@ def test_bad_position_sets_flag_and_skips_sequence(schedule, cfg):
     say("[bad pos] sequence 1 at pos == cap")
     ab.read_device_error()                             # clear any earlier flag
     ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"], dev["v_cache"],
-                         dev["pos"], cfg.rope_theta, cfg.eps, out=out, schedule=schedule)
+                         dev["pos"], cfg.rope_theta, cfg.eps, out=out, schedule=schedule, weight_layout="out_in")
     flag = ab.read_device_error()
     assert flag == 1
     assert torch.all(out[1] == 12345.0)               # its output row was left unwritten
@@ -317,14 +364,14 @@ def test_graph_replay_matches_eager(schedule):
     with torch.cuda.stream(s):  # warm-up call outside capture
         ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
                              dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws,
-                             schedule=schedule)
+                             schedule=schedule, weight_layout="out_in")
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
                              dev["v_cache"], dev["pos"], cfg.rope_theta, cfg.eps, out=out, workspace=ws,
-                             schedule=schedule)
+                             schedule=schedule, weight_layout="out_in")
     for i in range(4):
         out.zero_()
         torch.cuda.synchronize()
