@@ -17,7 +17,8 @@ from ._lib import DAB_BF16, DAB_F32, FFN_PHASES, READ_PROBE_BLOCKS, DabConfig, D
 __all__ = ["DabError", "DabConfig", "make_config", "workspace_size", "Workspace", "decode_attn_block",
            "decode_attn_block_timed", "read_device_error", "phase_names", "HipEvent", "lib_version",
            "DabFfnConfig", "FFN_PHASES", "ffn_workspace_size", "decode_ffn_block", "decode_ffn_block_timed",
-           "read_probe", "READ_PROBE_BLOCKS", "pack_weight", "attention_output", "WEIGHT_LAYOUTS"]
+           "read_probe", "READ_PROBE_BLOCKS", "pack_weight", "attention_output", "WEIGHT_LAYOUTS",
+           "decode_attn_block_noalloc"]
 
 # Weight layouts a call may name: "out_in" is the library's own ([out_features, in_features], one
 # output feature per row, as torch.nn.Linear stores its weight); "in_out" is the pages' ([in, out],
@@ -247,6 +248,20 @@ def attention_output(cfg: DabConfig, workspace: Workspace, out=None):
 def workspace_of(cfg: DabConfig, device) -> Workspace:
     """The default workspace calls without a `workspace` argument use for this configuration and device."""
     return _workspace_for(cfg, device)
+
+
+def decode_attn_block_noalloc(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta: float,
+                              eps: float = 1e-6, out=None, dbg_y=None, kv_chunk: int = 0, schedule: str = "auto"):
+    """decode_attn_block through dab_decode_attn_block_noalloc: the library's own per-GPU scratch serves
+    as the workspace, so the call allocates nothing on the device (give `out`, and the weights in the
+    library's [out, in] layout, for a call that allocates nothing at all).  Calls that overlap in time
+    on one GPU race on that scratch."""
+    cfg, out, w_qkv, w_o = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y,
+                                    kv_chunk, schedule, "out_in")
+    _check(_lib.load().dab_decode_attn_block_noalloc(
+        ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache), _ptr(v_cache),
+        _ptr(pos), _ptr(out), _ptr(dbg_y), _stream_ptr(hidden.device)), "dab_decode_attn_block_noalloc")
+    return out
 
 
 class HipEvent:

@@ -17,8 +17,9 @@ EXPORTS = (
     "dab_workspace_size", "dab_workspace_init", "dab_decode_attn_block", "dab_decode_attn_block_timed",
     "dab_phase_count", "dab_phase_name", "dab_read_device_error", "dab_status_string", "dab_version",
     "dab_last_hip_error", "dab_ffn_workspace_size", "dab_decode_ffn_block", "dab_decode_ffn_block_timed",
-    "dab_read_probe", "dab_attention_output", "dab_pack_weight",
+    "dab_read_probe", "dab_attention_output", "dab_pack_weight", "dab_decode_attn_block_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 16 << 20      # DAB_NOALLOC_SCRATCH_BYTES
 READ_PROBE_BLOCKS = 2048      # DAB_READ_PROBE_BLOCKS
 # names of the two FFN kernels, in launch order
 FFN_PHASES = ("ffn_rmsnorm_gate_up_silu", "ffn_down_residual")
@@ -92,6 +93,8 @@ def load() -> ctypes.CDLL:
     lib.dab_attention_output.restype = i32
     lib.dab_pack_weight.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, vp]
     lib.dab_pack_weight.restype = i32
+    lib.dab_decode_attn_block_noalloc.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dab_decode_attn_block_noalloc.restype = i32
     ffnp = ctypes.POINTER(DabFfnConfig)
     lib.dab_ffn_workspace_size.argtypes = [ffnp]
     lib.dab_ffn_workspace_size.restype = sz

@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "dab.h"
 #include "dab_kernels.h"
@@ -179,6 +180,62 @@ dab_status call(const dab_config* cfg, const void* hidden, const void* norm_w, c
     if (p.B == 0) return DAB_OK;
     const dab::StepArgs a = step_args(p, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y, workspace);
     return enqueue(p, a, static_cast<hipStream_t>(stream), events);
+}
+
+// Scratch of the allocation-free entry point: the workspace of its calls, a
+// file-scope device array of which every GPU holds its own copy at its own
+// address.  In host code `scratch` only names the symbol; the address of a
+// device's copy comes from hipGetSymbolAddress with that device current, once
+// per device, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[DAB_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kSlotDevices];
+
+dab_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kSlotDevices) return DAB_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p || ((uintptr_t)p % 256) != 0) return DAB_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DAB_OK;
+}
+
+dab_status call_noalloc(const dab_config* cfg, const void* hidden, const void* norm_w, const void* w_qkv,
+                        const void* w_o, void* k_cache, void* v_cache, const int32_t* pos, void* out, float* dbg_y,
+                        void* stream) {
+    Plan p;
+    dab_status st = plan(cfg, &p);
+    if (st != DAB_OK) return st;
+    if (p.ws_bytes > (size_t)DAB_NOALLOC_SCRATCH_BYTES) return DAB_ERR_WORKSPACE;
+    // the pointer checks first, against a stand-in address (no device call yet)
+    st = dab::check_call(p, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y,
+                         reinterpret_cast<void*>((uintptr_t)256), DAB_NOALLOC_SCRATCH_BYTES);
+    if (st != DAB_OK) return st;
+    if (p.B == 0) return DAB_OK;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != DAB_OK) return st;
+    st = dab::check_call(p, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y, ws,
+                         DAB_NOALLOC_SCRATCH_BYTES);
+    if (st != DAB_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the scratch keeps whatever the last call on this GPU left, of whatever
+    // configuration: the words that must start at zero (error flags, arrival
+    // and ready counts, panel counts: everything in front of q) are cleared
+    // by a fill kernel, which a graph capture records like any other kernel
+    st = hip_status(dab::launch_fill_zero(ws, p.off_q, s));
+    if (st != DAB_OK) return st;
+    const dab::StepArgs a = step_args(p, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y, ws);
+    return enqueue(p, a, s, nullptr);
 }
 
 dab_status ffn_call(const dab_ffn_config* cfg, const void* hidden, const void* norm_w, const void* w_gate,
@@ -406,6 +463,12 @@ dab_status dab_decode_attn_block_timed(const dab_config* cfg, const void* hidden
     if (!events) return DAB_ERR_INVALID_ARG;
     return call(cfg, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y, workspace, workspace_bytes,
                 stream, events, n_events);
+}
+
+dab_status dab_decode_attn_block_noalloc(const dab_config* cfg, const void* hidden, const void* norm_w,
+                                         const void* w_qkv, const void* w_o, void* k_cache, void* v_cache,
+                                         const int32_t* pos, void* out, float* dbg_y, void* stream) {
+    return call_noalloc(cfg, hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, out, dbg_y, stream);
 }
 
 int dab_phase_count(const dab_config* cfg) {

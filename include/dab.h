@@ -199,6 +199,33 @@ dab_status dab_decode_attn_block_timed(const dab_config* cfg,
                                        void* workspace, size_t workspace_bytes,
                                        void* stream, void* const* events, int n_events);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as dab_decode_attn_block, with the same arguments, results and
+ * errors, but no workspace argument.  Its workspace is a device array of
+ * DAB_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held from
+ * the library's load until the process ends; the call allocates nothing.
+ * The first call on a device looks up that device's copy
+ * (hipGetSymbolAddress), so make it outside a graph capture.  Every call
+ * first clears the scratch's counter words with a fill kernel on `stream`
+ * (so any configuration may follow any other), then enqueues the step's
+ * kernels.  Calls on one GPU share its scratch: calls that overlap in time
+ * on one GPU (on different streams, or the same graph launched twice
+ * concurrently) race and give wrong results.  Returns DAB_ERR_WORKSPACE,
+ * before anything is enqueued, when the configuration's workspace
+ * (dab_workspace_size) exceeds DAB_NOALLOC_SCRATCH_BYTES.  The device error
+ * flag of these calls is cleared by the next call and has no reader: a
+ * sequence with an out-of-range pos is still skipped.
+ */
+#define DAB_NOALLOC_SCRATCH_BYTES (16u << 20)
+dab_status dab_decode_attn_block_noalloc(const dab_config* cfg,
+                                         const void* hidden, const void* norm_w,
+                                         const void* w_qkv, const void* w_o,
+                                         void* k_cache, void* v_cache,
+                                         const int32_t* pos, void* out, float* dbg_y,
+                                         void* stream);
+
 /* Number of kernels one call enqueues for this configuration (0 if invalid). */
 int dab_phase_count(const dab_config* cfg);
 

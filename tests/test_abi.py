@@ -341,3 +341,28 @@ def test_python_wrapper_requires_a_weight_layout():
     for f in (ab.decode_attn_block, ab.decode_attn_block_timed, ab.decode_ffn_block, ab.decode_ffn_block_timed):
         p = inspect.signature(f).parameters["weight_layout"]
         assert p.kind is inspect.Parameter.KEYWORD_ONLY and p.default is inspect.Parameter.empty, f.__name__
+
+
+def test_noalloc_host_checks(lib):
+    """The allocation-free entry point rejects what the workspace entry point rejects, and a configuration
+    whose workspace exceeds its scratch, all before any device call (so this runs without a GPU)."""
+    vp = ctypes.c_void_p
+    f = FakePtrs()
+    ptrs = dict(hidden=f.take(1 << 20), norm_w=f.take(1 << 20), w_qkv=f.take(1 << 24), w_o=f.take(1 << 24),
+                k_cache=f.take(1 << 24), v_cache=f.take(1 << 24), pos=f.take(64), out=f.take(1 << 20), dbg_y=0)
+
+    def na(c, **over):
+        p = {**ptrs, **over}
+        return lib.dab_decode_attn_block_noalloc(ctypes.byref(c), *[vp(p[k]) for k in (
+            "hidden", "norm_w", "w_qkv", "w_o", "k_cache", "v_cache", "pos", "out", "dbg_y")], None)
+
+    assert na(cfg(head_dim=96)) == _lib.DAB_ERR_UNSUPPORTED
+    assert na(cfg(dtype=7)) == _lib.DAB_ERR_INVALID_ARG
+    assert na(cfg(), hidden=0) == _lib.DAB_ERR_INVALID_ARG
+    assert na(cfg(), out=ptrs["hidden"]) == _lib.DAB_ERR_INVALID_ARG
+    assert na(cfg(batch=0)) == _lib.DAB_OK                       # nothing to do, nothing enqueued
+    # a workspace larger than the scratch: 32 sequences of 64 chunks of 32 heads
+    big = cfg(batch=32, hidden=4096, n_q_heads=32, n_kv_heads=32, head_dim=128, cache_capacity=1 << 16,
+              dtype=_lib.DAB_BF16, rope_theta=1e4, kv_chunk=1024)
+    assert lib.dab_workspace_size(ctypes.byref(big)) > _lib.NOALLOC_SCRATCH_BYTES
+    assert na(big) == _lib.DAB_ERR_WORKSPACE
