@@ -371,10 +371,10 @@ def graph_time(step, steps: int, R: int) -> float:
     start, end = ab.HipEvent(), ab.HipEvent()
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    # ~1 ms of spinning ahead of the start event: the graphs are submitted while the GPU spins, so the
-    # interval between the events is the GPU time of the K steps, not the host's graph submission
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(2.4e6))
+    # one more untimed replay right ahead of the start event: the GPU keeps streaming (clocks up, caches
+    # and TLBs in their steady state) while the host submits the timed graphs, so the interval between
+    # the events is the GPU time of the K steps, not the host's submission or a cold start
+    g_main.replay()
     start.record(stream.cuda_stream)
     for _ in range(n_main):
         g_main.replay()
