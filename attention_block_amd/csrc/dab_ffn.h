@@ -201,108 +201,60 @@ __device__ void ffn_down_panel(const FfnArgs& a, int panel, int bgi, float* xs) 
     }
 }
 
-// MFMA panels (bf16, batch >= 8): 16 sequences per workgroup, kMfmaWaves
-// waves splitting K, v_mfma_f32_16x16x32_bf16 tiles of 16 rows x 16
-// sequences (the layout of the attention block's MFMA panels).
+// MFMA panels (bf16, batch >= 8): the matrix-core row panel of dab_mfma.h
+// for 16 or 32 sequences per workgroup.
 //   GATE_UP  tile 0: rows 16p .. 16p+15 of W_gate, tile 1: the same rows of
-//            W_up; the B operand is h .* norm_w rounded to bf16 (norm_w from
-//            LDS), with the sums of h^2 taken on the way; m = silu(r g)(r u)
+//            W_up; the batch operand is h .* norm_w rounded to bf16 (norm_w
+//            from LDS), with the sums of h^2 taken on the way; m = silu(r g)(r u)
 //            goes to the workspace rounded to bf16.
 //   down     TILES tiles of 16 rows of W_down against m (bf16); out = h + y.
-template <bool GATE_UP, int TILES>
-__device__ void ffn_mfma_panel(const FfnArgs& a, int panel, int bgi, MfmaShared& sm, const uint16_t* nw_lds) {
-    constexpr int ROWS = 16 * TILES;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+template <bool GATE_UP, int TILES, int NG>
+__device__ void ffn_mfma_panel(const FfnArgs& a, int panel, int bgi, MfmaLds<TILES, NG>& lds, const uint16_t* nw_lds) {
+    using Core = MfmaCore<TILES, NG, GATE_UP>;
+    constexpr int ROWS = GATE_UP ? 16 : 16 * TILES, NS = 16 * NG;
+    const int t = threadIdx.x, wave = t >> 6;
     const int K = GATE_UP ? a.H : a.F;
-    const int m = lane & 15, kg = lane >> 4;
-    const int row0 = GATE_UP ? panel * 16 + m : panel * ROWS + m;
-    const uint16_t* W0 = static_cast<const uint16_t*>(GATE_UP ? a.w_gate : a.w_down) + (size_t)row0 * K + kg * 8;
-    const uint16_t* W1 = GATE_UP ? static_cast<const uint16_t*>(a.w_up) + (size_t)row0 * K + kg * 8
-                                 : W0 + (size_t)16 * K;
-    // this lane's sequence (tile column m)
-    const int b = bgi * 16 + m;
-    const bool live = b < a.B;
-    const uint16_t* X = (GATE_UP ? static_cast<const uint16_t*>(a.hidden) : a.m16) + (size_t)(live ? b : 0) * K + kg * 8;
-
-    const int nsteps = K / (32 * kMfmaWaves), k_begin = wave * nsteps * 32;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-    float ssq = 0.f;
-    for (int s0 = 0; s0 < nsteps; s0 += kMfmaSteps) {
-        u32x4 w0[kMfmaSteps], w1[kMfmaSteps], x[kMfmaSteps];
+    const uint16_t* rows[Core::RPW];
 #pragma unroll
-        for (int s = 0; s < kMfmaSteps; ++s) {
-            const int k = k_begin + (s0 + s) * 32;
-            const bool in = s0 + s < nsteps;
-            w0[s] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W0 + k)) : u32x4{0u, 0u, 0u, 0u};
-            if constexpr (GATE_UP || TILES == 2)
-                w1[s] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W1 + k)) : u32x4{0u, 0u, 0u, 0u};
-            x[s] = in && live ? *reinterpret_cast<const u32x4*>(X + k) : u32x4{0u, 0u, 0u, 0u};
-        }
-        if (s0 == 0) DAB_TRACE_POINT(a, 1);
-#pragma unroll
-        for (int s = 0; s < kMfmaSteps; ++s) {
-            if (s0 + s >= nsteps) break;
-            bf16x8 bv;
-            if constexpr (GATE_UP) {
-                const int k = k_begin + (s0 + s) * 32 + kg * 8;
-                const u32x4 nw = *reinterpret_cast<const u32x4*>(nw_lds + k);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x0 = __uint_as_float(x[s][i] << 16), x1 = __uint_as_float(x[s][i] & 0xffff0000u);
-                    ssq = fmaf(x0, x0, ssq);
-                    ssq = fmaf(x1, x1, ssq);
-                    bv[2 * i] = (__bf16)(x0 * __uint_as_float(nw[i] << 16));
-                    bv[2 * i + 1] = (__bf16)(x1 * __uint_as_float(nw[i] & 0xffff0000u));
-                }
-            } else {
-                bv = as_bf16x8(x[s]);
-            }
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0[s]), bv, acc0, 0, 0, 0);
-            if constexpr (GATE_UP || TILES == 2)
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1[s]), bv, acc1, 0, 0, 0);
-        }
+    for (int r = 0; r < Core::RPW; ++r) {
+        const int pr = wave + 4 * r, tile = pr >> 4, m = pr & 15;
+        if constexpr (GATE_UP)
+            rows[r] = static_cast<const uint16_t*>(tile == 0 ? a.w_gate : a.w_up) + (size_t)(panel * 16 + m) * K;
+        else
+            rows[r] = static_cast<const uint16_t*>(a.w_down) + (size_t)(panel * ROWS + pr) * K;
     }
-
-    // partial tiles (and sums of h^2) to LDS, summed in wave order
+    const uint16_t* xrows[Core::XPT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        sm.c[wave][0][4 * kg + j][m] = acc0[j];
-        if constexpr (GATE_UP || TILES == 2) sm.c[wave][1][4 * kg + j][m] = acc1[j];
+    for (int i = 0; i < Core::XPT; ++i) {
+        const int b = bgi * NS + wave + 4 * i;
+        xrows[i] = b < a.B ? (GATE_UP ? static_cast<const uint16_t*>(a.hidden) : a.m16) + (size_t)b * K : nullptr;
     }
-    if constexpr (GATE_UP) {
-        ssq += __shfl_xor(ssq, 16);
-        ssq += __shfl_xor(ssq, 32);
-        if (kg == 0) sm.ss[m][wave] = ssq;
-    }
-    __syncthreads();
+    Core core;
+    DAB_TRACE_POINT(a, 1);
+    core.run(rows, xrows, nw_lds, K, lds.st);
+    core.publish_partials(lds.red);
     DAB_TRACE_POINT(a, 2);
+    const MfmaReduce<TILES, NG>& red = lds.red;
     if constexpr (GATE_UP) {
-        if (t >= 256) return;                                      // 16 rows x 16 sequences
-        const int r = t >> 4, n = t & 15;
-        const int bb = bgi * 16 + n;
-        if (bb >= a.B) return;
-        float g = 0.f, u = 0.f, ss = 0.f;
-#pragma unroll
-        for (int w = 0; w < kMfmaWaves; ++w) {
-            g += sm.c[w][0][r][n];
-            u += sm.c[w][1][r][n];
-            ss += sm.ss[n][w];
+        for (int idx = t; idx < 16 * NS; idx += kMfmaThreads) {
+            const int r = idx / NS, sq = idx % NS, g = sq >> 4, n = sq & 15;
+            const int bb = bgi * NS + sq;
+            if (bb >= a.B) continue;
+            const float rs = 1.0f / sqrtf(red.ss[sq] / (float)a.H + a.eps);
+            const float gt = mfma_sum(red, 0, g, r, n) * rs, up = mfma_sum(red, 1, g, r, n) * rs;
+            a.m16[(size_t)bb * a.F + panel * 16 + r] = from_f32<uint16_t>(gt / (1.0f + expf(-gt)) * up);
         }
-        const float rs = 1.0f / sqrtf(ss / (float)a.H + a.eps);
-        g *= rs;
-        u *= rs;
-        a.m16[(size_t)bb * a.F + panel * 16 + r] = from_f32<uint16_t>(g / (1.0f + expf(-g)) * u);
     } else {
-        if (t >= 256 * TILES) return;                              // tiles x 16 rows x 16 sequences
-        const int tile = t >> 8, r = (t >> 4) & 15, n = t & 15;
-        const int bb = bgi * 16 + n;
-        if (bb >= a.B) return;
-        float y = 0.f;
-#pragma unroll
-        for (int w = 0; w < kMfmaWaves; ++w) y += sm.c[w][tile][r][n];
-        const size_t i = (size_t)bb * a.H + panel * ROWS + tile * 16 + r;
-        static_cast<uint16_t*>(a.out)[i] = from_f32<uint16_t>(to_f32(static_cast<const uint16_t*>(a.hidden)[i]) + y);
-        if (a.dbg_y) a.dbg_y[i] = y;
+        for (int idx = t; idx < ROWS * NS; idx += kMfmaThreads) {
+            const int row = idx / NS, sq = idx % NS, g = sq >> 4, n = sq & 15;
+            const int bb = bgi * NS + sq;
+            if (bb >= a.B) continue;
+            const float y = mfma_sum(red, row >> 4, g, row & 15, n);
+            const size_t i = (size_t)bb * a.H + panel * ROWS + row;
+            static_cast<uint16_t*>(a.out)[i] =
+                from_f32<uint16_t>(to_f32(static_cast<const uint16_t*>(a.hidden)[i]) + y);
+            if (a.dbg_y) a.dbg_y[i] = y;
+        }
     }
 }
 

@@ -29,20 +29,20 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
     DAB_TRACE_POINT(a, 3);
 }
 
-template <bool GATE_UP, int TILES>
-__global__ __launch_bounds__(64 * kMfmaWaves) void ffn_mfma_kernel(FfnArgs a) {
-    __shared__ MfmaShared sm;
+template <bool GATE_UP, int TILES, int NG>
+__global__ __launch_bounds__(kMfmaThreads) void ffn_mfma_kernel(FfnArgs a) {
+    __shared__ MfmaLds<TILES, NG> lds;
     extern __shared__ u32x4 nw_raw[];    // gate/up: norm_w, H bf16 values
     DAB_TRACE_POINT(a, 0);
     if constexpr (GATE_UP) {
-        for (int k = threadIdx.x * 8; k < a.H; k += 64 * kMfmaWaves * 8)
+        for (int k = threadIdx.x * 8; k < a.H; k += kMfmaThreads * 8)
             nw_raw[k / 8] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.norm_w) + k);
         __syncthreads();
     }
     const PanelPlanDev& g = GATE_UP ? a.gu : a.down;
     int panel, bgi;
     if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi))
-        ffn_mfma_panel<GATE_UP, TILES>(a, panel, bgi, sm, reinterpret_cast<const uint16_t*>(nw_raw));
+        ffn_mfma_panel<GATE_UP, TILES, NG>(a, panel, bgi, lds, reinterpret_cast<const uint16_t*>(nw_raw));
     DAB_TRACE_POINT(a, 3);
 }
 
@@ -51,13 +51,21 @@ hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, const LaunchEvents& 
     if constexpr (sizeof(T) != 2) {
         return hipErrorInvalidValue;               // planned for bf16 only
     } else {
-        const dim3 block(64 * kMfmaWaves);
+        const dim3 block(kMfmaThreads);
         if constexpr (GATE_UP) {
-            dab_launch((ffn_mfma_kernel<true, 2>), dim3(a.gu.items), block, (size_t)a.H * 2, s, ev, a);
-        } else if (a.down_tiles == 2) {
-            dab_launch((ffn_mfma_kernel<false, 2>), dim3(a.down.items), block, 0, s, ev, a);
+            const dim3 grid(a.gu.items);
+            const size_t lds = (size_t)a.H * 2;
+            if (a.gu.nb == 32) dab_launch((ffn_mfma_kernel<true, 2, 2>), grid, block, lds, s, ev, a);
+            else dab_launch((ffn_mfma_kernel<true, 2, 1>), grid, block, lds, s, ev, a);
         } else {
-            dab_launch((ffn_mfma_kernel<false, 1>), dim3(a.down.items), block, 0, s, ev, a);
+            const dim3 grid(a.down.items);
+            const int key = (a.down_tiles == 2 ? 2 : 0) + (a.down.nb == 32 ? 1 : 0);
+            switch (key) {
+                case 0: dab_launch((ffn_mfma_kernel<false, 1, 1>), grid, block, 0, s, ev, a); break;
+                case 1: dab_launch((ffn_mfma_kernel<false, 1, 2>), grid, block, 0, s, ev, a); break;
+                case 2: dab_launch((ffn_mfma_kernel<false, 2, 1>), grid, block, 0, s, ev, a); break;
+                default: dab_launch((ffn_mfma_kernel<false, 2, 2>), grid, block, 0, s, ev, a); break;
+            }
         }
         return hipGetLastError();
     }

@@ -26,6 +26,7 @@
 #pragma once
 
 #include "dab_device.h"
+#include "dab_mfma.h"
 
 namespace dab {
 namespace dev {
@@ -494,148 +495,120 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
 // MFMA panels (bf16, batch >= 8)
 // ---------------------------------------------------------------------------
 //
-// A panel is TILES x 16 output rows (one or two tiles of 16) for 16
-// sequences, all of K: per 32 values of K, one v_mfma_f32_16x16x32_bf16 per
-// tile, the tiles sharing the batch operand.  The weight operand comes straight from 16-byte global loads
-// (lane i: row i % 16 of the tile, K values 8 (i / 16) .. +8 of the step,
-// contiguous in the [N, K] layout); the batch operand is x .* norm_w (QKV;
-// norm_w staged in LDS) or the bf16 copy of the attention output the merge
-// wrote (O projection) for sequence i % 16; C lane i holds rows 4 (i / 16) + j
-// of sequence i % 16.  The workgroup's kMfmaWaves waves split K; each
-// requests kMfmaSteps steps of operands at once (128 KB of weights per
-// workgroup in flight), and the partial tiles are summed through LDS in
-// fixed wave order.  For QKV each tile is 8 RoPE pairs of one head (rows e
-// and e + D/2 at tile rows r and r + 8), so each rotation stays in a tile;
-// the lane work after the sum is the one of the VALU panel.
+// The matrix-core row panel of dab_mfma.h for the QKV projection (each tile
+// 8 RoPE pairs of one head: rows e and e + D/2 at tile rows r and r + 8, so
+// that each rotation stays in a tile; the batch operand x .* norm_w, RMSNorm
+// applied as a scale after the sum, then the lane work of the VALU panel) and
+// for the output projection (the batch operand the bf16 copy of the attention
+// output; the residual added after the sum).
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-constexpr int kMfmaWaves = 8;            // waves per workgroup (512 threads)
-constexpr int kMfmaSteps = 8;            // K-steps of 32 requested at once per wave
-
-struct MfmaShared {
-    float c[kMfmaWaves][2][16][17];   // per-wave partial tiles [tile][row][sequence] (padded)
-    float ss[16][kMfmaWaves];         // QKV: per-sequence sums of x^2, one per wave
+// The rows of a panel: tile row (tile, m) -> a row of W (QKV: 8 RoPE pairs of
+// one head per tile, rows e and e + D/2 at tile rows r and r + 8).
+struct MfmaRows {
+    int hd = 0, e0 = 0;
+    __device__ MfmaRows(const StepArgs& a, bool qkv, int panel, int tiles) {
+        if (qkv) {
+            const int pr0 = panel * 8 * tiles;             // first RoPE pair of the panel
+            hd = pr0 / (a.D >> 1);
+            e0 = pr0 - hd * (a.D >> 1);
+        }
+    }
+    __device__ int qkv_row(const StepArgs& a, int tile, int m) const {
+        return hd * a.D + e0 + tile * 8 + (m & 7) + (m >= 8 ? a.D >> 1 : 0);
+    }
 };
 
-__device__ inline bf16x8 as_bf16x8(const u32x4& v) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[2 * i] = __builtin_bit_cast(__bf16, (uint16_t)(v[i] & 0xffffu));
-        r[2 * i + 1] = __builtin_bit_cast(__bf16, (uint16_t)(v[i] >> 16));
-    }
-    return r;
-}
-
-// nw_lds: QKV only, H bf16 values of norm_w (staged by the caller).
-template <bool QKV, int TILES>
-__device__ void mfma_panel(const StepArgs& a, int panel, int bgi, MfmaShared& sm, const uint16_t* nw_lds) {
-    constexpr int ROWS = 16 * TILES;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int K = QKV ? a.H : a.n_q;
-    const int m = lane & 15, kg = lane >> 4;
-    const int D = a.D, half = D >> 1;
-    // this lane's weight rows (row m of each tile)
-    int hd = 0, e0 = 0, row0, row1;
+// The lane work after the sums: sum(tile, g, r, n) is output row r of the
+// tile for sequence 16 g + n of the workgroup, ssq(sq) the sum of x^2 of
+// sequence sq (QKV).
+template <bool QKV, int TILES, int NG, int THREADS, class SUM, class SSQ>
+__device__ void mfma_finish(const StepArgs& a, int panel, int bgi, const MfmaRows& mr, SUM sum, SSQ ssq) {
+    constexpr int ROWS = 16 * TILES, NS = 16 * NG;
+    const int t = threadIdx.x, D = a.D;
     if constexpr (QKV) {
-        const int pr0 = panel * 8 * TILES;             // first RoPE pair of the panel
-        hd = pr0 / half;
-        e0 = pr0 - hd * half;
-        row0 = hd * D + e0 + (m & 7) + (m >= 8 ? half : 0);
-        row1 = row0 + 8;
-    } else {
-        row0 = panel * ROWS + m;
-        row1 = row0 + 16;
-    }
-    const uint16_t* Wbase = static_cast<const uint16_t*>(QKV ? a.w_qkv : a.w_o);
-    const uint16_t* W0 = Wbase + (size_t)row0 * K + kg * 8;
-    const uint16_t* W1 = Wbase + (size_t)row1 * K + kg * 8;
-    // this lane's sequence (tile column m)
-    const int b = bgi * 16 + m;
-    int p;
-    const bool live = b < a.B && (QKV || pos_valid(a, b, &p));
-    const uint16_t* X = (QKV ? static_cast<const uint16_t*>(a.hidden) : a.a16) + (size_t)(live ? b : 0) * K + kg * 8;
-
-    // this wave's steps: K / (32 kMfmaWaves) of them, in groups of kMfmaSteps
-    const int nsteps = K / (32 * kMfmaWaves), k_begin = wave * nsteps * 32;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-    float ssq = 0.f;
-    for (int s0 = 0; s0 < nsteps; s0 += kMfmaSteps) {
-        u32x4 w0[kMfmaSteps], w1[kMfmaSteps], x[kMfmaSteps];
-#pragma unroll
-        for (int s = 0; s < kMfmaSteps; ++s) {
-            const int k = k_begin + (s0 + s) * 32;
-            const bool in = s0 + s < nsteps;
-            w0[s] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W0 + k)) : u32x4{0u, 0u, 0u, 0u};
-            if constexpr (TILES == 2)
-                w1[s] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W1 + k)) : u32x4{0u, 0u, 0u, 0u};
-            x[s] = in && live ? *reinterpret_cast<const u32x4*>(X + k) : u32x4{0u, 0u, 0u, 0u};
-        }
-        if (s0 == 0) DAB_TRACE_POINT(a, 1);
-#pragma unroll
-        for (int s = 0; s < kMfmaSteps; ++s) {
-            if (s0 + s >= nsteps) break;
-            bf16x8 bv;
-            if constexpr (QKV) {
-                const int k = k_begin + (s0 + s) * 32 + kg * 8;
-                const u32x4 nw = *reinterpret_cast<const u32x4*>(nw_lds + k);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x0 = __uint_as_float(x[s][i] << 16), x1 = __uint_as_float(x[s][i] & 0xffff0000u);
-                    ssq = fmaf(x0, x0, ssq);
-                    ssq = fmaf(x1, x1, ssq);
-                    bv[2 * i] = (__bf16)(x0 * __uint_as_float(nw[i] << 16));
-                    bv[2 * i + 1] = (__bf16)(x1 * __uint_as_float(nw[i] & 0xffff0000u));
-                }
-            } else {
-                bv = as_bf16x8(x[s]);
-            }
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0[s]), bv, acc0, 0, 0, 0);
-            if constexpr (TILES == 2) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1[s]), bv, acc1, 0, 0, 0);
-        }
-    }
-
-    // partial tiles (and sums of x^2) to LDS, summed in wave order
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        sm.c[wave][0][4 * kg + j][m] = acc0[j];
-        if constexpr (TILES == 2) sm.c[wave][1][4 * kg + j][m] = acc1[j];
-    }
-    if constexpr (QKV) {
-        ssq += __shfl_xor(ssq, 16);
-        ssq += __shfl_xor(ssq, 32);
-        if (kg == 0) sm.ss[m][wave] = ssq;
-    }
-    __syncthreads();
-    DAB_TRACE_POINT(a, 2);
-    if (t >= 256 * TILES) return;                                // tiles x 16 rows x 16 sequences
-    const int tile = t >> 8, r = (t >> 4) & 15, n = t & 15;
-    const int bb = bgi * 16 + n;
-    if constexpr (QKV) {
-        // threads of the first 8 rows of a tile finish pair (r, r + 8) of sequence n
-        if (r < 8 && bb < a.B) {
-            float u0 = 0.f, u1 = 0.f, ss[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int w = 0; w < kMfmaWaves; ++w) {
-                u0 += sm.c[w][tile][r][n];
-                u1 += sm.c[w][tile][r + 8][n];
-                ss[w % 4] += sm.ss[n][w];
-            }
-            const int e = e0 + tile * 8 + r;
-            qkv_finish<uint16_t, kQkvPlain>(a, panel, tile * 8 + r, bb, hd, e, hd * D + e, u0, u1, ss);
+        // thread (tile, pair r, sequence) finishes pair (r, r + 8) of one sequence
+        for (int idx = t; idx < TILES * 8 * NS; idx += THREADS) {
+            const int tile = idx / (8 * NS), r = (idx / NS) % 8, sq = idx % NS, g = sq >> 4, n = sq & 15;
+            const int bb = bgi * NS + sq;
+            if (bb >= a.B) continue;
+            const float ss[4] = {ssq(sq), 0.f, 0.f, 0.f};
+            const int e = mr.e0 + tile * 8 + r;
+            qkv_finish<uint16_t, kQkvPlain>(a, panel, tile * 8 + r, bb, mr.hd, e, mr.hd * D + e, sum(tile, g, r, n),
+                                            sum(tile, g, r + 8, n), ss);
         }
     } else {
-        int pp;
-        if (bb < a.B && pos_valid(a, bb, &pp)) {
-            float y = 0.f;
-#pragma unroll
-            for (int w = 0; w < kMfmaWaves; ++w) y += sm.c[w][tile][r][n];
-            const size_t i = (size_t)bb * a.H + panel * ROWS + tile * 16 + r;
+        for (int idx = t; idx < ROWS * NS; idx += THREADS) {
+            const int row = idx / NS, sq = idx % NS, g = sq >> 4, n = sq & 15;
+            const int bb = bgi * NS + sq;
+            int pp;
+            if (bb >= a.B || !pos_valid(a, bb, &pp)) continue;
+            const float y = sum(row >> 4, g, row & 15, n);
+            const size_t i = (size_t)bb * a.H + panel * ROWS + row;
             static_cast<uint16_t*>(a.out)[i] = from_f32<uint16_t>(to_f32(static_cast<const uint16_t*>(a.hidden)[i]) + y);
             if (a.dbg_y) a.dbg_y[i] = y;
         }
     }
+}
+
+// The batch row of sequence b for a panel (QKV: the hidden row; output
+// projection: the bf16 attention output, for sequences with a valid position).
+template <bool QKV>
+__device__ inline const uint16_t* mfma_xrow(const StepArgs& a, int b) {
+    int p;
+    const bool live = b < a.B && (QKV || pos_valid(a, b, &p));
+    const int K = QKV ? a.H : a.n_q;
+    return live ? (QKV ? static_cast<const uint16_t*>(a.hidden) : a.a16) + (size_t)b * K : nullptr;
+}
+
+// Staged panel (dab_mfma.h MfmaCore): 256 threads, any K, 16 or 32 sequences.
+// nw_lds: QKV only, H bf16 values of norm_w (staged by the caller).
+template <bool QKV, int TILES, int NG>
+__device__ void mfma_panel(const StepArgs& a, int panel, int bgi, MfmaLds<TILES, NG>& lds, const uint16_t* nw_lds) {
+    using Core = MfmaCore<TILES, NG, QKV>;
+    constexpr int ROWS = 16 * TILES, NS = 16 * NG;
+    const int wave = threadIdx.x >> 6;
+    const int K = QKV ? a.H : a.n_q;
+    const uint16_t* W = static_cast<const uint16_t*>(QKV ? a.w_qkv : a.w_o);
+    const MfmaRows mr(a, QKV, panel, TILES);
+    const uint16_t* rows[Core::RPW];
+#pragma unroll
+    for (int r = 0; r < Core::RPW; ++r) {
+        const int pr = wave + 4 * r;
+        rows[r] = W + (size_t)(QKV ? mr.qkv_row(a, pr >> 4, pr & 15) : panel * ROWS + pr) * K;
+    }
+    const uint16_t* xrows[Core::XPT];
+#pragma unroll
+    for (int i = 0; i < Core::XPT; ++i) xrows[i] = mfma_xrow<QKV>(a, bgi * NS + wave + 4 * i);
+    Core core;
+    DAB_TRACE_POINT(a, 1);
+    core.run(rows, xrows, nw_lds, K, lds.st);
+    core.publish_partials(lds.red);
+    DAB_TRACE_POINT(a, 2);
+    const MfmaReduce<TILES, NG>& red = lds.red;
+    mfma_finish<QKV, TILES, NG, kMfmaThreads>(
+        a, panel, bgi, mr, [&](int tl, int g, int r, int n) { return mfma_sum(red, tl, g, r, n); },
+        [&](int sq) { return red.ss[sq]; });
+}
+
+// Resident-operand panel (dab_mfma.h MfmaResident): 512 threads, 16
+// sequences, K a multiple of 256 and at most kMfmaResMaxK.
+template <bool QKV, int TILES>
+__device__ void mfma_res_panel(const StepArgs& a, int panel, int bgi, MfmaResLds<TILES>& lds, const uint16_t* nw_lds) {
+    const int m = threadIdx.x & 15;
+    const int K = QKV ? a.H : a.n_q;
+    const uint16_t* W = static_cast<const uint16_t*>(QKV ? a.w_qkv : a.w_o);
+    const MfmaRows mr(a, QKV, panel, TILES);
+    const uint16_t* rows[TILES];
+#pragma unroll
+    for (int tl = 0; tl < TILES; ++tl)
+        rows[tl] = W + (size_t)(QKV ? mr.qkv_row(a, tl, m) : panel * 16 * TILES + tl * 16 + m) * K;
+    MfmaResident<TILES, QKV> core;
+    DAB_TRACE_POINT(a, 1);
+    core.run(rows, [&](int n) { return mfma_xrow<QKV>(a, bgi * 16 + n); }, nw_lds, K, lds);
+    DAB_TRACE_POINT(a, 2);
+    mfma_finish<QKV, TILES, 1, kMfmaResThreads>(
+        a, panel, bgi, mr, [&](int tl, int, int r, int n) { return mfma_res_sum(lds, tl, r, n); },
+        [&](int sq) { return lds.ss[sq]; });
 }
 
 }  // namespace dev

@@ -1,0 +1,348 @@
+// Matrix-core row panels for batches of 8 or more (bf16, gfx950, wave64).
+//
+// A panel is TILES tiles of 16 weight rows (W stored [N, K], one output
+// feature per row) against 16 * NG sequences, all of K, in one workgroup of
+// four waves, with v_mfma_f32_16x16x32_bf16.  K goes through in stages of
+// 512 values:
+//   - every weight row of the stage is one 1 KB wave-wide load (lane l: 16
+//     bytes at k + 8l), so the weight stream reads whole contiguous kilobytes
+//     of each row, as the VALU panels do; the matrix-core operand layout
+//     (16 rows x 64 bytes per wave-wide load) measured ~30% slower to stream;
+//   - the batch operand of the stage (16 * NG rows of 512 values, bf16;
+//     x .* norm_w with the sums of x^2 taken on the way where NORM) is
+//     loaded once per workgroup, not once per wave and tile;
+//   - both go to LDS, rows 1040 bytes apart (so that the 16 rows an operand
+//     read touches start 4 banks apart), and each wave takes every fourth
+//     32-value step of the stage, reading its A and B fragments from LDS;
+//   - the loads of the next kMfmaPrefetch stages are in flight (in
+//     registers) while a stage is computed.
+// The waves' partial tiles are summed in wave order through LDS by the
+// caller, after run() (MfmaLds::red aliases the stage buffers).
+#pragma once
+
+#include "dab_device.h"
+
+namespace dab {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline bf16x8 as_bf16x8(const u32x4& v) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = __builtin_bit_cast(__bf16, (uint16_t)(v[i] & 0xffffu));
+        r[2 * i + 1] = __builtin_bit_cast(__bf16, (uint16_t)(v[i] >> 16));
+    }
+    return r;
+}
+
+constexpr int kMfmaThreads = 256;                   // four waves
+// K values per stage: kMfmaSub 1 KB loads per weight row (1024 measured no faster for the 8B layer at
+// batch 16 on MI355X, and slower for its FFN)
+constexpr int kMfmaStageK = 512;
+constexpr int kMfmaSub = kMfmaStageK / 512;
+// stages whose loads are in flight ahead of the one computed (3 and 4 measured slower: 8B layer, batch 16,
+// QKV 22.5 -> 23.3 -> 24.3 us; its FFN 88 -> 93 -> 122 us)
+constexpr int kMfmaPrefetch = 2;
+constexpr int kMfmaRowLds = kMfmaStageK + 8;        // bf16 per LDS row (+16 bytes: rows start 4 banks apart)
+
+template <int TILES, int NG>
+struct MfmaStage {
+    uint16_t w[16 * TILES][kMfmaRowLds];   // the stage's weight rows
+    uint16_t x[16 * NG][kMfmaRowLds];      // the stage's batch operand
+};
+
+template <int TILES, int NG>
+struct MfmaReduce {
+    float c[4][TILES][NG][16][17];         // per-wave partial tiles [wave][tile][group][row][sequence]
+    float ss[16 * NG];                     // NORM: sums of x^2 per sequence
+};
+
+template <int TILES, int NG>
+union MfmaLds {
+    MfmaStage<TILES, NG> st;
+    MfmaReduce<TILES, NG> red;
+};
+
+template <int TILES, int NG, bool NORM>
+struct MfmaCore {
+    static constexpr int ROWS = 16 * TILES;
+    static constexpr int RPW = ROWS / 4;     // weight rows each wave loads per stage: wave + 4r
+    static constexpr int XPT = 4 * NG;       // batch rows each thread loads per stage: wave + 4i
+    static constexpr int WL = RPW * kMfmaSub, XL = XPT * kMfmaSub;   // 16-byte loads per thread and stage
+    f32x4 acc[TILES][NG];
+    float ssq[XPT];                          // NORM: sums of x^2 of this thread's batch rows (its k values)
+
+    // rows[r]: weight row wave + 4r of the panel; xrows[i]: batch row wave + 4i
+    // (nullptr past the batch: zeros); nw: norm_w in LDS (NORM).  Returns with
+    // the stage buffers free (after a barrier).
+    __device__ void run(const uint16_t* const (&rows)[RPW], const uint16_t* const (&xrows)[XPT],
+                        const uint16_t* nw, int K, MfmaStage<TILES, NG>& st) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int tl = 0; tl < TILES; ++tl)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[tl][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) ssq[i] = 0.f;
+        const int nst = (K + kMfmaStageK - 1) / kMfmaStageK;
+
+        auto issue_w = [&](u32x4 (&wr)[WL], int s) {
+#pragma unroll
+            for (int j = 0; j < kMfmaSub; ++j) {
+                const int k = s * kMfmaStageK + 512 * j + 8 * lane;
+#pragma unroll
+                for (int r = 0; r < RPW; ++r)
+                    wr[j * RPW + r] = k < K ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows[r] + k))
+                                            : u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        auto issue_x = [&](u32x4 (&xr)[XL], int s) {
+#pragma unroll
+            for (int j = 0; j < kMfmaSub; ++j) {
+                const int k = s * kMfmaStageK + 512 * j + 8 * lane;
+#pragma unroll
+                for (int i = 0; i < XPT; ++i)
+                    xr[j * XPT + i] = k < K && xrows[i] ? *reinterpret_cast<const u32x4*>(xrows[i] + k)
+                                                        : u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        auto store_w = [&](const u32x4 (&wr)[WL]) {
+#pragma unroll
+            for (int j = 0; j < kMfmaSub; ++j)
+#pragma unroll
+                for (int r = 0; r < RPW; ++r)
+                    *reinterpret_cast<u32x4*>(&st.w[wave + 4 * r][512 * j + 8 * lane]) = wr[j * RPW + r];
+        };
+        auto store_x = [&](const u32x4 (&xr)[XL], int s) {
+#pragma unroll
+            for (int j = 0; j < kMfmaSub; ++j) {
+                const int kl = 512 * j + 8 * lane, k = s * kMfmaStageK + kl;
+#pragma unroll
+                for (int i = 0; i < XPT; ++i) {
+                    u32x4 v = xr[j * XPT + i];
+                    if constexpr (NORM) {
+                        if (k < K) {
+                            const u32x4 w8 = *reinterpret_cast<const u32x4*>(nw + k);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float x0 = __uint_as_float(v[e] << 16), x1 = __uint_as_float(v[e] & 0xffff0000u);
+                                ssq[i] = fmaf(x0, x0, ssq[i]);
+                                ssq[i] = fmaf(x1, x1, ssq[i]);
+                                v[e] = pack_bf16x2(x0 * __uint_as_float(w8[e] << 16),
+                                                   x1 * __uint_as_float(w8[e] & 0xffff0000u));
+                            }
+                        }
+                    }
+                    *reinterpret_cast<u32x4*>(&st.x[wave + 4 * i][kl]) = v;
+                }
+            }
+        };
+        auto compute = [&]() {
+            const int m = lane & 15, kg = lane >> 4;
+#pragma unroll
+            for (int q = 0; q < kMfmaStageK / 32 / 4; ++q) {
+                const int kk = 32 * (wave + 4 * q) + 8 * kg;      // step wave + 4q of the stage
+                bf16x8 bfr[NG];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) bfr[g] = as_bf16x8(*reinterpret_cast<const u32x4*>(&st.x[16 * g + m][kk]));
+#pragma unroll
+                for (int tl = 0; tl < TILES; ++tl) {
+                    const bf16x8 afr = as_bf16x8(*reinterpret_cast<const u32x4*>(&st.w[16 * tl + m][kk]));
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        acc[tl][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[g], acc[tl][g], 0, 0, 0);
+                }
+            }
+        };
+
+        // a ring of kMfmaPrefetch register sets: stages s + 1 .. s + kMfmaPrefetch in flight while
+        // stage s is computed (the ring is unrolled, so every set stays in registers)
+        u32x4 wr[kMfmaPrefetch][WL], xr[kMfmaPrefetch][XL];
+#pragma unroll
+        for (int p = 0; p < kMfmaPrefetch; ++p)
+            if (p < nst) {
+                issue_w(wr[p], p);
+                issue_x(xr[p], p);
+            }
+        for (int s0 = 0; s0 < nst; s0 += kMfmaPrefetch) {
+#pragma unroll
+            for (int p = 0; p < kMfmaPrefetch; ++p) {
+                if (s0 + p < nst) {
+                    __syncthreads();                   // the previous stage is computed: LDS free
+                    store_w(wr[p]);
+                    store_x(xr[p], s0 + p);
+                    if (s0 + p + kMfmaPrefetch < nst) {
+                        issue_w(wr[p], s0 + p + kMfmaPrefetch);
+                        issue_x(xr[p], s0 + p + kMfmaPrefetch);
+                    }
+                    __syncthreads();
+                    compute();
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // Partial tiles (and, NORM, the sums of x^2 per sequence) to `red`; a
+    // barrier follows, then every wave's partials are readable.
+    __device__ void publish_partials(MfmaReduce<TILES, NG>& red) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int n = lane & 15, kg = lane >> 4;
+#pragma unroll
+        for (int tl = 0; tl < TILES; ++tl)
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) red.c[wave][tl][g][4 * kg + j][n] = acc[tl][g][j];
+        if constexpr (NORM) {
+#pragma unroll
+            for (int i = 0; i < XPT; ++i) {
+                const float s = wave_sum(ssq[i]);
+                if (lane == 0) red.ss[wave + 4 * i] = s;
+            }
+        }
+        __syncthreads();
+    }
+};
+
+// Sum over the four waves, in wave order, of output (tile, row r, sequence
+// 16 g + n) of the panel.
+template <int TILES, int NG>
+__device__ inline float mfma_sum(const MfmaReduce<TILES, NG>& red, int tile, int g, int r, int n) {
+    return red.c[0][tile][g][r][n] + red.c[1][tile][g][r][n] + red.c[2][tile][g][r][n] + red.c[3][tile][g][r][n];
+}
+
+
+// ---------------------------------------------------------------------------
+// The resident-operand panel: 16 sequences, K <= kMfmaResMaxK
+// ---------------------------------------------------------------------------
+//
+// Where the batch operand of 16 sequences fits in LDS whole (16 x K bf16,
+// 131 KB at K = 4096), a workgroup of eight waves stages it once, then each
+// wave streams its eighth of K of the panel's weight rows straight into the
+// matrix-core operand layout (lane i: row i % 16 of a tile, 16 bytes at
+// 8 (i / 16) of each 32-value step), kMfmaResSteps steps requested at once,
+// with the batch fragments read from LDS: no barrier in the stream and no
+// batch-operand loads from memory after the start.  (8B layer, batch 16, on
+// MI355X: QKV projection 18.7 us, output projection 10.4 us; with the batch
+// operand staged stage by stage as in MfmaCore 22.5 and 13.2; with all 16
+// steps of a wave requested at once 20.4 and 10.9.)
+// The waves' partial tiles are summed in wave order through LDS.
+
+constexpr int kMfmaResWaves = 8;
+constexpr int kMfmaResThreads = 64 * kMfmaResWaves;
+constexpr int kMfmaResSteps = 8;                   // steps of 32 per wave requested at once
+constexpr int kMfmaResMaxK = 4096;
+
+template <int TILES>
+struct MfmaResLds {
+    union {
+        uint16_t x[16][kMfmaResMaxK + 8];                  // the batch operand (rows 4 banks apart)
+        float c[kMfmaResWaves][TILES][16][17];             // per-wave partial tiles, after the stream
+    };
+    float ss[16];                                          // NORM: sums of x^2 per sequence
+};
+
+template <int TILES, bool NORM>
+struct MfmaResident {
+    f32x4 acc[TILES];
+
+    // rows[tile]: this lane's weight row of each tile (tile row lane % 16); xrow(n): batch row n (nullptr
+    // past the batch); nw: norm_w in LDS (NORM).  K a multiple of 32 * kMfmaResWaves, at most
+    // kMfmaResMaxK.  Ends with the partial tiles in lds.c and the sums of squares in lds.ss, after a
+    // barrier.
+    template <class XROW>
+    __device__ void run(const uint16_t* const (&rows)[TILES], XROW xrow, const uint16_t* nw, int K,
+                        MfmaResLds<TILES>& lds) {
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+        // 1. the batch operand into LDS: thread t takes sequence t / 32, 16-byte chunks t % 32 + 32 i
+        {
+            const int n = t >> 5, c0 = t & 31;
+            const uint16_t* xr = xrow(n);
+            float ssq = 0.f;
+            for (int c = c0; c * 8 < K; c += 32 * 8) {
+                u32x4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int k = (c + 32 * u) * 8;
+                    v[u] = xr && k < K ? *reinterpret_cast<const u32x4*>(xr + k) : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int k = (c + 32 * u) * 8;
+                    if (k < K) {
+                        if constexpr (NORM) {
+                            const u32x4 w8 = *reinterpret_cast<const u32x4*>(nw + k);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float x0 = __uint_as_float(v[u][e] << 16), x1 = __uint_as_float(v[u][e] & 0xffff0000u);
+                                ssq = fmaf(x0, x0, ssq);
+                                ssq = fmaf(x1, x1, ssq);
+                                v[u][e] = pack_bf16x2(x0 * __uint_as_float(w8[e] << 16),
+                                                      x1 * __uint_as_float(w8[e] & 0xffff0000u));
+                            }
+                        }
+                        *reinterpret_cast<u32x4*>(&lds.x[n][k]) = v[u];
+                    }
+                }
+            }
+            if constexpr (NORM) {
+#pragma unroll
+                for (int off = 16; off > 0; off >>= 1) ssq += __shfl_xor(ssq, off);
+                if ((t & 31) == 0) lds.ss[n] = ssq;
+            }
+        }
+        // 2. this wave's steps in groups of kMfmaResSteps, the weight fragments straight from memory,
+        // the batch fragments from LDS
+#pragma unroll
+        for (int tl = 0; tl < TILES; ++tl) acc[tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int m = lane & 15, kg = lane >> 4;
+        const int nsteps = K / (32 * kMfmaResWaves), k_begin = wave * nsteps * 32;
+        u32x4 w[TILES][kMfmaResSteps];
+        auto issue = [&](int s0) {
+#pragma unroll
+            for (int s = 0; s < kMfmaResSteps; ++s) {
+                const int k = k_begin + (s0 + s) * 32 + 8 * kg;
+#pragma unroll
+                for (int tl = 0; tl < TILES; ++tl)
+                    w[tl][s] = s0 + s < nsteps ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows[tl] + k))
+                                               : u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        issue(0);
+        __syncthreads();                                   // the batch operand is in LDS
+        for (int s0 = 0; s0 < nsteps; s0 += kMfmaResSteps) {
+#pragma unroll
+            for (int s = 0; s < kMfmaResSteps; ++s) {
+                if (s0 + s < nsteps) {
+                    const bf16x8 bfr =
+                        as_bf16x8(*reinterpret_cast<const u32x4*>(&lds.x[m][k_begin + (s0 + s) * 32 + 8 * kg]));
+#pragma unroll
+                    for (int tl = 0; tl < TILES; ++tl)
+                        acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[tl][s]), bfr, acc[tl], 0, 0, 0);
+                }
+            }
+            if (s0 + kMfmaResSteps < nsteps) issue(s0 + kMfmaResSteps);
+        }
+        // 4. partial tiles to LDS (over the batch operand, which no wave reads any more)
+        __syncthreads();
+#pragma unroll
+        for (int tl = 0; tl < TILES; ++tl)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lds.c[wave][tl][4 * kg + j][m] = acc[tl][j];
+        __syncthreads();
+    }
+};
+
+template <int TILES>
+__device__ inline float mfma_res_sum(const MfmaResLds<TILES>& lds, int tile, int r, int n) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMfmaResWaves; ++w) s += lds.c[w][tile][r][n];
+    return s;
+}
+
+}  // namespace dev
+}  // namespace dab

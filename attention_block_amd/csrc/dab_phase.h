@@ -222,27 +222,49 @@ __global__ __launch_bounds__(256) void oproj_kernel(StepArgs a) {
 }
 
 // MFMA panels of the phased schedule (bf16, batch >= 8)
-template <bool QKV, int TILES>
-__global__ __launch_bounds__(64 * kMfmaWaves) void mfma_panel_kernel(StepArgs a) {
-    __shared__ MfmaShared sm;
-    extern __shared__ u32x4 nw_raw[];    // QKV: norm_w, H bf16 values
-    DAB_TRACE_POINT(a, 0);
+template <bool QKV>
+__device__ inline void mfma_prologue(const StepArgs& a, u32x4* nw_raw, int threads) {
     if constexpr (QKV) {
-        for (int k = threadIdx.x * 8; k < a.H; k += 64 * kMfmaWaves * 8)
+        for (int k = threadIdx.x * 8; k < a.H; k += threads * 8)
             nw_raw[k / 8] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.norm_w) + k);
         __syncthreads();
-    }
-    if constexpr (!QKV) {
+    } else {
         // re-arm the panel counters of a one-launch QKV + attention that ran before
         if (blockIdx.x == 0)
-            for (int i = threadIdx.x; i < a.qkv.nbg * (a.nq + 2 * a.nkv); i += 64 * kMfmaWaves)
-                set_counter(&a.head_cnt[i], 0);
+            for (int i = threadIdx.x; i < a.qkv.nbg * (a.nq + 2 * a.nkv); i += threads) set_counter(&a.head_cnt[i], 0);
     }
+}
+
+template <bool QKV, int TILES, int NG>
+__global__ __launch_bounds__(kMfmaThreads) void mfma_panel_kernel(StepArgs a) {
+    __shared__ MfmaLds<TILES, NG> lds;
+    extern __shared__ u32x4 nw_raw[];    // QKV: norm_w, H bf16 values
+    DAB_TRACE_POINT(a, 0);
+    mfma_prologue<QKV>(a, nw_raw, kMfmaThreads);
     const PanelPlanDev& g = QKV ? a.qkv : a.oproj;
     int panel, bgi;
     if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi))
-        mfma_panel<QKV, TILES>(a, panel, bgi, sm, reinterpret_cast<const uint16_t*>(nw_raw));
+        mfma_panel<QKV, TILES, NG>(a, panel, bgi, lds, reinterpret_cast<const uint16_t*>(nw_raw));
     DAB_TRACE_POINT(a, 3);
+}
+
+template <bool QKV, int TILES>
+__global__ __launch_bounds__(kMfmaResThreads) void mfma_res_kernel(StepArgs a) {
+    __shared__ MfmaResLds<TILES> lds;
+    extern __shared__ u32x4 nw_raw[];    // QKV: norm_w, H bf16 values
+    DAB_TRACE_POINT(a, 0);
+    mfma_prologue<QKV>(a, nw_raw, kMfmaResThreads);
+    const PanelPlanDev& g = QKV ? a.qkv : a.oproj;
+    int panel, bgi;
+    if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi))
+        mfma_res_panel<QKV, TILES>(a, panel, bgi, lds, reinterpret_cast<const uint16_t*>(nw_raw));
+    DAB_TRACE_POINT(a, 3);
+}
+
+// The resident-operand panel applies to 16 sequences per workgroup and K a
+// multiple of 256 of at most kMfmaResMaxK.
+inline bool mfma_resident(const PanelPlan& g) {
+    return g.nb == 16 && g.K <= kMfmaResMaxK && g.K % (32 * kMfmaResWaves) == 0;
 }
 
 template <typename T, bool QKV>
@@ -252,10 +274,20 @@ hipError_t launch_mfma(const StepArgs& a, const Plan& p, hipStream_t s, const La
     } else {
         const PanelPlan& g = QKV ? p.qkv : p.oproj;
         const size_t lds = QKV ? (size_t)p.H * 2 : 0;
-        if (g.rows == 32)
-            dab_launch((mfma_panel_kernel<QKV, 2>), dim3(g.grid), dim3(64 * kMfmaWaves), lds, s, ev, a);
-        else
-            dab_launch((mfma_panel_kernel<QKV, 1>), dim3(g.grid), dim3(64 * kMfmaWaves), lds, s, ev, a);
+        const dim3 grid(g.grid);
+        if (mfma_resident(g)) {
+            if (g.rows == 32) dab_launch((mfma_res_kernel<QKV, 2>), grid, dim3(kMfmaResThreads), lds, s, ev, a);
+            else dab_launch((mfma_res_kernel<QKV, 1>), grid, dim3(kMfmaResThreads), lds, s, ev, a);
+            return hipGetLastError();
+        }
+        const dim3 block(kMfmaThreads);
+        const int key = (g.rows == 32 ? 2 : 0) + (g.nb == 32 ? 1 : 0);
+        switch (key) {
+            case 0: dab_launch((mfma_panel_kernel<QKV, 1, 1>), grid, block, lds, s, ev, a); break;
+            case 1: dab_launch((mfma_panel_kernel<QKV, 1, 2>), grid, block, lds, s, ev, a); break;
+            case 2: dab_launch((mfma_panel_kernel<QKV, 2, 1>), grid, block, lds, s, ev, a); break;
+            default: dab_launch((mfma_panel_kernel<QKV, 2, 2>), grid, block, lds, s, ev, a); break;
+        }
         return hipGetLastError();
     }
 }

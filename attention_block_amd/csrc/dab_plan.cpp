@@ -33,24 +33,31 @@ bool plan_panel(int K, int N, int batch, int rpw, PanelPlan* g) {
     return true;
 }
 
-// An MFMA panel: 16 or 32 rows x all K for 16 sequences (bf16, K a multiple
-// of 256: eight waves x steps of 32; for QKV, 8 or 16 RoPE pairs of one
-// head).  Two tiles share each load of the batch operand; they are used
-// where the panels still number 192 or more (at 128, half the CUs idled:
-// the 4096-row output projection at batch 16 measured 20.1 us with two
-// tiles, 17.6 with one).
+// An MFMA panel (bf16): one or two 16-row tiles x all K for 16 or 32
+// sequences, in stages of 512 K values (the last one partial where K is not
+// a multiple of 512); for QKV a tile is 8 RoPE pairs of one head.  32
+// sequences per workgroup (two groups of 16) above a batch of 16, so that
+// every weight byte is read by one workgroup; two tiles share each batch
+// operand where that still leaves at least 256 workgroups (one per CU) and
+// the groups are one, else one tile (more workgroups, each with less LDS).
 bool plan_mfma_panel(int K, int N, int batch, bool qkv, int half, PanelPlan* g) {
-    if (K % 256 != 0 || N % 16 != 0 || (qkv && half % 8 != 0)) return false;
-    const int nbg = ceil_div(batch, 16);
-    const bool two = N % 32 == 0 && (!qkv || half % 16 == 0) && (long long)(N / 32) * nbg >= 192;
+    if (K % 8 != 0 || N % 16 != 0 || (qkv && half % 8 != 0)) return false;
+    const int ng = batch > 16 ? 2 : 1;
+    const int nbg = ceil_div(batch, 16 * ng);
+    // two tiles: on the resident-operand panels (16 sequences, K <= 4096, one workgroup per CU) where
+    // that still leaves 192 workgroups, on the staged panels where it leaves 256 (fewer measured slower:
+    // 8B layer, batch 16, output projection 13.2 -> 19.8 us with 128 two-tile panels)
+    const bool resident = ng == 1 && K <= 4096 && K % 256 == 0;
+    const bool two = ng == 1 && N % 32 == 0 && (!qkv || half % 16 == 0) &&
+                     (long long)(N / 32) * nbg >= (resident ? 192 : 256);
     g->K = K;
     g->N = N;
     g->mfma = true;
     g->rows_per_wave = 0;
     g->rows = two ? 32 : 16;
     g->panels = N / g->rows;
-    g->nb = 16;
-    g->nbg = ceil_div(batch, 16);
+    g->nb = 16 * ng;
+    g->nbg = nbg;
     g->grid = g->nbg == 1 ? g->panels : (int)align_up((size_t)g->panels, 8) * g->nbg;
     g->lds = 0;
     return true;
@@ -285,16 +292,17 @@ dab_status make_ffn_plan(const dab_ffn_config* cfg, FfnPlan* p) {
     // VALU panel holds at most 4 and is bound by its arithmetic there).  The
     // gate/up panel is 16 rows of W_gate and the same 16 rows of W_up, one
     // MFMA tile each, so both sums of an output meet in one workgroup.
-    p->mfma = p->dtype == DAB_BF16 && B >= 8 && p->H % 256 == 0 && p->F % 256 == 0;
+    p->mfma = p->dtype == DAB_BF16 && B >= 8;
     if (p->mfma) {
+        // gate/up: 16 rows of W_gate (tile 0) and the same rows of W_up (tile 1)
         PanelPlan& g = p->gu;
         g.K = p->H;
         g.N = 2 * p->F;
         g.mfma = true;
         g.rows = 16;
         g.panels = p->F / 16;
-        g.nb = 16;
-        g.nbg = ceil_div(B, 16);
+        g.nb = B > 16 ? 32 : 16;
+        g.nbg = ceil_div(B, g.nb);
         g.grid = g.nbg == 1 ? g.panels : (int)align_up((size_t)g.panels, 8) * g.nbg;
         if (!plan_mfma_panel(p->F, p->H, B, false, 0, &p->down)) return DAB_ERR_UNSUPPORTED;
     } else if (!plan_panel(p->H, 2 * p->F, B, 2, &p->gu) || !plan_panel(p->F, p->H, B, 2, &p->down)) {

@@ -35,7 +35,7 @@ constexpr int merge_round(int G) { return G >= 8 ? 4 : 32 / G; }
 // cross workgroups.
 struct PanelPlan {
     int K = 0, N = 0;
-    bool mfma = false;      // MFMA panels: 32 rows x 16 sequences per workgroup (bf16, batch >= 8)
+    bool mfma = false;      // MFMA panels: 16 or 32 rows x 16 or 32 sequences per workgroup (bf16, batch >= 8)
     int rows_per_wave = 0;  // 1 or 2 (the QKV panel: one RoPE pair per wave)
     int rows = 0;           // 4 * rows_per_wave
     int panels = 0;         // N / rows
@@ -77,7 +77,7 @@ struct Plan {
 struct FfnPlan {
     int B = 0, H = 0, F = 0, dtype = 0, elem = 0;
     float eps = 0.f;
-    bool mfma = false;        // bf16, batch >= 8, H and F multiples of 256: MFMA panels for both GEMVs
+    bool mfma = false;        // bf16, batch >= 8: MFMA panels for both GEMVs
     PanelPlan gu, down;
     size_t off_m = 0, off_m16 = 0, ws_bytes = 0;
     size_t bytes_hidden = 0, bytes_norm = 0, bytes_wgu = 0, bytes_wdown = 0, bytes_out = 0, bytes_dbg = 0;

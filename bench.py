@@ -206,8 +206,10 @@ def ffn_phase_bytes(cfg: FfnConfig) -> dict:
 
 def phase_of(kernel_name: str):
     fn = kernel_name.split("(")[0].split("<")[0].split("::")[-1]
-    if fn == "mfma_panel_kernel":            # template argument QKV: true or false
+    if fn in ("mfma_panel_kernel", "mfma_res_kernel"):     # template argument QKV: true or false
         return "qkv_rmsnorm_rope_append" if "<true" in kernel_name else "oproj_residual"
+    if fn == "ffn_mfma_kernel":                               # template argument GATE_UP: true or false
+        return "ffn_rmsnorm_gate_up_silu" if "<true" in kernel_name else "ffn_down_residual"
     for k, ph in KERNEL_PHASES:
         if fn == k:
             return ph
