@@ -139,7 +139,7 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.log2_theta = log2((double)p.theta);
     a.qkv = panel_dev(p.qkv);
     a.oproj = panel_dev(p.oproj);
-    a.T = p.kv_chunk;
+    a.chunk = p.chunk;
     a.maxc = p.max_chunks;
     a.attn_items = p.attn_grid;
     a.split_merge = p.split_merge ? 1 : 0;

@@ -437,10 +437,11 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     int p;
     if (!pos_valid(a, b, &p)) return;
     // chunks cover the p cached tokens; the last one also takes the new token
-    const int nchunk = p > 0 ? (p + a.T - 1) / a.T : 1;
+    const int len = chunk_len(a.chunk, p);             // this sequence's chunk length
+    const int nchunk = p > 0 ? (p + len - 1) / len : 1;
     if (c >= nchunk) return;
-    const int t0 = c * a.T;
-    const int t1 = min(t0 + a.T, p);
+    const int t0 = c * len;
+    const int t1 = min(t0 + len, p);
     const bool has_new = c == nchunk - 1;
     const int nhb = (t1 - t0 + HB - 1) / HB;          // buffers of HB tokens (0 when there is no history)
 

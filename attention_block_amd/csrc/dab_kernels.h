@@ -52,7 +52,8 @@ struct StepArgs {
     double log2_theta;
     // plan
     PanelPlanDev qkv, oproj;
-    int T, maxc, attn_items;
+    ChunkRule chunk;        // split-KV chunk length of each sequence, from its position (chunk_len)
+    int maxc, attn_items;
     int split_merge;        // phased: chunk partials are merged by a kernel of their own
 #ifdef DAB_TRACE
     unsigned long long* trace;   // [items, 8] timestamps per workgroup (profiling builds only)

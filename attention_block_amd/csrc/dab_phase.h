@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
     const int b = blockIdx.x / a.nq, h = blockIdx.x - b * a.nq;
     int p;
     if (!pos_valid(a, b, &p)) return;
-    const int nchunk = p > 0 ? (p + a.T - 1) / a.T : 1;
+    const int nchunk = chunk_count(a.chunk, p);
     const size_t pbase = ((size_t)b * a.nq + h) * a.maxc;     // chunk cc: pbase + cc
     const int d = t % D, part = t / D;
     float v0[R];

@@ -187,20 +187,23 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
     // same merge kernel, on MI355X); longer only where the context would need
     // more than kMaxChunks chunks.
     const int hist = p->cap - 1 > 0 ? p->cap - 1 : 1;
-    int T = c.kv_chunk;
-    if (T == 0) {
+    ChunkRule& r = p->chunk;
+    r.fixed = c.kv_chunk;
+    if (r.fixed == 0) {
         const int half_batch = 256 / (p->D / 8) * 4;
         int want = ceil_div(512, (long long)B * p->nkv);              // chunks per sequence and kv head
         if (want > 64) want = 64;
-        T = (ceil_div(hist, want) + 15) / 16 * 16;
-        if (T < half_batch) T = half_batch;
-        if (T > 448) T = 448;
+        r.want = want;
+        r.lo = half_batch;
+        r.hi = 448;
         // One query head per kv head: an attention workgroup loads one whole
         // buffer of 256 / (D/8) x 8 tokens per round trip, so a chunk is a
         // whole number of buffers (7B layer, batch 1, 1K tokens: 64-token
         // chunks 34.9 us, 128-token chunks 33.7 us per step on MI355X; at 4K
         // the 256 tokens of the rule above are two buffers already).
-        if (p->G == 1) T = (T + 2 * half_batch - 1) / (2 * half_batch) * (2 * half_batch);
+        r.whole = p->G == 1 ? 2 * half_batch : 16;
+        r.maxc = kMaxChunks;
+        int T = chunk_len(r, hist);
         // Phased schedule: where those chunks need more than one round of the
         // attention kernel's resident workgroups, take two chunks per CU (all
         // resident at once) if that still gives every (sequence, kv head) a
@@ -213,13 +216,18 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
         const long long two_per_cu = 2LL * attn_cus;
         if (p->schedule == DAB_SCHEDULE_PHASED && attn_cus > 0 && attn_per_cu >= 2 &&
             pairs * ceil_div(hist, T) > (long long)attn_cus * attn_per_cu && pairs <= two_per_cu) {
-            const int T1 = (ceil_div(hist, two_per_cu / pairs) + 15) / 16 * 16;
-            if (T1 <= 1024 && T1 > T) T = T1;
+            r.want2 = (int)(two_per_cu / pairs);
+            r.hi2 = 1024;
+            T = chunk_len(r, hist);
         }
         while (ceil_div(hist, T) > kMaxChunks) T += 512;
+        r.maxc = ceil_div(hist, T);
+    } else {
+        r.maxc = ceil_div(hist, r.fixed);
     }
+    const int T = chunk_len(r, hist);
     p->kv_chunk = T;
-    p->max_chunks = ceil_div(hist, T);
+    p->max_chunks = r.maxc;
     if (p->max_chunks > kMaxChunks) return DAB_ERR_UNSUPPORTED;
     const long long attn_grid = (long long)B * p->nkv * p->max_chunks;
     if (attn_grid + p->qkv.grid + p->oproj.grid > (1LL << 30)) return DAB_ERR_UNSUPPORTED;

@@ -29,6 +29,52 @@ constexpr int kReadyStride = 32;     // ints
 // requests at once (32 loads in flight per thread).
 constexpr int merge_round(int G) { return G >= 8 ? 4 : 32 / G; }
 
+#if defined(__HIPCC__)
+#define DAB_HOST_DEVICE __host__ __device__
+#else
+#define DAB_HOST_DEVICE
+#endif
+
+// The split-KV chunk length rule.  The host evaluates it at the cache
+// capacity (cap - 1 cached tokens) to size the grid (max_chunks chunk slots
+// per (sequence, kv head)); every attention workgroup evaluates it at its own
+// sequence's position, so that a sequence with far fewer tokens than the
+// capacity still gets about `want` chunks instead of a few long ones.
+struct ChunkRule {
+    int fixed = 0;          // > 0: the caller's kv_chunk, the same for every sequence
+    int want = 1;           // chunks per (sequence, kv head) aimed at
+    int lo = 16, hi = 448;  // clamps of the length, in tokens
+    int whole = 16;         // the length is rounded up to a multiple of this
+    int want2 = 0;          // > 0: the longer chunks of the two-per-CU rule: length ceil(p / want2) ...
+    int hi2 = 0;            //   ... where that is longer and at most hi2
+    int maxc = 1;           // chunk slots per (sequence, kv head) in the grid
+};
+
+// Chunk length for a sequence with `hist` cached tokens: never more than
+// r.maxc chunks.
+DAB_HOST_DEVICE inline int chunk_len(const ChunkRule& r, int hist) {
+    if (r.fixed > 0) return r.fixed;
+    const int h = hist > 0 ? hist : 1;
+    int T = ((h + r.want - 1) / r.want + 15) / 16 * 16;
+    if (T < r.lo) T = r.lo;
+    if (T > r.hi) T = r.hi;
+    T = (T + r.whole - 1) / r.whole * r.whole;
+    if (r.want2 > 0) {
+        const int T1 = ((h + r.want2 - 1) / r.want2 + 15) / 16 * 16;
+        if (T1 <= r.hi2 && T1 > T) T = T1;
+    }
+    const int floor = ((h + r.maxc - 1) / r.maxc + 15) / 16 * 16;
+    return T > floor ? T : floor;
+}
+
+// Chunks of a sequence at position p (cached tokens): the last one also takes
+// the new token; a sequence with no history has one chunk, for that token.
+DAB_HOST_DEVICE inline int chunk_count(const ChunkRule& r, int p) {
+    if (p <= 0) return 1;
+    const int T = chunk_len(r, p);
+    return (p + T - 1) / T;
+}
+
 // A row-panel GEMV y[b, n] = sum_k W[n, k] x[b, k] with W stored [N, K]
 // (every output's K weights contiguous).  A workgroup owns `rows` = 4 waves
 // x rows_per_wave outputs and all K for `nb` batch rows, so no partial sums
@@ -56,7 +102,8 @@ struct Plan {
     bool qkv_attn_ok = false;             // the one-launch QKV + attention is built for this shape
     bool fused_ok = false;                // the one-launch whole step is built for this shape
     PanelPlan qkv, oproj;
-    int kv_chunk = 0, max_chunks = 0, attn_grid = 0;
+    int kv_chunk = 0, max_chunks = 0, attn_grid = 0;   // kv_chunk: the length at the capacity
+    ChunkRule chunk;                                  // the length for each sequence's position
     bool split_merge = false;             // phased: the LSE merge runs as a kernel of its own
 
     // workspace layout, byte offsets (each 256-byte aligned); the flags

@@ -105,6 +105,11 @@ EDGE = [
      [299, 0, 17, 256, 1, 128, 64, 200, 33], 0),
     ("mfma batch 20, two tiles", small_cfg("m2", 20, 2048, 16, 4, 128, "bf16"), 130, list(range(3, 130, 6))[:20], 0),
     ("mfma d64 group 8", small_cfg("m3", 8, 1024, 16, 2, 64, "bf16", 5e5), 90, [89, 0, 5, 64, 33, 80, 12, 1], 32),
+    # caches far larger than the contexts: the grid is sized for the capacity, each sequence's chunks
+    # for its own position
+    ("large cap mha bf16", small_cfg("lc1", 2, 512, 4, 4, 128, "bf16"), 20000, [1000, 37], 0),
+    ("large cap gqa bf16", small_cfg("lc2", 3, 512, 8, 2, 128, "bf16", 5e5), 12000, [3000, 0, 700], 0),
+    ("large cap f32 d64", small_cfg("lc3", 2, 256, 4, 2, 64, "f32"), 9000, [8999, 5], 0),
     # groups of 5, 6 and 7 (merge rounds of 6, 5 and 4 chunks per thread), in bf16 (pair dot products)
     # and fp32, with the merge inside the attention kernel and in a kernel of its own (63 chunks)
     ("group 5 bf16", small_cfg("g5b", 2, 640, 10, 2, 64, "bf16", 5e5), 300, [299, 150], 32),
@@ -134,6 +139,7 @@ EDGE_ONE_LAUNCH = [
     ("bf16 many chunks per workgroup", small_cfg("o8", 2, 4096, 32, 32, 128, "bf16"), 2000, [1999, 1000], 64),
 ]
 EDGE_ONE_LAUNCH += [
+    ("bf16 large cap", small_cfg("o12", 1, 4096, 32, 32, 128, "bf16"), 8192, [1000], 0),
     ("bf16 fused batch 3 ragged", small_cfg("o9", 3, 1024, 32, 8, 128, "bf16", 5e5), 900, [899, 0, 450], 64),
     ("f32 fused d64 group 2 batch 2", small_cfg("o10", 2, 2048, 32, 16, 64, "f32"), 260, [259, 100], 32),
     ("bf16 fused group 8 H 8192", small_cfg("o11", 1, 8192, 64, 8, 64, "bf16"), 520, [519], 0),

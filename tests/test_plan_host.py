@@ -28,12 +28,14 @@ def plan_host(tmp_path_factory):
            os.path.join(ROOT, "tests", "plan_host.cpp"), os.path.join(CSRC, "dab_plan.cpp"), "-o", exe]
     subprocess.run(cmd, check=True, capture_output=True)
 
-    def run(B, H, nq, nkv, D, cap, schedule=AUTO, cus=0, per_cu=0, dtype=BF16):
-        out = subprocess.run([exe] + [str(v) for v in (B, H, nq, nkv, D, cap, dtype, schedule, cus, per_cu)],
+    def run(B, H, nq, nkv, D, cap, schedule=AUTO, cus=0, per_cu=0, dtype=BF16, probe=0):
+        out = subprocess.run([exe] + [str(v) for v in (B, H, nq, nkv, D, cap, dtype, schedule, cus, per_cu, probe)],
                              check=True, capture_output=True, text=True).stdout.split()
-        st, sched, T, maxc, grid, split = map(int, out)
+        st, sched, T, maxc, grid, split, worst, bad, at_probe = map(int, out)
         assert st == 0
-        return dict(schedule=sched, T=T, max_chunks=maxc, grid=grid, split_merge=bool(split))
+        assert bad == 0 and worst <= maxc          # every position's chunks fit the grid and cover its tokens
+        return dict(schedule=sched, T=T, max_chunks=maxc, grid=grid, split_merge=bool(split), worst=worst,
+                    T_at=at_probe)
     return run
 
 
@@ -79,3 +81,21 @@ def test_chunks_cover_every_cached_token(plan_host):
         p = plan_host(B, 1024, 2 * nkv, nkv, 128, cap, cus=256, per_cu=per_cu)
         assert p["T"] % 16 == 0 and p["T"] * p["max_chunks"] >= cap - 1 > p["T"] * (p["max_chunks"] - 1)
         assert p["grid"] == B * nkv * p["max_chunks"]
+
+
+def test_chunk_length_follows_the_position(plan_host):
+    """A preallocated cache far larger than the context: the grid is sized for the capacity, and each
+    sequence's chunks are sized for its own position, so a 4K context in a 32K cache gets the chunks a
+    4K cache would give it."""
+    big = plan_host(1, 4096, 32, 32, 128, 32768, cus=256, per_cu=5, probe=4096)
+    small = plan_host(1, 4096, 32, 32, 128, 4097, cus=256, per_cu=5, probe=4096)
+    assert big["T_at"] == small["T"] == 256
+    assert big["max_chunks"] >= small["max_chunks"]
+    # grouped heads and a batch: the same
+    big = plan_host(16, 4096, 32, 8, 128, 32768, cus=256, per_cu=4, probe=4096)
+    small = plan_host(16, 4096, 32, 8, 128, 4097, cus=256, per_cu=4, probe=4096)
+    assert big["T_at"] == small["T"]
+    # other shapes and capacities: the walk over every position checks each plan
+    for cap in (100, 2049, 65536):
+        plan_host(3, 1024, 8, 2, 64, cap, cus=256, per_cu=3)
+        plan_host(1, 1024, 8, 8, 128, cap, cus=0, per_cu=0)
