@@ -212,12 +212,15 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
         // workgroups resident per CU, on MI355X: 512 chunks of 1024 tokens
         // 86.4 us per step, 768 of 688 86.9, 1024 of 512 89.0, partial rounds
         // of 640 or 896 chunks 91-94.)
+        // (The rule is evaluated again at every sequence's position, so the
+        // round count is judged for the tokens the sequences hold.)
         const long long pairs = (long long)B * p->nkv;
         const long long two_per_cu = 2LL * attn_cus;
-        if (p->schedule == DAB_SCHEDULE_PHASED && attn_cus > 0 && attn_per_cu >= 2 &&
-            pairs * ceil_div(hist, T) > (long long)attn_cus * attn_per_cu && pairs <= two_per_cu) {
+        if (p->schedule == DAB_SCHEDULE_PHASED && attn_cus > 0 && attn_per_cu >= 2 && pairs <= two_per_cu) {
             r.want2 = (int)(two_per_cu / pairs);
             r.hi2 = 1024;
+            r.pairs = (int)pairs;
+            r.resident = attn_cus * attn_per_cu;
             T = chunk_len(r, hist);
         }
         while (ceil_div(hist, T) > kMaxChunks) T += 512;

@@ -45,8 +45,10 @@ struct ChunkRule {
     int want = 1;           // chunks per (sequence, kv head) aimed at
     int lo = 16, hi = 448;  // clamps of the length, in tokens
     int whole = 16;         // the length is rounded up to a multiple of this
-    int want2 = 0;          // > 0: the longer chunks of the two-per-CU rule: length ceil(p / want2) ...
-    int hi2 = 0;            //   ... where that is longer and at most hi2
+    int want2 = 0;          // > 0: the two-per-CU rule: where pairs * chunks would exceed `resident`,
+    int hi2 = 0;            //   chunks of ceil(p / want2) tokens where that is longer and at most hi2
+    int pairs = 0;          //   (sequences x kv heads)
+    int resident = 0;       //   (attention workgroups the device holds at once)
     int maxc = 1;           // chunk slots per (sequence, kv head) in the grid
 };
 
@@ -59,7 +61,7 @@ DAB_HOST_DEVICE inline int chunk_len(const ChunkRule& r, int hist) {
     if (T < r.lo) T = r.lo;
     if (T > r.hi) T = r.hi;
     T = (T + r.whole - 1) / r.whole * r.whole;
-    if (r.want2 > 0) {
+    if (r.want2 > 0 && (long long)r.pairs * ((h + T - 1) / T) > r.resident) {
         const int T1 = ((h + r.want2 - 1) / r.want2 + 15) / 16 * 16;
         if (T1 <= r.hi2 && T1 > T) T = T1;
     }

@@ -91,10 +91,12 @@ def test_chunk_length_follows_the_position(plan_host):
     small = plan_host(1, 4096, 32, 32, 128, 4097, cus=256, per_cu=5, probe=4096)
     assert big["T_at"] == small["T"] == 256
     assert big["max_chunks"] >= small["max_chunks"]
-    # grouped heads and a batch: the same
-    big = plan_host(16, 4096, 32, 8, 128, 32768, cus=256, per_cu=4, probe=4096)
-    small = plan_host(16, 4096, 32, 8, 128, 4097, cus=256, per_cu=4, probe=4096)
-    assert big["T_at"] == small["T"]
+    # grouped heads and a batch: the same, the two-per-CU rule included (judged at the position: 4
+    # chunks of 1024 tokens per kv head at 4K tokens in a 16K or 32K cache, as in a 4K cache)
+    for cap in (16384, 32768):
+        big = plan_host(16, 4096, 32, 8, 128, cap, cus=256, per_cu=4, probe=4096)
+        small = plan_host(16, 4096, 32, 8, 128, 4097, cus=256, per_cu=4, probe=4096)
+        assert big["T_at"] == small["T"] == 1024
     # other shapes and capacities: the walk over every position checks each plan
     for cap in (100, 2049, 65536):
         plan_host(3, 1024, 8, 2, 64, cap, cus=256, per_cu=3)
