@@ -254,3 +254,85 @@ def algorithmic_flops(cfg: BlockConfig, pos: Sequence[int]) -> int:
     B, H, nq, D = cfg.batch, cfg.hidden, cfg.n_q_heads, cfg.head_dim
     total = int(np.sum(np.asarray(pos, dtype=np.int64) + 1))
     return 2 * B * H * cfg.n_qkv + 2 * B * nq * D * H + 4 * nq * D * total
+
+
+# ---------------------------------------------------------------------------
+# multi-head latent attention (MLA) decode over a latent cache
+# ---------------------------------------------------------------------------
+#
+# The ClusterFusion page (section 5.2) runs DeepSeek's latent attention through
+# the fused decode step at 4K and 16K tokens; these workloads take DeepSeek-V3's
+# attention shape (128 heads, a 512-wide latent cache row and a 64-wide shared
+# rotary key per token, softmax scale 1/sqrt(128 + 64)) and DeepSeek-V2-Lite's
+# (16 heads, the same widths).  The query arrives already folded through the
+# key up-projection.  No trained weights: synthetic stand-ins whose scores are
+# of order one.  Draw order: (1) ragged lengths (none here); (2) q_lat
+# [B, nh, R] ~ N(0, 1/4) (a 128-wide N(0, 1) query through an N(0, 1/512)
+# projection); (3) q_rope [B, nh, P] ~ N(0, 1); (4) c_new [B, R], kr_new [B, P]
+# ~ N(0, 1); (5) per sequence c_b [pos_b, R] then kr_b [pos_b, P] ~ N(0, 1).
+# q in fp32; the cache rows and the new token's rows in the storage type.
+
+@dataclasses.dataclass(frozen=True)
+class MlaConfig:
+    """Shape of one MLA decode-attention workload."""
+    name: str
+    batch: int
+    n_heads: int
+    pos: int
+    kv_lora_rank: int = 512
+    rope_dim: int = 64
+    softmax_scale: float = 1.0 / np.sqrt(128 + 64)
+    dtype: str = "bf16"
+
+
+MLA_CONFIGS = {
+    "mla_tiny": MlaConfig("mla_tiny", 2, 16, 100),
+    "deepseek_v2_lite_mla_bs1_4k": MlaConfig("deepseek_v2_lite_mla_bs1_4k", 1, 16, 4096),
+    "deepseek_v3_mla_bs1_4k": MlaConfig("deepseek_v3_mla_bs1_4k", 1, 128, 4096),
+    "deepseek_v3_mla_bs1_16k": MlaConfig("deepseek_v3_mla_bs1_16k", 1, 128, 16384),
+    "deepseek_v3_mla_bs16_4k": MlaConfig("deepseek_v3_mla_bs16_4k", 16, 128, 4096),
+}
+
+
+def make_mla_inputs(cfg: MlaConfig, seed: int, *, cap: Optional[int] = None,
+                    pos: Optional[Sequence[int]] = None, nan_tail: bool = True) -> dict:
+    """One seeded MLA input set: q_lat, q_rope (fp32), c_new [B, R], kr_new [B, P], caches c_cache
+    [B, cap, R] and kr_cache [B, cap, P] (storage form; rows >= pos hold the NaN sentinel), pos [B]."""
+    rng = np.random.default_rng(seed)
+    B, nh, R, P = cfg.batch, cfg.n_heads, cfg.kv_lora_rank, cfg.rope_dim
+    p = np.asarray(pos, dtype=np.int32) if pos is not None else np.full(B, cfg.pos, dtype=np.int32)
+    if p.shape != (B,):
+        raise ValueError(f"pos must have shape ({B},)")
+    if cap is None:
+        cap = int(p.max()) + 1
+    if int(p.max()) >= cap or int(p.min()) < 0:
+        raise ValueError("every pos must lie in [0, cap)")
+    q_lat = (0.5 * rng.standard_normal((B, nh, R), dtype=np.float32)).astype(np.float32)
+    q_rope = rng.standard_normal((B, nh, P), dtype=np.float32)
+    c_new = rng.standard_normal((B, R), dtype=np.float32)
+    kr_new = rng.standard_normal((B, P), dtype=np.float32)
+    sdt = np.uint16 if cfg.dtype == "bf16" else np.float32
+    fill = (BF16_NAN if cfg.dtype == "bf16" else np.float32(np.nan)) if nan_tail else sdt(0)
+    c_cache = np.full((B, cap, R), fill, dtype=sdt)
+    kr_cache = np.full((B, cap, P), fill, dtype=sdt)
+    for b in range(B):
+        n = int(p[b])
+        c_cache[b, :n] = _store(rng.standard_normal((n, R), dtype=np.float32), cfg.dtype)
+        kr_cache[b, :n] = _store(rng.standard_normal((n, P), dtype=np.float32), cfg.dtype)
+    return {"cfg": cfg, "q_lat": q_lat, "q_rope": q_rope, "c_new": _store(c_new, cfg.dtype),
+            "kr_new": _store(kr_new, cfg.dtype), "c_cache": c_cache, "kr_cache": kr_cache, "pos": p, "cap": cap}
+
+
+def mla_algorithmic_bytes(cfg: MlaConfig, pos: Sequence[int]) -> int:
+    """The latent cache rows of every cached token read once, the new rows read and appended, q (fp32) in
+    and the latent output (fp32) out, and the positions."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    B, nh, R, P = cfg.batch, cfg.n_heads, cfg.kv_lora_rank, cfg.rope_dim
+    total = int(np.sum(np.asarray(pos, dtype=np.int64)))
+    return s * (R + P) * total + 2 * s * (R + P) * B + 4 * B * nh * (R + P) + 4 * B * nh * R + 4 * B
+
+
+def mla_algorithmic_flops(cfg: MlaConfig, pos: Sequence[int]) -> int:
+    """Scores over R + P values and the weighted sum over R, per head and attended token."""
+    total = int(np.sum(np.asarray(pos, dtype=np.int64) + 1))
+    return 2 * cfg.n_heads * (2 * cfg.kv_lora_rank + cfg.rope_dim) * total

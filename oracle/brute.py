@@ -139,3 +139,50 @@ def ffn_step_brute(hidden, norm_w, w_gate, w_up, w_down, *, eps, digits=50):
                 s += m[j] * f(w_down[j][c])
             y.append(s)
         return {"out": [h[c] + y[c] for c in range(H)], "y": y, "m": m}
+
+
+def mla_decode_brute(q_lat, q_rope, c_hist, kr_hist, c_new, kr_new, *, scale, digits=50):
+    """Latent attention decode for one sequence, in explicit loops over mpmath numbers.
+
+    q_lat [nh][R], q_rope [nh][P], c_hist [pos][R], kr_hist [pos][P] (the cached tokens), c_new [R],
+    kr_new [P].  Head h scores token t as (q_lat_h . c_t + q_rope_h . kr_t) * scale over the history and
+    the new token, and returns the softmax-weighted sum of the latent rows c_t.
+    Returns dict: out [nh][R], probs [nh][pos+1].
+    """
+    with mpmath.workdps(digits):
+        f = mpmath.mpf
+        nh, R, P = len(q_lat), len(c_new), len(kr_new)
+        pos = len(c_hist)
+
+        def row_c(t):
+            return c_new if t == pos else c_hist[t]
+
+        def row_r(t):
+            return kr_new if t == pos else kr_hist[t]
+
+        out, probs = [], []
+        for h in range(nh):
+            sc = []
+            for t in range(pos + 1):
+                s = f(0)
+                ct, rt = row_c(t), row_r(t)
+                for e in range(R):
+                    s += f(q_lat[h][e]) * f(ct[e])
+                for e in range(P):
+                    s += f(q_rope[h][e]) * f(rt[e])
+                sc.append(s * f(scale))
+            top = max(sc)
+            ex = [mpmath.exp(s - top) for s in sc]
+            tot = f(0)
+            for e_ in ex:
+                tot += e_
+            pr = [e_ / tot for e_ in ex]
+            probs.append(pr)
+            o = []
+            for e in range(R):
+                s = f(0)
+                for t in range(pos + 1):
+                    s += pr[t] * f(row_c(t)[e])
+                o.append(s)
+            out.append(o)
+        return {"out": out, "probs": probs}
