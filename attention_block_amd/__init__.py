@@ -12,13 +12,14 @@ import ctypes
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import DAB_BF16, DAB_F32, FFN_PHASES, READ_PROBE_BLOCKS, DabConfig, DabFfnConfig
+from ._lib import DAB_BF16, DAB_F32, FFN_PHASES, MLA_PHASES, READ_PROBE_BLOCKS, DabConfig, DabFfnConfig, DabMlaConfig
 
 __all__ = ["DabError", "DabConfig", "make_config", "workspace_size", "Workspace", "decode_attn_block",
            "decode_attn_block_timed", "read_device_error", "phase_names", "HipEvent", "lib_version",
            "DabFfnConfig", "FFN_PHASES", "ffn_workspace_size", "decode_ffn_block", "decode_ffn_block_timed",
            "read_probe", "READ_PROBE_BLOCKS", "pack_weight", "attention_output", "WEIGHT_LAYOUTS",
-           "decode_attn_block_noalloc"]
+           "decode_attn_block_noalloc", "DabMlaConfig", "MLA_PHASES", "mla_workspace_size",
+           "mla_decode_attn", "mla_decode_attn_timed"]
 
 # Weight layouts a call may name: "out_in" is the library's own ([out_features, in_features], one
 # output feature per row, as torch.nn.Linear stores its weight); "in_out" is the pages' ([in, out],
@@ -406,6 +407,81 @@ def decode_ffn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_gate, w
         ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
         _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device), arr, len(events)),
         "dab_decode_ffn_block_timed")
+    return out
+
+
+# latent attention (MLA) decode over a latent cache
+# ---------------------------------------------------------------------------
+
+def mla_workspace_size(cfg: DabMlaConfig) -> int:
+    n = _lib.load().dab_mla_workspace_size(ctypes.byref(cfg))
+    if n == 0:
+        raise DabError(_lib.DAB_ERR_INVALID_ARG, "dab_mla_workspace_size")
+    return n
+
+
+_mla_ws = {}
+
+
+def _prepare_mla(q_lat, q_rope, c_new, kr_new, c_cache, kr_cache, pos, softmax_scale, kv_chunk, out, workspace):
+    import torch
+    dev = q_lat.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    need = dict(q_lat=(q_lat, torch.float32), q_rope=(q_rope, torch.float32), c_new=(c_new, torch.bfloat16),
+                kr_new=(kr_new, torch.bfloat16), c_cache=(c_cache, torch.bfloat16),
+                kr_cache=(kr_cache, torch.bfloat16), pos=(pos, torch.int32))
+    for name, (t, dt) in need.items():
+        if t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+    if q_lat.dim() != 3 or c_cache.dim() != 3:
+        raise ValueError("q_lat must be [B, nh, R] and c_cache [B, cap, R]")
+    B, nh, R = q_lat.shape
+    cap = c_cache.shape[1]
+    P = q_rope.shape[-1]
+    if (q_rope.shape != (B, nh, P) or c_new.shape != (B, R) or kr_new.shape != (B, P)
+            or c_cache.shape != (B, cap, R) or kr_cache.shape != (B, cap, P) or pos.shape != (B,)):
+        raise ValueError("need q_lat [B, nh, R], q_rope [B, nh, P], c_new [B, R], kr_new [B, P], "
+                         "c_cache [B, cap, R], kr_cache [B, cap, P], pos [B]")
+    if out is None:
+        out = torch.empty((B, nh, R), dtype=torch.float32, device=dev)
+    elif out.shape != (B, nh, R) or out.dtype != torch.float32 or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, nh, R] tensor")
+    cfg = DabMlaConfig(B, nh, R, P, cap, softmax_scale, kv_chunk)
+    if workspace is None:
+        key = (dev.type, dev.index, B, nh, R, P, cap, kv_chunk)
+        workspace = _mla_ws.get(key)
+        if workspace is None:
+            workspace = _mla_ws[key] = Workspace(mla_workspace_size(cfg), dev)
+    return cfg, out, workspace
+
+
+def mla_decode_attn(q_lat, q_rope, c_new, kr_new, c_cache, kr_cache, pos, softmax_scale: float, kv_chunk: int = 0,
+                    out=None, workspace: Optional[Workspace] = None):
+    """Latent attention decode on the current stream; returns `out` (float32 [B, nh, R]), the softmax-weighted
+    latent rows of each head, and appends c_new / kr_new at row pos[b] of the caches.
+
+    q_lat [B, nh, R] and q_rope [B, nh, P] float32; c_new [B, R], kr_new [B, P], c_cache [B, cap, R],
+    kr_cache [B, cap, P] bfloat16; pos int32 [B]; R = 512, P = 64, nh a multiple of 16.
+    """
+    cfg, out, ws = _prepare_mla(q_lat, q_rope, c_new, kr_new, c_cache, kr_cache, pos, softmax_scale, kv_chunk,
+                                out, workspace)
+    _check(_lib.load().dab_mla_decode_attn(
+        ctypes.byref(cfg), _ptr(q_lat), _ptr(q_rope), _ptr(c_new), _ptr(kr_new), _ptr(c_cache), _ptr(kr_cache),
+        _ptr(pos), _ptr(out), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(q_lat.device)), "dab_mla_decode_attn")
+    return out
+
+
+def mla_decode_attn_timed(events: Sequence[HipEvent], q_lat, q_rope, c_new, kr_new, c_cache, kr_cache, pos,
+                          softmax_scale: float, kv_chunk: int = 0, out=None, workspace: Optional[Workspace] = None):
+    """mla_decode_attn that records events[0..3] at the start and end of its two kernels."""
+    cfg, out, ws = _prepare_mla(q_lat, q_rope, c_new, kr_new, c_cache, kr_cache, pos, softmax_scale, kv_chunk,
+                                out, workspace)
+    arr = (ctypes.c_void_p * len(events))(*[e.handle.value for e in events])
+    _check(_lib.load().dab_mla_decode_attn_timed(
+        ctypes.byref(cfg), _ptr(q_lat), _ptr(q_rope), _ptr(c_new), _ptr(kr_new), _ptr(c_cache), _ptr(kr_cache),
+        _ptr(pos), _ptr(out), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(q_lat.device), arr, len(events)),
+        "dab_mla_decode_attn_timed")
     return out
 
 

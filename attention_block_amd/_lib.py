@@ -18,6 +18,7 @@ EXPORTS = (
     "dab_phase_count", "dab_phase_name", "dab_read_device_error", "dab_status_string", "dab_version",
     "dab_last_hip_error", "dab_ffn_workspace_size", "dab_decode_ffn_block", "dab_decode_ffn_block_timed",
     "dab_read_probe", "dab_attention_output", "dab_pack_weight", "dab_decode_attn_block_noalloc",
+    "dab_mla_workspace_size", "dab_mla_decode_attn", "dab_mla_decode_attn_timed",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20      # DAB_NOALLOC_SCRATCH_BYTES
 READ_PROBE_BLOCKS = 2048      # DAB_READ_PROBE_BLOCKS
@@ -50,6 +51,21 @@ class DabFfnConfig(ctypes.Structure):
         ("eps", ctypes.c_float),
     ]
 
+
+class DabMlaConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("kv_lora_rank", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("cache_capacity", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("kv_chunk", ctypes.c_int32),
+    ]
+
+
+# names of the two latent-attention kernels, in launch order
+MLA_PHASES = ("mla_chunk", "mla_merge")
 
 _lib = None
 
@@ -103,5 +119,13 @@ def load() -> ctypes.CDLL:
     lib.dab_decode_ffn_block.restype = i32
     lib.dab_decode_ffn_block_timed.argtypes = ffn_call + [ctypes.POINTER(vp), i32]
     lib.dab_decode_ffn_block_timed.restype = i32
+    mlap = ctypes.POINTER(DabMlaConfig)
+    lib.dab_mla_workspace_size.argtypes = [mlap]
+    lib.dab_mla_workspace_size.restype = sz
+    mla_call = [mlap, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dab_mla_decode_attn.argtypes = mla_call
+    lib.dab_mla_decode_attn.restype = i32
+    lib.dab_mla_decode_attn_timed.argtypes = mla_call + [ctypes.POINTER(vp), i32]
+    lib.dab_mla_decode_attn_timed.restype = i32
     _lib = lib
     return lib

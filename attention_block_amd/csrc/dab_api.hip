@@ -290,6 +290,11 @@ dab_status ffn_call(const dab_ffn_config* cfg, const void* hidden, const void* n
 }  // namespace
 
 namespace dab {
+
+// The status of a HIP result, recorded for dab_last_hip_error (other sources of the library report
+// their launch failures through it).
+dab_status record_hip_status(hipError_t e) { return hip_status(e); }
+
 namespace {
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {

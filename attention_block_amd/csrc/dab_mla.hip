@@ -1,0 +1,610 @@
+// Latent attention (MLA) decode over a latent cache: kernels, plan and C ABI
+// (declared in include/dab.h).
+//
+// The ClusterFusion page (section 5.2) runs DeepSeek's latent attention by
+// splitting the latent key/value cache across clusters and merging their
+// partial results with a sparse reduction.  Here a chunk of one sequence's
+// tokens is one workgroup, the partial softmax states go through memory and
+// a second kernel merges them by log-sum-exp weights (the merge of the
+// ClusterFusion page, section 3.2, written for a chunk count that varies per
+// sequence).
+//
+// Every head of a sequence reads the same latent rows, so a chunk is a dense
+// contraction: with nh = 128 heads, 2176 flops per 1152 bytes of cache.  The
+// chunk kernel puts both products on the matrix cores
+// (v_mfma_f32_16x16x32_bf16):
+//   scores   S^T[t, h] = K[t, :] . Q[h, :]   A = 16 tokens x 32 dims of the
+//            K rows [c_t | kr_t] from a token-major LDS tile, B = 16 heads'
+//            query, held in registers for the whole chunk
+//            (q * scale * log2 e, bf16);
+//   values   O^T[r, h] += C^T[r, t] . P^T[t, h]   B = the weights, taken
+//            straight from the score accumulators (a lane holds head l % 16,
+//            tokens 4 (l / 16) + i of each 16-token tile: the k index of an
+//            MFMA may be any fixed permutation, so these eight tokens are its
+//            k slots), A = a transposed copy of the latent rows in LDS
+//            ([dim][token], written from the load registers with 16-bit
+//            stores), two 8-byte reads per fragment in that token order.
+// A workgroup of four waves takes 64 heads (one wave: 16 heads where nh is
+// not a multiple of 64); each wave owns a tile of 16 heads, its query
+// fragments (72 registers) and its 16 x 512 output tile (128 accumulator
+// registers).  Tokens go through LDS 32 at a time (rows of the token-major
+// tile 1168 bytes apart, so that the 16 rows an operand read touches start
+// 36 banks apart); with four waves the next 32 rows are requested into
+// registers while a tile is computed, and the operand fragments of both
+// products are read from LDS a few steps ahead of their MFMA.  The online
+// softmax keeps a per-head reference that moves only when a score exceeds it
+// by more than 2^8 (weights stay below 256, exact in fp32 and bf16), so the
+// 512-wide output rows are rescaled almost never.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <atomic>
+
+#include "dab.h"
+#include "dab_mfma.h"
+
+namespace dab {
+
+dab_status record_hip_status(hipError_t e);    // the library's last-error record (dab_api.hip)
+
+namespace mla {
+
+using dev::as_bf16x8;
+using dev::bf16x8;
+using dev::f32x4;
+using dev::u32x4;
+
+constexpr int kR = 512;                  // latent width
+constexpr int kP = 64;                   // rotary key width
+constexpr int kKD = kR + kP;             // score contraction: 576 = 18 steps of 32
+constexpr int kSteps = kKD / 32;
+constexpr int kDimTiles = kR / 16;       // output tiles of 16 latent dims
+constexpr int kTB = 32;                  // tokens per LDS tile
+constexpr int kRow = kKD + 8;            // bf16 per LDS row (1168 bytes)
+constexpr int kPieces = kKD / 8;         // 16-byte pieces per token row (64 latent + 8 rotary)
+constexpr int kCtRow = kTB + 8;          // bf16 per row of the transposed latent tile (80 bytes)
+#ifndef DAB_MLA_DEPTH
+#define DAB_MLA_DEPTH 4
+#endif
+constexpr int kDepth = DAB_MLA_DEPTH;    // operand fragments in flight (LDS reads ahead of their MFMA)
+constexpr float kLazy = 8.f;             // the softmax reference moves when a score passes it by 2^8
+constexpr int kMergeThreads = 256;       // two heads x 128 threads of four dims
+constexpr int kMaxHeads = 1024;
+constexpr int kMaxChunk = 65536;
+
+struct MlaArgs {
+    const float* q_lat;       // [B, nh, R]
+    const float* q_rope;      // [B, nh, P]
+    const uint16_t* c_new;    // [B, R]
+    const uint16_t* kr_new;   // [B, P]
+    uint16_t* c_cache;        // [B, cap, R]
+    uint16_t* kr_cache;       // [B, cap, P]
+    const int32_t* pos;       // [B]
+    float* out;               // [B, nh, R]
+    float* part_ml;           // [B, splits, nh, 2]: (max, sum) per chunk and head, log2 units
+    float* part_o;            // [B, splits, nh, R]: unnormalised weighted latent sums
+    int* err;                 // sticky device error flag
+    int nh, cap, hblocks;     // heads, cache rows, workgroups of heads per chunk
+    int splits;               // chunk slots per sequence (grid and partial layout)
+    int fixed;                // > 0: every chunk has this many tokens
+    int lmin;                 // automatic chunks: at least this many tokens
+    float qscale;             // softmax_scale * log2(e)
+};
+
+// Tokens per chunk of a sequence of n attended tokens: a fixed length, or
+// the shortest multiple of 32 that covers n in `splits` chunks, at least
+// lmin.  Either way ceil(n / len) <= splits.
+__host__ __device__ inline int chunk_len(int fixed, int splits, int lmin, int n) {
+    if (fixed > 0) return fixed;
+    int len = (n + splits - 1) / splits;
+    len = len > lmin ? len : lmin;
+    return (len + kTB - 1) / kTB * kTB;
+}
+
+__device__ inline bool seq_range(const MlaArgs& a, int b, int* p_out, int* len_out, int* nchunks_out) {
+    const int p = a.pos[b];
+    if (p < 0 || p >= a.cap) return false;
+    const int n = p + 1;
+    const int len = chunk_len(a.fixed, a.splits, a.lmin, n);
+    *p_out = p;
+    *len_out = len;
+    *nchunks_out = (n + len - 1) / len;
+    return true;
+}
+
+// Loading one tile of 32 token rows.  The 2048 latent pieces (16 bytes
+// each) go to thread t as token t % 32, pieces t / 32 + (NT / 32) k, so that
+// the transposed copy's 16-bit stores of one instruction cover 32 tokens of
+// one latent dim (two dims 8 rows apart per wave: banks 32 apart); the 256
+// rotary pieces go as token (t + NT k) / 8, piece t % 8.  Rows at or past t1
+// are zeros.
+template <int NT>
+struct TileLoad {
+    static constexpr int PC = 32 * (kR / 8) / NT;        // latent pieces per thread
+    static constexpr int PK = 32 * (kP / 8) / NT;        // rotary pieces per thread
+    static_assert(PC * NT == 32 * (kR / 8) && PK * NT == 32 * (kP / 8), "pieces must split evenly");
+};
+
+// Chunk (sequence blockIdx.y; chunk s, head block hb from blockIdx.x).
+// Workgroups are dispatched to the eight XCDs round-robin by linear index,
+// so index x goes to XCD x % 8: slot x / 8 of an XCD takes head block
+// slot % hblocks of chunk 8 (slot / hblocks) + x % 8, and the head blocks of
+// one chunk run on one XCD one after the other, the later ones reading the
+// chunk's rows from that XCD's L2.  gridDim.x is 8 hblocks ceil(splits / 8).
+template <int HT, int NW>
+__global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
+    constexpr int NT = 64 * NW;
+    constexpr int PC = TileLoad<NT>::PC, PK = TileLoad<NT>::PK;
+    constexpr bool PREFETCH = NW >= 4;                 // next tile in registers while one is computed
+    constexpr int GROUP = PREFETCH ? PC : 8;           // latent pieces requested at once
+    __shared__ __attribute__((aligned(16))) uint16_t kt[kTB][kRow];      // [c_t | kr_t] token-major
+    __shared__ __attribute__((aligned(16))) uint16_t ct[kR][kCtRow];     // c transposed: [dim][token]
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int b = blockIdx.y, slot = blockIdx.x / 8;
+    const int hb = slot % a.hblocks, s = slot / a.hblocks * 8 + blockIdx.x % 8;
+    int p, len, nchunks;
+    if (!seq_range(a, b, &p, &len, &nchunks)) {
+        if (s == 0 && hb == 0 && t == 0) atomicOr(a.err, 1);
+        return;
+    }
+    if (s >= nchunks) return;
+    const int t0 = s * len, t1 = min(p + 1, t0 + len);
+    const size_t row0 = (size_t)b * a.cap;
+
+    // the new token's rows are appended by the one workgroup whose chunk holds them (every chunk
+    // reads the new token from c_new / kr_new, never from the cache row being written)
+    if (hb == 0 && p >= t0 && p < t1) {
+        for (int i = t; i < kPieces; i += NT) {
+            if (i < kR / 8)
+                *reinterpret_cast<u32x4*>(a.c_cache + (row0 + p) * kR + 8 * i) =
+                    *reinterpret_cast<const u32x4*>(a.c_new + (size_t)b * kR + 8 * i);
+            else
+                *reinterpret_cast<u32x4*>(a.kr_cache + (row0 + p) * kP + 8 * (i - kR / 8)) =
+                    *reinterpret_cast<const u32x4*>(a.kr_new + (size_t)b * kP + 8 * (i - kR / 8));
+        }
+    }
+
+    // this wave's query fragments: head (tile ht, column m), dims 32 ks + 8 g .. + 8
+    const int head0 = (hb * NW + wave) * 16 * HT;
+    bf16x8 qf[HT][kSteps];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const size_t h = (size_t)b * a.nh + head0 + 16 * ht + m;
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks) {
+            const int d = 32 * ks + 8 * g;
+            const float* src = d < kR ? a.q_lat + h * kR + d : a.q_rope + h * kP + (d - kR);
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+            const u32x4 v = {dev::pack_bf16x2(x0[0] * a.qscale, x0[1] * a.qscale),
+                             dev::pack_bf16x2(x0[2] * a.qscale, x0[3] * a.qscale),
+                             dev::pack_bf16x2(x1[0] * a.qscale, x1[1] * a.qscale),
+                             dev::pack_bf16x2(x1[2] * a.qscale, x1[3] * a.qscale)};
+            qf[ht][ks] = as_bf16x8(v);
+        }
+    }
+
+    f32x4 oacc[HT][kDimTiles];
+    float mref[HT], lsum[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        mref[ht] = -INFINITY;
+        lsum[ht] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < kDimTiles; ++dt) oacc[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int lr = t % kTB, lc = t / kTB;              // this thread's latent token and first piece
+    const uint16_t* c_new = a.c_new + (size_t)b * kR;
+    const uint16_t* kr_new = a.kr_new + (size_t)b * kP;
+    auto c_src = [&](int tok, int c) -> const uint16_t* {
+        return tok < p ? a.c_cache + (row0 + tok) * kR + 8 * c : c_new + 8 * c;
+    };
+    auto kr_src = [&](int tok, int c) -> const uint16_t* {
+        return tok < p ? a.kr_cache + (row0 + tok) * kP + 8 * c : kr_new + 8 * c;
+    };
+    u32x4 pc[GROUP], pk[PK];
+    // latent pieces k0 .. k0 + GROUP - 1 of tile j into pc
+    // rows past t1 read the last attended row (always valid memory) and are zeroed after the load
+    auto issue_c = [&](int j, int k0) {
+        const int tok = t0 + kTB * j + lr;
+        const uint16_t* base = c_src(min(tok, t1 - 1), lc);
+#pragma unroll
+        for (int k = 0; k < GROUP; ++k)
+            pc[k] = *reinterpret_cast<const u32x4*>(base + 8 * (NT / kTB) * (k0 + k));
+        if (tok >= t1)
+#pragma unroll
+            for (int k = 0; k < GROUP; ++k) pc[k] = u32x4{0u, 0u, 0u, 0u};
+    };
+    auto issue_k = [&](int j) {
+#pragma unroll
+        for (int k = 0; k < PK; ++k) {
+            const int q = t + NT * k, tok = t0 + kTB * j + q / 8;
+            pk[k] = *reinterpret_cast<const u32x4*>(kr_src(min(tok, t1 - 1), q % 8));
+            if (tok >= t1) pk[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_c = [&](int k0) {
+#pragma unroll
+        for (int k = 0; k < GROUP; ++k) {
+            const int c = lc + (NT / kTB) * (k0 + k);
+            *reinterpret_cast<u32x4*>(&kt[lr][8 * c]) = pc[k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ct[8 * c + 2 * e][lr] = (uint16_t)(pc[k][e] & 0xffffu);
+                ct[8 * c + 2 * e + 1][lr] = (uint16_t)(pc[k][e] >> 16);
+            }
+        }
+    };
+    auto store_k = [&]() {
+#pragma unroll
+        for (int k = 0; k < PK; ++k) {
+            const int q = t + NT * k;
+            *reinterpret_cast<u32x4*>(&kt[q / 8][kR + 8 * (q % 8)]) = pk[k];
+        }
+    };
+
+    const int ntiles = (t1 - t0 + kTB - 1) / kTB;
+    if (PREFETCH) {
+        issue_c(0, 0);
+        issue_k(0);
+    }
+    for (int j = 0; j < ntiles; ++j) {
+        __syncthreads();                               // the previous tile is consumed
+        if (PREFETCH) {
+            store_c(0);
+            store_k();
+            if (j + 1 < ntiles) {
+                issue_c(j + 1, 0);
+                issue_k(j + 1);
+            }
+        } else {
+            for (int k0 = 0; k0 < PC; k0 += GROUP) {
+                issue_c(j, k0);
+                store_c(k0);
+            }
+            issue_k(j);
+            store_k();
+        }
+        __syncthreads();
+
+        // scores: S[token 16 tt + 4 g + i][head 16 ht + m] = sum over e of sacc[e][tt][ht][i] (the even
+        // and odd 32-dim steps accumulate apart: four independent chains per head tile).  The K
+        // fragments of step ks + kDepth - 1 are requested while step ks is multiplied.
+        f32x4 sacc[2][2][HT];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) sacc[e][tt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            bf16x8 fr[kDepth][2];
+            auto read_k = [&](int ks, bf16x8 (&f)[2]) {
+                f[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[m][32 * ks + 8 * g]));
+                f[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[16 + m][32 * ks + 8 * g]));
+            };
+#pragma unroll
+            for (int d = 0; d < kDepth - 1; ++d) read_k(d, fr[d]);
+#pragma unroll
+            for (int ks = 0; ks < kSteps; ++ks) {
+                if (ks + kDepth - 1 < kSteps) read_k(ks + kDepth - 1, fr[(ks + kDepth - 1) % kDepth]);
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+                        sacc[ks & 1][tt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            fr[ks % kDepth][tt], qf[ht][ks], sacc[ks & 1][tt][ht], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) sacc[0][tt][ht] += sacc[1][tt][ht];
+
+        // online softmax per head; weights to bf16 in the k-slot order of the value product
+        const int valid = t1 - t0 - kTB * j;           // tokens of this tile that are attended (>= 1)
+        bf16x8 pf[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * tt + 4 * g + i < valid) mx = fmaxf(mx, sacc[0][tt][ht][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const bool move = mx > mref[ht] + kLazy;
+            if (__ballot(move)) {
+                const float mnew = move ? mx : mref[ht];
+                const float alpha = __builtin_amdgcn_exp2f(mref[ht] - mnew);   // 0 on the first tile
+                lsum[ht] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < kDimTiles; ++dt) oacc[ht][dt] *= alpha;
+                mref[ht] = mnew;
+            }
+            uint32_t w[4];
+            float rowsum = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2) {
+                    float e[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int i = 2 * i2 + u;
+                        e[u] = 16 * tt + 4 * g + i < valid ? __builtin_amdgcn_exp2f(sacc[0][tt][ht][i] - mref[ht]) : 0.f;
+                    }
+                    w[2 * tt + i2] = dev::pack_bf16x2(e[0], e[1]);
+                    // the sum takes the weights as rounded, so that they sum to the normaliser exactly
+                    rowsum += __uint_as_float(w[2 * tt + i2] << 16) + __uint_as_float(w[2 * tt + i2] & 0xffff0000u);
+                }
+            lsum[ht] += rowsum;
+            pf[ht] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+        }
+
+        // values: A = latent dim 16 dt + m of tokens 4 g .. 4 g + 3, then 16 + 4 g .. 16 + 4 g + 3; the
+        // fragment of dim tile dt + kDepth - 1 is requested while tile dt is multiplied
+        {
+            bf16x8 fv[kDepth];
+            auto read_c = [&](int dt) -> bf16x8 {
+                const uint16_t* row = &ct[16 * dt + m][4 * g];
+                const uint2 lo = *reinterpret_cast<const uint2*>(row);
+                const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+                return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+            };
+#pragma unroll
+            for (int d = 0; d < kDepth - 1; ++d) fv[d] = read_c(d);
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) {
+                if (dt + kDepth - 1 < kDimTiles) fv[(dt + kDepth - 1) % kDepth] = read_c(dt + kDepth - 1);
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+                    oacc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fv[dt % kDepth], pf[ht], oacc[ht][dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+
+    // lane (m, g) holds dims 16 dt + 4 g + i of head 16 ht + m
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        float l = lsum[ht];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const size_t h = head0 + 16 * ht + m;
+        if (nchunks == 1) {
+            const float inv = 1.f / l;
+            float* o = a.out + ((size_t)b * a.nh + h) * kR + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[ht][dt] * inv;
+        } else {
+            const size_t slot = ((size_t)b * a.splits + s) * a.nh + h;
+            float* o = a.part_o + slot * kR + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[ht][dt];
+            if (g == 0) {
+                a.part_ml[2 * slot] = mref[ht];
+                a.part_ml[2 * slot + 1] = l;
+            }
+        }
+    }
+}
+
+// Merge of one sequence's chunks for two heads (grid: nh / 2 x B): weights
+// exp2(m_c - M) with M the largest chunk reference, in chunk order.
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
+    const int b = blockIdx.y, h = 2 * blockIdx.x + (threadIdx.x >> 7), d = 4 * (threadIdx.x & 127);
+    int p, len, nchunks;
+    if (!seq_range(a, b, &p, &len, &nchunks) || nchunks == 1) return;
+    const size_t slot0 = (size_t)b * a.splits * a.nh + h, stride = a.nh;
+    float M = -INFINITY;
+    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, a.part_ml[2 * (slot0 + c * stride)]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int c = 0; c < nchunks; ++c) {
+        const size_t slot = slot0 + c * stride;
+        const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * slot] - M);
+        den = fmaf(w, a.part_ml[2 * slot + 1], den);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + slot * kR + d);
+        acc += w * o;
+    }
+    *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.nh + h) * kR + d) = acc * (1.f / den);
+}
+
+// ---------------------------------------------------------------------------
+// host plan
+// ---------------------------------------------------------------------------
+
+struct MlaPlan {
+    int B = 0, nh = 0, cap = 0, ht = 0, nw = 0, hblocks = 0, splits = 0, fixed = 0, lmin = 0;
+    float scale = 0.f;
+    size_t off_ml = 0, off_o = 0, ws_bytes = 0;
+};
+
+// automatic chunks hold at least this many tokens: a chunk reads the query of all its heads
+// (nh x 576 values) once, as many bytes as ~250 cached tokens at nh = 128
+constexpr int kAutoMinChunk = 256;
+
+std::atomic<int> g_mla_cus[16];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    int cus = g_mla_cus[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            cus = -1;
+        }
+        g_mla_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus > 0 ? cus : 0;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+dab_status make_plan(const dab_mla_config* cfg, MlaPlan* p) {
+    if (!cfg) return DAB_ERR_INVALID_ARG;
+    if (cfg->batch < 0 || cfg->n_heads <= 0 || cfg->cache_capacity <= 0 || !(cfg->softmax_scale > 0.f) ||
+        !isfinite(cfg->softmax_scale) || cfg->kv_chunk < 0)
+        return DAB_ERR_INVALID_ARG;
+    if (cfg->kv_lora_rank != kR || cfg->rope_dim != kP || cfg->n_heads % 16 != 0 || cfg->n_heads > kMaxHeads)
+        return DAB_ERR_UNSUPPORTED;
+    if (cfg->kv_chunk != 0 && (cfg->kv_chunk % kTB != 0 || cfg->kv_chunk > kMaxChunk)) return DAB_ERR_UNSUPPORTED;
+    if ((int64_t)cfg->batch * cfg->cache_capacity > (int64_t)1 << 31) return DAB_ERR_UNSUPPORTED;
+    MlaPlan q;
+    q.B = cfg->batch;
+    q.nh = cfg->n_heads;
+    q.cap = cfg->cache_capacity;
+    q.scale = cfg->softmax_scale;
+    // 64 heads per workgroup of four waves (two head tiles per wave spill at 512 registers), else
+    // one wave of 16 heads
+    q.ht = 1;
+    q.nw = q.nh % 64 == 0 ? 4 : 1;
+    q.hblocks = q.nh / (16 * q.ht * q.nw);
+    if (cfg->kv_chunk > 0) {
+        q.fixed = cfg->kv_chunk;
+        q.splits = (q.cap + q.fixed - 1) / q.fixed;
+    } else {
+        // one chunk workgroup per compute unit over the batch (the 128-head workgroup holds a
+        // compute unit's registers), never more chunks than the capacity needs
+        int cus = device_cus();
+        if (cus <= 0) cus = 256;
+        const int per_cu = q.nw == 1 ? 4 : 1;
+        const int64_t wgs = (int64_t)q.B * q.hblocks;
+        int sp = (int)(wgs > 0 ? ((int64_t)cus * per_cu + wgs - 1) / wgs : 1);
+        const int most = (q.cap + kAutoMinChunk - 1) / kAutoMinChunk;
+        sp = sp < 1 ? 1 : sp > most ? most : sp;
+        q.splits = sp;
+        q.lmin = kAutoMinChunk;
+    }
+    if ((int64_t)8 * q.hblocks * ((q.splits + 7) / 8) > (int64_t)1 << 30 || q.B > 65535) return DAB_ERR_UNSUPPORTED;
+    q.off_ml = 256;
+    const size_t slots = (size_t)q.B * q.splits * q.nh;
+    q.off_o = align256(q.off_ml + slots * 2 * sizeof(float));
+    q.ws_bytes = align256(q.off_o + slots * kR * sizeof(float));
+    *p = q;
+    return DAB_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+dab_status hip_status(hipError_t e) { return record_hip_status(e); }
+
+template <typename K>
+hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t start, hipEvent_t stop, MlaArgs a) {
+    void* args[] = {&a};
+    const void* f = reinterpret_cast<const void*>(kernel);
+    if (start || stop) return hipExtLaunchKernel(f, grid, block, args, 0, s, start, stop, 0);
+    return hipLaunchKernel(f, grid, block, args, 0, s);
+}
+
+dab_status call(const dab_mla_config* cfg, const float* q_lat, const float* q_rope, const void* c_new,
+                const void* kr_new, void* c_cache, void* kr_cache, const int32_t* pos, float* out, void* workspace,
+                size_t workspace_bytes, void* stream, void* const* events, int n_events) {
+    MlaPlan p;
+    dab_status st = make_plan(cfg, &p);
+    if (st != DAB_OK) return st;
+    if (!workspace) return DAB_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DAB_ERR_INVALID_ARG;
+    if (workspace_bytes < p.ws_bytes) return DAB_ERR_WORKSPACE;
+    if (events) {
+        if (n_events != 4) return DAB_ERR_INVALID_ARG;
+        for (int i = 0; i < 4; ++i)
+            if (!events[i]) return DAB_ERR_INVALID_ARG;
+    }
+    if (p.B == 0) return DAB_OK;
+    const void* req[] = {q_lat, q_rope, c_new, kr_new, c_cache, kr_cache, out};
+    for (const void* r : req)
+        if (!r || !aligned(r, 16)) return DAB_ERR_INVALID_ARG;
+    if (!pos || !aligned(pos, 4)) return DAB_ERR_INVALID_ARG;
+    const size_t B = p.B, nh = p.nh, cap = p.cap;
+    struct Span { const void* ptr; size_t n; bool written; };
+    const Span spans[] = {
+        {q_lat, B * nh * kR * 4, false}, {q_rope, B * nh * kP * 4, false}, {c_new, B * kR * 2, false},
+        {kr_new, B * kP * 2, false},     {pos, B * 4, false},             {c_cache, B * cap * kR * 2, true},
+        {kr_cache, B * cap * kP * 2, true}, {out, B * nh * kR * 4, true}, {workspace, p.ws_bytes, true},
+    };
+    const int ns = (int)(sizeof(spans) / sizeof(spans[0]));
+    for (int i = 0; i < ns; ++i)
+        for (int j = i + 1; j < ns; ++j)
+            if ((spans[i].written || spans[j].written) && overlaps(spans[i].ptr, spans[i].n, spans[j].ptr, spans[j].n))
+                return DAB_ERR_INVALID_ARG;
+
+    MlaArgs a{};
+    a.q_lat = q_lat;
+    a.q_rope = q_rope;
+    a.c_new = static_cast<const uint16_t*>(c_new);
+    a.kr_new = static_cast<const uint16_t*>(kr_new);
+    a.c_cache = static_cast<uint16_t*>(c_cache);
+    a.kr_cache = static_cast<uint16_t*>(kr_cache);
+    a.pos = pos;
+    a.out = out;
+    char* ws = static_cast<char*>(workspace);
+    a.err = reinterpret_cast<int*>(ws);                 // the flags word at offset 0 of every workspace
+    a.part_ml = reinterpret_cast<float*>(ws + p.off_ml);
+    a.part_o = reinterpret_cast<float*>(ws + p.off_o);
+    a.nh = p.nh;
+    a.cap = p.cap;
+    a.hblocks = p.hblocks;
+    a.splits = p.splits;
+    a.fixed = p.fixed;
+    a.lmin = p.lmin;
+    a.qscale = p.scale * 1.4426950408889634f;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (events)
+        for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+    const dim3 grid((unsigned)(8 * p.hblocks * ((p.splits + 7) / 8)), (unsigned)p.B);
+    hipError_t e;
+    if (p.nw == 4) e = launch(mla_chunk_kernel<1, 4>, grid, dim3(256), s, ev[0], ev[1], a);
+    else e = launch(mla_chunk_kernel<1, 1>, grid, dim3(64), s, ev[0], ev[1], a);
+    if (e == hipSuccess) e = hipGetLastError();
+    if ((st = hip_status(e)) != DAB_OK) return st;
+    e = launch(mla_merge_kernel, dim3((unsigned)(p.nh / 2), (unsigned)p.B), dim3(kMergeThreads), s, ev[2], ev[3], a);
+    if (e == hipSuccess) e = hipGetLastError();
+    return hip_status(e);
+}
+
+}  // namespace mla
+}  // namespace dab
+
+extern "C" {
+
+size_t dab_mla_workspace_size(const dab_mla_config* cfg) {
+    dab::mla::MlaPlan p;
+    return dab::mla::make_plan(cfg, &p) == DAB_OK ? p.ws_bytes : 0;
+}
+
+dab_status dab_mla_decode_attn(const dab_mla_config* cfg, const float* q_lat, const float* q_rope, const void* c_new,
+                               const void* kr_new, void* c_cache, void* kr_cache, const int32_t* pos, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return dab::mla::call(cfg, q_lat, q_rope, c_new, kr_new, c_cache, kr_cache, pos, out, workspace, workspace_bytes,
+                          stream, nullptr, 0);
+}
+
+dab_status dab_mla_decode_attn_timed(const dab_mla_config* cfg, const float* q_lat, const float* q_rope,
+                                     const void* c_new, const void* kr_new, void* c_cache, void* kr_cache,
+                                     const int32_t* pos, float* out, void* workspace, size_t workspace_bytes,
+                                     void* stream, void* const* events, int n_events) {
+    if (!events) return DAB_ERR_INVALID_ARG;
+    return dab::mla::call(cfg, q_lat, q_rope, c_new, kr_new, c_cache, kr_cache, pos, out, workspace, workspace_bytes,
+                          stream, events, n_events);
+}
+
+}  // extern "C"

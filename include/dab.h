@@ -371,6 +371,98 @@ dab_status dab_decode_ffn_block_timed(const dab_ffn_config* cfg,
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       void* const* events, int n_events);
 
+/*
+ * Latent attention decode (DeepSeek's multi-head latent attention, MLA),
+ * the second attention workload the ClusterFusion page runs through its
+ * fused decode step (section 5.2: the latent key/value cache is split across
+ * clusters and the partial results are merged with a sparse reduction; the
+ * page measures it at 4K and 16K tokens).  The page gives no formulas; the
+ * reading taken is the absorbed decode form of latent attention.  Every
+ * cached token t of a sequence holds one latent row c_t (R = kv_lora_rank
+ * values) and one rotary key kr_t (P = rope_dim values), both shared by all
+ * heads; head h's query arrives already folded through the key
+ * up-projection (q_lat_h, R values) with its rotary part q_rope_h (P values):
+ *
+ *   s_{h,t} = (q_lat_h . c_t + q_rope_h . kr_t) * softmax_scale
+ *   o_h     = sum_t softmax_t(s_{h,.}) c_t        over t = 0 .. pos_b
+ *
+ * where token pos_b is the new token, whose rows are appended to the caches
+ * at row pos_b and attended with the history.  o_h is a latent vector: the
+ * value up-projection and the output projection follow outside this call.
+ *
+ * On MI355X the latent cache of one sequence is split into chunks of tokens,
+ * each one workgroup that reads every cached row once for all of its heads
+ * (scores and weighted sums on the matrix cores, bf16 operands, fp32
+ * accumulation); the chunks' partial softmax states are merged by
+ * log-sum-exp weights in a second kernel.
+ */
+typedef struct {
+    int32_t batch;           /* B >= 0 sequences (0: nothing to do)                     */
+    int32_t n_heads;         /* nh, a multiple of 16, at most 1024                      */
+    int32_t kv_lora_rank;    /* R: 512                                                  */
+    int32_t rope_dim;        /* P: 64                                                   */
+    int32_t cache_capacity;  /* cap >= 1: token rows per sequence in each cache         */
+    float softmax_scale;     /* > 0 (DeepSeek-V3: 1/sqrt(128 + 64))                     */
+    int32_t kv_chunk;        /* tokens per chunk: 0 = automatic (sized per sequence from */
+                             /* its position and the current device's compute units),  */
+                             /* else a multiple of 32 in [32, 65536]                    */
+} dab_mla_config;
+
+/*
+ * Bytes of device workspace one latent-attention call needs (0 when the
+ * configuration is invalid): the device error flag, then the chunks'
+ * partial softmax states (max, sum) and unnormalised latent outputs, fp32.
+ * Every call writes each partial before it reads it, so the workspace needs
+ * no initialisation beyond a zeroed flag word (dab_workspace_init once);
+ * calls that share one workspace must not overlap.  With kv_chunk = 0 the
+ * size depends on the current device's compute-unit count: size and call on
+ * the same device.
+ */
+size_t dab_mla_workspace_size(const dab_mla_config* cfg);
+
+/*
+ * One latent-attention decode step for every sequence of the batch, two
+ * kernels on `stream` (chunks, then the merge).
+ *
+ *   q_lat    fp32 [B, nh, R]     query folded through the key up-projection
+ *   q_rope   fp32 [B, nh, P]     rotary part of the query (already rotated)
+ *   c_new    bf16 [B, R]         the new token's latent row
+ *   kr_new   bf16 [B, P]         the new token's rotary key (already rotated)
+ *   c_cache  bf16 [B, cap, R]    token-major.  Rows t < pos[b] are read; row
+ *   kr_cache bf16 [B, cap, P]    pos[b] is written with c_new[b] (resp.
+ *                                kr_new[b]), bits unchanged; nothing else
+ *                                is written
+ *   pos      int32 [B]           tokens already cached = index of the new
+ *                                token, 0 <= pos[b] < cap
+ *   out      fp32 [B, nh, R]     o; must not overlap any other argument
+ *   workspace, workspace_bytes   at least dab_mla_workspace_size bytes
+ *
+ * Numerics: q * softmax_scale * log2(e) and the softmax weights are rounded
+ * to bf16 (nearest-even, relative 2^-9 each) as matrix-core operands; the
+ * scores, the running max and sum and every weighted sum are fp32.  Every
+ * sum has a fixed order: the call is deterministic.  Errors a host can see
+ * return a status before anything is enqueued; an out-of-range pos[b]
+ * leaves that sequence's rows untouched and sets bit 0 of the device flag
+ * (dab_read_device_error).
+ */
+dab_status dab_mla_decode_attn(const dab_mla_config* cfg,
+                               const float* q_lat, const float* q_rope,
+                               const void* c_new, const void* kr_new,
+                               void* c_cache, void* kr_cache, const int32_t* pos, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Same, recording events[0] / events[1] at the start / end of the chunk
+ * kernel and events[2] / events[3] at those of the merge kernel (as in
+ * dab_decode_attn_block_timed); n_events must be 4.
+ */
+dab_status dab_mla_decode_attn_timed(const dab_mla_config* cfg,
+                                     const float* q_lat, const float* q_rope,
+                                     const void* c_new, const void* kr_new,
+                                     void* c_cache, void* kr_cache, const int32_t* pos, float* out,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events, int n_events);
+
 #ifdef __cplusplus
 }
 #endif
