@@ -60,9 +60,10 @@ constexpr int kKD = kR + kP;             // score contraction: 576 = 18 steps of
 constexpr int kSteps = kKD / 32;
 constexpr int kDimTiles = kR / 16;       // output tiles of 16 latent dims
 constexpr int kTB = 32;                  // tokens per LDS tile
-constexpr int kRow = kKD + 8;            // bf16 per LDS row (1168 bytes)
+constexpr int kCRow = kR + 8;            // bf16 per latent row of an LDS tile (1040 bytes: rows start 4 banks apart)
+constexpr int kKrOff = kTB * kCRow;      // the tile's rotary keys follow its latent rows: 32 x 128 bytes, swizzled
+constexpr int kTile = kKrOff + kTB * kP; // bf16 per LDS tile (37,376 bytes)
 constexpr int kPieces = kKD / 8;         // 16-byte pieces per token row (64 latent + 8 rotary)
-constexpr int kCtRow = kTB + 8;          // bf16 per row of the transposed latent tile (80 bytes)
 #ifndef DAB_MLA_DEPTH
 #define DAB_MLA_DEPTH 4
 #endif
@@ -112,18 +113,72 @@ __device__ inline bool seq_range(const MlaArgs& a, int b, int* p_out, int* len_o
     return true;
 }
 
-// Loading one tile of 32 token rows.  The 2048 latent pieces (16 bytes
-// each) go to thread t as token t % 32, pieces t / 32 + (NT / 32) k, so that
-// the transposed copy's 16-bit stores of one instruction cover 32 tokens of
-// one latent dim (two dims 8 rows apart per wave: banks 32 apart); the 256
-// rotary pieces go as token (t + NT k) / 8, piece t % 8.  Rows at or past t1
-// are zeros.
-template <int NT>
-struct TileLoad {
-    static constexpr int PC = 32 * (kR / 8) / NT;        // latent pieces per thread
-    static constexpr int PK = 32 * (kP / 8) / NT;        // rotary pieces per thread
-    static_assert(PC * NT == 32 * (kR / 8) && PK * NT == 32 * (kP / 8), "pieces must split evenly");
+// Tiles of 32 token rows reach LDS by direct loads (global_load_lds_dwordx4:
+// lane l's 16 bytes land at the LDS byte address in M0 + 16 l, no registers
+// involved): one 64-lane load per 1 KB latent row, and one per eight tokens'
+// 128-byte rotary keys, which sit together after the latent rows with their
+// 16-byte pieces XOR-swizzled (piece q of token t at q ^ (t / 2 % 8)), so
+// that the 16 rows an operand read touches hit distinct banks.  Each wave
+// requests its share of the next tiles one load at a time between the MFMAs
+// of a step: a direct load holds up its wave's issue for a while (~60 ns
+// measured), long enough to stall the matrix cores if a tile's loads go out
+// back to back.
+// DEPTH tiles are in flight while one is computed, in DEPTH + 1 buffers.
+// Each wave waits for its own loads with s_waitcnt vmcnt, then a bare
+// s_barrier (inline asm, memory clobber: no fence, which would wait for every
+// load in flight) makes the tile visible to all waves.  The direct loads are
+// issued from inline asm: the compiler's builtin for them makes it wait for
+// every one in flight (vmcnt(0)) before any LDS read it cannot prove
+// disjoint, i.e. before every tile.  Rows past t1 read row t1 - 1 again;
+// their weights are zero.
+template <int NW>
+struct TilePipe {
+    static constexpr int DEPTH = NW >= 4 ? 3 : 1;
+    static constexpr int NBUF = DEPTH + 1;
+    static constexpr int TPW = kTB / NW;                   // latent rows each wave loads per tile
+    static constexpr int KRW = kTB / 8 / NW > 0 ? kTB / 8 / NW : 1;   // rotary loads per wave (8 tokens each)
+    static constexpr int PER_TILE = TPW + KRW;             // direct loads per wave and tile
+    static_assert((DEPTH - 1) * PER_TILE <= 63, "vmcnt holds at most 63");
+    static_assert(KRW * NW * 8 == kTB, "rotary loads must cover the tile");
 };
+
+template <int N>
+__device__ inline void wait_vm() {
+    // s_waitcnt vmcnt(N), expcnt and lgkmcnt left alone
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0): this wave's LDS reads done
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// 16 bytes per lane from src into LDS at byte lds + 16 * lane (lds wave-uniform).  M0 holds the LDS
+// address; no other instruction of the kernels here uses M0 (no dynamic register indexing, no message
+// or GDS instructions), so setting it in the asm is safe.  The load has no register result.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void lds_load16(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ inline uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Four 16-bit values of a transposing LDS read (ds_read_b64_tr_b16): in each
+// 16-lane group, lane i receives element i % 4 of the 8 bytes addressed by
+// lanes 4j + i / 4 of its group, j = 0..3.
+__device__ inline v4i16 read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)((__attribute__((address_space(3))) char*)(p)));
+}
 
 // Chunk (sequence blockIdx.y; chunk s, head block hb from blockIdx.x).
 // Workgroups are dispatched to the eight XCDs round-robin by linear index,
@@ -131,14 +186,12 @@ struct TileLoad {
 // slot % hblocks of chunk 8 (slot / hblocks) + x % 8, and the head blocks of
 // one chunk run on one XCD one after the other, the later ones reading the
 // chunk's rows from that XCD's L2.  gridDim.x is 8 hblocks ceil(splits / 8).
-template <int HT, int NW>
+template <int NW>
 __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
     constexpr int NT = 64 * NW;
-    constexpr int PC = TileLoad<NT>::PC, PK = TileLoad<NT>::PK;
-    constexpr bool PREFETCH = NW >= 4;                 // next tile in registers while one is computed
-    constexpr int GROUP = PREFETCH ? PC : 8;           // latent pieces requested at once
-    __shared__ __attribute__((aligned(16))) uint16_t kt[kTB][kRow];      // [c_t | kr_t] token-major
-    __shared__ __attribute__((aligned(16))) uint16_t ct[kR][kCtRow];     // c transposed: [dim][token]
+    constexpr int DEPTH = TilePipe<NW>::DEPTH, NBUF = TilePipe<NW>::NBUF, PT = TilePipe<NW>::PER_TILE;
+    constexpr int TPW = TilePipe<NW>::TPW, KRW = TilePipe<NW>::KRW;
+    __shared__ __attribute__((aligned(16))) uint16_t kt[NBUF][kTile];   // latent rows, then rotary keys
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -152,6 +205,60 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
     if (s >= nchunks) return;
     const int t0 = s * len, t1 = min(p + 1, t0 + len);
     const size_t row0 = (size_t)b * a.cap;
+    const uint16_t* c_new = a.c_new + (size_t)b * kR;
+    const uint16_t* kr_new = a.kr_new + (size_t)b * kP;
+
+    // this wave's query fragments (head 16 (hb NW + wave) + m, dims 32 ks + 8 g .. + 8), requested first,
+    // so that their latency runs under the issue of the first tiles' direct loads
+    const int head = (hb * NW + wave) * 16 + m;
+    f32x4 qraw[kSteps][2];
+    {
+        const size_t h = (size_t)b * a.nh + head;
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks) {
+            const int d = 32 * ks + 8 * g;
+            const float* src = d < kR ? a.q_lat + h * kR + d : a.q_rope + h * kP + (d - kR);
+            qraw[ks][0] = *reinterpret_cast<const f32x4*>(src);
+            qraw[ks][1] = *reinterpret_cast<const f32x4*>(src + 4);
+        }
+    }
+
+    // direct load i (0 <= i < PT) of this wave for tile j: latent row wave * TPW + i for i < TPW, else
+    // the rotary keys of tokens 8 k .. 8 k + 7, k = wave * KRW + i - TPW (lane l: token 8 k + l / 8,
+    // landing at piece l % 8, so it fetches piece (l % 8) ^ (token / 2 % 8))
+    const uint32_t kt0 = lds_address(&kt[0][0]);
+    auto issue = [&](int j, int i) {
+        const uint32_t dst = kt0 + (uint32_t)(j % NBUF) * (kTile * 2);
+        const int base = t0 + kTB * j;
+        if (i < TPW) {
+            const int r = wave * TPW + i;
+            const int tok = min(base + r, t1 - 1);
+            const uint16_t* cs = tok < p ? a.c_cache + (row0 + tok) * kR : c_new;
+            lds_load16(cs + 8 * lane, dst + r * (kCRow * 2));
+        } else {
+            const int k = wave * KRW + (i - TPW), r = 8 * k + (lane >> 3);
+            const int tok = min(base + r, t1 - 1);
+            const uint16_t* ks = tok < p ? a.kr_cache + (row0 + tok) * kP : kr_new;
+            lds_load16(ks + 8 * ((lane & 7) ^ ((r >> 1) & 7)), dst + kKrOff * 2 + 8 * k * (kP * 2));
+        }
+    };
+    const int ntiles = (t1 - t0 + kTB - 1) / kTB;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (d < ntiles)
+#pragma unroll
+            for (int i = 0; i < PT; ++i) issue(d, i);
+
+    bf16x8 qf[kSteps];
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+        const f32x4 x0 = qraw[ks][0], x1 = qraw[ks][1];
+        const u32x4 v = {dev::pack_bf16x2(x0[0] * a.qscale, x0[1] * a.qscale),
+                         dev::pack_bf16x2(x0[2] * a.qscale, x0[3] * a.qscale),
+                         dev::pack_bf16x2(x1[0] * a.qscale, x1[1] * a.qscale),
+                         dev::pack_bf16x2(x1[2] * a.qscale, x1[3] * a.qscale)};
+        qf[ks] = as_bf16x8(v);
+    }
 
     // the new token's rows are appended by the one workgroup whose chunk holds them (every chunk
     // reads the new token from c_new / kr_new, never from the cache row being written)
@@ -159,173 +266,94 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
         for (int i = t; i < kPieces; i += NT) {
             if (i < kR / 8)
                 *reinterpret_cast<u32x4*>(a.c_cache + (row0 + p) * kR + 8 * i) =
-                    *reinterpret_cast<const u32x4*>(a.c_new + (size_t)b * kR + 8 * i);
+                    *reinterpret_cast<const u32x4*>(c_new + 8 * i);
             else
                 *reinterpret_cast<u32x4*>(a.kr_cache + (row0 + p) * kP + 8 * (i - kR / 8)) =
-                    *reinterpret_cast<const u32x4*>(a.kr_new + (size_t)b * kP + 8 * (i - kR / 8));
+                    *reinterpret_cast<const u32x4*>(kr_new + 8 * (i - kR / 8));
         }
     }
 
-    // this wave's query fragments: head (tile ht, column m), dims 32 ks + 8 g .. + 8
-    const int head0 = (hb * NW + wave) * 16 * HT;
-    bf16x8 qf[HT][kSteps];
+    f32x4 oacc[kDimTiles];
+    float mref = -INFINITY, lsum = 0.f;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const size_t h = (size_t)b * a.nh + head0 + 16 * ht + m;
-#pragma unroll
-        for (int ks = 0; ks < kSteps; ++ks) {
-            const int d = 32 * ks + 8 * g;
-            const float* src = d < kR ? a.q_lat + h * kR + d : a.q_rope + h * kP + (d - kR);
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-            const u32x4 v = {dev::pack_bf16x2(x0[0] * a.qscale, x0[1] * a.qscale),
-                             dev::pack_bf16x2(x0[2] * a.qscale, x0[3] * a.qscale),
-                             dev::pack_bf16x2(x1[0] * a.qscale, x1[1] * a.qscale),
-                             dev::pack_bf16x2(x1[2] * a.qscale, x1[3] * a.qscale)};
-            qf[ht][ks] = as_bf16x8(v);
-        }
-    }
+    for (int dt = 0; dt < kDimTiles; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    f32x4 oacc[HT][kDimTiles];
-    float mref[HT], lsum[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        mref[ht] = -INFINITY;
-        lsum[ht] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < kDimTiles; ++dt) oacc[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const int lr = t % kTB, lc = t / kTB;              // this thread's latent token and first piece
-    const uint16_t* c_new = a.c_new + (size_t)b * kR;
-    const uint16_t* kr_new = a.kr_new + (size_t)b * kP;
-    auto c_src = [&](int tok, int c) -> const uint16_t* {
-        return tok < p ? a.c_cache + (row0 + tok) * kR + 8 * c : c_new + 8 * c;
-    };
-    auto kr_src = [&](int tok, int c) -> const uint16_t* {
-        return tok < p ? a.kr_cache + (row0 + tok) * kP + 8 * c : kr_new + 8 * c;
-    };
-    u32x4 pc[GROUP], pk[PK];
-    // latent pieces k0 .. k0 + GROUP - 1 of tile j into pc
-    // rows past t1 read the last attended row (always valid memory) and are zeroed after the load
-    auto issue_c = [&](int j, int k0) {
-        const int tok = t0 + kTB * j + lr;
-        const uint16_t* base = c_src(min(tok, t1 - 1), lc);
-#pragma unroll
-        for (int k = 0; k < GROUP; ++k)
-            pc[k] = *reinterpret_cast<const u32x4*>(base + 8 * (NT / kTB) * (k0 + k));
-        if (tok >= t1)
-#pragma unroll
-            for (int k = 0; k < GROUP; ++k) pc[k] = u32x4{0u, 0u, 0u, 0u};
-    };
-    auto issue_k = [&](int j) {
-#pragma unroll
-        for (int k = 0; k < PK; ++k) {
-            const int q = t + NT * k, tok = t0 + kTB * j + q / 8;
-            pk[k] = *reinterpret_cast<const u32x4*>(kr_src(min(tok, t1 - 1), q % 8));
-            if (tok >= t1) pk[k] = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store_c = [&](int k0) {
-#pragma unroll
-        for (int k = 0; k < GROUP; ++k) {
-            const int c = lc + (NT / kTB) * (k0 + k);
-            *reinterpret_cast<u32x4*>(&kt[lr][8 * c]) = pc[k];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ct[8 * c + 2 * e][lr] = (uint16_t)(pc[k][e] & 0xffffu);
-                ct[8 * c + 2 * e + 1][lr] = (uint16_t)(pc[k][e] >> 16);
-            }
-        }
-    };
-    auto store_k = [&]() {
-#pragma unroll
-        for (int k = 0; k < PK; ++k) {
-            const int q = t + NT * k;
-            *reinterpret_cast<u32x4*>(&kt[q / 8][kR + 8 * (q % 8)]) = pk[k];
-        }
-    };
-
-    const int ntiles = (t1 - t0 + kTB - 1) / kTB;
-    if (PREFETCH) {
-        issue_c(0, 0);
-        issue_k(0);
-    }
     for (int j = 0; j < ntiles; ++j) {
-        __syncthreads();                               // the previous tile is consumed
-        if (PREFETCH) {
-            store_c(0);
-            store_k();
-            if (j + 1 < ntiles) {
-                issue_c(j + 1, 0);
-                issue_k(j + 1);
-            }
+        // tile j has landed once at most min(DEPTH - 1, ntiles - 1 - j) later tiles' loads are in flight
+        const int later = min(DEPTH - 1, ntiles - 1 - j);
+        if constexpr (DEPTH >= 3) {
+            if (later >= 2) wait_vm<2 * PT>();
+            else if (later == 1) wait_vm<PT>();
+            else wait_vm<0>();
+        } else if constexpr (DEPTH == 2) {
+            if (later >= 1) wait_vm<PT>();
+            else wait_vm<0>();
         } else {
-            for (int k0 = 0; k0 < PC; k0 += GROUP) {
-                issue_c(j, k0);
-                store_c(k0);
-            }
-            issue_k(j);
-            store_k();
+            wait_vm<0>();
         }
-        __syncthreads();
+        lds_barrier();                     // every wave's loads of tile j are in; tile j - 1 is consumed
+        const bool more = j + DEPTH < ntiles;    // tile j + DEPTH goes out during this tile's score steps
+        const uint16_t* tile = kt[j % NBUF];
 
-        // scores: S[token 16 tt + 4 g + i][head 16 ht + m] = sum over e of sacc[e][tt][ht][i] (the even
-        // and odd 32-dim steps accumulate apart: four independent chains per head tile).  The K
-        // fragments of step ks + kDepth - 1 are requested while step ks is multiplied.
-        f32x4 sacc[2][2][HT];
+        // scores: S[token 16 tt + 4 g + i][head] = sum over e of sacc[e][tt][i] (the even and odd 32-dim
+        // steps accumulate apart: four independent chains).  The K fragments of step ks + kDepth - 1
+        // are requested while step ks is multiplied.
+        f32x4 sacc[2][2];
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) sacc[e][tt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < 2; ++tt) sacc[e][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
             bf16x8 fr[kDepth][2];
             auto read_k = [&](int ks, bf16x8 (&f)[2]) {
-                f[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[m][32 * ks + 8 * g]));
-                f[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[16 + m][32 * ks + 8 * g]));
+                if (ks < kR / 32) {
+                    f[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + m * kCRow + 32 * ks + 8 * g));
+                    f[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + (16 + m) * kCRow + 32 * ks + 8 * g));
+                } else {
+                    const int q = (4 * (ks - kR / 32) + g) ^ ((m >> 1) & 7);   // tokens m and 16 + m swizzle alike
+                    f[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + kKrOff + m * kP + 8 * q));
+                    f[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + kKrOff + (16 + m) * kP + 8 * q));
+                }
             };
 #pragma unroll
             for (int d = 0; d < kDepth - 1; ++d) read_k(d, fr[d]);
 #pragma unroll
             for (int ks = 0; ks < kSteps; ++ks) {
+                // this step's share of tile j + DEPTH's direct loads
+#pragma unroll
+                for (int i = ks * PT / kSteps; i < (ks + 1) * PT / kSteps; ++i)
+                    if (more) issue(j + DEPTH, i);
                 if (ks + kDepth - 1 < kSteps) read_k(ks + kDepth - 1, fr[(ks + kDepth - 1) % kDepth]);
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-                        sacc[ks & 1][tt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            fr[ks % kDepth][tt], qf[ht][ks], sacc[ks & 1][tt][ht], 0, 0, 0);
+                for (int tt = 0; tt < 2; ++tt)
+                    sacc[ks & 1][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[ks % kDepth][tt], qf[ks],
+                                                                                sacc[ks & 1][tt], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) sacc[0][tt][ht] += sacc[1][tt][ht];
+        sacc[0][0] += sacc[1][0];
+        sacc[0][1] += sacc[1][1];
 
-        // online softmax per head; weights to bf16 in the k-slot order of the value product
+        // online softmax of this wave's heads; weights to bf16 in the k-slot order of the value product
         const int valid = t1 - t0 - kTB * j;           // tokens of this tile that are attended (>= 1)
-        bf16x8 pf[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
+        bf16x8 pf;
+        {
             float mx = -INFINITY;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (16 * tt + 4 * g + i < valid) mx = fmaxf(mx, sacc[0][tt][ht][i]);
+                    if (16 * tt + 4 * g + i < valid) mx = fmaxf(mx, sacc[0][tt][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const bool move = mx > mref[ht] + kLazy;
+            const bool move = mx > mref + kLazy;
             if (__ballot(move)) {
-                const float mnew = move ? mx : mref[ht];
-                const float alpha = __builtin_amdgcn_exp2f(mref[ht] - mnew);   // 0 on the first tile
-                lsum[ht] *= alpha;
+                const float mnew = move ? mx : mref;
+                const float alpha = __builtin_amdgcn_exp2f(mref - mnew);   // 0 on the first tile
+                lsum *= alpha;
 #pragma unroll
-                for (int dt = 0; dt < kDimTiles; ++dt) oacc[ht][dt] *= alpha;
-                mref[ht] = mnew;
+                for (int dt = 0; dt < kDimTiles; ++dt) oacc[dt] *= alpha;
+                mref = mnew;
             }
             uint32_t w[4];
             float rowsum = 0.f;
@@ -337,24 +365,28 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         const int i = 2 * i2 + u;
-                        e[u] = 16 * tt + 4 * g + i < valid ? __builtin_amdgcn_exp2f(sacc[0][tt][ht][i] - mref[ht]) : 0.f;
+                        e[u] = 16 * tt + 4 * g + i < valid ? __builtin_amdgcn_exp2f(sacc[0][tt][i] - mref) : 0.f;
                     }
                     w[2 * tt + i2] = dev::pack_bf16x2(e[0], e[1]);
                     // the sum takes the weights as rounded, so that they sum to the normaliser exactly
                     rowsum += __uint_as_float(w[2 * tt + i2] << 16) + __uint_as_float(w[2 * tt + i2] & 0xffff0000u);
                 }
-            lsum[ht] += rowsum;
-            pf[ht] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+            lsum += rowsum;
+            pf = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
         }
 
-        // values: A = latent dim 16 dt + m of tokens 4 g .. 4 g + 3, then 16 + 4 g .. 16 + 4 g + 3; the
-        // fragment of dim tile dt + kDepth - 1 is requested while tile dt is multiplied
+        // values: A = latent dim 16 dt + m of tokens 4 g + j, then 16 + 4 g + j (j = 0..3), two
+        // transposing reads of the token-major tile: lane (m, g) addresses token 16 u + 4 g + m / 4,
+        // dims 16 dt + 4 (m % 4) .. + 3.  The fragment of dim tile dt + kDepth - 1 is requested while
+        // tile dt is multiplied.
         {
             bf16x8 fv[kDepth];
             auto read_c = [&](int dt) -> bf16x8 {
-                const uint16_t* row = &ct[16 * dt + m][4 * g];
-                const uint2 lo = *reinterpret_cast<const uint2*>(row);
-                const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+                // whole 64-bit results as two dwords each (per-element 16-bit extraction of the short4
+                // result lost its upper dword in hipcc's code for gfx950)
+                const uint16_t* at = tile + (4 * g + (m >> 2)) * kCRow + 16 * dt + 4 * (m & 3);
+                const uint2 lo = __builtin_bit_cast(uint2, read_tr16(at));
+                const uint2 hi = __builtin_bit_cast(uint2, read_tr16(at + 16 * kCRow));
                 return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
             };
 #pragma unroll
@@ -362,35 +394,29 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
 #pragma unroll
             for (int dt = 0; dt < kDimTiles; ++dt) {
                 if (dt + kDepth - 1 < kDimTiles) fv[(dt + kDepth - 1) % kDepth] = read_c(dt + kDepth - 1);
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-                    oacc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fv[dt % kDepth], pf[ht], oacc[ht][dt], 0, 0, 0);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fv[dt % kDepth], pf, oacc[dt], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
 
-    // lane (m, g) holds dims 16 dt + 4 g + i of head 16 ht + m
+    // lane (m, g) holds dims 16 dt + 4 g + i of its head
+    float l = lsum;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (nchunks == 1) {
+        const float inv = 1.f / l;
+        float* o = a.out + ((size_t)b * a.nh + head) * kR + 4 * g;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        float l = lsum[ht];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const size_t h = head0 + 16 * ht + m;
-        if (nchunks == 1) {
-            const float inv = 1.f / l;
-            float* o = a.out + ((size_t)b * a.nh + h) * kR + 4 * g;
+        for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[dt] * inv;
+    } else {
+        const size_t sl = ((size_t)b * a.splits + s) * a.nh + head;
+        float* o = a.part_o + sl * kR + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[ht][dt] * inv;
-        } else {
-            const size_t slot = ((size_t)b * a.splits + s) * a.nh + h;
-            float* o = a.part_o + slot * kR + 4 * g;
-#pragma unroll
-            for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[ht][dt];
-            if (g == 0) {
-                a.part_ml[2 * slot] = mref[ht];
-                a.part_ml[2 * slot + 1] = l;
-            }
+        for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[dt];
+        if (g == 0) {
+            a.part_ml[2 * sl] = mref;
+            a.part_ml[2 * sl + 1] = l;
         }
     }
 }
@@ -572,8 +598,8 @@ dab_status call(const dab_mla_config* cfg, const float* q_lat, const float* q_ro
         for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
     const dim3 grid((unsigned)(8 * p.hblocks * ((p.splits + 7) / 8)), (unsigned)p.B);
     hipError_t e;
-    if (p.nw == 4) e = launch(mla_chunk_kernel<1, 4>, grid, dim3(256), s, ev[0], ev[1], a);
-    else e = launch(mla_chunk_kernel<1, 1>, grid, dim3(64), s, ev[0], ev[1], a);
+    if (p.nw == 4) e = launch(mla_chunk_kernel<4>, grid, dim3(256), s, ev[0], ev[1], a);
+    else e = launch(mla_chunk_kernel<1>, grid, dim3(64), s, ev[0], ev[1], a);
     if (e == hipSuccess) e = hipGetLastError();
     if ((st = hip_status(e)) != DAB_OK) return st;
     e = launch(mla_merge_kernel, dim3((unsigned)(p.nh / 2), (unsigned)p.B), dim3(kMergeThreads), s, ev[2], ev[3], a);
