@@ -422,22 +422,44 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
 }
 
 // Merge of one sequence's chunks for two heads (grid: nh / 2 x B): weights
-// exp2(m_c - M) with M the largest chunk reference, in chunk order.
+// exp2(m_c - M) with M the largest chunk reference, in chunk order.  The
+// chunks' statistics and partial rows are requested kMergeBatch at a time,
+// all in flight together, before any of them is used.
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
     const int b = blockIdx.y, h = 2 * blockIdx.x + (threadIdx.x >> 7), d = 4 * (threadIdx.x & 127);
     int p, len, nchunks;
     if (!seq_range(a, b, &p, &len, &nchunks) || nchunks == 1) return;
     const size_t slot0 = (size_t)b * a.splits * a.nh + h, stride = a.nh;
     float M = -INFINITY;
-    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, a.part_ml[2 * (slot0 + c * stride)]);
+    for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
+        float mm[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+            mm[u] = c0 + u < nchunks ? a.part_ml[2 * (slot0 + (c0 + u) * stride)] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, mm[u]);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-        const size_t slot = slot0 + c * stride;
-        const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * slot] - M);
-        den = fmaf(w, a.part_ml[2 * slot + 1], den);
-        const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + slot * kR + d);
-        acc += w * o;
+    for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
+        float mm[kMergeBatch], ll[kMergeBatch];
+        f32x4 oo[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const size_t slot = slot0 + (size_t)min(c0 + u, nchunks - 1) * stride;
+            mm[u] = a.part_ml[2 * slot];
+            ll[u] = a.part_ml[2 * slot + 1];
+            oo[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * kR + d);
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+            if (c0 + u < nchunks) {
+                const float w = __builtin_amdgcn_exp2f(mm[u] - M);
+                den = fmaf(w, ll[u], den);
+                acc += w * oo[u];
+            }
     }
     *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.nh + h) * kR + d) = acc * (1.f / den);
 }
