@@ -32,12 +32,14 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
-from attention_block_amd.inputs import (CONFIGS, FFN_CONFIGS, HEADLINE, BlockConfig, FfnConfig,  # noqa: E402
-                                        algorithmic_bytes, algorithmic_flops, ffn_algorithmic_bytes,
-                                        ffn_algorithmic_flops, layer_ffn, positions)
+from attention_block_amd.inputs import (CONFIGS, FFN_CONFIGS, HEADLINE, MLA_CONFIGS, BlockConfig,  # noqa: E402
+                                        FfnConfig, MlaConfig, algorithmic_bytes, algorithmic_flops,
+                                        ffn_algorithmic_bytes, ffn_algorithmic_flops, layer_ffn,
+                                        mla_algorithmic_bytes, mla_algorithmic_flops, positions)
 
 METRIC = "µs per decode block step and achieved HBM GB/s (% of peak), 7B layer bs1 4K"
 FFN_METRIC = "µs per FFN half-layer decode step and achieved HBM GB/s (% of peak)"
+MLA_METRIC = "µs per latent-attention (MLA) decode step and achieved HBM GB/s (% of peak)"
 CHAIN_METRIC = "µs per token through a chain of synthetic decoder layers (attention block + FFN each)"
 PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 1024 * 1024
@@ -192,7 +194,8 @@ KERNEL_PHASES = [("fused_kernel", "decode_block_fused"),
                  ("qkv_kernel", "qkv_rmsnorm_rope_append"), ("attn_kernel", "attention_split_kv"),
                  ("oproj_kernel", "oproj_residual"), ("merge_kernel", "attention_merge"),
                  ("ffn_gate_up_kernel", "ffn_rmsnorm_gate_up_silu"),
-                 ("ffn_down_kernel", "ffn_down_residual")]
+                 ("ffn_down_kernel", "ffn_down_residual"),
+                 ("mla_chunk_kernel", "mla_chunk"), ("mla_merge_kernel", "mla_merge")]
 
 
 def ffn_phase_bytes(cfg: FfnConfig) -> dict:
@@ -202,6 +205,12 @@ def ffn_phase_bytes(cfg: FfnConfig) -> dict:
     # hidden is counted with the first kernel, out with the second
     return {"ffn_rmsnorm_gate_up_silu": s * 2 * H * F + s * H + s * B * H,
             "ffn_down_residual": s * H * F + s * B * H}
+
+
+def mla_phase_bytes(cfg: MlaConfig, pos) -> dict:
+    """Algorithmic bytes of the two latent-attention kernels: the chunk kernel moves all of them (cache rows,
+    q, the new rows read and appended, the output), the merge kernel only workspace partials."""
+    return {"mla_chunk": mla_algorithmic_bytes(cfg, pos), "mla_merge": 0}
 
 
 def phase_of(kernel_name: str):
@@ -224,6 +233,9 @@ def summarize_profiles(kt_dir: str, fetch_dir: str, write_dir: str, workload: st
     import csv
     if workload in FFN_CONFIGS:
         pb = ffn_phase_bytes(FFN_CONFIGS[workload])
+    elif workload in MLA_CONFIGS:
+        mc = MLA_CONFIGS[workload]
+        pb = mla_phase_bytes(mc, np.full(mc.batch, mc.pos))
     else:
         pb = phase_bytes(CONFIGS[workload], positions(CONFIGS[workload], 0))
     digest = source_digest()
@@ -508,6 +520,118 @@ def bench_ffn(args, dev) -> int:
     return 0
 
 
+def make_mla_set(cfg: MlaConfig, cap: int, gen, device):
+    import torch
+    B, nh, R, P = cfg.batch, cfg.n_heads, cfg.kv_lora_rank, cfg.rope_dim
+
+    def randn(*shape, scale=1.0, dt=torch.bfloat16):
+        return (torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * scale).to(dt)
+
+    ls = {"q_lat": randn(B, nh, R, scale=0.5, dt=torch.float32), "q_rope": randn(B, nh, P, dt=torch.float32),
+          "c_new": randn(B, R), "kr_new": randn(B, P),
+          "c_cache": torch.zeros(B, cap, R, dtype=torch.bfloat16, device=device),
+          "kr_cache": torch.zeros(B, cap, P, dtype=torch.bfloat16, device=device),
+          "pos": torch.full((B,), cfg.pos, dtype=torch.int32, device=device)}
+    ls["c_cache"][:, :cfg.pos] = randn(B, cfg.pos, R)
+    ls["kr_cache"][:, :cfg.pos] = randn(B, cfg.pos, P)
+    ls["out"] = torch.empty(B, nh, R, dtype=torch.float32, device=device)
+    return ls
+
+
+def mla_cpu_baseline(cfg: MlaConfig, seed: int, budget_s: float) -> dict:
+    """The fp64 latent-attention oracle on the host, on whole sequences of this workload."""
+    import oracle
+    from attention_block_amd.inputs import make_mla_inputs
+    one = MlaConfig(cfg.name, 1, cfg.n_heads, cfg.pos, cfg.kv_lora_rank, cfg.rope_dim, cfg.softmax_scale, cfg.dtype)
+    inp = make_mla_inputs(one, seed)
+    host = host_cpu()
+    with blas_threads(host["cores"]):
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            oracle.mla_decode_from_inputs(inp)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > budget_s or len(times) >= 200:
+                break
+    med = float(np.median(times)) * cfg.batch
+    return {"value": med * 1e6, "unit": "us/step", "cores": host["cores"], "cpu_model": host["model"],
+            "kind": "oracle",
+            "sample": f"{len(times)} single-sequence {cfg.name} steps (seed {seed}) of the fp64 numpy MLA "
+                      f"oracle (bf16 upcast included), median x batch {cfg.batch}; BLAS threads = cores"}
+
+
+def bench_mla(args, dev) -> int:
+    """Latent attention decode (chunk kernel + merge kernel), one JSON line."""
+    import torch
+    import attention_block_amd as ab
+    cfg = MLA_CONFIGS[args.config]
+    pos = np.full(cfg.batch, cfg.pos)
+    cap = max(args.cap, cfg.pos + 1)
+    nbytes = mla_algorithmic_bytes(cfg, pos)
+    flops = mla_algorithmic_flops(cfg, pos)
+    R = max(3, math.ceil(2 * MALL_BYTES / nbytes) + 1)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2468 + args.seed)
+    sets = [make_mla_set(cfg, cap, gen, dev) for _ in range(R)]
+    c = ab.DabMlaConfig(cfg.batch, cfg.n_heads, cfg.kv_lora_rank, cfg.rope_dim, cap, cfg.softmax_scale, args.kv_chunk)
+    ws = ab.Workspace(ab.mla_workspace_size(c), dev)
+    phases = list(ab.MLA_PHASES)
+
+    def step(i, events=None):
+        s = sets[i % R]
+        a = (s["q_lat"], s["q_rope"], s["c_new"], s["kr_new"], s["c_cache"], s["kr_cache"], s["pos"],
+             cfg.softmax_scale)
+        if events is None:
+            ab.mla_decode_attn(*a, kv_chunk=args.kv_chunk, out=s["out"], workspace=ws)
+        else:
+            ab.mla_decode_attn_timed(events, *a, kv_chunk=args.kv_chunk, out=s["out"], workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if ab.read_device_error(ws) != 0:
+        print("device error flag raised during warm-up", file=sys.stderr)
+        return 1
+    us = graph_time(step, args.steps, R)
+    phase_us = None if args.no_phase_timing else event_phase_times(step, len(phases), args.steps)
+    pb = mla_phase_bytes(cfg, pos)
+    roofline = phase_report = None
+    if phase_us is not None:
+        k = max(range(len(phases)), key=lambda i: phase_us[i])
+        dom = phases[k]
+        ach = pb[dom] / (phase_us[k] * 1e-6) / 1e9
+        # 240 flops per byte at 128 heads: below the bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312), so HBM bounds it
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_GBPS, 4), "traffic": measured_traffic(dom, cfg.name), "kernel": dom,
+                    "bytes_per_launch": pb[dom], "avg_launch_us": round(phase_us[k], 3),
+                    "mfma_tflops": round(flops / (phase_us[k] * 1e-6) / 1e12, 1)}
+        phase_report = {n: {"us": round(phase_us[i], 3), "bytes": pb[n],
+                            "gbps": round(pb[n] / (phase_us[i] * 1e-6) / 1e9, 1)} for i, n in enumerate(phases)}
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+    cpu = None if args.no_cpu_baseline else mla_cpu_baseline(cfg, args.seed, args.cpu_budget)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    line = {
+        "metric": MLA_METRIC, "value": round(us, 3), "unit": "us/step", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "heads": cfg.n_heads, "kv_lora_rank": cfg.kv_lora_rank,
+                   "rope_dim": cfg.rope_dim, "kv_tokens": cfg.pos, "cache_capacity": cap, "layer_sets": R,
+                   "kv_chunk": args.kv_chunk, "parallelism": "single GPU", "schedule": "+".join(phases)},
+        "hbm_gbps": round(gbps, 1), "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+        "roofline": roofline, "phases": phase_report, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_chain(args, dev) -> int:
     """--layers N: one token through N decoder layers, each the attention block of --config followed by
     its FFN (distinct weights and caches per layer; layer l's output is layer l + 1's input), all N
@@ -589,8 +713,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default=HEADLINE, choices=sorted(CONFIGS) + sorted(FFN_CONFIGS),
-                    help="a decode attention block workload, or an FFN half-layer workload (*_ffn_*)")
+    ap.add_argument("--config", default=HEADLINE,
+                    choices=sorted(CONFIGS) + sorted(FFN_CONFIGS) + sorted(MLA_CONFIGS),
+                    help="a decode attention block workload, an FFN half-layer workload (*_ffn_*), or a "
+                         "latent-attention (MLA) workload (*_mla_*)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0,
                     help="time one token through this many decoder layers (attention block of --config + its "
@@ -640,6 +766,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.config in FFN_CONFIGS:
         return bench_ffn(args, dev)
+    if args.config in MLA_CONFIGS:
+        return bench_mla(args, dev)
     if args.layers > 0:
         return bench_chain(args, dev)
     cfg = CONFIGS[args.config]
