@@ -702,7 +702,13 @@ def bench_chain(args, dev) -> int:
         "hbm_gbps": round(gbps, 1), "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         "algorithmic_bytes": nbytes, "us_per_layer": round(us / N, 3),
         "algorithmic_flops": N * (algorithmic_flops(cfg, pos) + ffn_algorithmic_flops(fcfg)),
-        "roofline": None, "cpu_baseline": cpu,
+        # per-kernel events are not taken through the chain's graph: the entry covers the whole token
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_GBPS, 4), "traffic": None,
+                     "kernel": f"whole token: {N} layers x (" + "+".join(ab.phase_names(acfg)) + " | " +
+                               "+".join(ab.FFN_PHASES) + ")", "bytes_per_launch": nbytes,
+                     "avg_launch_us": round(us, 3)},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
