@@ -69,7 +69,7 @@ constexpr int kPieces = kKD / 8;         // 16-byte pieces per token row (64 lat
 #endif
 constexpr int kDepth = DAB_MLA_DEPTH;    // operand fragments in flight (LDS reads ahead of their MFMA)
 constexpr float kLazy = 8.f;             // the softmax reference moves when a score passes it by 2^8
-constexpr int kMergeThreads = 256;       // two heads x 128 threads of four dims
+constexpr int kMergeHeadThreads = 128;   // threads per head in the merge: four dims each
 constexpr int kMaxHeads = 1024;
 constexpr int kMaxChunk = 65536;
 
@@ -421,40 +421,43 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
     }
 }
 
-// Merge of one sequence's chunks for two heads (grid: nh / 2 x B): weights
-// exp2(m_c - M) with M the largest chunk reference, in chunk order.  The
-// chunks' statistics and partial rows are requested kMergeBatch at a time,
-// all in flight together, before any of them is used.
-constexpr int kMergeBatch = 8;
-
-__global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
-    const int b = blockIdx.y, h = 2 * blockIdx.x + (threadIdx.x >> 7), d = 4 * (threadIdx.x & 127);
+// Merge of one sequence's chunks for HEADS heads (grid: nh / HEADS x B):
+// weights exp2(m_c - M) with M the largest chunk reference, in chunk order.
+// The chunks' statistics and partial rows are requested BATCH at a time, all
+// in flight together, before any of them is used.  Few workgroups (batch 1:
+// 128 heads) take one head and 16 chunks at a time, many take two heads and 8
+// (DeepSeek-V3 shape on MI355X: bs1 16K merge 24.0 -> 20.1 us with the
+// former; bs16 4K 7.3 us with the latter against 8.5 with the former).
+template <int HEADS, int BATCH>
+__global__ __launch_bounds__(HEADS * kMergeHeadThreads) void mla_merge_kernel(MlaArgs a) {
+    const int b = blockIdx.y, h = HEADS * blockIdx.x + threadIdx.x / kMergeHeadThreads;
+    const int d = 4 * (threadIdx.x % kMergeHeadThreads);
     int p, len, nchunks;
     if (!seq_range(a, b, &p, &len, &nchunks) || nchunks == 1) return;
     const size_t slot0 = (size_t)b * a.splits * a.nh + h, stride = a.nh;
     float M = -INFINITY;
-    for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
-        float mm[kMergeBatch];
+    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
+        float mm[BATCH];
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u)
+        for (int u = 0; u < BATCH; ++u)
             mm[u] = c0 + u < nchunks ? a.part_ml[2 * (slot0 + (c0 + u) * stride)] : -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, mm[u]);
+        for (int u = 0; u < BATCH; ++u) M = fmaxf(M, mm[u]);
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
-        float mm[kMergeBatch], ll[kMergeBatch];
-        f32x4 oo[kMergeBatch];
+    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
+        float mm[BATCH], ll[BATCH];
+        f32x4 oo[BATCH];
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
+        for (int u = 0; u < BATCH; ++u) {
             const size_t slot = slot0 + (size_t)min(c0 + u, nchunks - 1) * stride;
             mm[u] = a.part_ml[2 * slot];
             ll[u] = a.part_ml[2 * slot + 1];
             oo[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * kR + d);
         }
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u)
+        for (int u = 0; u < BATCH; ++u)
             if (c0 + u < nchunks) {
                 const float w = __builtin_amdgcn_exp2f(mm[u] - M);
                 den = fmaf(w, ll[u], den);
@@ -624,7 +627,12 @@ dab_status call(const dab_mla_config* cfg, const float* q_lat, const float* q_ro
     else e = launch(mla_chunk_kernel<1>, grid, dim3(64), s, ev[0], ev[1], a);
     if (e == hipSuccess) e = hipGetLastError();
     if ((st = hip_status(e)) != DAB_OK) return st;
-    e = launch(mla_merge_kernel, dim3((unsigned)(p.nh / 2), (unsigned)p.B), dim3(kMergeThreads), s, ev[2], ev[3], a);
+    if ((int64_t)p.B * p.nh < 1024)
+        e = launch(mla_merge_kernel<1, 16>, dim3((unsigned)p.nh, (unsigned)p.B), dim3(kMergeHeadThreads), s, ev[2],
+                   ev[3], a);
+    else
+        e = launch(mla_merge_kernel<2, 8>, dim3((unsigned)(p.nh / 2), (unsigned)p.B), dim3(2 * kMergeHeadThreads), s,
+                   ev[2], ev[3], a);
     if (e == hipSuccess) e = hipGetLastError();
     return hip_status(e);
 }
