@@ -373,10 +373,14 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 
 hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev) {
 #ifdef DAB_TRACE
-    StepArgs t = a;   // phases trace at consecutive item numbers: QKV, attention, output
-    // consecutive item numbers: QKV, attention, output projection
-    const bool oproj_only = phase == 2 || (phase == 1 && p.schedule == DAB_SCHEDULE_QKV_ATTN);
-    t.trace_base = phase == 0 ? 0 : oproj_only ? p.qkv.grid + p.attn_grid : p.qkv.grid;
+    // phases trace at consecutive item numbers: QKV, attention, output
+    // projection, then the merge kernel's workgroups (phased, split merge)
+    StepArgs t = a;
+    const bool merge = p.split_merge && phase == 2;
+    const bool oproj_only = (phase == 2 && !p.split_merge) || phase == 3 ||
+                            (phase == 1 && p.schedule == DAB_SCHEDULE_QKV_ATTN);
+    t.trace_base = phase == 0 ? 0 : merge ? p.qkv.grid + p.attn_grid + p.oproj.grid
+                 : oproj_only ? p.qkv.grid + p.attn_grid : p.qkv.grid;
     return p.dtype == DAB_BF16 ? launch_phase_bf16(t, p, phase, s, ev) : launch_phase_f32(t, p, phase, s, ev);
 #else
     return p.dtype == DAB_BF16 ? launch_phase_bf16(a, p, phase, s, ev) : launch_phase_f32(a, p, phase, s, ev);
@@ -390,6 +394,17 @@ extern "C" {
 #ifdef DAB_TRACE
 // Profiling builds only: device buffer of [grid, 4] timestamps for later calls (null: off).
 void dab_trace_set_buffer(void* p) { g_trace = static_cast<unsigned long long*>(p); }
+// Profiling builds only: workgroups of the QKV, attention, output projection and merge kernels.
+dab_status dab_trace_layout(const dab_config* cfg, int32_t* grids) {
+    Plan p;
+    const dab_status st = plan(cfg, &p);
+    if (st != DAB_OK) return st;
+    grids[0] = p.qkv.grid;
+    grids[1] = p.attn_grid;
+    grids[2] = p.oproj.grid;
+    grids[3] = p.split_merge ? p.B * p.nq : 0;
+    return DAB_OK;
+}
 #endif
 
 size_t dab_workspace_size(const dab_config* cfg) {

@@ -118,6 +118,12 @@ EDGE = [
     ("group 6 f32", small_cfg("g6f", 2, 768, 12, 2, 128, "f32"), 300, [299, 1], 64),
     ("group 7 bf16", small_cfg("g7b", 2, 896, 14, 2, 64, "bf16"), 300, [299, 0], 32),
     ("group 7 f32 merge kernel", small_cfg("g7f", 1, 896, 14, 2, 64, "f32", 5e5), 2100, [2000], 32),
+    # the merge kernel over ragged batches: 160 heads of 47 chunks (bf16), 144 heads of 79 chunks (fp32,
+    # D 64: four chunk sums per output)
+    ("merge kernel ragged bf16", small_cfg("mk1", 5, 512, 32, 8, 128, "bf16", 5e5), 3000,
+     [2999, 100, 2048, 1500, 64], 64),
+    ("merge kernel ragged f32 d64", small_cfg("mk2", 9, 256, 16, 4, 64, "f32"), 2500,
+     [2499, 0, 2048, 17, 1200, 2400, 2450, 33, 1600], 32),
 ]
 
 
