@@ -611,5 +611,29 @@ __device__ void mfma_res_panel(const StepArgs& a, int panel, int bgi, MfmaResLds
         [&](int sq) { return lds.ss[sq]; });
 }
 
+// Streamed panel (dab_mfma.h MfmaStream): 512 threads, 16 or 32 sequences,
+// K = 1024 NWIN.
+template <bool QKV, int TILES, int NG, int NWIN>
+__device__ void mfma_str_panel(const StepArgs& a, int panel, int bgi, MfmaStrLds<TILES, NG>& lds) {
+    constexpr int NS = 16 * NG;
+    const int K = QKV ? a.H : a.n_q;
+    const uint16_t* W = static_cast<const uint16_t*>(QKV ? a.w_qkv : a.w_o);
+    const MfmaRows mr(a, QKV, panel, TILES);
+    MfmaStream<TILES, NG, QKV, NWIN> core;
+    DAB_TRACE_POINT(a, 1);
+    core.run([&](int tl, int r) { return W + (size_t)(QKV ? mr.qkv_row(a, tl, r) : panel * 16 * TILES + tl * 16 + r) * K; },
+             [&](int n) { return mfma_xrow<QKV>(a, bgi * NS + n); }, static_cast<const uint16_t*>(a.norm_w), K, lds,
+#ifdef DAB_TRACE
+             a.trace ? a.trace + (size_t)(a.trace_base + blockIdx.x) * 8 : nullptr
+#else
+             nullptr
+#endif
+    );
+    DAB_TRACE_POINT(a, 2);
+    mfma_finish<QKV, TILES, NG, kMfmaStrThreads>(
+        a, panel, bgi, mr, [&](int tl, int g, int r, int n) { return mfma_str_sum(lds, tl, g, r, n); },
+        [&](int sq) { return mfma_str_ssq(lds, sq); });
+}
+
 }  // namespace dev
 }  // namespace dab

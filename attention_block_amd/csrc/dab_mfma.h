@@ -37,6 +37,53 @@ __device__ inline bf16x8 as_bf16x8(const u32x4& v) {
     return r;
 }
 
+// ---------------------------------------------------------------------------
+// direct loads into LDS (global_load_lds_dwordx4) and their waits
+// ---------------------------------------------------------------------------
+//
+// Issued from inline asm: the compiler's builtin for them makes it wait for
+// every load in flight (vmcnt(0)) before any LDS read it cannot prove
+// disjoint.  The kernels that use them count their own loads: wait_vm<N>
+// leaves the N most recent in flight.
+
+template <int N>
+__device__ inline void wait_vm() {
+    // s_waitcnt vmcnt(N), expcnt and lgkmcnt left alone
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0): this wave's LDS reads done
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// 16 bytes per lane from src into LDS at byte lds + 16 * lane (lds wave-uniform).  M0 holds the LDS
+// address; no other instruction of the kernels here uses M0 (no dynamic register indexing, no message
+// or GDS instructions), so setting it in the asm is safe.  The load has no register result.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void lds_load16(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ inline uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Four 16-bit values of a transposing LDS read (ds_read_b64_tr_b16): in each
+// 16-lane group, lane i receives element i % 4 of the 8 bytes addressed by
+// lanes 4j + i / 4 of its group, j = 0..3.
+__device__ inline v4i16 read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)((__attribute__((address_space(3))) char*)(p)));
+}
+
 constexpr int kMfmaThreads = 256;                   // four waves
 // K values per stage: kMfmaSub 1 KB loads per weight row (1024 measured no faster for the 8B layer at
 // batch 16 on MI355X, and slower for its FFN)
@@ -341,6 +388,240 @@ __device__ inline float mfma_res_sum(const MfmaResLds<TILES>& lds, int tile, int
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < kMfmaResWaves; ++w) s += lds.c[w][tile][r][n];
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// The streamed panel: 16 or 32 sequences, K a multiple of 1024, at most 4096
+// ---------------------------------------------------------------------------
+//
+// Eight waves; wave w owns K values [w K/8, (w + 1) K/8) of every row of the
+// panel.  Its batch fragments for those K values (sequence 16 g + i % 16,
+// 8 values at 8 (i / 16) of each 32-value step), and with the RMSNorm its
+// norm_w fragments, are loaded once into registers, so no LDS holds the
+// batch operand and no barrier stages it.  The weight rows go through LDS by
+// direct loads (global_load_lds_dwordx4): a window is 128 K values (256
+// bytes) of a tile's 16 rows, four loads of 4 rows x 256 bytes, each row's
+// 16-byte pieces XOR-swizzled by the row (piece c of row r at c ^ r) so that
+// the operand reads (16 rows, one piece each) hit distinct banks.  Each wave
+// keeps mfma_str_ring windows in flight in a ring of its own, waits for the
+// oldest with s_waitcnt vmcnt, reads its operands, runs its four steps and
+// requests the next window into the freed slot: no barrier in the stream.
+// The direct loads use the compiler's builtin, so its own waits for the
+// batch fragments (requested first) count them and wait for nothing else;
+// the ring is read from inline asm (the four reads and their wait in one
+// block), so the compiler sees no LDS read that could alias a load in flight
+// and adds no wait for every load before it.
+// The waves' partial tiles are summed in wave order through LDS.
+
+constexpr int kMfmaStrWaves = 8;
+constexpr int kMfmaStrThreads = 64 * kMfmaStrWaves;
+constexpr int kMfmaStrWin = 128;                   // K values of a window
+// Windows in flight per wave: two (8B layer, batch 16, on MI355X: QKV projection 14.3, 14.9, 15.2 and
+// 15.4 us with one, two, three and four; output projection 9.4, 9.0, 9.7 and 10.1 us; a read probe of the
+// same pattern without the matrix work: 10.5 us with two, 13.6 with four).  The batch and norm_w
+// fragments are requested before the stream's first loads (after them measured no faster).
+template <int NG> constexpr int mfma_str_ring() { return 2; }
+constexpr int kMfmaStrMaxK = 4096;
+constexpr int kMfmaStrSteps = kMfmaStrMaxK / kMfmaStrWaves / 32;   // 32-value steps per wave at most
+
+template <int TILES, int NG>
+struct MfmaStrLds {
+    union {
+        u32x4 ring[kMfmaStrWaves][mfma_str_ring<NG>()][256];   // per wave: windows of 16 rows x 256 bytes
+        float c[kMfmaStrWaves][TILES][NG][16][17];         // partial tiles, after the stream
+    };
+    float ss[kMfmaStrWaves][16 * NG];                      // NORM: per-wave sums of x^2
+};
+
+// Four 16-byte LDS reads (byte addresses) and their wait, in one block.
+__device__ inline void lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4& r0, u32x4& r1, u32x4& r2,
+                                 u32x4& r3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+
+template <int TILES, int NG, bool NORM, int NWIN>
+struct MfmaStream {
+    static_assert(NWIN >= 1 && NWIN * kMfmaStrWin * kMfmaStrWaves <= kMfmaStrMaxK, "K = 1024 NWIN");
+    static constexpr int RING = mfma_str_ring<NG>();
+    f32x4 acc[TILES][NG];
+
+    // rowp(tile, r): weight row r of a tile; xrow(n): batch row n of the workgroup (nullptr past the
+    // batch: zeros); norm_w: the RMSNorm weights (NORM).  K = 1024 NWIN (every loop and wait static).
+    // Ends with the partial tiles in lds.c and the per-wave sums of x^2 in lds.ss, after a barrier.
+    // trace: profiling builds only, this workgroup's timestamp slots (stage ends at 4 and 5), or null.
+    template <class ROWP, class XROW>
+    __device__ void run(ROWP rowp, XROW xrow, const uint16_t* norm_w, int K, MfmaStrLds<TILES, NG>& lds,
+                        unsigned long long* trace = nullptr) {
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+        const int m = lane & 15, kg = lane >> 4;
+        (void)K;
+        constexpr int ks = NWIN * kMfmaStrWin, nsteps = ks / 32, nwin = NWIN, nw_all = TILES * NWIN;
+        const int k0 = wave * ks;                                 // this wave's K values
+        // 1. this wave's batch fragments (raw) and norm_w fragments, requested first, without branches
+        // (rows past the batch read a valid address, and are zeroed after); w00 also serves the windows
+        // past the panel's (see issue)
+        const uint16_t* w00 = rowp(0, 0);
+        u32x4 xf[NG][nsteps];
+        bool xlive[NG];
+        u32x4 nf[NORM ? nsteps : 1];
+        auto load_x = [&]() {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint16_t* xr = xrow(16 * g + m);
+                xlive[g] = xr != nullptr;
+                const uint16_t* xb = xr ? xr + k0 + 8 * kg : w00;
+#pragma unroll
+                for (int s = 0; s < nsteps; ++s) xf[g][s] = *reinterpret_cast<const u32x4*>(xb + (xr ? 32 * s : 0));
+            }
+            if constexpr (NORM) {
+#pragma unroll
+                for (int s = 0; s < nsteps; ++s) nf[s] = *reinterpret_cast<const u32x4*>(norm_w + k0 + 32 * s + 8 * kg);
+            }
+        };
+        load_x();
+        // 2. the first windows of weight rows in flight: window j is tile j / nwin, K values
+        // k0 + 128 (j % nwin) ..; load q of a window takes rows 4q .. 4q + 3, lane i row 4q + i / 16 and
+        // piece (i % 16) ^ row, so that the piece lands at (i % 16) = piece ^ row.  (A window past the
+        // panel's: see issue.)
+        const uint16_t* src[TILES][4];
+#pragma unroll
+        for (int tl = 0; tl < TILES; ++tl)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 4 * q + (lane >> 4);
+                src[tl][q] = rowp(tl, r) + k0 + 8 * ((lane & 15) ^ r);
+            }
+        // Window j past the panel's: every lane reads the same 16 bytes (one cached line), so that each
+        // window of the panel waits for the same count of loads in flight behind it; never read.
+        auto issue = [&](int j) {
+            const int tj = j / nwin, kw = j - tj * nwin;
+            u32x4* dst = &lds.ring[wave][j % RING][0];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint16_t* sp = src[0][q];
+#pragma unroll
+                for (int tl = 1; tl < TILES; ++tl)
+                    if (tj == tl) sp = src[tl][q];
+                __builtin_amdgcn_global_load_lds(j < nw_all ? sp + kMfmaStrWin * kw : w00,
+                                                 (__attribute__((address_space(3))) void*)(
+                                                     (__attribute__((address_space(3))) char*)(dst + 64 * q)),
+                                                 16, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < RING; ++j) issue(j);
+        // nothing below moves above the stream's first loads
+        __builtin_amdgcn_sched_barrier(0);
+        float ssq[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) ssq[g] = 0.f;
+#ifdef DAB_TRACE
+        if (trace && t == 0) trace[4] = __builtin_amdgcn_s_memrealtime();
+#endif
+        // 4. the windows: wait for the oldest, read its operands, four steps, request the next into its slot
+#pragma unroll
+        for (int tl = 0; tl < TILES; ++tl)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[tl][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t ring0 = lds_address(&lds.ring[wave][0][0]);
+        uint32_t rd[4];                                          // this lane's operand pieces in a slot
+#pragma unroll
+        for (int s = 0; s < 4; ++s) rd[s] = 16u * (uint32_t)((m >> 2) * 64 + (m & 3) * 16 + (((4 * s + kg) ^ m) & 15));
+#pragma unroll
+        for (int tl = 0; tl < TILES; ++tl) {
+#pragma unroll
+            for (int kw = 0; kw < NWIN; ++kw) {
+                {
+                    const int j = tl * nwin + kw;
+                    wait_vm<4 * (RING - 1)>();
+                    __builtin_amdgcn_sched_barrier(0);  // nothing that uses this window moves above the wait
+                    const uint32_t slot = ring0 + (uint32_t)(j % RING) * 4096u;
+                    u32x4 w[4];
+                    lds_read4(slot + rd[0], slot + rd[1], slot + rd[2], slot + rd[3], w[0], w[1], w[2], w[3]);
+                    // first tile: the window's batch steps are zeroed past the batch and, NORM, become
+                    // x .* norm_w rounded to bf16 with the sums of x^2 taken on the way (here, after the
+                    // wait above, so that the compiler's own wait for these fragments does not wait for
+                    // the whole stream)
+                    if (tl == 0) {
+#pragma unroll
+                        for (int s = 4 * kw; s < 4 * kw + 4; ++s)
+#pragma unroll
+                            for (int g = 0; g < NG; ++g)
+                                if (!xlive[g]) xf[g][s] = u32x4{0u, 0u, 0u, 0u};
+                    }
+                    if constexpr (NORM) {
+                        if (tl == 0) {
+#pragma unroll
+                            for (int s = 4 * kw; s < 4 * kw + 4; ++s)
+#pragma unroll
+                                for (int g = 0; g < NG; ++g)
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) {
+                                        const float x0 = __uint_as_float(xf[g][s][e] << 16);
+                                        const float x1 = __uint_as_float(xf[g][s][e] & 0xffff0000u);
+                                        ssq[g] = fmaf(x0, x0, ssq[g]);
+                                        ssq[g] = fmaf(x1, x1, ssq[g]);
+                                        xf[g][s][e] = pack_bf16x2(x0 * __uint_as_float(nf[s][e] << 16),
+                                                                  x1 * __uint_as_float(nf[s][e] & 0xffff0000u));
+                                    }
+                        }
+                    }
+                    issue(j + RING);            // into the slot just read (its reads are done)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int g = 0; g < NG; ++g)
+                            acc[tl][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[s]), as_bf16x8(xf[g][4 * kw + s]),
+                                                                                  acc[tl][g], 0, 0, 0);
+                }
+            }
+        }
+        // 5. partial tiles and sums of x^2 to LDS (over the ring, which no wave reads any more)
+#ifdef DAB_TRACE
+        if (trace && t == 0) trace[5] = __builtin_amdgcn_s_memrealtime();
+#endif
+        __syncthreads();
+#pragma unroll
+        for (int tl = 0; tl < TILES; ++tl)
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lds.c[wave][tl][g][4 * kg + j][m] = acc[tl][g][j];
+        if constexpr (NORM) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                float v = ssq[g];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                if (lane < 16) lds.ss[wave][16 * g + lane] = v;
+            }
+        }
+        __syncthreads();
+    }
+};
+
+template <int TILES, int NG>
+__device__ inline float mfma_str_sum(const MfmaStrLds<TILES, NG>& lds, int tile, int g, int r, int n) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMfmaStrWaves; ++w) s += lds.c[w][tile][g][r][n];
+    return s;
+}
+
+template <int TILES, int NG>
+__device__ inline float mfma_str_ssq(const MfmaStrLds<TILES, NG>& lds, int sq) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMfmaStrWaves; ++w) s += lds.ss[w][sq];
     return s;
 }
 

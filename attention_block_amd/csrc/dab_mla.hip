@@ -53,6 +53,11 @@ using dev::as_bf16x8;
 using dev::bf16x8;
 using dev::f32x4;
 using dev::u32x4;
+using dev::lds_address;
+using dev::lds_barrier;
+using dev::lds_load16;
+using dev::read_tr16;
+using dev::wait_vm;
 
 constexpr int kR = 512;                  // latent width
 constexpr int kP = 64;                   // rotary key width
@@ -141,44 +146,6 @@ struct TilePipe {
     static_assert((DEPTH - 1) * PER_TILE <= 63, "vmcnt holds at most 63");
     static_assert(KRW * NW * 8 == kTB, "rotary loads must cover the tile");
 };
-
-template <int N>
-__device__ inline void wait_vm() {
-    // s_waitcnt vmcnt(N), expcnt and lgkmcnt left alone
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0): this wave's LDS reads done
-    asm volatile("s_barrier" ::: "memory");
-}
-
-// 16 bytes per lane from src into LDS at byte lds + 16 * lane (lds wave-uniform).  M0 holds the LDS
-// address; no other instruction of the kernels here uses M0 (no dynamic register indexing, no message
-// or GDS instructions), so setting it in the asm is safe.  The load has no register result.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void lds_load16(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
-                 "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ inline uint32_t lds_address(const void* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// Four 16-bit values of a transposing LDS read (ds_read_b64_tr_b16): in each
-// 16-lane group, lane i receives element i % 4 of the 8 bytes addressed by
-// lanes 4j + i / 4 of its group, j = 0..3.
-__device__ inline v4i16 read_tr16(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16*)((__attribute__((address_space(3))) char*)(p)));
-}
 
 // Chunk (sequence blockIdx.y; chunk s, head block hb from blockIdx.x).
 // Workgroups are dispatched to the eight XCDs round-robin by linear index,

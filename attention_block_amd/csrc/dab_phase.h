@@ -261,6 +261,36 @@ __global__ __launch_bounds__(kMfmaResThreads) void mfma_res_kernel(StepArgs a) {
     DAB_TRACE_POINT(a, 3);
 }
 
+template <bool QKV, int TILES, int NG, int NWIN>
+__global__ __launch_bounds__(kMfmaStrThreads) void mfma_str_kernel(StepArgs a) {
+    __shared__ MfmaStrLds<TILES, NG> lds;
+    DAB_TRACE_POINT(a, 0);
+    if constexpr (!QKV) mfma_prologue<false>(a, nullptr, kMfmaStrThreads);
+    const PanelPlanDev& g = QKV ? a.qkv : a.oproj;
+    int panel, bgi;
+    if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi))
+        mfma_str_panel<QKV, TILES, NG, NWIN>(a, panel, bgi, lds);
+    DAB_TRACE_POINT(a, 3);
+}
+
+// The streamed panel applies to 16 or 32 sequences per workgroup and K of
+// 1024, 2048 or 4096.
+inline bool mfma_streamed(const PanelPlan& g) {
+    return (g.nb == 16 || g.nb == 32) && (g.K == 1024 || g.K == 2048 || g.K == 4096);
+}
+
+template <bool QKV, int NWIN>
+void launch_mfma_str(const StepArgs& a, const PanelPlan& g, hipStream_t s, const LaunchEvents& ev) {
+    const dim3 grid(g.grid), block(kMfmaStrThreads);
+    const int key = (g.rows == 32 ? 2 : 0) + (g.nb == 32 ? 1 : 0);
+    switch (key) {
+        case 0: dab_launch((mfma_str_kernel<QKV, 1, 1, NWIN>), grid, block, 0, s, ev, a); break;
+        case 1: dab_launch((mfma_str_kernel<QKV, 1, 2, NWIN>), grid, block, 0, s, ev, a); break;
+        case 2: dab_launch((mfma_str_kernel<QKV, 2, 1, NWIN>), grid, block, 0, s, ev, a); break;
+        default: dab_launch((mfma_str_kernel<QKV, 2, 2, NWIN>), grid, block, 0, s, ev, a); break;
+    }
+}
+
 // The resident-operand panel applies to 16 sequences per workgroup and K a
 // multiple of 256 of at most kMfmaResMaxK.
 inline bool mfma_resident(const PanelPlan& g) {
@@ -275,6 +305,12 @@ hipError_t launch_mfma(const StepArgs& a, const Plan& p, hipStream_t s, const La
         const PanelPlan& g = QKV ? p.qkv : p.oproj;
         const size_t lds = QKV ? (size_t)p.H * 2 : 0;
         const dim3 grid(g.grid);
+        if (mfma_streamed(g)) {
+            if (g.K == 4096) launch_mfma_str<QKV, 4>(a, g, s, ev);
+            else if (g.K == 2048) launch_mfma_str<QKV, 2>(a, g, s, ev);
+            else launch_mfma_str<QKV, 1>(a, g, s, ev);
+            return hipGetLastError();
+        }
         if (mfma_resident(g)) {
             if (g.rows == 32) dab_launch((mfma_res_kernel<QKV, 2>), grid, dim3(kMfmaResThreads), lds, s, ev, a);
             else dab_launch((mfma_res_kernel<QKV, 1>), grid, dim3(kMfmaResThreads), lds, s, ev, a);

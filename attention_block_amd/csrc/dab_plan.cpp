@@ -44,9 +44,11 @@ bool plan_mfma_panel(int K, int N, int batch, bool qkv, int half, PanelPlan* g) 
     if (K % 8 != 0 || N % 16 != 0 || (qkv && half % 8 != 0)) return false;
     const int ng = batch > 16 ? 2 : 1;
     const int nbg = ceil_div(batch, 16 * ng);
-    // two tiles: on the resident-operand panels (16 sequences, K <= 4096, one workgroup per CU) where
-    // that still leaves 192 workgroups, on the staged panels where it leaves 256 (fewer measured slower:
-    // 8B layer, batch 16, output projection 13.2 -> 19.8 us with 128 two-tile panels)
+    // two tiles: on the streamed and resident-operand panels (16 sequences, K <= 4096, one workgroup
+    // per CU) where that still leaves 192 workgroups, on the staged panels where it leaves 256 (fewer
+    // measured slower: 8B layer, batch 16, output projection 13.2 -> 19.8 us with 128 two-tile panels;
+    // its QKV projection on the streamed panel 16.2 us with 192 two-tile panels, 23.2 us with 384
+    // one-tile panels, a round and a half)
     const bool resident = ng == 1 && K <= 4096 && K % 256 == 0;
     const bool two = ng == 1 && N % 32 == 0 && (!qkv || half % 16 == 0) &&
                      (long long)(N / 32) * nbg >= (resident ? 192 : 256);
