@@ -52,6 +52,20 @@ __device__ inline void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(n) for an n the compiler folds to a constant (an unrolled loop's count).
+__device__ inline void wait_vm_n(int n) {
+    switch (n) {
+#define DAB_WAIT_CASE(N) case N: wait_vm<N>(); break;
+        DAB_WAIT_CASE(0) DAB_WAIT_CASE(1) DAB_WAIT_CASE(2) DAB_WAIT_CASE(3) DAB_WAIT_CASE(4) DAB_WAIT_CASE(5)
+        DAB_WAIT_CASE(6) DAB_WAIT_CASE(7) DAB_WAIT_CASE(8) DAB_WAIT_CASE(9) DAB_WAIT_CASE(10) DAB_WAIT_CASE(11)
+        DAB_WAIT_CASE(12) DAB_WAIT_CASE(13) DAB_WAIT_CASE(14) DAB_WAIT_CASE(15) DAB_WAIT_CASE(16)
+        DAB_WAIT_CASE(17) DAB_WAIT_CASE(18) DAB_WAIT_CASE(19) DAB_WAIT_CASE(20) DAB_WAIT_CASE(21)
+        DAB_WAIT_CASE(22) DAB_WAIT_CASE(23) DAB_WAIT_CASE(24)
+#undef DAB_WAIT_CASE
+        default: wait_vm<0>(); break;
+    }
+}
+
 __device__ inline void lds_barrier() {
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0): this wave's LDS reads done
     asm volatile("s_barrier" ::: "memory");
@@ -432,6 +446,7 @@ struct MfmaStrLds {
         float c[kMfmaStrWaves][TILES][NG][16][17];         // partial tiles, after the stream
     };
     float ss[kMfmaStrWaves][16 * NG];                      // NORM: per-wave sums of x^2
+    u32x4 nw[kMfmaStrWaves][64];                           // NORM: each wave's norm_w values
 };
 
 // Four 16-byte LDS reads (byte addresses) and their wait, in one block.
@@ -466,32 +481,37 @@ struct MfmaStream {
         (void)K;
         constexpr int ks = NWIN * kMfmaStrWin, nsteps = ks / 32, nwin = NWIN, nw_all = TILES * NWIN;
         const int k0 = wave * ks;                                 // this wave's K values
-        // 1. this wave's batch fragments (raw) and norm_w fragments, requested first, without branches
-        // (rows past the batch read a valid address, and are zeroed after); w00 also serves the windows
-        // past the panel's (see issue)
+        // 1. this wave's batch fragments (raw) and norm_w fragments, four steps at a time, each group
+        // requested just before the weight window that first uses them (all of them at the start, the
+        // panel's first window waited ~4 us for them: every workgroup reads the same batch rows); rows
+        // past the batch read a valid address and are zeroed after
         const uint16_t* w00 = rowp(0, 0);
         u32x4 xf[NG][nsteps];
         bool xlive[NG];
-        u32x4 nf[NORM ? nsteps : 1];
-        auto load_x = [&]() {
+        // NORM: the wave's norm_w values reach its LDS by one direct load with the first window (lane i:
+        // values 8 (i mod ks/8) ..) and are read from there (a load per step and lane read the same 16
+        // bytes 16 times over, and the loads a CU issues are what bound this panel)
+        const uint16_t* xb[NG];
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const uint16_t* xr = xrow(16 * g + m);
-                xlive[g] = xr != nullptr;
-                const uint16_t* xb = xr ? xr + k0 + 8 * kg : w00;
+        for (int g = 0; g < NG; ++g) {
+            const uint16_t* xr = xrow(16 * g + m);
+            xlive[g] = xr != nullptr;
+            xb[g] = xr ? xr + k0 + 8 * kg : w00;
+        }
+        // the batch (and norm_w) fragments of window w of the first tile: its four steps
+        auto load_aux = [&](int w) {
 #pragma unroll
-                for (int s = 0; s < nsteps; ++s) xf[g][s] = *reinterpret_cast<const u32x4*>(xb + (xr ? 32 * s : 0));
-            }
-            if constexpr (NORM) {
+            for (int s = 4 * w; s < 4 * w + 4; ++s) {
 #pragma unroll
-                for (int s = 0; s < nsteps; ++s) nf[s] = *reinterpret_cast<const u32x4*>(norm_w + k0 + 32 * s + 8 * kg);
+                for (int g = 0; g < NG; ++g)
+                    xf[g][s] = *reinterpret_cast<const u32x4*>(xb[g] + (xlive[g] ? 32 * s : 0));
             }
         };
-        load_x();
+        // loads requested per window: its batch fragments (first tile only) and its four weight loads
+        auto count = [&](int w) { return (w < nwin ? 4 * NG : 0) + 4; };
         // 2. the first windows of weight rows in flight: window j is tile j / nwin, K values
         // k0 + 128 (j % nwin) ..; load q of a window takes rows 4q .. 4q + 3, lane i row 4q + i / 16 and
-        // piece (i % 16) ^ row, so that the piece lands at (i % 16) = piece ^ row.  (A window past the
-        // panel's: see issue.)
+        // piece (i % 16) ^ row, so that the piece lands at (i % 16) = piece ^ row
         const uint16_t* src[TILES][4];
 #pragma unroll
         for (int tl = 0; tl < TILES; ++tl)
@@ -500,25 +520,38 @@ struct MfmaStream {
                 const int r = 4 * q + (lane >> 4);
                 src[tl][q] = rowp(tl, r) + k0 + 8 * ((lane & 15) ^ r);
             }
-        // Window j past the panel's: every lane reads the same 16 bytes (one cached line), so that each
-        // window of the panel waits for the same count of loads in flight behind it; never read.
+        // The wait counts below assume the loads go out in program order: the batch fragments of a
+        // window, then its four weight loads; scheduling barriers keep the compiler from moving loads
+        // across a window's weight loads.
         auto issue = [&](int j) {
             const int tj = j / nwin, kw = j - tj * nwin;
             u32x4* dst = &lds.ring[wave][j % RING][0];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint16_t* sp = src[0][q];
 #pragma unroll
                 for (int tl = 1; tl < TILES; ++tl)
                     if (tj == tl) sp = src[tl][q];
-                __builtin_amdgcn_global_load_lds(j < nw_all ? sp + kMfmaStrWin * kw : w00,
+                __builtin_amdgcn_global_load_lds(sp + kMfmaStrWin * kw,
                                                  (__attribute__((address_space(3))) void*)(
                                                      (__attribute__((address_space(3))) char*)(dst + 64 * q)),
                                                  16, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         };
 #pragma unroll
-        for (int j = 0; j < RING; ++j) issue(j);
+        for (int j = 0; j < RING; ++j)
+            if (j < nw_all) {
+                if (j < nwin) load_aux(j);
+                if (NORM && j == 0)
+                    __builtin_amdgcn_global_load_lds(norm_w + k0 + 8 * (lane % (ks / 8)),
+                                                     (__attribute__((address_space(3))) void*)(
+                                                         (__attribute__((address_space(3))) char*)(&lds.nw[wave][0])),
+                                                     16, 0, 0);
+                issue(j);
+            }
+        const uint32_t nw0 = lds_address(&lds.nw[wave][0]);
         // nothing below moves above the stream's first loads
         __builtin_amdgcn_sched_barrier(0);
         float ssq[NG];
@@ -542,7 +575,13 @@ struct MfmaStream {
             for (int kw = 0; kw < NWIN; ++kw) {
                 {
                     const int j = tl * nwin + kw;
-                    wait_vm<4 * (RING - 1)>();
+                    // this window's loads (and every older one) are in: the windows requested after it
+                    // may still be in flight
+                    int later = 0;
+#pragma unroll
+                    for (int w = j + 1; w < j + RING; ++w)
+                        if (w < nw_all) later += count(w);
+                    wait_vm_n(later);
                     __builtin_amdgcn_sched_barrier(0);  // nothing that uses this window moves above the wait
                     const uint32_t slot = ring0 + (uint32_t)(j % RING) * 4096u;
                     u32x4 w[4];
@@ -560,8 +599,13 @@ struct MfmaStream {
                     }
                     if constexpr (NORM) {
                         if (tl == 0) {
+                            u32x4 nfw[4];                     // norm_w of the window's steps (piece 4 s + kg)
+                            lds_read4(nw0 + 16u * (16 * kw + kg), nw0 + 16u * (16 * kw + 4 + kg),
+                                      nw0 + 16u * (16 * kw + 8 + kg), nw0 + 16u * (16 * kw + 12 + kg), nfw[0], nfw[1],
+                                      nfw[2], nfw[3]);
 #pragma unroll
-                            for (int s = 4 * kw; s < 4 * kw + 4; ++s)
+                            for (int s = 4 * kw; s < 4 * kw + 4; ++s) {
+                                const u32x4 nf = nfw[s - 4 * kw];
 #pragma unroll
                                 for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -570,12 +614,16 @@ struct MfmaStream {
                                         const float x1 = __uint_as_float(xf[g][s][e] & 0xffff0000u);
                                         ssq[g] = fmaf(x0, x0, ssq[g]);
                                         ssq[g] = fmaf(x1, x1, ssq[g]);
-                                        xf[g][s][e] = pack_bf16x2(x0 * __uint_as_float(nf[s][e] << 16),
-                                                                  x1 * __uint_as_float(nf[s][e] & 0xffff0000u));
+                                        xf[g][s][e] = pack_bf16x2(x0 * __uint_as_float(nf[e] << 16),
+                                                                  x1 * __uint_as_float(nf[e] & 0xffff0000u));
                                     }
+                            }
                         }
                     }
-                    issue(j + RING);            // into the slot just read (its reads are done)
+                    if (j + RING < nw_all) {            // into the slot just read (its reads are done)
+                        if (j + RING < nwin) load_aux(j + RING);
+                        issue(j + RING);
+                    }
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
 #pragma unroll
