@@ -49,8 +49,12 @@ bool plan_mfma_panel(int K, int N, int batch, bool qkv, int half, PanelPlan* g) 
     // measured slower: 8B layer, batch 16, output projection 13.2 -> 19.8 us with 128 two-tile panels;
     // its QKV projection on the streamed panel 16.2 us with 192 two-tile panels, 23.2 us with 384
     // one-tile panels, a round and a half)
-    const bool resident = ng == 1 && K <= 4096 && K % 256 == 0;
-    const bool two = ng == 1 && N % 32 == 0 && (!qkv || half % 16 == 0) &&
+    // (The streamed panel, K of 1024, 2048 or 4096, takes two tiles with 32 sequences as well: the GQA
+    // layer's ragged batch of 32, QKV projection 25.5 us with 384 one-tile panels, 16.9 us with 192
+    // two-tile panels, on MI355X.)
+    const bool streamed = K == 1024 || K == 2048 || K == 4096;
+    const bool resident = streamed || (ng == 1 && K <= 4096 && K % 256 == 0);
+    const bool two = (ng == 1 || streamed) && N % 32 == 0 && (!qkv || half % 16 == 0) &&
                      (long long)(N / 32) * nbg >= (resident ? 192 : 256);
     g->K = K;
     g->N = N;
