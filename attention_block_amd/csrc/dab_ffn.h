@@ -258,5 +258,33 @@ __device__ void ffn_mfma_panel(const FfnArgs& a, int panel, int bgi, MfmaLds<TIL
     }
 }
 
+// Gate/up on the streamed panel (dab_mfma.h MfmaStream, H = 1024 NWIN): tile
+// 0 rows 16p .. 16p+15 of W_gate, tile 1 the same rows of W_up, 16 or 32
+// sequences; the finish is the staged panel's.
+template <int NG, int NWIN>
+__device__ void ffn_str_gate_up(const FfnArgs& a, int panel, int bgi, MfmaStrLds<2, NG>& lds) {
+    constexpr int NS = 16 * NG;
+    const int t = threadIdx.x, K = a.H;
+    MfmaStream<2, NG, true, NWIN> core;
+    DAB_TRACE_POINT(a, 1);
+    core.run([&](int tl, int r) {
+                 return static_cast<const uint16_t*>(tl == 0 ? a.w_gate : a.w_up) + (size_t)(panel * 16 + r) * K;
+             },
+             [&](int n) {
+                 const int b = bgi * NS + n;
+                 return b < a.B ? static_cast<const uint16_t*>(a.hidden) + (size_t)b * K : nullptr;
+             },
+             static_cast<const uint16_t*>(a.norm_w), K, lds);
+    DAB_TRACE_POINT(a, 2);
+    for (int idx = t; idx < 16 * NS; idx += kMfmaStrThreads) {
+        const int r = idx / NS, sq = idx % NS, g = sq >> 4, n = sq & 15;
+        const int bb = bgi * NS + sq;
+        if (bb >= a.B) continue;
+        const float rs = 1.0f / sqrtf(mfma_str_ssq(lds, sq) / (float)a.H + a.eps);
+        const float gt = mfma_str_sum(lds, 0, g, r, n) * rs, up = mfma_str_sum(lds, 1, g, r, n) * rs;
+        a.m16[(size_t)bb * a.F + panel * 16 + r] = from_f32<uint16_t>(gt / (1.0f + expf(-gt)) * up);
+    }
+}
+
 }  // namespace dev
 }  // namespace dab
