@@ -286,5 +286,31 @@ __device__ void ffn_str_gate_up(const FfnArgs& a, int panel, int bgi, MfmaStrLds
     }
 }
 
+// Down projection on the streamed panel (one tile of 16 rows of W_down, K = F
+// = 1024 NWIN, 16 or 32 sequences against m in bf16); out = h + y.
+template <int NG, int NWIN>
+__device__ void ffn_str_down(const FfnArgs& a, int panel, int bgi, MfmaStrLds<1, NG>& lds) {
+    constexpr int NS = 16 * NG;
+    const int t = threadIdx.x, K = a.F;
+    MfmaStream<1, NG, false, NWIN> core;
+    DAB_TRACE_POINT(a, 1);
+    core.run([&](int, int r) { return static_cast<const uint16_t*>(a.w_down) + (size_t)(panel * 16 + r) * K; },
+             [&](int n) {
+                 const int b = bgi * NS + n;
+                 return b < a.B ? a.m16 + (size_t)b * K : nullptr;
+             },
+             nullptr, K, lds);
+    DAB_TRACE_POINT(a, 2);
+    for (int idx = t; idx < 16 * NS; idx += kMfmaStrThreads) {
+        const int row = idx / NS, sq = idx % NS, g = sq >> 4, n = sq & 15;
+        const int bb = bgi * NS + sq;
+        if (bb >= a.B) continue;
+        const float y = mfma_str_sum(lds, 0, g, row, n);
+        const size_t i = (size_t)bb * a.H + panel * 16 + row;
+        static_cast<uint16_t*>(a.out)[i] = from_f32<uint16_t>(to_f32(static_cast<const uint16_t*>(a.hidden)[i]) + y);
+        if (a.dbg_y) a.dbg_y[i] = y;
+    }
+}
+
 }  // namespace dev
 }  // namespace dab

@@ -63,6 +63,28 @@ void launch_ffn_str(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
     else dab_launch((ffn_str_kernel<1, NWIN>), grid, block, 0, s, ev, a);
 }
 
+template <int NG, int NWIN>
+__global__ __launch_bounds__(kMfmaStrThreads) void ffn_str_down_kernel(FfnArgs a) {
+    __shared__ MfmaStrLds<1, NG> lds;
+    DAB_TRACE_POINT(a, 0);
+    int panel, bgi;
+    if (panel_decode(a.down.nbg, a.down.panels, blockIdx.x, &panel, &bgi)) ffn_str_down<NG, NWIN>(a, panel, bgi, lds);
+    DAB_TRACE_POINT(a, 3);
+}
+
+template <int NWIN>
+void launch_ffn_str_down(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
+    const dim3 grid(a.down.items), block(kMfmaStrThreads);
+    if (a.down.nb == 32) dab_launch((ffn_str_down_kernel<2, NWIN>), grid, block, 0, s, ev, a);
+    else dab_launch((ffn_str_down_kernel<1, NWIN>), grid, block, 0, s, ev, a);
+}
+
+// The streamed down panel: one tile, F = 1024 NWIN for these NWIN (others take the staged panel).
+inline bool ffn_str_down_ok(const FfnArgs& a) {
+    const int nw = a.F / 1024;
+    return a.down_tiles == 1 && a.F % 1024 == 0 && (nw == 1 || nw == 2 || nw == 4 || nw == 8 || nw == 14);
+}
+
 template <typename T, bool GATE_UP>
 hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
     if constexpr (sizeof(T) != 2) {
@@ -82,6 +104,16 @@ hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, const LaunchEvents& 
             if (a.gu.nb == 32) dab_launch((ffn_mfma_kernel<true, 2, 2>), grid, block, lds, s, ev, a);
             else dab_launch((ffn_mfma_kernel<true, 2, 1>), grid, block, lds, s, ev, a);
         } else {
+            if (ffn_str_down_ok(a)) {
+                switch (a.F / 1024) {
+                    case 1: launch_ffn_str_down<1>(a, s, ev); break;
+                    case 2: launch_ffn_str_down<2>(a, s, ev); break;
+                    case 4: launch_ffn_str_down<4>(a, s, ev); break;
+                    case 8: launch_ffn_str_down<8>(a, s, ev); break;
+                    default: launch_ffn_str_down<14>(a, s, ev); break;
+                }
+                return hipGetLastError();
+            }
             const dim3 grid(a.down.items);
             const int key = (a.down_tiles == 2 ? 2 : 0) + (a.down.nb == 32 ? 1 : 0);
             switch (key) {

@@ -436,8 +436,11 @@ constexpr int kMfmaStrWin = 128;                   // K values of a window
 // same pattern without the matrix work: 10.5 us with two, 13.6 with four).  The batch and norm_w
 // fragments are requested before the stream's first loads (after them measured no faster).
 template <int NG> constexpr int mfma_str_ring() { return 2; }
+// K = 1024 NWIN: at most 4096 with two tiles or the RMSNorm (a window's batch fragments serve every
+// tile, so they stay in registers for the panel; norm_w is one direct load per wave), 16384 with one
+// tile (each window's fragments are dead after its four steps)
 constexpr int kMfmaStrMaxK = 4096;
-constexpr int kMfmaStrSteps = kMfmaStrMaxK / kMfmaStrWaves / 32;   // 32-value steps per wave at most
+constexpr int kMfmaStrMaxK1 = 16384;
 
 template <int TILES, int NG>
 struct MfmaStrLds {
@@ -465,7 +468,8 @@ __device__ inline void lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t
 
 template <int TILES, int NG, bool NORM, int NWIN>
 struct MfmaStream {
-    static_assert(NWIN >= 1 && NWIN * kMfmaStrWin * kMfmaStrWaves <= kMfmaStrMaxK, "K = 1024 NWIN");
+    static_assert(NWIN >= 1 && NWIN * kMfmaStrWin * kMfmaStrWaves <= (TILES == 1 && !NORM ? kMfmaStrMaxK1 : kMfmaStrMaxK),
+                  "K = 1024 NWIN");
     static constexpr int RING = mfma_str_ring<NG>();
     f32x4 acc[TILES][NG];
 

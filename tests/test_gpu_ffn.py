@@ -87,6 +87,10 @@ EDGE = [
     FfnConfig("m1", 8, 2048, 5120, "bf16"),
     FfnConfig("m2", 17, 1024, 1280, "bf16"),
     FfnConfig("m3", 12, 8192, 2816, "bf16"),
+    # the streamed panels: gate/up over H of 1024 and 2048, down over F of 14336 (one tile, 14 windows a
+    # wave) and 8192 with 32 sequences a workgroup (a batch of 20: 12 padding rows)
+    FfnConfig("s1", 8, 1024, 14336, "bf16"),
+    FfnConfig("s2", 20, 2048, 8192, "bf16"),
 ]
 
 
