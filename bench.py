@@ -195,6 +195,7 @@ KERNEL_PHASES = [("fused_kernel", "decode_block_fused"),
                  ("oproj_kernel", "oproj_residual"), ("merge_kernel", "attention_merge"),
                  ("ffn_gate_up_kernel", "ffn_rmsnorm_gate_up_silu"),
                  ("ffn_down_kernel", "ffn_down_residual"),
+                 ("ffn_str_kernel", "ffn_rmsnorm_gate_up_silu"), ("ffn_str_down_kernel", "ffn_down_residual"),
                  ("mla_chunk_kernel", "mla_chunk"), ("mla_merge_kernel", "mla_merge")]
 
 
@@ -214,8 +215,8 @@ def mla_phase_bytes(cfg: MlaConfig, pos) -> dict:
 
 
 def phase_of(kernel_name: str):
-    fn = kernel_name.split("(")[0].split("<")[0].split("::")[-1]
-    if fn in ("mfma_panel_kernel", "mfma_res_kernel"):     # template argument QKV: true or false
+    fn = kernel_name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0].split("::")[-1]
+    if fn in ("mfma_panel_kernel", "mfma_res_kernel", "mfma_str_kernel"):   # template argument QKV: true or false
         return "qkv_rmsnorm_rope_append" if "<true" in kernel_name else "oproj_residual"
     if fn == "ffn_mfma_kernel":                               # template argument GATE_UP: true or false
         return "ffn_rmsnorm_gate_up_silu" if "<true" in kernel_name else "ffn_down_residual"
