@@ -140,7 +140,6 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.qkv = panel_dev(p.qkv);
     a.oproj = panel_dev(p.oproj);
     a.chunk = p.chunk;
-    a.spec_len = dab::chunk_len(p.chunk, p.cap - 1 > 0 ? p.cap - 1 : 1);
     a.maxc = p.max_chunks;
     a.attn_items = p.attn_grid;
     a.split_merge = p.split_merge ? 1 : 0;

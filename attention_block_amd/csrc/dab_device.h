@@ -434,18 +434,31 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     using Geo = AttnGeom<D, G>;
     constexpr int LPR = Geo::LPR, NSLOT = Geo::NSLOT, U = Geo::U, HB = Geo::HB;
     const int nkv = a.nkv;
+    int p;
+    if (!pos_valid(a, b, &p)) return;
+    // chunks cover the p cached tokens; the last one also takes the new token
+    const int len = chunk_len(a.chunk, p);             // this sequence's chunk length
+    const int nchunk = p > 0 ? (p + len - 1) / len : 1;
+    if (c >= nchunk) return;
+    const int t0 = c * len;
+    const int t1 = min(t0 + len, p);
+    const bool has_new = c == nchunk - 1;
+    const int nhb = (t1 - t0 + HB - 1) / HB;          // buffers of HB tokens (0 when there is no history)
+
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int slot = t / LPR, l = t % LPR;
     const size_t row = (size_t)nkv * D;
     const size_t base = ((size_t)b * a.cap * nkv + g) * D + l * 8;
     const T* Kp = static_cast<const T*>(a.k_cache) + base;
     const T* Vp = static_cast<const T*>(a.v_cache) + base;
+
+    // 1. the first buffer(s) of history rows in flight
     Vec8<T> kA[U], vA[U], kB[U], vB[U];
-    auto issue = [&](Vec8<T> (&kr)[U], Vec8<T> (&vr)[U], int hb0, int lim) {
+    auto issue = [&](Vec8<T> (&kr)[U], Vec8<T> (&vr)[U], int hb0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int tok = hb0 + slot + NSLOT * u;
-            if (tok < lim) {
+            if (tok < t1) {
                 kr[u].load(Kp + (size_t)tok * row);
                 vr[u].load(Vp + (size_t)tok * row);
             } else {
@@ -454,36 +467,8 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
             }
         }
     };
-    // 1. the first buffer(s) of history rows in flight before the position is read: the chunk as it
-    // is at the capacity's chunk length, rows below cap - 1 (in bounds whatever the position); the
-    // position then says whether they are the chunk's (the length is the same: always where the cache
-    // holds just the context) or the chunk is requested again
-    const int t0s = c * a.spec_len, t1s = min(t0s + a.spec_len, a.cap - 1);
-    issue(kA, vA, t0s, t1s);
-    if constexpr (Geo::PIPE) issue(kB, vB, t0s + HB, t1s);
-    int p;
-    if (!pos_valid(a, b, &p)) {
-        __builtin_amdgcn_s_waitcnt(0);                // no load of this wave left in flight
-        return;
-    }
-    // chunks cover the p cached tokens; the last one also takes the new token
-    const int len = chunk_len(a.chunk, p);             // this sequence's chunk length
-    const int nchunk = p > 0 ? (p + len - 1) / len : 1;
-    if (c >= nchunk) {
-        __builtin_amdgcn_s_waitcnt(0);
-        return;
-    }
-    const int t0 = c * len;
-    const int t1 = min(t0 + len, p);
-    const bool has_new = c == nchunk - 1;
-    const int nhb = (t1 - t0 + HB - 1) / HB;          // buffers of HB tokens (0 when there is no history)
-    // rows at or past t1 in the first buffers where they were requested up to t1s > t1
-    const bool respec = t0 != t0s || t1 > t1s;
-    const int clip_end = respec || t1 >= t1s ? t0 : t0 + 2 * HB;
-    if (respec) {                                      // not the chunk requested: request it
-        issue(kA, vA, t0, t1);
-        if constexpr (Geo::PIPE) issue(kB, vB, t0 + HB, t1);
-    }
+    issue(kA, vA, t0);
+    if constexpr (Geo::PIPE) issue(kB, vB, t0 + HB);
     DAB_TRACE_POINT(a, 1);
 
     // 2. q of this group's heads, in log2 units
@@ -650,18 +635,6 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     // lane of the workgroup runs it (the trip count is uniform), the lanes of
     // a slot agree on how many of its tokens are valid
     auto process = [&](Vec8<T> (&kr)[U], Vec8<T> (&vr)[U], int hb0) {
-        if constexpr (DOT2) {
-            // rows past t1 of a buffer requested before the position was read: zeros (the pair
-            // products take two rows at a time, and a row past the cache's context may hold anything)
-            if (hb0 < clip_end) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (hb0 + slot + NSLOT * u >= t1) {
-                        kr[u].zero();
-                        vr[u].zero();
-                    }
-            }
-        }
         float s[G][U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -675,15 +648,15 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     if constexpr (Geo::PIPE) {
         for (int k = 0; k < nhb; k += 2) {
             process(kA, vA, t0 + k * HB);
-            if (k + 2 < nhb) issue(kA, vA, t0 + (k + 2) * HB, t1);
+            if (k + 2 < nhb) issue(kA, vA, t0 + (k + 2) * HB);
             if (k + 1 < nhb) {
                 process(kB, vB, t0 + (k + 1) * HB);
-                if (k + 3 < nhb) issue(kB, vB, t0 + (k + 3) * HB, t1);
+                if (k + 3 < nhb) issue(kB, vB, t0 + (k + 3) * HB);
             }
         }
     } else {
         for (int k = 0; k < nhb; ++k) {
-            if (k > 0) issue(kA, vA, t0 + k * HB, t1);
+            if (k > 0) issue(kA, vA, t0 + k * HB);
             process(kA, vA, t0 + k * HB);
         }
     }

@@ -53,8 +53,6 @@ struct StepArgs {
     // plan
     PanelPlanDev qkv, oproj;
     ChunkRule chunk;        // split-KV chunk length of each sequence, from its position (chunk_len)
-    int spec_len;           // the chunk length at the capacity (chunk_len at cap - 1): a chunk's first
-                            // loads are requested for it before the position is read
     int maxc, attn_items;
     int split_merge;        // phased: chunk partials are merged by a kernel of their own
 #ifdef DAB_TRACE
