@@ -635,5 +635,61 @@ __device__ void mfma_str_panel(const StepArgs& a, int panel, int bgi, MfmaStrLds
         [&](int sq) { return mfma_str_ssq(lds, sq); });
 }
 
+// QKV projection in 24-row panels on the streamed panel: three half tiles
+// of 4 RoPE pairs each (rows e .. e+3 and e+D/2 .. e+D/2+3 of one head),
+// half tiles A and B in tile 0 (A at tile rows 0-3 and 8-11, B at 4-7 and
+// 12-15), C in tile 1 (rows 0-3 and 8-11; the rest unused), so that pair
+// (r, r + 8) of a tile stays one rotation.  A panel's half tiles may belong
+// to different heads.  (The 6144 rows of the 8B GQA layer make 256 such
+// panels, one per CU, against 192 of 32 rows.)
+struct QkvHalfTiles {
+    int hd[3], e0[3];
+    __device__ QkvHalfTiles(const StepArgs& a, int panel) {
+        const int per_head = a.D >> 3;                    // half tiles per head
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int ht = panel * 3 + i;
+            hd[i] = ht / per_head;
+            e0[i] = (ht - hd[i] * per_head) * 4;
+        }
+    }
+    // half tile of tile row m of tile tl (the unused rows of tile 1 map to C's)
+    __device__ int which(int tl, int m) const { return tl == 0 ? (m >> 2) & 1 : 2; }
+    __device__ int row(const StepArgs& a, int tl, int m) const {
+        const int i = which(tl, m);
+        return hd[i] * a.D + e0[i] + (m & 3) + (m >= 8 ? a.D >> 1 : 0);
+    }
+};
+
+template <int NG, int NWIN>
+__device__ void mfma_str_qkv24(const StepArgs& a, int panel, int bgi, MfmaStrLds<2, NG>& lds) {
+    constexpr int NS = 16 * NG;
+    const int t = threadIdx.x, K = a.H, D = a.D;
+    const uint16_t* W = static_cast<const uint16_t*>(a.w_qkv);
+    const QkvHalfTiles ht(a, panel);
+    MfmaStream<2, NG, true, NWIN, true> core;
+    DAB_TRACE_POINT(a, 1);
+    core.run([&](int tl, int r) { return W + (size_t)ht.row(a, tl, r) * K; },
+             [&](int n) { return mfma_xrow<true>(a, bgi * NS + n); }, static_cast<const uint16_t*>(a.norm_w), K, lds,
+#ifdef DAB_TRACE
+             a.trace ? a.trace + (size_t)(a.trace_base + blockIdx.x) * 8 : nullptr
+#else
+             nullptr
+#endif
+    );
+    DAB_TRACE_POINT(a, 2);
+    // thread (pair slot, sequence): slots 0-7 are tile 0's pairs (A, then B), 8-11 tile 1's (C)
+    for (int idx = t; idx < 12 * NS; idx += kMfmaStrThreads) {
+        const int ps = idx / NS, sq = idx % NS, g = sq >> 4, n = sq & 15;
+        const int bb = bgi * NS + sq;
+        if (bb >= a.B) continue;
+        const int tl = ps >> 3, r = ps & 7, i = ht.which(tl, r);
+        const float ss[4] = {mfma_str_ssq(lds, sq), 0.f, 0.f, 0.f};
+        const int e = ht.e0[i] + (r & 3);
+        qkv_finish<uint16_t, kQkvPlain>(a, panel, ps, bb, ht.hd[i], e, ht.hd[i] * D + e, mfma_str_sum(lds, tl, g, r, n),
+                                        mfma_str_sum(lds, tl, g, r + 8, n), ss);
+    }
+}
+
 }  // namespace dev
 }  // namespace dab

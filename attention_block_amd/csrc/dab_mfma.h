@@ -466,10 +466,13 @@ __device__ inline void lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t
         : "memory");
 }
 
-template <int TILES, int NG, bool NORM, int NWIN>
+// HALF2: the second tile is half used (its rows 0-3 and 8-11; 24-row panels): its other rows are never
+// loaded, and what the MFMA makes of them (whatever the slot held) is never read.
+template <int TILES, int NG, bool NORM, int NWIN, bool HALF2 = false>
 struct MfmaStream {
     static_assert(NWIN >= 1 && NWIN * kMfmaStrWin * kMfmaStrWaves <= (TILES == 1 && !NORM ? kMfmaStrMaxK1 : kMfmaStrMaxK),
                   "K = 1024 NWIN");
+    static_assert(!HALF2 || TILES == 2, "a half-used second tile");
     static constexpr int RING = mfma_str_ring<NG>();
     f32x4 acc[TILES][NG];
 
@@ -512,7 +515,7 @@ struct MfmaStream {
             }
         };
         // loads requested per window: its batch fragments (first tile only) and its four weight loads
-        auto count = [&](int w) { return (w < nwin ? 4 * NG : 0) + 4; };
+        auto count = [&](int w) { return (w < nwin ? 4 * NG : 0) + (HALF2 && w >= nwin ? 2 : 4); };
         // 2. the first windows of weight rows in flight: window j is tile j / nwin, K values
         // k0 + 128 (j % nwin) ..; load q of a window takes rows 4q .. 4q + 3, lane i row 4q + i / 16 and
         // piece (i % 16) ^ row, so that the piece lands at (i % 16) = piece ^ row
@@ -533,6 +536,7 @@ struct MfmaStream {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                if (HALF2 && tj == 1 && (q & 1)) continue;   // rows 4-7 and 12-15 of a half-used tile
                 const uint16_t* sp = src[0][q];
 #pragma unroll
                 for (int tl = 1; tl < TILES; ++tl)

@@ -273,6 +273,15 @@ __global__ __launch_bounds__(kMfmaStrThreads) void mfma_str_kernel(StepArgs a) {
     DAB_TRACE_POINT(a, 3);
 }
 
+template <int NG, int NWIN>
+__global__ __launch_bounds__(kMfmaStrThreads) void mfma_str_qkv24_kernel(StepArgs a) {
+    __shared__ MfmaStrLds<2, NG> lds;
+    DAB_TRACE_POINT(a, 0);
+    int panel, bgi;
+    if (panel_decode(a.qkv.nbg, a.qkv.panels, blockIdx.x, &panel, &bgi)) mfma_str_qkv24<NG, NWIN>(a, panel, bgi, lds);
+    DAB_TRACE_POINT(a, 3);
+}
+
 // The streamed panel applies to 16 or 32 sequences per workgroup and K of
 // 1024, 2048 or 4096.
 inline bool mfma_streamed(const PanelPlan& g) {
@@ -282,6 +291,11 @@ inline bool mfma_streamed(const PanelPlan& g) {
 template <bool QKV, int NWIN>
 void launch_mfma_str(const StepArgs& a, const PanelPlan& g, hipStream_t s, const LaunchEvents& ev) {
     const dim3 grid(g.grid), block(kMfmaStrThreads);
+    if (QKV && g.rows == 24) {
+        if (g.nb == 32) dab_launch((mfma_str_qkv24_kernel<2, NWIN>), grid, block, 0, s, ev, a);
+        else dab_launch((mfma_str_qkv24_kernel<1, NWIN>), grid, block, 0, s, ev, a);
+        return;
+    }
     const int key = (g.rows == 32 ? 2 : 0) + (g.nb == 32 ? 1 : 0);
     switch (key) {
         case 0: dab_launch((mfma_str_kernel<QKV, 1, 1, NWIN>), grid, block, 0, s, ev, a); break;

@@ -56,11 +56,16 @@ bool plan_mfma_panel(int K, int N, int batch, bool qkv, int half, PanelPlan* g) 
     const bool resident = streamed || (ng == 1 && K <= 4096 && K % 256 == 0);
     const bool two = (ng == 1 || streamed) && N % 32 == 0 && (!qkv || half % 16 == 0) &&
                      (long long)(N / 32) * nbg >= (resident ? 192 : 256);
+    // QKV on the streamed panel: 24-row panels (three half tiles of 4 RoPE pairs) where they make at
+    // most one per CU and more than the 32-row panels would (8B GQA layer: 256 against 192)
+    const int cus = 256;
+    const bool rows24 = qkv && streamed && half % 4 == 0 && N % 24 == 0 && (long long)(N / 24) * nbg <= cus &&
+                        (N / 24) * nbg > (two ? (N / 32) * nbg : (N / 16) * nbg);
     g->K = K;
     g->N = N;
     g->mfma = true;
     g->rows_per_wave = 0;
-    g->rows = two ? 32 : 16;
+    g->rows = rows24 ? 24 : two ? 32 : 16;
     g->panels = N / g->rows;
     g->nb = 16 * ng;
     g->nbg = nbg;

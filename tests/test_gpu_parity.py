@@ -105,9 +105,12 @@ EDGE = [
      [299, 0, 17, 256, 1, 128, 64, 200, 33], 0),
     ("mfma batch 20, two tiles", small_cfg("m2", 20, 2048, 16, 4, 128, "bf16"), 130, list(range(3, 130, 6))[:20], 0),
     ("mfma d64 group 8", small_cfg("m3", 8, 1024, 16, 2, 64, "bf16", 5e5), 90, [89, 0, 5, 64, 33, 80, 12, 1], 32),
-    # 6144 QKV rows at batch 20: 192 two-tile panels of 32 sequences (the streamed panel)
-    ("mfma batch 20, two tiles of 32 sequences", small_cfg("m4", 20, 1024, 32, 8, 128, "bf16", 5e5), 150,
+    # 6144 QKV rows: 256 panels of 24 rows (three half tiles of 4 RoPE pairs, some panels across two
+    # heads) with 32 sequences (batch 20) and with 16 sequences at D 64
+    ("mfma batch 20, 24-row QKV panels of 32 sequences", small_cfg("m4", 20, 1024, 32, 8, 128, "bf16", 5e5), 150,
      [149, 0, 7, 100, 1, 64, 33, 120, 17, 90, 3, 140, 50, 12, 77, 128, 99, 5, 60, 145], 0),
+    ("mfma batch 16, 24-row QKV panels, D 64", small_cfg("m5", 16, 1024, 64, 16, 64, "bf16", 5e5), 120,
+     [119, 0, 3, 64, 1, 100, 33, 110, 17, 90, 5, 115, 50, 12, 77, 96], 0),
     # caches far larger than the contexts: the grid is sized for the capacity, each sequence's chunks
     # for its own position
     ("large cap mha bf16", small_cfg("lc1", 2, 512, 4, 4, 128, "bf16"), 20000, [1000, 37], 0),
