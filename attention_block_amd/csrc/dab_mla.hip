@@ -388,48 +388,85 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
     }
 }
 
-// Merge of one sequence's chunks for HEADS heads (grid: nh / HEADS x B):
-// weights exp2(m_c - M) with M the largest chunk reference, in chunk order.
-// The chunks' statistics and partial rows are requested BATCH at a time, all
-// in flight together, before any of them is used.  Few workgroups (batch 1:
-// 128 heads) take one head and 16 chunks at a time, many take two heads and 8
-// (DeepSeek-V3 shape on MI355X: bs1 16K merge 24.0 -> 20.1 us with the
-// former; bs16 4K 7.3 us with the latter against 8.5 with the former).
-template <int HEADS, int BATCH>
-__global__ __launch_bounds__(HEADS * kMergeHeadThreads) void mla_merge_kernel(MlaArgs a) {
-    const int b = blockIdx.y, h = HEADS * blockIdx.x + threadIdx.x / kMergeHeadThreads;
-    const int d = 4 * (threadIdx.x % kMergeHeadThreads);
+// Merge of one sequence's chunks for one head (grid: nh x B), SUB sub-groups
+// of 128 threads (four dims each): sub-group g takes chunks g, g + SUB, ...,
+// PER of them per round, every statistic and partial row of a round requested
+// together (and the first round with the position, for every chunk slot the
+// workspace has: slots past the sequence's chunks are read and not used), so
+// that the common case (up to SUB PER chunks) is one trip to memory.  Each
+// sub-group keeps a running reference M_g (rescaling its sums when a round
+// raises it), then the sub-groups' (M_g, sum, row) are combined in order
+// through LDS.  (DeepSeek-V3 shape on MI355X, four sub-groups of 16: bs1 4K
+// 6.9 -> 4.1 us, bs1 16K 19.8 -> 6.2 us against the former merge, maxima
+// first and then the rows, 16 chunks at a time.)
+template <int SUB, int PER>
+__global__ __launch_bounds__(SUB * kMergeHeadThreads) void mla_merge_kernel(MlaArgs a) {
+    __shared__ float s_m[SUB], s_l[SUB];
+    __shared__ f32x4 s_acc[SUB > 1 ? SUB - 1 : 1][kMergeHeadThreads];
+    const int b = blockIdx.y, h = blockIdx.x;
+    const int g = threadIdx.x / kMergeHeadThreads, i = threadIdx.x % kMergeHeadThreads, d = 4 * i;
+    const size_t slot0 = (size_t)b * a.splits * a.nh + h, stride = a.nh;
+    float mm[PER], ll[PER];
+    f32x4 oo[PER];
+    auto request = [&](int c0, int lim) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int c = c0 + g + SUB * u;
+            if (c < lim) {                                  // past lim: never used
+                const size_t slot = slot0 + (size_t)c * stride;
+                mm[u] = a.part_ml[2 * slot];
+                ll[u] = a.part_ml[2 * slot + 1];
+                oo[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * kR + d);
+            }
+        }
+    };
+    request(0, a.splits);
     int p, len, nchunks;
     if (!seq_range(a, b, &p, &len, &nchunks) || nchunks == 1) return;
-    const size_t slot0 = (size_t)b * a.splits * a.nh + h, stride = a.nh;
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
-        float mm[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u)
-            mm[u] = c0 + u < nchunks ? a.part_ml[2 * (slot0 + (c0 + u) * stride)] : -INFINITY;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) M = fmaxf(M, mm[u]);
-    }
+    float M = -INFINITY, den = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
-        float mm[BATCH], ll[BATCH];
-        f32x4 oo[BATCH];
+    for (int c0 = 0; c0 < nchunks; c0 += SUB * PER) {
+        if (c0 > 0) request(c0, nchunks);
+        float Mr = M;
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const size_t slot = slot0 + (size_t)min(c0 + u, nchunks - 1) * stride;
-            mm[u] = a.part_ml[2 * slot];
-            ll[u] = a.part_ml[2 * slot + 1];
-            oo[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * kR + d);
+        for (int u = 0; u < PER; ++u)
+            if (c0 + g + SUB * u < nchunks) Mr = fmaxf(Mr, mm[u]);
+        if (Mr > M) {                                      // the reference rises (always on the first round)
+            const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mr);
+            den *= r;
+            acc *= r;
+            M = Mr;
         }
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u)
-            if (c0 + u < nchunks) {
+        for (int u = 0; u < PER; ++u)
+            if (c0 + g + SUB * u < nchunks) {
                 const float w = __builtin_amdgcn_exp2f(mm[u] - M);
                 den = fmaf(w, ll[u], den);
                 acc += w * oo[u];
             }
+    }
+    if constexpr (SUB > 1) {
+        // a sub-group without chunks (nchunks < SUB) keeps M = -inf and weighs 0 below; sub-group 0
+        // always has chunk 0
+        if (i == 0) {
+            s_m[g] = M;
+            s_l[g] = den;
+        }
+        if (g > 0) s_acc[g - 1][i] = acc;
+        __syncthreads();
+        if (g > 0) return;
+        float Mt = M;
+#pragma unroll
+        for (int q = 1; q < SUB; ++q) Mt = fmaxf(Mt, s_m[q]);
+        const float w0 = __builtin_amdgcn_exp2f(M - Mt);
+        den *= w0;
+        acc *= w0;
+#pragma unroll
+        for (int q = 1; q < SUB; ++q) {
+            const float wq = s_m[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[q] - Mt);
+            den = fmaf(wq, s_l[q], den);
+            acc += wq * s_acc[q - 1][i];
+        }
     }
     *reinterpret_cast<f32x4*>(a.out + ((size_t)b * a.nh + h) * kR + d) = acc * (1.f / den);
 }
@@ -444,9 +481,12 @@ struct MlaPlan {
     size_t off_ml = 0, off_o = 0, ws_bytes = 0;
 };
 
-// automatic chunks hold at least this many tokens: a chunk reads the query of all its heads
-// (nh x 576 values) once, as many bytes as ~250 cached tokens at nh = 128
-constexpr int kAutoMinChunk = 256;
+// automatic chunks hold at least this many tokens (a chunk reads the query of all its heads, nh x 576
+// values, once: as many bytes as ~250 cached tokens at nh = 128), and a sequence has at most
+// kAutoMaxSplits of them (DeepSeek-V3 shape, batch 1, on MI355X with the sub-group merge: 4K in 128-token
+// chunks 25.6 us against 30.7 in 256-token ones; 16K in 256-token chunks 35.5 us against 44.5 in 128)
+constexpr int kAutoMinChunk = 128;
+constexpr int kAutoMaxSplits = 64;
 
 std::atomic<int> g_mla_cus[16];
 
@@ -499,7 +539,7 @@ dab_status make_plan(const dab_mla_config* cfg, MlaPlan* p) {
         const int per_cu = q.nw == 1 ? 4 : 1;
         const int64_t wgs = (int64_t)q.B * q.hblocks;
         int sp = (int)(wgs > 0 ? ((int64_t)cus * per_cu + wgs - 1) / wgs : 1);
-        const int most = (q.cap + kAutoMinChunk - 1) / kAutoMinChunk;
+        const int most = min((q.cap + kAutoMinChunk - 1) / kAutoMinChunk, kAutoMaxSplits);
         sp = sp < 1 ? 1 : sp > most ? most : sp;
         q.splits = sp;
         q.lmin = kAutoMinChunk;
@@ -594,12 +634,13 @@ dab_status call(const dab_mla_config* cfg, const float* q_lat, const float* q_ro
     else e = launch(mla_chunk_kernel<1>, grid, dim3(64), s, ev[0], ev[1], a);
     if (e == hipSuccess) e = hipGetLastError();
     if ((st = hip_status(e)) != DAB_OK) return st;
+    // few heads (batch 1): four sub-groups of 16 chunks a round; many heads: one of 8
     if ((int64_t)p.B * p.nh < 1024)
-        e = launch(mla_merge_kernel<1, 16>, dim3((unsigned)p.nh, (unsigned)p.B), dim3(kMergeHeadThreads), s, ev[2],
-                   ev[3], a);
-    else
-        e = launch(mla_merge_kernel<2, 8>, dim3((unsigned)(p.nh / 2), (unsigned)p.B), dim3(2 * kMergeHeadThreads), s,
+        e = launch(mla_merge_kernel<4, 16>, dim3((unsigned)p.nh, (unsigned)p.B), dim3(4 * kMergeHeadThreads), s,
                    ev[2], ev[3], a);
+    else
+        e = launch(mla_merge_kernel<1, 8>, dim3((unsigned)p.nh, (unsigned)p.B), dim3(kMergeHeadThreads), s, ev[2],
+                   ev[3], a);
     if (e == hipSuccess) e = hipGetLastError();
     return hip_status(e);
 }
