@@ -526,7 +526,10 @@ dab_status make_plan(const dab_mla_config* cfg, MlaPlan* p) {
     // 64 heads per workgroup of four waves (two head tiles per wave spill at 512 registers), else
     // one wave of 16 heads
     q.ht = 1;
-    q.nw = q.nh % 64 == 0 ? 4 : 1;
+    // (A single sequence of at most 8192 tokens takes one-wave workgroups too: four times the
+    // workgroups, each loading a quarter of the query, on more CUs; DeepSeek-V3 shape on MI355X, 4K:
+    // 25.5 -> 22.0 us; at 16K the shared cache tiles pay more: 36.4 against 40.1 us.)
+    q.nw = q.nh % 64 == 0 && !(q.B == 1 && q.cap <= 8192) ? 4 : 1;
     q.hblocks = q.nh / (16 * q.ht * q.nw);
     if (cfg->kv_chunk > 0) {
         q.fixed = cfg->kv_chunk;
