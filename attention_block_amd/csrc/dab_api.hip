@@ -264,6 +264,7 @@ dab_status ffn_call(const dab_ffn_config* cfg, const void* hidden, const void* n
     a.m16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + p.off_m16);
     a.mfma = p.mfma ? 1 : 0;
     a.down_tiles = p.down.rows == 32 ? 2 : 1;
+    a.gu_tiles = p.gu_tiles;
     a.B = p.B;
     a.H = p.H;
     a.F = p.F;

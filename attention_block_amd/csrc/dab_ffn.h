@@ -258,17 +258,19 @@ __device__ void ffn_mfma_panel(const FfnArgs& a, int panel, int bgi, MfmaLds<TIL
     }
 }
 
-// Gate/up on the streamed panel (dab_mfma.h MfmaStream, H = 1024 NWIN): tile
-// 0 rows 16p .. 16p+15 of W_gate, tile 1 the same rows of W_up, 16 or 32
-// sequences; the finish is the staged panel's.
-template <int NG, int NWIN>
-__device__ void ffn_str_gate_up(const FfnArgs& a, int panel, int bgi, MfmaStrLds<2, NG>& lds) {
+// Gate/up on the streamed panel (dab_mfma.h MfmaStream, H = 1024 NWIN), T
+// mixed tiles per panel: tile j holds features f0 + 8j .. f0 + 8j + 7, their
+// W_gate rows at tile rows 0-7 and their W_up rows at 8-15, so that the gate
+// and up sums of a feature are rows r and r + 8 of one tile (as a RoPE pair
+// in the QKV panel); 16 or 32 sequences; the finish is the staged panel's.
+template <int T, int NG, int NWIN>
+__device__ void ffn_str_gate_up(const FfnArgs& a, int panel, int bgi, MfmaStrLds<T, NG>& lds) {
     constexpr int NS = 16 * NG;
-    const int t = threadIdx.x, K = a.H;
-    MfmaStream<2, NG, true, NWIN> core;
+    const int t = threadIdx.x, K = a.H, f0 = panel * 8 * T;
+    MfmaStream<T, NG, true, NWIN> core;
     DAB_TRACE_POINT(a, 1);
     core.run([&](int tl, int r) {
-                 return static_cast<const uint16_t*>(tl == 0 ? a.w_gate : a.w_up) + (size_t)(panel * 16 + r) * K;
+                 return static_cast<const uint16_t*>(r < 8 ? a.w_gate : a.w_up) + (size_t)(f0 + 8 * tl + (r & 7)) * K;
              },
              [&](int n) {
                  const int b = bgi * NS + n;
@@ -276,13 +278,13 @@ __device__ void ffn_str_gate_up(const FfnArgs& a, int panel, int bgi, MfmaStrLds
              },
              static_cast<const uint16_t*>(a.norm_w), K, lds);
     DAB_TRACE_POINT(a, 2);
-    for (int idx = t; idx < 16 * NS; idx += kMfmaStrThreads) {
-        const int r = idx / NS, sq = idx % NS, g = sq >> 4, n = sq & 15;
+    for (int idx = t; idx < T * 8 * NS; idx += kMfmaStrThreads) {
+        const int f = idx / NS, sq = idx % NS, g = sq >> 4, n = sq & 15, tl = f >> 3, r = f & 7;
         const int bb = bgi * NS + sq;
         if (bb >= a.B) continue;
         const float rs = 1.0f / sqrtf(mfma_str_ssq(lds, sq) / (float)a.H + a.eps);
-        const float gt = mfma_str_sum(lds, 0, g, r, n) * rs, up = mfma_str_sum(lds, 1, g, r, n) * rs;
-        a.m16[(size_t)bb * a.F + panel * 16 + r] = from_f32<uint16_t>(gt / (1.0f + expf(-gt)) * up);
+        const float gt = mfma_str_sum(lds, tl, g, r, n) * rs, up = mfma_str_sum(lds, tl, g, r + 8, n) * rs;
+        a.m16[(size_t)bb * a.F + f0 + f] = from_f32<uint16_t>(gt / (1.0f + expf(-gt)) * up);
     }
 }
 

@@ -47,20 +47,31 @@ __global__ __launch_bounds__(kMfmaThreads) void ffn_mfma_kernel(FfnArgs a) {
 }
 
 // One workgroup per CU (two, at 128 registers: 8B FFN at batch 16, gate/up 49.4 -> 56.7 us on MI355X).
-template <int NG, int NWIN>
+template <int T, int NG, int NWIN>
 __global__ __launch_bounds__(kMfmaStrThreads) void ffn_str_kernel(FfnArgs a) {
-    __shared__ MfmaStrLds<2, NG> lds;
+    __shared__ MfmaStrLds<T, NG> lds;
     DAB_TRACE_POINT(a, 0);
     int panel, bgi;
-    if (panel_decode(a.gu.nbg, a.gu.panels, blockIdx.x, &panel, &bgi)) ffn_str_gate_up<NG, NWIN>(a, panel, bgi, lds);
+    if (panel_decode(a.gu.nbg, a.gu.panels, blockIdx.x, &panel, &bgi)) ffn_str_gate_up<T, NG, NWIN>(a, panel, bgi, lds);
     DAB_TRACE_POINT(a, 3);
+}
+
+template <int T, int NWIN>
+void launch_ffn_str_t(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
+    const dim3 grid(a.gu.items), block(kMfmaStrThreads);
+    if (a.gu.nb == 32) dab_launch((ffn_str_kernel<T, 2, NWIN>), grid, block, 0, s, ev, a);
+    else dab_launch((ffn_str_kernel<T, 1, NWIN>), grid, block, 0, s, ev, a);
 }
 
 template <int NWIN>
 void launch_ffn_str(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
-    const dim3 grid(a.gu.items), block(kMfmaStrThreads);
-    if (a.gu.nb == 32) dab_launch((ffn_str_kernel<2, NWIN>), grid, block, 0, s, ev, a);
-    else dab_launch((ffn_str_kernel<1, NWIN>), grid, block, 0, s, ev, a);
+    switch (a.gu_tiles) {
+        case 1: launch_ffn_str_t<1, NWIN>(a, s, ev); break;
+        case 2: launch_ffn_str_t<2, NWIN>(a, s, ev); break;
+        case 4: launch_ffn_str_t<4, NWIN>(a, s, ev); break;
+        case 7: launch_ffn_str_t<7, NWIN>(a, s, ev); break;
+        default: launch_ffn_str_t<8, NWIN>(a, s, ev); break;
+    }
 }
 
 template <int NG, int NWIN>
@@ -93,7 +104,7 @@ hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, const LaunchEvents& 
         const dim3 block(kMfmaThreads);
         if constexpr (GATE_UP) {
             // the streamed panel where H is 1024, 2048 or 4096
-            if (a.H == 4096 || a.H == 2048 || a.H == 1024) {
+            if (a.gu_tiles > 0) {
                 if (a.H == 4096) launch_ffn_str<4>(a, s, ev);
                 else if (a.H == 2048) launch_ffn_str<2>(a, s, ev);
                 else launch_ffn_str<1>(a, s, ev);

@@ -81,6 +81,7 @@ struct FfnArgs {
     float eps;
     int mfma;               // MFMA panels (bf16, batch >= 8): 16 sequences per workgroup
     int down_tiles;         // MFMA down panel: 1 or 2 tiles of 16 rows
+    int gu_tiles;           // streamed gate/up panel: mixed tiles (8 features) per panel, 0: not streamed
     PanelPlanDev gu, down;
 #ifdef DAB_TRACE
     unsigned long long* trace;

@@ -323,6 +323,24 @@ dab_status make_ffn_plan(const dab_ffn_config* cfg, FfnPlan* p) {
         g.mfma = true;
         g.rows = 16;
         g.panels = p->F / 16;
+        // H of 1024, 2048 or 4096 (the streamed panel): panels of T mixed tiles, each 8 features with
+        // their gate rows at tile rows 0-7 and their up rows at 8-15, T the smallest of 1, 2, 4, 7, 8
+        // that makes at most one panel per CU and divides F (8B layer, F 14336: 256 panels of 7 tiles,
+        // one round, against 896 two-tile panels in three and a half)
+        if (p->H == 1024 || p->H == 2048 || p->H == 4096) {
+            const int cus = 256, mixed = p->F / 8;
+            const int choices[5] = {1, 2, 4, 7, 8};
+            int tiles = 0;
+            for (int i = 0; i < 5 && tiles == 0; ++i)
+                if (mixed % choices[i] == 0 && mixed / choices[i] <= cus) tiles = choices[i];
+            for (int i = 4; i >= 0 && tiles == 0; --i)           // many features: the largest that divides
+                if (mixed % choices[i] == 0) tiles = choices[i];
+            if (tiles > 0 && p->F % 8 == 0) {
+                p->gu_tiles = tiles;
+                g.rows = 8 * tiles;
+                g.panels = p->F / (8 * tiles);
+            }
+        }
         g.nb = B > 16 ? 32 : 16;
         g.nbg = ceil_div(B, g.nb);
         g.grid = g.nbg == 1 ? g.panels : (int)align_up((size_t)g.panels, 8) * g.nbg;

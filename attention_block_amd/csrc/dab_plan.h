@@ -127,6 +127,7 @@ struct FfnPlan {
     int B = 0, H = 0, F = 0, dtype = 0, elem = 0;
     float eps = 0.f;
     bool mfma = false;        // bf16, batch >= 8: MFMA panels for both GEMVs
+    int gu_tiles = 0;         // gate/up on the streamed panel: mixed tiles (8 features, gate and up) per panel
     PanelPlan gu, down;
     size_t off_m = 0, off_m16 = 0, ws_bytes = 0;
     size_t bytes_hidden = 0, bytes_norm = 0, bytes_wgu = 0, bytes_wdown = 0, bytes_out = 0, bytes_dbg = 0;
