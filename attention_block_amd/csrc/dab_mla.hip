@@ -88,7 +88,7 @@ struct MlaArgs {
     const int32_t* pos;       // [B]
     float* out;               // [B, nh, R]
     float* part_ml;           // [B, splits, nh, 2]: (max, sum) per chunk and head, log2 units
-    float* part_o;            // [B, splits, nh, R]: unnormalised weighted latent sums
+    void* part_o;             // [B, splits, nh, R]: unnormalised weighted latent sums, fp32 or bf16 (below)
     int* err;                 // sticky device error flag
     int nh, cap, hblocks;     // heads, cache rows, workgroups of heads per chunk
     int splits;               // chunk slots per sequence (grid and partial layout)
@@ -153,7 +153,7 @@ struct TilePipe {
 // slot % hblocks of chunk 8 (slot / hblocks) + x % 8, and the head blocks of
 // one chunk run on one XCD one after the other, the later ones reading the
 // chunk's rows from that XCD's L2.  gridDim.x is 8 hblocks ceil(splits / 8).
-template <int NW>
+template <int NW, bool PB>
 __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
     constexpr int NT = 64 * NW;
     constexpr int DEPTH = TilePipe<NW>::DEPTH, NBUF = TilePipe<NW>::NBUF, PT = TilePipe<NW>::PER_TILE;
@@ -378,9 +378,17 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
         for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[dt] * inv;
     } else {
         const size_t sl = ((size_t)b * a.splits + s) * a.nh + head;
-        float* o = a.part_o + sl * kR + 4 * g;
+        if constexpr (PB) {
+            uint16_t* o = static_cast<uint16_t*>(a.part_o) + sl * kR + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[dt];
+            for (int dt = 0; dt < kDimTiles; ++dt)
+                *reinterpret_cast<uint2*>(o + 16 * dt) = uint2{dev::pack_bf16x2(oacc[dt][0], oacc[dt][1]),
+                                                               dev::pack_bf16x2(oacc[dt][2], oacc[dt][3])};
+        } else {
+            float* o = static_cast<float*>(a.part_o) + sl * kR + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[dt];
+        }
         if (g == 0) {
             a.part_ml[2 * sl] = mref;
             a.part_ml[2 * sl + 1] = l;
@@ -399,7 +407,7 @@ __global__ __launch_bounds__(64 * NW) void mla_chunk_kernel(MlaArgs a) {
 // through LDS.  (DeepSeek-V3 shape on MI355X, four sub-groups of 16: bs1 4K
 // 6.9 -> 4.1 us, bs1 16K 19.8 -> 6.2 us against the former merge, maxima
 // first and then the rows, 16 chunks at a time.)
-template <int SUB, int PER>
+template <int SUB, int PER, bool PB>
 __global__ __launch_bounds__(SUB * kMergeHeadThreads) void mla_merge_kernel(MlaArgs a) {
     __shared__ float s_m[SUB], s_l[SUB];
     __shared__ f32x4 s_acc[SUB > 1 ? SUB - 1 : 1][kMergeHeadThreads];
@@ -416,7 +424,13 @@ __global__ __launch_bounds__(SUB * kMergeHeadThreads) void mla_merge_kernel(MlaA
                 const size_t slot = slot0 + (size_t)c * stride;
                 mm[u] = a.part_ml[2 * slot];
                 ll[u] = a.part_ml[2 * slot + 1];
-                oo[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * kR + d);
+                if constexpr (PB) {
+                    const uint2 w2 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.part_o) + slot * kR + d);
+                    oo[u] = f32x4{__uint_as_float(w2.x << 16), __uint_as_float(w2.x & 0xffff0000u),
+                                  __uint_as_float(w2.y << 16), __uint_as_float(w2.y & 0xffff0000u)};
+                } else {
+                    oo[u] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + slot * kR + d);
+                }
             }
         }
     };
@@ -477,6 +491,7 @@ __global__ __launch_bounds__(SUB * kMergeHeadThreads) void mla_merge_kernel(MlaA
 
 struct MlaPlan {
     int B = 0, nh = 0, cap = 0, ht = 0, nw = 0, hblocks = 0, splits = 0, fixed = 0, lmin = 0;
+    bool part_bf16 = false;   // partial rows stored in bf16
     float scale = 0.f;
     size_t off_ml = 0, off_o = 0, ws_bytes = 0;
 };
@@ -551,7 +566,10 @@ dab_status make_plan(const dab_mla_config* cfg, MlaPlan* p) {
     q.off_ml = 256;
     const size_t slots = (size_t)q.B * q.splits * q.nh;
     q.off_o = align256(q.off_ml + slots * 2 * sizeof(float));
-    q.ws_bytes = align256(q.off_o + slots * kR * sizeof(float));
+    // many heads (batch 16): the partial rows in bf16, half their traffic (DeepSeek-V3 shape, batch 16, on
+    // MI355X: 56.5 -> 54.4 us); at batch 1 the merge of bf16 rows measured slower (16K: 4.6 -> 7.5 us)
+    q.part_bf16 = (int64_t)q.B * q.nh >= 1024;
+    q.ws_bytes = align256(q.off_o + slots * kR * (q.part_bf16 ? sizeof(uint16_t) : sizeof(float)));
     *p = q;
     return DAB_OK;
 }
@@ -618,7 +636,7 @@ dab_status call(const dab_mla_config* cfg, const float* q_lat, const float* q_ro
     char* ws = static_cast<char*>(workspace);
     a.err = reinterpret_cast<int*>(ws);                 // the flags word at offset 0 of every workspace
     a.part_ml = reinterpret_cast<float*>(ws + p.off_ml);
-    a.part_o = reinterpret_cast<float*>(ws + p.off_o);
+    a.part_o = ws + p.off_o;
     a.nh = p.nh;
     a.cap = p.cap;
     a.hblocks = p.hblocks;
@@ -633,16 +651,18 @@ dab_status call(const dab_mla_config* cfg, const float* q_lat, const float* q_ro
         for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
     const dim3 grid((unsigned)(8 * p.hblocks * ((p.splits + 7) / 8)), (unsigned)p.B);
     hipError_t e;
-    if (p.nw == 4) e = launch(mla_chunk_kernel<4>, grid, dim3(256), s, ev[0], ev[1], a);
-    else e = launch(mla_chunk_kernel<1>, grid, dim3(64), s, ev[0], ev[1], a);
+    if (p.nw == 4 && p.part_bf16) e = launch(mla_chunk_kernel<4, true>, grid, dim3(256), s, ev[0], ev[1], a);
+    else if (p.nw == 4) e = launch(mla_chunk_kernel<4, false>, grid, dim3(256), s, ev[0], ev[1], a);
+    else if (p.part_bf16) e = launch(mla_chunk_kernel<1, true>, grid, dim3(64), s, ev[0], ev[1], a);
+    else e = launch(mla_chunk_kernel<1, false>, grid, dim3(64), s, ev[0], ev[1], a);
     if (e == hipSuccess) e = hipGetLastError();
     if ((st = hip_status(e)) != DAB_OK) return st;
     // few heads (batch 1): four sub-groups of 16 chunks a round; many heads: one of 8
     if ((int64_t)p.B * p.nh < 1024)
-        e = launch(mla_merge_kernel<4, 16>, dim3((unsigned)p.nh, (unsigned)p.B), dim3(4 * kMergeHeadThreads), s,
+        e = launch(mla_merge_kernel<4, 16, false>, dim3((unsigned)p.nh, (unsigned)p.B), dim3(4 * kMergeHeadThreads), s,
                    ev[2], ev[3], a);
     else
-        e = launch(mla_merge_kernel<1, 8>, dim3((unsigned)p.nh, (unsigned)p.B), dim3(kMergeHeadThreads), s, ev[2],
+        e = launch(mla_merge_kernel<1, 8, true>, dim3((unsigned)p.nh, (unsigned)p.B), dim3(kMergeHeadThreads), s, ev[2],
                    ev[3], a);
     if (e == hipSuccess) e = hipGetLastError();
     return hip_status(e);

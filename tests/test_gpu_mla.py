@@ -107,6 +107,9 @@ CASES = [
     ("128 heads chunks of 32, ragged tail", cfg_of("h128c", 2, 128, 0), 300, [290, 33], 32),
     ("128 heads chunks of 256", cfg_of("h128d", 1, 128, 0), 1100, [1000], 256),
     ("128 heads auto, batch 5", cfg_of("h128e", 5, 128, 0), 1000, [999, 1, 500, 256, 257], 0),
+    # 1152 (sequence, head) pairs: partial rows in bf16, one-head merge; ragged, with a one-chunk sequence
+    ("128 heads batch 9, bf16 partials", cfg_of("h128f", 9, 128, 0), 900, [899, 0, 450, 64, 63, 700, 129, 300, 31],
+     64),
     ("V2-Lite 16 heads bs1 4K", MLA_CONFIGS["deepseek_v2_lite_mla_bs1_4k"], None, None, 0),
     ("V3 128 heads bs1 4K", MLA_CONFIGS["deepseek_v3_mla_bs1_4k"], None, None, 0),
     ("V3 128 heads bs1 4K chunks of 64", MLA_CONFIGS["deepseek_v3_mla_bs1_4k"], None, None, 64),
