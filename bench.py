@@ -196,6 +196,7 @@ KERNEL_PHASES = [("fused_kernel", "decode_block_fused"),
                  ("ffn_gate_up_kernel", "ffn_rmsnorm_gate_up_silu"),
                  ("ffn_down_kernel", "ffn_down_residual"),
                  ("ffn_str_kernel", "ffn_rmsnorm_gate_up_silu"), ("ffn_str_down_kernel", "ffn_down_residual"),
+                 ("mfma_str_qkv24_kernel", "qkv_rmsnorm_rope_append"),
                  ("mla_chunk_kernel", "mla_chunk"), ("mla_merge_kernel", "mla_merge")]
 
 
