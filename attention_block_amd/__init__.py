@@ -17,6 +17,7 @@ from ._lib import DAB_BF16, DAB_F32, FFN_PHASES, MLA_PHASES, READ_PROBE_BLOCKS, 
 __all__ = ["DabError", "DabConfig", "make_config", "workspace_size", "Workspace", "decode_attn_block",
            "decode_attn_block_timed", "read_device_error", "phase_names", "HipEvent", "lib_version",
            "DabFfnConfig", "FFN_PHASES", "ffn_workspace_size", "decode_ffn_block", "decode_ffn_block_timed",
+           "decode_layer", "layer_overlapped",
            "read_probe", "READ_PROBE_BLOCKS", "pack_weight", "attention_output", "WEIGHT_LAYOUTS",
            "decode_attn_block_noalloc", "DabMlaConfig", "MLA_PHASES", "mla_workspace_size",
            "mla_decode_attn", "mla_decode_attn_timed"]
@@ -408,6 +409,40 @@ def decode_ffn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_gate, w
         _ptr(dbg_y), ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(hidden.device), arr, len(events)),
         "dab_decode_ffn_block_timed")
     return out
+
+
+def layer_overlapped(cfg: DabConfig, ffn_cfg: DabFfnConfig) -> bool:
+    """Whether decode_layer's "overlap" schedule is built for these configurations (dab_layer_overlapped)."""
+    r = _lib.load().dab_layer_overlapped(ctypes.byref(cfg), ctypes.byref(ffn_cfg))
+    if r < 0:
+        raise DabError(_lib.DAB_ERR_INVALID_ARG, "dab_layer_overlapped")
+    return r == 1
+
+
+def decode_layer(hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, ffn_norm_w, w_gate, w_up, w_down,
+                 rope_theta: float, eps: float = 1e-6, ffn_eps: Optional[float] = None, h=None, out=None,
+                 workspace: Optional[Workspace] = None, ffn_workspace: Optional[Workspace] = None,
+                 kv_chunk: int = 0, schedule: str = "auto", layer_schedule: str = "auto", *, weight_layout: str):
+    """One decoder layer (dab_decode_layer): the attention block into `h`, its FFN into `out`; returns
+    (h, out).  The arguments are those of decode_attn_block and decode_ffn_block (ffn_eps defaults to
+    eps).  layer_schedule: "sequential" (the two blocks' kernels one after the other), "overlap" (the
+    FFN's weight stream started under the attention block, where layer_overlapped(...) holds) or
+    "auto" (sequential, the faster on MI355X).  Every schedule gives the bits of those two calls.  The
+    FFN workspace is zeroed on allocation (Workspace), as "overlap" needs."""
+    if layer_schedule not in _lib.LAYER_SCHEDULES:
+        raise ValueError(f"layer_schedule must be one of {sorted(_lib.LAYER_SCHEDULES)}, not {layer_schedule!r}")
+    h_cfg, h, w_qkv, w_o = _prepare(hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, h,
+                                    None, kv_chunk, schedule, weight_layout)
+    f_cfg, out, fws, w_gate, w_up, w_down = _prepare_ffn(h, ffn_norm_w, w_gate, w_up, w_down,
+                                                         eps if ffn_eps is None else ffn_eps, out, None,
+                                                         ffn_workspace, weight_layout)
+    ws = workspace if workspace is not None else _workspace_for(h_cfg, hidden.device)
+    _check(_lib.load().dab_decode_layer(
+        ctypes.byref(h_cfg), ctypes.byref(f_cfg), _ptr(hidden), _ptr(attn_norm_w), _ptr(w_qkv), _ptr(w_o),
+        _ptr(k_cache), _ptr(v_cache), _ptr(pos), _ptr(ffn_norm_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(h), _ptr(out), ctypes.c_void_p(ws.ptr), ws.nbytes, ctypes.c_void_p(fws.ptr), fws.nbytes,
+        _lib.LAYER_SCHEDULES[layer_schedule], _stream_ptr(hidden.device)), "dab_decode_layer")
+    return h, out
 
 
 # latent attention (MLA) decode over a latent cache

@@ -11,6 +11,7 @@ LIB_PATH = os.environ.get("DAB_LIBRARY") or os.path.join(HERE, "libdab.so")
 DAB_OK, DAB_ERR_INVALID_ARG, DAB_ERR_UNSUPPORTED, DAB_ERR_WORKSPACE, DAB_ERR_HIP = range(5)
 DAB_F32, DAB_BF16 = 0, 1
 SCHEDULES = {"auto": 0, "phased": 1, "attn_oproj": 2, "qkv_attn": 3, "fused": 4}
+LAYER_SCHEDULES = {"auto": 0, "sequential": 1, "overlap": 2}       # dab_layer_schedule
 
 # every symbol include/dab.h declares
 EXPORTS = (
@@ -18,7 +19,8 @@ EXPORTS = (
     "dab_phase_count", "dab_phase_name", "dab_read_device_error", "dab_status_string", "dab_version",
     "dab_last_hip_error", "dab_ffn_workspace_size", "dab_decode_ffn_block", "dab_decode_ffn_block_timed",
     "dab_read_probe", "dab_attention_output", "dab_pack_weight", "dab_decode_attn_block_noalloc",
-    "dab_mla_workspace_size", "dab_mla_decode_attn", "dab_mla_decode_attn_timed",
+    "dab_mla_workspace_size", "dab_mla_decode_attn", "dab_mla_decode_attn_timed", "dab_decode_layer",
+    "dab_layer_overlapped",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20      # DAB_NOALLOC_SCRATCH_BYTES
 READ_PROBE_BLOCKS = 2048      # DAB_READ_PROBE_BLOCKS
@@ -119,6 +121,10 @@ def load() -> ctypes.CDLL:
     lib.dab_decode_ffn_block.restype = i32
     lib.dab_decode_ffn_block_timed.argtypes = ffn_call + [ctypes.POINTER(vp), i32]
     lib.dab_decode_ffn_block_timed.restype = i32
+    lib.dab_decode_layer.argtypes = [cfgp, ffnp] + [vp] * 13 + [vp, sz, vp, sz, i32, vp]
+    lib.dab_decode_layer.restype = i32
+    lib.dab_layer_overlapped.argtypes = [cfgp, ffnp]
+    lib.dab_layer_overlapped.restype = i32
     mlap = ctypes.POINTER(DabMlaConfig)
     lib.dab_mla_workspace_size.argtypes = [mlap]
     lib.dab_mla_workspace_size.restype = sz

@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdab.so")
 
-SOURCES = ["dab_api.hip", "dab_phase_bf16.hip", "dab_phase_f32.hip", "dab_ffn.hip", "dab_mla.hip", "dab_plan.cpp"]
+SOURCES = ["dab_api.hip", "dab_phase_bf16.hip", "dab_phase_f32.hip", "dab_ffn.hip", "dab_layer.hip", "dab_mla.hip",
+           "dab_plan.cpp"]
 
 # Packed fp32 instructions are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

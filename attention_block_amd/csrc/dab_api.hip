@@ -238,6 +238,10 @@ dab_status call_noalloc(const dab_config* cfg, const void* hidden, const void* n
     return enqueue(p, a, s, nullptr);
 }
 
+dab::FfnArgs ffn_args(const dab::FfnPlan& p, const void* hidden, const void* norm_w, const void* w_gate,
+                      const void* w_up, const void* w_down, void* out, float* dbg_y, void* workspace);
+dab_status ffn_enqueue(const dab::FfnPlan& p, dab::FfnArgs a, int first, hipStream_t s, void* const* events);
+
 dab_status ffn_call(const dab_ffn_config* cfg, const void* hidden, const void* norm_w, const void* w_gate,
                     const void* w_up, const void* w_down, void* out, float* dbg_y, void* workspace,
                     size_t workspace_bytes, void* stream, void* const* events, int n_events) {
@@ -252,6 +256,12 @@ dab_status ffn_call(const dab_ffn_config* cfg, const void* hidden, const void* n
             if (!events[i]) return DAB_ERR_INVALID_ARG;
     }
     if (p.B == 0) return DAB_OK;
+    const dab::FfnArgs a = ffn_args(p, hidden, norm_w, w_gate, w_up, w_down, out, dbg_y, workspace);
+    return ffn_enqueue(p, a, 0, static_cast<hipStream_t>(stream), events);
+}
+
+dab::FfnArgs ffn_args(const dab::FfnPlan& p, const void* hidden, const void* norm_w, const void* w_gate,
+                      const void* w_up, const void* w_down, void* out, float* dbg_y, void* workspace) {
     dab::FfnArgs a{};
     a.hidden = hidden;
     a.norm_w = norm_w;
@@ -271,8 +281,12 @@ dab_status ffn_call(const dab_ffn_config* cfg, const void* hidden, const void* n
     a.eps = p.eps;
     a.gu = panel_dev(p.gu);
     a.down = panel_dev(p.down);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    for (int phase = 0; phase < 2; ++phase) {
+    return a;
+}
+
+// The FFN's kernels from `first` (0: gate/up, 1: down) on.
+dab_status ffn_enqueue(const dab::FfnPlan& p, dab::FfnArgs a, int first, hipStream_t s, void* const* events) {
+    for (int phase = first; phase < 2; ++phase) {
         dab::LaunchEvents ev;
         if (events) {
             ev.start = static_cast<hipEvent_t>(events[2 * phase]);
@@ -282,10 +296,68 @@ dab_status ffn_call(const dab_ffn_config* cfg, const void* hidden, const void* n
         a.trace = g_trace;
         a.trace_base = phase == 0 ? 0 : p.gu.grid;
 #endif
-        st = hip_status(dab::launch_ffn_phase(a, p.dtype, phase, s, ev));
+        const dab_status st = hip_status(dab::launch_ffn_phase(a, p.dtype, phase, s, ev));
         if (st != DAB_OK) return st;
     }
     return DAB_OK;
+}
+
+// Both plans of a layer call, checked against each other.
+dab_status layer_plans(const dab_config* cfg, const dab_ffn_config* ffn_cfg, Plan* p, dab::FfnPlan* fp) {
+    if (!cfg || !ffn_cfg) return DAB_ERR_INVALID_ARG;
+    dab_status st = plan(cfg, p);
+    if (st != DAB_OK) return st;
+    st = dab::make_ffn_plan(ffn_cfg, fp);
+    if (st != DAB_OK) return st;
+    if (fp->B != p->B || fp->H != p->H || fp->dtype != p->dtype) return DAB_ERR_INVALID_ARG;
+    return DAB_OK;
+}
+
+dab_status layer_call(const dab_config* cfg, const dab_ffn_config* ffn_cfg, const void* hidden,
+                      const void* attn_norm_w, const void* w_qkv, const void* w_o, void* k_cache, void* v_cache,
+                      const int32_t* pos, const void* ffn_norm_w, const void* w_gate, const void* w_up,
+                      const void* w_down, void* h, void* out, void* workspace, size_t workspace_bytes,
+                      void* ffn_workspace, size_t ffn_workspace_bytes, int32_t layer_schedule, void* stream) {
+    if (layer_schedule != DAB_LAYER_AUTO && layer_schedule != DAB_LAYER_SEQUENTIAL &&
+        layer_schedule != DAB_LAYER_OVERLAP)
+        return DAB_ERR_INVALID_ARG;
+    Plan p;
+    dab::FfnPlan fp;
+    dab_status st = layer_plans(cfg, ffn_cfg, &p, &fp);
+    if (st != DAB_OK) return st;
+    if (layer_schedule == DAB_LAYER_OVERLAP && !dab::layer_overlap_ok(p, fp)) return DAB_ERR_UNSUPPORTED;
+    st = dab::check_layer_call(p, fp, hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, ffn_norm_w, w_gate,
+                               w_up, w_down, h, out, workspace, workspace_bytes, ffn_workspace, ffn_workspace_bytes);
+    if (st != DAB_OK) return st;
+    if (p.B == 0) return DAB_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    dab::StepArgs a = step_args(p, hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, h, nullptr, workspace);
+    dab::FfnArgs f = ffn_args(fp, h, ffn_norm_w, w_gate, w_up, w_down, out, nullptr, ffn_workspace);
+    // AUTO: the sequential schedule, measured faster than the overlapped one
+    // on MI355X wherever both are built (7B layer, batch 1: 92.2 against 93.1
+    // us at 4K tokens, 83.6 against 85.1 at 1K)
+    if (layer_schedule != DAB_LAYER_OVERLAP) {
+        st = enqueue(p, a, s, nullptr);
+        return st != DAB_OK ? st : ffn_enqueue(fp, f, 0, s, nullptr);
+    }
+    int* hand = reinterpret_cast<int*>(static_cast<char*>(ffn_workspace) + fp.off_hand);
+    a.hand = hand;
+    f.hand = hand;
+    f.flags = a.flags;
+    f.h_panels = p.oproj.panels;
+    st = hip_status(dab::launch_phase(a, p, 0, s, dab::LaunchEvents{}));      // QKV
+    if (st != DAB_OK) return st;
+#ifdef DAB_TRACE
+    a.trace_base = p.qkv.grid;
+    f.trace = a.trace;
+    f.trace_base = a.trace_base;
+#endif
+    st = hip_status(dab::launch_layer_attn_ffn(a, f, p, fp, s, dab::LaunchEvents{}));
+    if (st != DAB_OK) return st;
+#ifdef DAB_TRACE
+    f.trace_base = a.trace_base + p.attn_grid + p.oproj.grid + fp.gu.grid;
+#endif
+    return hip_status(dab::launch_ffn_phase(f, fp.dtype, 1, s, dab::LaunchEvents{}));   // down (re-arms the flags)
 }
 
 }  // namespace
@@ -553,6 +625,24 @@ dab_status dab_decode_ffn_block_timed(const dab_ffn_config* cfg, const void* hid
     if (!events) return DAB_ERR_INVALID_ARG;
     return ffn_call(cfg, hidden, norm_w, w_gate, w_up, w_down, out, dbg_y, workspace, workspace_bytes, stream,
                     events, n_events);
+}
+
+dab_status dab_decode_layer(const dab_config* cfg, const dab_ffn_config* ffn_cfg, const void* hidden,
+                            const void* attn_norm_w, const void* w_qkv, const void* w_o, void* k_cache,
+                            void* v_cache, const int32_t* pos, const void* ffn_norm_w, const void* w_gate,
+                            const void* w_up, const void* w_down, void* h, void* out, void* workspace,
+                            size_t workspace_bytes, void* ffn_workspace, size_t ffn_workspace_bytes,
+                            int32_t layer_schedule, void* stream) {
+    return layer_call(cfg, ffn_cfg, hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, ffn_norm_w, w_gate, w_up,
+                      w_down, h, out, workspace, workspace_bytes, ffn_workspace, ffn_workspace_bytes, layer_schedule,
+                      stream);
+}
+
+int dab_layer_overlapped(const dab_config* cfg, const dab_ffn_config* ffn_cfg) {
+    Plan p;
+    dab::FfnPlan fp;
+    if (layer_plans(cfg, ffn_cfg, &p, &fp) != DAB_OK) return -1;
+    return dab::layer_overlap_ok(p, fp) ? 1 : 0;
 }
 
 const char* dab_version(void) { return "dab 0.1.0 (gfx950)"; }

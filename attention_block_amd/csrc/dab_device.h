@@ -186,6 +186,28 @@ __device__ inline void fetch2(const float* p, float* out) {
     out[1] = __uint_as_float((uint32_t)(w >> 32));
 }
 
+// Two adjacent storage values (4- or 8-byte aligned) in one device-coherent store.
+__device__ inline void publish_pair(uint16_t* p, uint16_t v0, uint16_t v1) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), (uint32_t)v0 | ((uint32_t)v1 << 16), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void publish_pair(float* p, float v0, float v1) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p),
+                       (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16 bytes of published data in two device-coherent loads.
+__device__ inline void fetch16(const void* p, uint32_t* w) {
+    const uint64_t* q = static_cast<const uint64_t*>(p);
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w[0] = (uint32_t)lo;
+    w[1] = (uint32_t)(lo >> 32);
+    w[2] = (uint32_t)hi;
+    w[3] = (uint32_t)(hi >> 32);
+}
+
 __device__ inline int load_counter(const int* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -30,7 +30,12 @@ struct FfnShared {
 };
 
 // Gate/up panel `panel` for batch rows [bgi * NB, +NB).  xs: NB x H floats of LDS.
-template <typename T, int NB, bool EXACT>
+// WAIT (the overlapped layer): h is written by the output projection's
+// panels of the same launch; the panel streams its weights, waits for its
+// sequences' ready counts, then reads h with device-coherent loads.  Each thread takes
+// the same elements in the same order either way, so the results are
+// bit-identical.
+template <typename T, int NB, bool EXACT, bool WAIT = false>
 __device__ void ffn_gate_up_panel(const FfnArgs& a, int panel, int bgi, float* xs, FfnShared<NB>& sm) {
     constexpr int N = W16<T>::N;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -45,21 +50,29 @@ __device__ void ffn_gate_up_panel(const FfnArgs& a, int panel, int bgi, float* x
     // 1. this thread's first input vectors, then the weight stream (a
     // wave's loads complete in issue order)
     W16<T> xr[kStageAhead][NB], wr[kStageAhead];
+    if constexpr (!WAIT) {
 #pragma unroll
-    for (int i = 0; i < kStageAhead; ++i) {
-        const int k = (i * 256 + t) * N;
-        if (k < H) {
-            wr[i].load_cached(nw + k);
+        for (int i = 0; i < kStageAhead; ++i) {
+            const int k = (i * 256 + t) * N;
+            if (k < H) {
+                wr[i].load_cached(nw + k);
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                if (b0 + j < a.B) xr[i][j].load_cached(hid + (size_t)(b0 + j) * H + k);
-                else xr[i][j].zero();
+                for (int j = 0; j < NB; ++j) {
+                    if (b0 + j < a.B) xr[i][j].load_cached(hid + (size_t)(b0 + j) * H + k);
+                    else xr[i][j].zero();
+                }
             }
         }
     }
     PanelDot<T, 2, NB, EXACT> dot;
     dot.issue(rows, 0, H, lane);
     DAB_TRACE_POINT(a, 1);
+    if constexpr (WAIT) {
+        if (t < NB && b0 + t < a.B)
+            wait_at_least<8>(&a.hand[h_flag_at(b0 + t, panel % kHCopies)], h_subs(a.h_panels), a.flags);
+        __syncthreads();
+        DAB_TRACE_POINT(a, 4);
+    }
 
     // 2. h .* norm_w into LDS, and the sum of h^2 per sequence
     float ss[NB];
@@ -83,20 +96,46 @@ __device__ void ffn_gate_up_panel(const FfnArgs& a, int panel, int bgi, float* x
                     f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
         }
     };
+    if constexpr (WAIT) {
+        // rounds of kHRound vectors per thread, every load of a round issued
+        // before any is used (h from the coherence point, norm_w as usual)
+        constexpr int kHRound = 4;
+        for (int k0 = 0; k0 < H; k0 += kHRound * 256 * N) {
+            W16<T> hv[kHRound][NB], nv[kHRound];
 #pragma unroll
-    for (int i = 0; i < kStageAhead; ++i) {
-        const int k = (i * 256 + t) * N;
-        if (k < H) stage(k, wr[i], xr[i]);
-    }
-    for (int k = (kStageAhead * 256 + t) * N; k < H; k += 256 * N) {
-        W16<T> wv, xv[NB];
-        wv.load_cached(nw + k);
+            for (int i = 0; i < kHRound; ++i) {
+                const int k = k0 + (i * 256 + t) * N;
+                if (k < H) {
+                    nv[i].load_cached(nw + k);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            if (b0 + j < a.B) xv[j].load_cached(hid + (size_t)(b0 + j) * H + k);
-            else xv[j].zero();
+                    for (int j = 0; j < NB; ++j) {
+                        if (b0 + j < a.B) hv[i][j].fetch(hid + (size_t)(b0 + j) * H + k);
+                        else hv[i][j].zero();
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kHRound; ++i) {
+                const int k = k0 + (i * 256 + t) * N;
+                if (k < H) stage(k, nv[i], hv[i]);
+            }
         }
-        stage(k, wv, xv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kStageAhead; ++i) {
+            const int k = (i * 256 + t) * N;
+            if (k < H) stage(k, wr[i], xr[i]);
+        }
+        for (int k = (kStageAhead * 256 + t) * N; k < H; k += 256 * N) {
+            W16<T> wv, xv[NB];
+            wv.load_cached(nw + k);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (b0 + j < a.B) xv[j].load_cached(hid + (size_t)(b0 + j) * H + k);
+                else xv[j].zero();
+            }
+            stage(k, wv, xv);
+        }
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {

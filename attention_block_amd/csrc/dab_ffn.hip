@@ -23,6 +23,11 @@ template <typename T, int NB, bool EXACT>
 __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
     extern __shared__ f32x4 xs_raw[];
     DAB_TRACE_POINT(a, 0);
+    // after the overlapped layer's launch: its gate/up panels are past their
+    // waits, so the ready counts of h go back to zero for the next call
+    if (a.hand && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < a.B * kHCopies; i += blockDim.x)
+            set_counter(&a.hand[h_flag_at(i / kHCopies, i % kHCopies)], 0);
     int panel, bgi;
     if (panel_decode(a.down.nbg, a.down.panels, blockIdx.x, &panel, &bgi))
         ffn_down_panel<T, 2, NB, EXACT>(a, panel, bgi, reinterpret_cast<float*>(xs_raw));

@@ -39,6 +39,11 @@ template <> struct W16<uint16_t> {
     u32x4 r;
     __device__ void load(const uint16_t* p) { r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
     __device__ void load_cached(const uint16_t* p) { r = *reinterpret_cast<const u32x4*>(p); }
+    __device__ void fetch(const uint16_t* p) {          // published by another workgroup of the launch
+        uint32_t w[4];
+        fetch16(p, w);
+        r = u32x4{w[0], w[1], w[2], w[3]};
+    }
     __device__ void zero() { r = u32x4{0u, 0u, 0u, 0u}; }
     __device__ void unpack(float* f) const {
 #pragma unroll
@@ -54,6 +59,11 @@ template <> struct W16<float> {
     f32x4 r;
     __device__ void load(const float* p) { r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)); }
     __device__ void load_cached(const float* p) { r = *reinterpret_cast<const f32x4*>(p); }
+    __device__ void fetch(const float* p) {
+        uint32_t w[4];
+        fetch16(p, w);
+        r = f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
+    }
     __device__ void zero() { r = f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ void unpack(float* f) const {
 #pragma unroll
@@ -336,8 +346,15 @@ __device__ void qkv_panel(const StepArgs& a, int panel, int bgi, float* xs, QkvS
 // panel 0 re-arms the sequences' QKV panel counts (every attention chunk of
 // those sequences, the only readers, has finished: the merges they fed are
 // done).
-template <typename T, int RW, int NB, bool EXACT, bool WAIT, bool REARM = false>
+//
+// PUBLISH (the overlapped layer, RW = 2): h goes out with device-coherent
+// stores (a lane's two rows are adjacent, one 4- or 8-byte store), then every
+// sequence of the group counts the panel at its sub-counter; the panel that
+// completes a sub-counter re-arms it and adds one to each of the sequence's
+// ready counts, which the FFN panels of the same launch poll.
+template <typename T, int RW, int NB, bool EXACT, bool WAIT, bool REARM = false, bool PUBLISH = false>
 __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
+    static_assert(!PUBLISH || RW == 2, "published rows go out in pairs");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int K = a.n_q, H = a.H;
     const int row0 = (panel * 4 + wave) * RW;
@@ -481,6 +498,37 @@ __device__ void oproj_panel(const StepArgs& a, int panel, int bgi, float* xs) {
 #pragma unroll
             for (int r = 0; r < RW; ++r) y[r] = dot.acc[r][j];
         }
+    if constexpr (PUBLISH) {
+        if (mine) {
+            const size_t i = (size_t)(b0 + lane) * H + row0;
+            publish_pair(static_cast<T*>(a.out) + i, from_f32<T>(xres[0] + y[0]), from_f32<T>(xres[1] + y[1]));
+            if (a.dbg_y) {
+                a.dbg_y[i] = y[0];
+                a.dbg_y[i + 1] = y[1];
+            }
+        }
+        drain_and_sync();
+        DAB_TRACE_POINT(a, 4);
+        if (wave == 0) {
+            bool done = false;
+            if (lane < NB && b0 + lane < a.B) {
+                const int b = b0 + lane, sub = panel % kHSub;
+                const int per_sub = (a.oproj.panels - sub + kHSub - 1) / kHSub;
+                if (bump(&a.hand[h_sub_at(b, sub)]) == per_sub - 1) {
+                    set_counter(&a.hand[h_sub_at(b, sub)], 0);
+                    done = true;
+                }
+            }
+            uint64_t last = __ballot(done);
+            while (last) {
+                const int b = b0 + __builtin_ctzll(last);
+                last &= last - 1;
+                static_assert(kHCopies == 64, "one ready count per lane");
+                add_counter(&a.hand[h_flag_at(b, lane)]);
+            }
+        }
+        return;
+    }
     if (!mine) return;
     const int bb = b0 + lane;
 #pragma unroll

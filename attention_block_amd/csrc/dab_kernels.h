@@ -39,6 +39,7 @@ struct StepArgs {
                             // attention; re-armed by the output projection kernel) or per (sequence, head)
                             // [B, nq + 2 nkv] (whole step in one launch; re-armed by its projection panels)
     int head_cnt_per_seq;   // 1: head_cnt is per (sequence, head)
+    int* hand;              // layer launch: the FFN workspace's hand-off of h (h_sub_at, h_flag_at), else null
     int ready_copies;       // copies of seq_ready in use: min(kReadyCopies, output projection panels)
     float* q;               // [B, n_q] rotated q
     float* kv_new;          // [B, 2, nkv, D] the new token's rotated k and v
@@ -83,6 +84,10 @@ struct FfnArgs {
     int down_tiles;         // MFMA down panel: 1 or 2 tiles of 16 rows
     int gu_tiles;           // streamed gate/up panel: mixed tiles (8 features) per panel, 0: not streamed
     PanelPlanDev gu, down;
+    int* hand;              // layer launch: hand-off of h from the projection panels (the down kernel
+                            // re-arms its ready counts), else null
+    int* flags;             // layer launch: the attention workspace's error bits, else null
+    int h_panels;           // layer launch: the output projection's panels, which publish h
 #ifdef DAB_TRACE
     unsigned long long* trace;
     int trace_base;
@@ -94,6 +99,14 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_ffn_phase(const FfnArgs& a, int dtype, int phase, hipStream_t s, const LaunchEvents& ev);
 // Kernel `phase` of the plan's schedule (0 .. phase_count - 1).
 hipError_t launch_phase(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev);
+
+// The layer in two launches after the QKV kernel: attention + output
+// projection + FFN gate/up in one launch (the gate/up panels stream their
+// weights before h is complete), then the FFN down kernel.  layer_overlap_ok:
+// the plans this is built for.
+bool layer_overlap_ok(const Plan& p, const FfnPlan& f);
+hipError_t launch_layer_attn_ffn(const StepArgs& a, const FfnArgs& f, const Plan& p, const FfnPlan& fp, hipStream_t s,
+                                 const LaunchEvents& ev);
 
 // per-dtype instantiations (separate translation units)
 hipError_t launch_phase_bf16(const StepArgs& a, const Plan& p, int phase, hipStream_t s, const LaunchEvents& ev);

@@ -23,12 +23,12 @@
 namespace dab {
 namespace dev {
 
-// Launch `kernel(a)` on `s`; with events, through hipExtLaunchKernel, which
-// records them at the kernel's own start and end.
-template <typename K, typename A>
+// Launch `kernel(a...)` on `s`; with events, through hipExtLaunchKernel,
+// which records them at the kernel's own start and end.
+template <typename K, typename... A>
 inline hipError_t dab_launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const LaunchEvents& ev,
-                             A a) {
-    void* args[] = {&a};
+                             A... a) {
+    void* args[] = {static_cast<void*>(&a)...};
     const void* f = reinterpret_cast<const void*>(kernel);
     if (ev.start || ev.stop) return hipExtLaunchKernel(f, grid, block, args, lds, s, ev.start, ev.stop, 0);
     return hipLaunchKernel(f, grid, block, args, lds, s);

@@ -350,7 +350,8 @@ dab_status make_ffn_plan(const dab_ffn_config* cfg, FfnPlan* p) {
     }
     p->off_m = 0;
     p->off_m16 = align_up(sizeof(float) * (size_t)B * p->F, 256);
-    p->ws_bytes = p->off_m16 + align_up(sizeof(uint16_t) * (size_t)B * p->F, 256);
+    p->off_hand = p->off_m16 + align_up(sizeof(uint16_t) * (size_t)B * p->F, 256);
+    p->ws_bytes = p->off_hand + align_up(sizeof(int32_t) * (size_t)h_region(B), 256);
     const size_t e = (size_t)p->elem;
     p->bytes_hidden = e * p->B * p->H;
     p->bytes_norm = e * p->H;
@@ -413,6 +414,36 @@ dab_status check_call(const Plan& p, const void* hidden, const void* norm_w, con
             if ((spans[i].written || spans[j].written) &&
                 overlaps(spans[i].p, spans[i].n, spans[j].p, spans[j].n))
                 return DAB_ERR_INVALID_ARG;
+    return DAB_OK;
+}
+
+dab_status check_layer_call(const Plan& p, const FfnPlan& f, const void* hidden, const void* attn_norm_w,
+                            const void* w_qkv, const void* w_o, const void* k_cache, const void* v_cache,
+                            const int32_t* pos, const void* ffn_norm_w, const void* w_gate, const void* w_up,
+                            const void* w_down, const void* h, const void* out, const void* workspace,
+                            size_t ws_bytes, const void* ffn_workspace, size_t ffn_ws_bytes) {
+    if (f.B != p.B || f.H != p.H || f.dtype != p.dtype) return DAB_ERR_INVALID_ARG;
+    dab_status st = check_call(p, hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, h, nullptr, workspace,
+                               ws_bytes);
+    if (st != DAB_OK) return st;
+    st = check_ffn_call(f, h, ffn_norm_w, w_gate, w_up, w_down, out, nullptr, ffn_workspace, ffn_ws_bytes);
+    if (st != DAB_OK) return st;
+    if (p.B == 0) return DAB_OK;
+    // across the halves: what one half writes overlaps nothing of the other
+    struct Span { const void* p; size_t n; };
+    const Span attn[] = {{hidden, p.bytes_hidden}, {attn_norm_w, p.bytes_norm}, {w_qkv, p.bytes_wqkv},
+                         {w_o, p.bytes_wo},         {pos, p.bytes_pos},          {k_cache, p.bytes_cache},
+                         {v_cache, p.bytes_cache},  {workspace, p.ws_bytes},   {h, p.bytes_out}};
+    const Span ffn[] = {{ffn_norm_w, f.bytes_norm}, {w_gate, f.bytes_wgu}, {w_up, f.bytes_wgu},
+                        {w_down, f.bytes_wdown},     {out, f.bytes_out},    {ffn_workspace, f.ws_bytes}};
+    const int n_attn = (int)(sizeof(attn) / sizeof(attn[0])), n_ffn = (int)(sizeof(ffn) / sizeof(ffn[0]));
+    for (int i = 0; i < n_attn; ++i)
+        for (int j = 0; j < n_ffn; ++j) {
+            // attention inputs read only (hidden, weights, pos) against FFN inputs read only
+            const bool attn_written = i >= 5, ffn_written = j >= 4;
+            if ((attn_written || ffn_written) && overlaps(attn[i].p, attn[i].n, ffn[j].p, ffn[j].n))
+                return DAB_ERR_INVALID_ARG;
+        }
     return DAB_OK;
 }
 

@@ -25,6 +25,25 @@ constexpr int kPanelLds = 64 * 1024;
 // queueing on one.
 constexpr int kReadyCopies = 16;
 constexpr int kReadyStride = 32;     // ints
+// Hand-off of the attention block's output h to the FFN panels of the same
+// launch (the overlapped layer), per sequence, each counter on a line of its
+// own: the output-projection panels arrive at kHSub counters (panel p at
+// p % kHSub), and the last arrival at each adds one, with no reply
+// requested, to all kHCopies ready counts, which the FFN panels poll (2752
+// of them for the 7B layer: about 43 per copy) until they reach the number
+// of counters in use.  One counter for all 512 panels of the 7B layer
+// measured 7.4 us of serialised arrivals; every panel adding to its counter
+// in 8 sets, with the FFN panels polling all 16 counters of a set, measured
+// 1.2 us slower than this.  In the FFN workspace, at off_hand; the last
+// arrival at a counter re-arms it, the FFN down kernel the ready counts.
+constexpr int kHSub = 16;
+constexpr int kHCopies = 64;
+constexpr int kHLines = kHSub + kHCopies;
+constexpr int h_region(int B) { return B * kHLines * kReadyStride; }              // ints for B sequences
+constexpr int h_sub_at(int b, int i) { return (b * kHLines + i) * kReadyStride; }
+constexpr int h_flag_at(int b, int c) { return (b * kHLines + kHSub + c) * kReadyStride; }
+// counters in use for a projection of `panels` panels
+constexpr int h_subs(int panels) { return panels < kHSub ? panels : kHSub; }
 // Chunks per thread and head that the attention kernel's in-launch merge
 // requests at once (32 loads in flight per thread).
 constexpr int merge_round(int G) { return G >= 8 ? 4 : 32 / G; }
@@ -129,7 +148,7 @@ struct FfnPlan {
     bool mfma = false;        // bf16, batch >= 8: MFMA panels for both GEMVs
     int gu_tiles = 0;         // gate/up on the streamed panel: mixed tiles (8 features, gate and up) per panel
     PanelPlan gu, down;
-    size_t off_m = 0, off_m16 = 0, ws_bytes = 0;
+    size_t off_m = 0, off_m16 = 0, off_hand = 0, ws_bytes = 0;
     size_t bytes_hidden = 0, bytes_norm = 0, bytes_wgu = 0, bytes_wdown = 0, bytes_out = 0, bytes_dbg = 0;
 };
 
@@ -138,6 +157,15 @@ dab_status make_ffn_plan(const dab_ffn_config* cfg, FfnPlan* plan);
 dab_status check_ffn_call(const FfnPlan& p, const void* hidden, const void* norm_w, const void* w_gate,
                           const void* w_up, const void* w_down, const void* out, const float* dbg_y,
                           const void* workspace, size_t ws_bytes);
+
+// Both halves' checks (h the attention block's out and the FFN's input),
+// then every pair across the halves in which either side is written must
+// not overlap.  Makes no HIP calls and dereferences nothing.
+dab_status check_layer_call(const Plan& p, const FfnPlan& f, const void* hidden, const void* attn_norm_w,
+                            const void* w_qkv, const void* w_o, const void* k_cache, const void* v_cache,
+                            const int32_t* pos, const void* ffn_norm_w, const void* w_gate, const void* w_up,
+                            const void* w_down, const void* h, const void* out, const void* workspace,
+                            size_t ws_bytes, const void* ffn_workspace, size_t ffn_ws_bytes);
 
 // Validate `cfg` and fill `plan`.  Returns DAB_OK, DAB_ERR_INVALID_ARG or
 // DAB_ERR_UNSUPPORTED.  Makes no HIP calls.

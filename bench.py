@@ -658,19 +658,37 @@ def bench_chain(args, dev) -> int:
                           head_dim=cfg.head_dim, cache_capacity=cap, dtype=cfg.dtype, rope_theta=cfg.rope_theta,
                           eps=cfg.eps, kv_chunk=args.kv_chunk, schedule=args.schedule)
     ws = ab.Workspace(ab.workspace_size(acfg), dev)
-    fws = ab.Workspace(ab.ffn_workspace_size(ab.DabFfnConfig(
-        fcfg.batch, fcfg.hidden, fcfg.intermediate, ab.DAB_BF16 if fcfg.dtype == "bf16" else ab.DAB_F32,
-        fcfg.eps)), dev)
+    ffn_c = ab.DabFfnConfig(fcfg.batch, fcfg.hidden, fcfg.intermediate,
+                            ab.DAB_BF16 if fcfg.dtype == "bf16" else ab.DAB_F32, fcfg.eps)
+    fws = ab.Workspace(ab.ffn_workspace_size(ffn_c), dev)
+    # one dab_decode_layer call per layer in --layer-schedule, or with --two-calls the attention block and
+    # the FFN as calls of their own
+    overlapped = not args.two_calls and args.layer_schedule == "overlap"
+    if overlapped and not ab.layer_overlapped(acfg, ffn_c):
+        print(f"--layer-schedule overlap is not built for {args.config}", file=sys.stderr)
+        return 2
+    if overlapped:
+        schedule = ab.phase_names(acfg)[0] + "+attention_oproj_ffn_gate_up+" + ab.FFN_PHASES[1]
+    else:
+        schedule = "+".join(ab.phase_names(acfg)) + " | " + "+".join(ab.FFN_PHASES)
 
     def token(_i=0):
         x = x0
         for attn, ffn in layers:
-            h = ab.decode_attn_block(x, attn["norm_w"], attn["w_qkv"], attn["w_o"], attn["k_cache"],
-                                     attn["v_cache"], attn["pos"], cfg.rope_theta, cfg.eps, out=attn["out"],
-                                     workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule,
-                                     weight_layout="out_in")
-            x = ab.decode_ffn_block(h, ffn["norm_w"], ffn["w_gate"], ffn["w_up"], ffn["w_down"], fcfg.eps,
-                                    out=ffn["out"], workspace=fws, weight_layout="out_in")
+            if args.two_calls:
+                h = ab.decode_attn_block(x, attn["norm_w"], attn["w_qkv"], attn["w_o"], attn["k_cache"],
+                                         attn["v_cache"], attn["pos"], cfg.rope_theta, cfg.eps, out=attn["out"],
+                                         workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule,
+                                         weight_layout="out_in")
+                x = ab.decode_ffn_block(h, ffn["norm_w"], ffn["w_gate"], ffn["w_up"], ffn["w_down"], fcfg.eps,
+                                        out=ffn["out"], workspace=fws, weight_layout="out_in")
+            else:
+                _, x = ab.decode_layer(x, attn["norm_w"], attn["w_qkv"], attn["w_o"], attn["k_cache"],
+                                       attn["v_cache"], attn["pos"], ffn["norm_w"], ffn["w_gate"], ffn["w_up"],
+                                       ffn["w_down"], cfg.rope_theta, cfg.eps, fcfg.eps, h=attn["out"],
+                                       out=ffn["out"], workspace=ws, ffn_workspace=fws, kv_chunk=args.kv_chunk,
+                                       schedule=args.schedule, layer_schedule=args.layer_schedule,
+                                       weight_layout="out_in")
 
     for i in range(max(1, args.warmup // 10)):
         token(i)
@@ -700,15 +718,15 @@ def bench_chain(args, dev) -> int:
                    "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "intermediate": fcfg.intermediate, "kv_tokens": int(pos[0]) if cfg.ragged is None else
                    f"ragged sum {int(np.sum(pos))}", "parallelism": "single GPU",
-                   "schedule": "+".join(ab.phase_names(acfg)) + " | " + "+".join(ab.FFN_PHASES)},
+                   "schedule": schedule, "layer_call": "two calls" if args.two_calls else
+                   f"dab_decode_layer ({args.layer_schedule})", "overlapped": bool(overlapped)},
         "hbm_gbps": round(gbps, 1), "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         "algorithmic_bytes": nbytes, "us_per_layer": round(us / N, 3),
         "algorithmic_flops": N * (algorithmic_flops(cfg, pos) + ffn_algorithmic_flops(fcfg)),
         # per-kernel events are not taken through the chain's graph: the entry covers the whole token
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_GBPS, 4), "traffic": None,
-                     "kernel": f"whole token: {N} layers x (" + "+".join(ab.phase_names(acfg)) + " | " +
-                               "+".join(ab.FFN_PHASES) + ")", "bytes_per_launch": nbytes,
+                     "kernel": f"whole token: {N} layers x ({schedule})", "bytes_per_launch": nbytes,
                      "avg_launch_us": round(us, 3)},
         "cpu_baseline": cpu,
     }
@@ -726,6 +744,11 @@ def main() -> int:
                     help="a decode attention block workload, an FFN half-layer workload (*_ffn_*), or a "
                          "latent-attention (MLA) workload (*_mla_*)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--layer-schedule", default="auto", choices=["auto", "sequential", "overlap"],
+                    help="with --layers: dab_decode_layer's schedule (auto: sequential, measured faster)")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="with --layers: run each layer as dab_decode_attn_block + dab_decode_ffn_block instead "
+                         "of one dab_decode_layer call")
     ap.add_argument("--layers", type=int, default=0,
                     help="time one token through this many decoder layers (attention block of --config + its "
                          "FFN), one HIP graph; 0: the single attention block step")

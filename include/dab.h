@@ -331,8 +331,11 @@ typedef struct {
 
 /*
  * Bytes of device workspace one FFN call needs (0 when the configuration is
- * invalid): m [B, F] in fp32.  Every call writes it before reading it, so it
- * needs no initialisation; calls that share one workspace must not overlap.
+ * invalid): m [B, F] in fp32 and its bf16 copy, and the ready flags of
+ * dab_decode_layer.  dab_decode_ffn_block writes what it reads, so for it the
+ * workspace needs no initialisation; dab_decode_layer needs it zeroed once
+ * (dab_workspace_init) before its first call, and leaves it ready for the
+ * next.  Calls that share one workspace must not overlap.
  */
 size_t dab_ffn_workspace_size(const dab_ffn_config* cfg);
 
@@ -370,6 +373,78 @@ dab_status dab_decode_ffn_block_timed(const dab_ffn_config* cfg,
                                       void* out, float* dbg_y,
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       void* const* events, int n_events);
+
+/*
+ * One decoder layer: the attention block, then the FFN on its output.  The
+ * operator-fusion page, section 1, chains the two halves in this order
+ * through the residual h.
+ *
+ * layer_schedule (dab_layer_schedule):
+ *   DAB_LAYER_SEQUENTIAL  the attention block's kernels, then the FFN's, on
+ *                         `stream` (what the two calls below enqueue).
+ *   DAB_LAYER_OVERLAP     the FFN's weight stream started under the
+ *                         attention block's tail, as the ClusterFusion page,
+ *                         section 3.3, overlaps a stage's loads with the work
+ *                         in front of it: after the QKV kernel one launch
+ *                         holds the attention chunks, the output projection
+ *                         and the FFN's gate/up panels, which load their rows
+ *                         of W_gate and W_up as soon as they have a compute
+ *                         unit and wait on device counters for h; the down
+ *                         kernel follows (three kernels against four).
+ *                         Built for the configurations dab_layer_overlapped
+ *                         reports; DAB_ERR_UNSUPPORTED elsewhere.  On MI355X
+ *                         it measured about 1 us per layer slower than
+ *                         SEQUENTIAL for the 7B layer at batch 1 (93.1
+ *                         against 92.2 us at 4K tokens, 85.1 against 83.6 at
+ *                         1K): the hand-off of h inside the launch costs more
+ *                         than the kernel boundary it removes.
+ *   DAB_LAYER_AUTO        SEQUENTIAL (the faster on every configuration
+ *                         measured).
+ * Every schedule gives the same bits: those of h = dab_decode_attn_block(
+ * hidden, ...) in `h` and out = dab_decode_ffn_block(h, ...) in `out`.
+ *
+ *   cfg, hidden .. pos        as dab_decode_attn_block (attn_norm_w its norm_w)
+ *   ffn_cfg                   as dab_decode_ffn_block; batch, hidden and
+ *                             dtype equal to cfg's
+ *   ffn_norm_w .. w_down      as dab_decode_ffn_block
+ *   h        [B, H]           the attention block's output (the FFN's input
+ *                             and residual); must not overlap any other
+ *                             argument
+ *   out      [B, H]           the layer's output; must not overlap any other
+ *                             argument
+ *   workspace, ffn_workspace  as for the two calls; for DAB_LAYER_OVERLAP the
+ *                             FFN workspace zeroed once before the first call
+ *                             (see dab_ffn_workspace_size)
+ *
+ * Returns what the two calls return for their arguments (nothing enqueued on
+ * an argument error); DAB_ERR_INVALID_ARG if the two configurations disagree
+ * or layer_schedule is not a dab_layer_schedule.  Calls that share either
+ * workspace must not overlap.
+ */
+typedef enum {
+    DAB_LAYER_AUTO = 0,
+    DAB_LAYER_SEQUENTIAL = 1,
+    DAB_LAYER_OVERLAP = 2
+} dab_layer_schedule;
+
+dab_status dab_decode_layer(const dab_config* cfg, const dab_ffn_config* ffn_cfg,
+                            const void* hidden, const void* attn_norm_w, const void* w_qkv, const void* w_o,
+                            void* k_cache, void* v_cache, const int32_t* pos,
+                            const void* ffn_norm_w, const void* w_gate, const void* w_up, const void* w_down,
+                            void* h, void* out,
+                            void* workspace, size_t workspace_bytes,
+                            void* ffn_workspace, size_t ffn_workspace_bytes,
+                            int32_t layer_schedule, void* stream);
+
+/*
+ * 1 if DAB_LAYER_OVERLAP is built for these configurations (one query head
+ * per kv head on the one-launch attention + projection schedule, head dim 64
+ * or 128, the FFN on its VALU panels (fp32, or bf16 below batch 8), H a whole
+ * number of 4096 bf16 or 2048 fp32 values, the two projections' batch
+ * grouping alike), 0 if not, -1 if a configuration is invalid or the two
+ * disagree.
+ */
+int dab_layer_overlapped(const dab_config* cfg, const dab_ffn_config* ffn_cfg);
 
 /*
  * Latent attention decode (DeepSeek's multi-head latent attention, MLA),

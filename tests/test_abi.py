@@ -366,3 +366,77 @@ def test_noalloc_host_checks(lib):
               dtype=_lib.DAB_BF16, rope_theta=1e4, kv_chunk=1024)
     assert lib.dab_workspace_size(ctypes.byref(big)) > _lib.NOALLOC_SCRATCH_BYTES
     assert na(big) == _lib.DAB_ERR_WORKSPACE
+
+
+# the decoder layer (dab_decode_layer): selection of the overlapped schedule, host checks
+
+def test_layer_overlapped_selection(lib):
+    def ov(c, f):
+        return lib.dab_layer_overlapped(ctypes.byref(c), ctypes.byref(f))
+    bf, f32 = _lib.DAB_BF16, _lib.DAB_F32
+    mha7b = dict(hidden=4096, n_q_heads=32, n_kv_heads=32, head_dim=128, cache_capacity=4097)
+    # the 7B layer at batch 1 and 4 (bf16), an fp32 layer of 2048
+    assert ov(cfg(dtype=bf, **mha7b), ffn_cfg(hidden=4096, intermediate=11008)) == 1
+    assert ov(cfg(batch=4, dtype=bf, **mha7b), ffn_cfg(batch=4, hidden=4096, intermediate=11008)) == 1
+    assert ov(cfg(hidden=2048, n_q_heads=32, n_kv_heads=32, head_dim=64, dtype=f32),
+              ffn_cfg(hidden=2048, intermediate=4096, dtype=f32)) == 1
+    # run as two calls: grouped heads (phased schedule), partial K-blocks, the FFN's MFMA panels at
+    # batch 8, a schedule forced to phased
+    assert ov(cfg(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype=bf),
+              ffn_cfg(hidden=4096, intermediate=14336)) == 0
+    assert ov(cfg(dtype=bf), ffn_cfg()) == 0
+    assert ov(cfg(batch=8, dtype=bf, **mha7b), ffn_cfg(batch=8, hidden=4096, intermediate=11008)) == 0
+    assert ov(cfg(dtype=bf, schedule=1, **mha7b), ffn_cfg(hidden=4096, intermediate=11008)) == 0
+    # the two configurations disagree, or one is invalid
+    assert ov(cfg(dtype=bf, **mha7b), ffn_cfg(batch=2, hidden=4096, intermediate=11008)) == -1
+    assert ov(cfg(dtype=bf, **mha7b), ffn_cfg(hidden=2048, intermediate=11008)) == -1
+    assert ov(cfg(dtype=f32, **mha7b), ffn_cfg(hidden=4096, intermediate=11008)) == -1
+    assert ov(cfg(dtype=bf, head_dim=96), ffn_cfg()) == -1
+
+
+def layer_call(lib, c, fc, schedule=0, **over):
+    f = FakePtrs()
+    names = ("hidden", "attn_norm_w", "w_qkv", "w_o", "k_cache", "v_cache", "pos", "ffn_norm_w", "w_gate", "w_up",
+             "w_down", "h", "out")
+    ptrs = {k: f.take(1 << 26) for k in names}
+    ptrs["ws"] = f.take(1 << 26)
+    ptrs["fws"] = f.take(1 << 26)
+    ws_bytes = over.pop("ws_bytes", lib.dab_workspace_size(ctypes.byref(c)))
+    fws_bytes = over.pop("fws_bytes", lib.dab_ffn_workspace_size(ctypes.byref(fc)))
+    ptrs.update(over)
+    vp = ctypes.c_void_p
+    return lib.dab_decode_layer(ctypes.byref(c), ctypes.byref(fc), *[vp(ptrs[k]) for k in names],
+                                vp(ptrs["ws"]), ws_bytes, vp(ptrs["fws"]), fws_bytes, schedule, None)
+
+
+def test_layer_host_checks(lib):
+    # every check fails before anything is enqueued (the pointers are never touched)
+    c, fc = cfg(), ffn_cfg(dtype=_lib.DAB_F32)
+    for name in ("hidden", "attn_norm_w", "w_qkv", "w_o", "k_cache", "v_cache", "pos", "ffn_norm_w", "w_gate",
+                 "w_up", "w_down", "h", "out"):
+        assert layer_call(lib, c, fc, **{name: 0}) == _lib.DAB_ERR_INVALID_ARG, name
+    for name in ("hidden", "w_gate", "h", "out"):
+        assert layer_call(lib, c, fc, **{name: (1 << 46) + 8}) == _lib.DAB_ERR_INVALID_ARG, name
+    assert layer_call(lib, c, fc, ws=0) == _lib.DAB_ERR_WORKSPACE
+    assert layer_call(lib, c, fc, fws=0) == _lib.DAB_ERR_WORKSPACE
+    assert layer_call(lib, c, fc, fws_bytes=lib.dab_ffn_workspace_size(ctypes.byref(fc)) - 256) == \
+        _lib.DAB_ERR_WORKSPACE
+    # overlaps within a half and across the halves
+    shared = FakePtrs().take(1 << 20) + (1 << 47)
+    for a, b in (("hidden", "h"), ("h", "out"), ("h", "w_gate"), ("out", "w_qkv"), ("out", "k_cache"),
+                 ("fws", "ws"), ("fws", "hidden"), ("v_cache", "w_down"), ("ws", "ffn_norm_w")):
+        assert layer_call(lib, c, fc, **{a: shared, b: shared + 256}) == _lib.DAB_ERR_INVALID_ARG, (a, b)
+    # inputs read by both halves may coincide
+    assert layer_call(lib, cfg(batch=0), ffn_cfg(batch=0, dtype=_lib.DAB_F32),
+                      w_up=shared, w_gate=shared) == _lib.DAB_OK
+    # mismatched configurations
+    assert layer_call(lib, c, ffn_cfg(batch=2, dtype=_lib.DAB_F32)) == _lib.DAB_ERR_INVALID_ARG
+    assert layer_call(lib, c, ffn_cfg()) == _lib.DAB_ERR_INVALID_ARG          # bf16 FFN after an fp32 block
+    # nothing is enqueued for an empty batch
+    assert layer_call(lib, cfg(batch=0), ffn_cfg(batch=0, dtype=_lib.DAB_F32)) == _lib.DAB_OK
+    # layer schedules: not a dab_layer_schedule; the overlapped one where it is not built (H 256)
+    for bad in (-1, 3, 7):
+        assert layer_call(lib, c, fc, schedule=bad) == _lib.DAB_ERR_INVALID_ARG, bad
+    assert layer_call(lib, c, fc, schedule=_lib.LAYER_SCHEDULES["overlap"]) == _lib.DAB_ERR_UNSUPPORTED
+    assert layer_call(lib, cfg(batch=0), ffn_cfg(batch=0, dtype=_lib.DAB_F32),
+                      schedule=_lib.LAYER_SCHEDULES["sequential"]) == _lib.DAB_OK
