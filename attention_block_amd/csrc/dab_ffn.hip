@@ -19,8 +19,12 @@ __global__ __launch_bounds__(256) void ffn_gate_up_kernel(FfnArgs a) {
     DAB_TRACE_POINT(a, 3);
 }
 
-template <typename T, int NB, bool EXACT>
-__global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
+// NBLK 2..4 (bf16): the double-buffered dot product, held to the 168
+// registers that keep three workgroups on a CU, as the LDS does (m of
+// 11008 fp32 values: 44 KB each).
+template <typename T, int NB, bool EXACT, int NBLK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NBLK >= 2 ? 3 : 1)))
+void ffn_down_kernel(FfnArgs a) {
     extern __shared__ f32x4 xs_raw[];
     DAB_TRACE_POINT(a, 0);
     // after the overlapped layer's launch: its gate/up panels are past their
@@ -30,7 +34,7 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
             set_counter(&a.hand[h_flag_at(i / kHCopies, i % kHCopies)], 0);
     int panel, bgi;
     if (panel_decode(a.down.nbg, a.down.panels, blockIdx.x, &panel, &bgi))
-        ffn_down_panel<T, 2, NB, EXACT>(a, panel, bgi, reinterpret_cast<float*>(xs_raw));
+        ffn_down_panel<T, 2, NB, EXACT, NBLK>(a, panel, bgi, reinterpret_cast<float*>(xs_raw));
     DAB_TRACE_POINT(a, 3);
 }
 
@@ -156,17 +160,30 @@ hipError_t launch_gate_up_e(const FfnArgs& a, hipStream_t s, const LaunchEvents&
     return hipGetLastError();
 }
 
-template <typename T, bool EXACT>
-hipError_t launch_down_e(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
+template <typename T, bool EXACT, int NBLK>
+hipError_t launch_down_n(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
     const dim3 grid(a.down.items), block(kThreads);
     const size_t lds = (size_t)a.down.nb * a.F * sizeof(float);
     switch (a.down.nb) {
-        case 1: dab_launch((ffn_down_kernel<T, 1, EXACT>), grid, block, lds, s, ev, a); break;
-        case 2: dab_launch((ffn_down_kernel<T, 2, EXACT>), grid, block, lds, s, ev, a); break;
-        case 4: dab_launch((ffn_down_kernel<T, 4, EXACT>), grid, block, lds, s, ev, a); break;
+        case 1: dab_launch((ffn_down_kernel<T, 1, EXACT, NBLK>), grid, block, lds, s, ev, a); break;
+        case 2: dab_launch((ffn_down_kernel<T, 2, EXACT, NBLK>), grid, block, lds, s, ev, a); break;
+        case 4: dab_launch((ffn_down_kernel<T, 4, EXACT, NBLK>), grid, block, lds, s, ev, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// bf16 rows of 2 to 4 K-blocks (F in (4096, 16384]) on the double-buffered
+// dot product, the rest on PanelDot
+template <typename T, bool EXACT>
+hipError_t launch_down_e(const FfnArgs& a, hipStream_t s, const LaunchEvents& ev) {
+    if constexpr (sizeof(T) == 2) {
+        const int kb = PanelDot<T, 1, 1, true>::KB, nblk = (a.F + kb - 1) / kb;
+        if (nblk == 2) return launch_down_n<T, EXACT, 2>(a, s, ev);
+        if (nblk == 3) return launch_down_n<T, EXACT, 3>(a, s, ev);
+        if (nblk == 4) return launch_down_n<T, EXACT, 4>(a, s, ev);
+    }
+    return launch_down_n<T, EXACT, 0>(a, s, ev);
 }
 
 template <typename T>
