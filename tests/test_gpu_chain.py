@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from attention_block_amd.inputs import layer_ffn, make_ffn_inputs, make_inputs
-from gpu_util import rel_l2, small_cfg, storage_values, to_device, tol_for
+from gpu_util import RECORD, rel_l2, small_cfg, storage_values, to_device, tol_for
 from test_gpu_ffn import ffn_to_device
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +49,8 @@ def test_layer_chain_parity(label, cfg, pos, n_layers):
         torch.cuda.synchronize()
         err = rel_l2(storage_values(gpu_x), ref_f["out"])
         print(f"[chain] {label}: layer {layer}: rel-L2(out) = {err:.2e}", flush=True)
+        if layer == n_layers - 1:
+            RECORD.append((f"chain {cfg.name}, layer {layer}", cfg.dtype, {"out": err, "out_all": err}))
         assert np.all(np.isfinite(storage_values(gpu_x)))
         assert err <= tol_for(cfg.dtype), (layer, err)
 

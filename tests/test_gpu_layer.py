@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from attention_block_amd.inputs import f32_to_bf16_bits, layer_ffn, make_ffn_inputs, make_inputs
-from gpu_util import rel_l2, small_cfg, storage_bits, storage_values, to_device, tol_for
+from gpu_util import RECORD, rel_l2, small_cfg, storage_bits, storage_values, to_device, tol_for
 from test_gpu_ffn import ffn_to_device
 
 pytestmark = pytest.mark.gpu
@@ -101,6 +101,8 @@ def test_layer_matches_two_calls_and_oracle(label, cfg, pos, cap, overlapped):
         errs_seq = [rel_l2(storage_values(out1)[b], ref_f["out"][b]) for b in range(cfg.batch)]
         say(f"[layer] {label}: call {call} ({sched}): identical {same}; rel-L2(out) {err:.2e}, "
             f"worst sequence {max(errs_seq):.2e}")
+        if call < len(schedules):
+            RECORD.append((f"layer {sched} {cfg.name}", cfg.dtype, {"out": max(errs_seq), "out_all": err}))
         assert all(same.values()), same
         assert np.all(np.isfinite(storage_values(out1)))
         assert max(errs_seq) <= tol_for(cfg.dtype), errs_seq
