@@ -393,11 +393,12 @@ dab_status dab_decode_ffn_block_timed(const dab_ffn_config* cfg,
  *                         kernel follows (three kernels against four).
  *                         Built for the configurations dab_layer_overlapped
  *                         reports; DAB_ERR_UNSUPPORTED elsewhere.  On MI355X
- *                         it measured about 1 us per layer slower than
- *                         SEQUENTIAL for the 7B layer at batch 1 (93.1
- *                         against 92.2 us at 4K tokens, 85.1 against 83.6 at
- *                         1K): the hand-off of h inside the launch costs more
- *                         than the kernel boundary it removes.
+ *                         it measured 0.8 to 1.5 us per layer slower than
+ *                         SEQUENTIAL for the 7B layer at batch 1 (91.3
+ *                         against 90.5 us at 4K tokens, 83.1 against 81.8 at
+ *                         1K, 32 layers in a graph): the hand-off of h inside
+ *                         the launch costs more than the kernel boundary it
+ *                         removes.
  *   DAB_LAYER_AUTO        SEQUENTIAL (the faster on every configuration
  *                         measured).
  * Every schedule gives the same bits: those of h = dab_decode_attn_block(
