@@ -36,7 +36,37 @@ def plan_host(tmp_path_factory):
         assert bad == 0 and worst <= maxc          # every position's chunks fit the grid and cover its tokens
         return dict(schedule=sched, T=T, max_chunks=maxc, grid=grid, split_merge=bool(split), worst=worst,
                     T_at=at_probe)
+    run.exe = exe
     return run
+
+
+def ffn_plan(plan_host, B, H, F, dtype=BF16):
+    out = subprocess.run([plan_host.exe, "ffn", str(B), str(H), str(F), str(dtype)], check=True,
+                         capture_output=True, text=True).stdout.split()
+    vals = list(map(int, out))
+    if len(vals) == 1:
+        return dict(status=vals[0])
+    keys = ["status", "mfma", "gu_tiles", "gu_panels", "gu_nb", "down_panels", "layout_ok", "hand_at",
+            "ws_bytes", "check", "h_on_w_gate", "out_on_ws", "ws_on_fws", "w_gate_on_hidden"]
+    return dict(zip(keys, vals))
+
+
+def test_ffn_plan_and_layer_checks(plan_host):
+    # the 7B FFN at batch 1 (VALU panels: 2752 gate/up panels of one feature per wave, 512 down panels)
+    # and the 8B FFN at batch 16 (streamed gate/up panels of 7 mixed tiles, one 16-row down tile per CU);
+    # the layout holds the overlapped layer's hand-off region after m and its bf16 copy, and the layer
+    # call's check accepts disjoint arguments and rejects every written argument that overlaps another
+    # half's (host sanitizers on)
+    p7 = ffn_plan(plan_host, 1, 4096, 11008)
+    assert (p7["status"], p7["mfma"], p7["gu_panels"], p7["gu_nb"], p7["down_panels"]) == (0, 0, 2752, 1, 512)
+    p8 = ffn_plan(plan_host, 16, 4096, 14336)
+    assert (p8["status"], p8["mfma"], p8["gu_tiles"], p8["gu_panels"], p8["down_panels"]) == (0, 1, 7, 256, 256)
+    for p in (p7, p8, ffn_plan(plan_host, 3, 2048, 5632, dtype=0), ffn_plan(plan_host, 40, 4096, 14336)):
+        assert p["status"] == 0 and p["layout_ok"] == 1
+        assert p["check"] == 0
+        assert p["h_on_w_gate"] == p["out_on_ws"] == p["ws_on_fws"] == 1      # DAB_ERR_INVALID_ARG
+        assert p["w_gate_on_hidden"] == 0                                      # read-only inputs may coincide
+    assert ffn_plan(plan_host, 1, 100, 11008)["status"] == 2          # DAB_ERR_UNSUPPORTED: H not a multiple of 64
 
 
 def test_two_chunks_per_cu_beyond_one_round(plan_host):
