@@ -106,3 +106,64 @@ def test_layer_matches_two_calls_and_oracle(label, cfg, pos, cap, overlapped):
         assert all(same.values()), same
         assert np.all(np.isfinite(storage_values(out1)))
         assert max(errs_seq) <= tol_for(cfg.dtype), errs_seq
+
+
+def test_layer_bad_position_completes_and_flags():
+    """Sequence 1 at position == capacity in the overlapped layer: the projection panels still count it,
+    so every FFN panel's wait ends (a wait that ran out would add bit 2 to the flag); its h row is left
+    unwritten, the other sequences match the composed oracles, and the next call on the same workspaces
+    gives the two calls' bits."""
+    import torch
+    import attention_block_amd as ab
+    from attention_block_amd import _lib
+    cfg = small_cfg("lbad", 3, 2048, 16, 16, 128, "f32")
+    fcfg = layer_ffn(cfg)
+    cap = 40
+    acfg = ab.make_config(batch=3, hidden=2048, n_q_heads=16, n_kv_heads=16, head_dim=128, cache_capacity=cap,
+                          dtype="f32", rope_theta=cfg.rope_theta, eps=cfg.eps)
+    ffn_c = _lib.DabFfnConfig(3, 2048, fcfg.intermediate, _lib.DAB_F32, fcfg.eps)
+    assert ab.layer_overlapped(acfg, ffn_c)
+    ws = ab.Workspace(ab.workspace_size(acfg), torch.device("cuda"))
+    fws = ab.Workspace(ab.ffn_workspace_size(ffn_c), torch.device("cuda"))
+
+    inp = make_inputs(cfg, 4, cap=cap, pos=[10, 13, 16])
+    finp = make_ffn_inputs(fcfg, 5)
+    ref_a = oracle.decode_step_from_inputs(inp)
+    finp["hidden"] = to_storage(ref_a["out_stored"], cfg.dtype)
+    ref_f = oracle.ffn_step_from_inputs(finp)
+    dev = to_device(inp)
+    fdev = ffn_to_device(finp)
+    dev["pos"][1] = cap                                  # out of range, seen only on the device
+    h = torch.full_like(dev["hidden"], 12345.0)
+    say("[layer] bad position: sequence 1 at pos == cap, overlapped schedule")
+    ab.read_device_error(ws)                             # clear any earlier flag
+    _, out = ab.decode_layer(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
+                             dev["v_cache"], dev["pos"], fdev["norm_w"], fdev["w_gate"], fdev["w_up"],
+                             fdev["w_down"], cfg.rope_theta, cfg.eps, fcfg.eps, h=h, workspace=ws,
+                             ffn_workspace=fws, layer_schedule="overlap", weight_layout="out_in")
+    torch.cuda.synchronize()
+    assert ab.read_device_error(ws) == 1
+    assert torch.all(h[1] == 12345.0)
+    got = storage_values(out)
+    for b in (0, 2):
+        assert rel_l2(got[b], ref_f["out"][b]) <= tol_for(cfg.dtype), b
+
+    # a valid call after it, on the same workspaces
+    inp = make_inputs(cfg, 6, cap=cap, pos=[39, 0, 20])
+    finp = make_ffn_inputs(fcfg, 7)
+    dev = to_device(inp)
+    fdev = ffn_to_device(finp)
+    kc, vc = dev["k_cache"].clone(), dev["v_cache"].clone()
+    h2 = ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], kc, vc, dev["pos"],
+                              cfg.rope_theta, cfg.eps, weight_layout="out_in")
+    out2 = ab.decode_ffn_block(h2, fdev["norm_w"], fdev["w_gate"], fdev["w_up"], fdev["w_down"], fcfg.eps,
+                               weight_layout="out_in")
+    h1, out1 = ab.decode_layer(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"],
+                               dev["v_cache"], dev["pos"], fdev["norm_w"], fdev["w_gate"], fdev["w_up"],
+                               fdev["w_down"], cfg.rope_theta, cfg.eps, fcfg.eps, workspace=ws, ffn_workspace=fws,
+                               layer_schedule="overlap", weight_layout="out_in")
+    torch.cuda.synchronize()
+    assert ab.read_device_error(ws) == 0
+    assert np.array_equal(storage_bits(h1), storage_bits(h2))
+    assert np.array_equal(storage_bits(out1), storage_bits(out2))
+    say("[layer] bad position: flag 1, other sequences right, the next call identical to the two calls")
