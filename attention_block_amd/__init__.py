@@ -51,15 +51,16 @@ def lib_version() -> str:
 
 def make_config(*, batch: int, hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                 cache_capacity: int, dtype: str, rope_theta: float, eps: float = 1e-6,
-                kv_chunk: int = 0, schedule: str = "auto") -> DabConfig:
-    """Build the C config struct.  dtype is "bf16" or "f32"; schedule one of _lib.SCHEDULES."""
+                kv_chunk: int = 0, schedule: str = "auto", max_position: int = 0) -> DabConfig:
+    """Build the C config struct.  dtype is "bf16" or "f32"; schedule one of _lib.SCHEDULES;
+    max_position the largest position a call's sequences hold (0: not given)."""
     if dtype not in ("bf16", "f32"):
         raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
     if schedule not in _lib.SCHEDULES:
         raise ValueError(f"schedule must be one of {sorted(_lib.SCHEDULES)}")
     return DabConfig(batch, hidden, n_q_heads, n_kv_heads, head_dim, cache_capacity,
                      DAB_BF16 if dtype == "bf16" else DAB_F32, rope_theta, eps, kv_chunk,
-                     _lib.SCHEDULES[schedule])
+                     _lib.SCHEDULES[schedule], max_position)
 
 
 def workspace_size(cfg: DabConfig) -> int:
@@ -155,7 +156,7 @@ def _layout(weight_layout: str) -> None:
 
 
 def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y, kv_chunk,
-             schedule, weight_layout):
+             schedule, weight_layout, max_position=0):
     import torch
     _layout(weight_layout)
     if hidden.dtype not in (torch.bfloat16, torch.float32):
@@ -201,13 +202,13 @@ def _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps,
         raise ValueError("dbg_y must be a contiguous float32 [B, H] tensor")
     cfg = make_config(batch=B, hidden=H, n_q_heads=nq, n_kv_heads=nkv, head_dim=D, cache_capacity=cap,
                       dtype="bf16" if dt == torch.bfloat16 else "f32", rope_theta=rope_theta, eps=eps,
-                      kv_chunk=kv_chunk, schedule=schedule)
+                      kv_chunk=kv_chunk, schedule=schedule, max_position=max_position)
     return cfg, out, w_qkv, w_o
 
 
 def decode_attn_block(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta: float, eps: float = 1e-6,
                       out=None, dbg_y=None, workspace: Optional[Workspace] = None, kv_chunk: int = 0,
-                      schedule: str = "auto", *, weight_layout: str):
+                      schedule: str = "auto", *, weight_layout: str, max_position: int = 0):
     """One decode step on the current stream; returns `out`.
 
     Shapes: hidden [B, H]; norm_w [H]; k_cache, v_cache [B, cap, nkv, D] (row
@@ -221,10 +222,12 @@ def decode_attn_block(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_th
     receives the pre-residual attention-output projection.
     schedule: "phased" (one kernel per phase), "attn_oproj" (attention and
     the output projection in one launch), "qkv_attn" (QKV and attention in
-    one launch) or "auto" (the fastest that applies).
+    one launch) or "auto" (the fastest that applies).  max_position (optional): the largest
+    position in pos, so that the work is sized for the tokens in use rather than the capacity; a
+    sequence beyond it is rejected on the device (the error flag) like one past the capacity.
     """
     cfg, out, w_qkv, w_o = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y,
-                                    kv_chunk, schedule, weight_layout)
+                                    kv_chunk, schedule, weight_layout, max_position)
     ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)
     _check(_lib.load().dab_decode_attn_block(
         ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache), _ptr(v_cache),
@@ -253,13 +256,14 @@ def workspace_of(cfg: DabConfig, device) -> Workspace:
 
 
 def decode_attn_block_noalloc(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta: float,
-                              eps: float = 1e-6, out=None, dbg_y=None, kv_chunk: int = 0, schedule: str = "auto"):
+                              eps: float = 1e-6, out=None, dbg_y=None, kv_chunk: int = 0, schedule: str = "auto",
+                              max_position: int = 0):
     """decode_attn_block through dab_decode_attn_block_noalloc: the library's own per-GPU scratch serves
     as the workspace, so the call allocates nothing on the device (give `out`, and the weights in the
     library's [out, in] layout, for a call that allocates nothing at all).  Calls that overlap in time
     on one GPU race on that scratch."""
     cfg, out, w_qkv, w_o = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y,
-                                    kv_chunk, schedule, "out_in")
+                                    kv_chunk, schedule, "out_in", max_position)
     _check(_lib.load().dab_decode_attn_block_noalloc(
         ctypes.byref(cfg), _ptr(hidden), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache), _ptr(v_cache),
         _ptr(pos), _ptr(out), _ptr(dbg_y), _stream_ptr(hidden.device)), "dab_decode_attn_block_noalloc")
@@ -314,11 +318,11 @@ class HipEvent:
 def decode_attn_block_timed(events: Sequence[HipEvent], hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos,
                             rope_theta: float, eps: float = 1e-6, out=None, dbg_y=None,
                             workspace: Optional[Workspace] = None, kv_chunk: int = 0, schedule: str = "auto", *,
-                            weight_layout: str):
+                            weight_layout: str, max_position: int = 0):
     """decode_attn_block that also records events[2i], events[2i + 1] at the start and end of kernel i
     (2 * len(phase_names) events; taken by each kernel's own dispatch)."""
     cfg, out, w_qkv, w_o = _prepare(hidden, norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, out, dbg_y,
-                                    kv_chunk, schedule, weight_layout)
+                                    kv_chunk, schedule, weight_layout, max_position)
     ws = workspace if workspace is not None else _workspace_for(cfg, hidden.device)
     arr = (ctypes.c_void_p * len(events))(*[e.handle.value for e in events])
     _check(_lib.load().dab_decode_attn_block_timed(
@@ -422,7 +426,8 @@ def layer_overlapped(cfg: DabConfig, ffn_cfg: DabFfnConfig) -> bool:
 def decode_layer(hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, ffn_norm_w, w_gate, w_up, w_down,
                  rope_theta: float, eps: float = 1e-6, ffn_eps: Optional[float] = None, h=None, out=None,
                  workspace: Optional[Workspace] = None, ffn_workspace: Optional[Workspace] = None,
-                 kv_chunk: int = 0, schedule: str = "auto", layer_schedule: str = "auto", *, weight_layout: str):
+                 kv_chunk: int = 0, schedule: str = "auto", layer_schedule: str = "auto", *, weight_layout: str,
+                 max_position: int = 0):
     """One decoder layer (dab_decode_layer): the attention block into `h`, its FFN into `out`; returns
     (h, out).  The arguments are those of decode_attn_block and decode_ffn_block (ffn_eps defaults to
     eps).  layer_schedule: "sequential" (the two blocks' kernels one after the other), "overlap" (the
@@ -432,7 +437,7 @@ def decode_layer(hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, ffn_nor
     if layer_schedule not in _lib.LAYER_SCHEDULES:
         raise ValueError(f"layer_schedule must be one of {sorted(_lib.LAYER_SCHEDULES)}, not {layer_schedule!r}")
     h_cfg, h, w_qkv, w_o = _prepare(hidden, attn_norm_w, w_qkv, w_o, k_cache, v_cache, pos, rope_theta, eps, h,
-                                    None, kv_chunk, schedule, weight_layout)
+                                    None, kv_chunk, schedule, weight_layout, max_position)
     f_cfg, out, fws, w_gate, w_up, w_down = _prepare_ffn(h, ffn_norm_w, w_gate, w_up, w_down,
                                                          eps if ffn_eps is None else ffn_eps, out, None,
                                                          ffn_workspace, weight_layout)

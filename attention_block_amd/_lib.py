@@ -41,6 +41,7 @@ class DabConfig(ctypes.Structure):
         ("eps", ctypes.c_float),
         ("kv_chunk", ctypes.c_int32),
         ("schedule", ctypes.c_int32),
+        ("max_position", ctypes.c_int32),
     ]
 
 

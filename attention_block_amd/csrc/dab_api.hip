@@ -132,6 +132,7 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.D = p.D;
     a.G = p.G;
     a.cap = p.cap;
+    a.pos_end = p.pos_end;
     a.n_qkv = p.n_qkv;
     a.n_q = p.n_q;
     a.eps = p.eps;

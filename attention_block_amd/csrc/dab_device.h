@@ -261,10 +261,11 @@ __device__ inline bool arrive_last(int* counter, int expected, int* s_flag) {
     return *s_flag != 0;
 }
 
+// A sequence's position is in the cache and within the max_position hint.
 __device__ inline bool pos_valid(const StepArgs& a, int b, int* p_out) {
     const int p = a.pos[b];
     *p_out = p;
-    return p >= 0 && p < a.cap;
+    return p >= 0 && p < a.pos_end;
 }
 
 // ---------------------------------------------------------------------------

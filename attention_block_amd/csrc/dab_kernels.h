@@ -49,6 +49,7 @@ struct StepArgs {
     uint16_t* a16;          // [B, n_q] the same rounded to bf16 (bf16 storage, phased schedule: MFMA input)
     // shapes and numerics
     int B, H, nq, nkv, D, G, cap, n_qkv, n_q;
+    int pos_end;            // valid positions: [0, pos_end) (the max_position hint + 1, else cap)
     float eps, qscale;      // qscale = log2(e) / sqrt(D)
     double log2_theta;
     // plan

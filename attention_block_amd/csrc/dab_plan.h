@@ -114,6 +114,7 @@ struct PanelPlan {
 
 struct Plan {
     int B = 0, H = 0, nq = 0, nkv = 0, D = 0, cap = 0, dtype = 0, G = 0;
+    int pos_end = 0;             // positions in [0, pos_end) are valid: max_position + 1, else cap
     int n_qkv = 0, n_q = 0;      // (nq + 2 nkv) D, nq D
     float theta = 0.f, eps = 0.f;
     int elem = 0;                // bytes per stored element

@@ -755,6 +755,9 @@ def main() -> int:
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--cap", type=int, default=0,
                     help="cache capacity per sequence (token rows); 0: the largest position + 1")
+    ap.add_argument("--pos-hint", action="store_true",
+                    help="give the library the batch's largest position (dab_config.max_position), so that a "
+                         "--cap far above the positions provisions no idle work")
     ap.add_argument("--schedule", default="auto", choices=["auto", "phased", "attn_oproj", "qkv_attn", "fused"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -809,6 +812,8 @@ def main() -> int:
             print(f"--cap {args.cap} is below the largest position + 1 ({cap})", file=sys.stderr)
             return 2
         cap = args.cap
+    # --pos-hint: the configuration carries the batch's largest position (dab_config.max_position)
+    max_position = int(pos.max()) if args.pos_hint and int(pos.max()) > 0 else 0
     nbytes = algorithmic_bytes(cfg, pos)
     flops = algorithmic_flops(cfg, pos)
     R = max(3, math.ceil(2 * MALL_BYTES / nbytes) + 1)
@@ -818,7 +823,7 @@ def main() -> int:
     sets = [make_layer_set(cfg, pos, cap, gen, dev) for _ in range(R)]
     c = ab.make_config(batch=cfg.batch, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
                        head_dim=cfg.head_dim, cache_capacity=cap, dtype=cfg.dtype, rope_theta=cfg.rope_theta,
-                       eps=cfg.eps, kv_chunk=args.kv_chunk, schedule=args.schedule)
+                       eps=cfg.eps, kv_chunk=args.kv_chunk, schedule=args.schedule, max_position=max_position)
     ws = ab.Workspace(ab.workspace_size(c), dev)
     phases = ab.phase_names(c)
 
@@ -827,12 +832,13 @@ def main() -> int:
         if events is None:
             ab.decode_attn_block(s["hidden"], s["norm_w"], s["w_qkv"], s["w_o"], s["k_cache"], s["v_cache"],
                                  s["pos"], cfg.rope_theta, cfg.eps, out=s["out"], workspace=ws,
-                                 kv_chunk=args.kv_chunk, schedule=args.schedule, weight_layout="out_in")
+                                 kv_chunk=args.kv_chunk, schedule=args.schedule, weight_layout="out_in",
+                                 max_position=max_position)
         else:
             ab.decode_attn_block_timed(events, s["hidden"], s["norm_w"], s["w_qkv"], s["w_o"], s["k_cache"],
                                        s["v_cache"], s["pos"], cfg.rope_theta, cfg.eps, out=s["out"],
                                        workspace=ws, kv_chunk=args.kv_chunk, schedule=args.schedule,
-                                     weight_layout="out_in")
+                                       weight_layout="out_in", max_position=max_position)
 
     for i in range(args.warmup):
         step(i)
@@ -894,7 +900,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "batch": cfg.batch, "hidden": cfg.hidden,
                    "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "kv_tokens": int(pos[0]) if cfg.ragged is None else f"ragged sum {int(np.sum(pos))}",
-                   "cache_capacity": cap, "layer_sets": R, "parallelism": "single GPU",
+                   "cache_capacity": cap, "max_position": max_position, "layer_sets": R, "parallelism": "single GPU",
                    "schedule": "+".join(phases)},
         "hbm_gbps": round(gbps, 1),
         "hbm_pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),

@@ -91,6 +91,12 @@ typedef struct {
                              /* (sized for the current device: see dab_workspace_size), */
                              /* else a multiple of 16 in [32, 4096]                     */
     int32_t schedule;        /* dab_schedule: how the step is laid out on the GPU        */
+    int32_t max_position;    /* the largest position any sequence of the call holds      */
+                             /* (0: not given, cap - 1), at most cap - 1.  It sizes the  */
+                             /* split-KV grid and workspace from the tokens in use       */
+                             /* rather than the capacity; a sequence beyond it is        */
+                             /* rejected on the device as one past the capacity is (the  */
+                             /* error flag, its row and cache left untouched)            */
 } dab_config;
 
 /*

@@ -440,3 +440,18 @@ def test_layer_host_checks(lib):
     assert layer_call(lib, c, fc, schedule=_lib.LAYER_SCHEDULES["overlap"]) == _lib.DAB_ERR_UNSUPPORTED
     assert layer_call(lib, cfg(batch=0), ffn_cfg(batch=0, dtype=_lib.DAB_F32),
                       schedule=_lib.LAYER_SCHEDULES["sequential"]) == _lib.DAB_OK
+
+
+def test_max_position_hint(lib):
+    # the hint is the largest position a call's sequences hold: 0 (not given) up to cap - 1
+    for bad in (-1, 129, 500):
+        assert lib.dab_workspace_size(ctypes.byref(cfg(max_position=bad))) == 0, bad
+    for ok in (0, 1, 64, 128):
+        assert lib.dab_workspace_size(ctypes.byref(cfg(max_position=ok))) > 0, ok
+    # grouped heads at batch 16 in a 16K cache with 4K tokens in use: the split-KV partials are sized
+    # for the hint, as for a cache of 4097
+    gqa = dict(batch=16, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype=_lib.DAB_BF16)
+    big = lib.dab_workspace_size(ctypes.byref(cfg(cache_capacity=16384, **gqa)))
+    hinted = lib.dab_workspace_size(ctypes.byref(cfg(cache_capacity=16384, max_position=4096, **gqa)))
+    small = lib.dab_workspace_size(ctypes.byref(cfg(cache_capacity=4097, **gqa)))
+    assert hinted == small < big

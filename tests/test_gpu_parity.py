@@ -15,7 +15,8 @@ import pytest
 
 import oracle
 from attention_block_amd.inputs import CONFIGS, BlockConfig, make_inputs
-from gpu_util import check_errs, compare, run_gpu, small_cfg, storage_bits, storage_values, tol_for, to_device
+from gpu_util import (RECORD, check_errs, compare, rel_l2, run_gpu, small_cfg, storage_bits, storage_values, tol_for,
+                      to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -397,3 +398,45 @@ def test_graph_replay_matches_eager(schedule):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
         _ = (dev["hidden"].float() * 2).sum().item()   # unrelated eager work between replays
+
+
+HINT = [("phased", small_cfg("hint_gqa", 4, 1024, 16, 4, 128, "bf16", 5e5)),
+        ("attn_oproj", small_cfg("hint_mha", 2, 2048, 16, 16, 128, "f32"))]
+
+
+@pytest.mark.parametrize("schedule,cfg", HINT, ids=[f"{s}-{c.name}" for s, c in HINT])
+def test_max_position_hint(schedule, cfg):
+    """A cache of 3000 rows with positions up to 299: with max_position = 299 the step is planned for 300
+    tokens and every sequence matches the oracle; with a hint of 260 the sequence at 299 is rejected on
+    the device (the flag, its output row and cache rows untouched) and the others stay right."""
+    import torch
+    import attention_block_amd as ab
+    pos = [100, 299, 7, 250][:cfg.batch]
+    inp = make_inputs(cfg, 11, cap=3000, pos=pos)
+    ref = oracle.decode_step_from_inputs(inp)
+    dev = to_device(inp)
+    say(f"[hint] {schedule} {cfg.name}: cap 3000, pos {pos}, max_position {max(pos)}")
+    ab.read_device_error()
+    out = ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"].clone(),
+                               dev["v_cache"].clone(), dev["pos"], cfg.rope_theta, cfg.eps, schedule=schedule,
+                               weight_layout="out_in", max_position=max(pos))
+    assert ab.read_device_error() == 0
+    got = storage_values(out)
+    errs = [rel_l2(got[b], ref["out"][b]) for b in range(cfg.batch)]
+    RECORD.append((f"hint {schedule} {cfg.name}", cfg.dtype, {"out": max(errs), "out_all": rel_l2(got, ref["out"])}))
+    assert max(errs) <= tol_for(cfg.dtype), errs
+
+    say(f"[hint] {schedule} {cfg.name}: max_position 260 with a sequence at 299")
+    out = torch.full_like(dev["hidden"], 12345.0)
+    before = (storage_bits(dev["k_cache"]), storage_bits(dev["v_cache"]))
+    ab.decode_attn_block(dev["hidden"], dev["norm_w"], dev["w_qkv"], dev["w_o"], dev["k_cache"], dev["v_cache"],
+                         dev["pos"], cfg.rope_theta, cfg.eps, out=out, schedule=schedule, weight_layout="out_in",
+                         max_position=260)
+    assert ab.read_device_error() == 1
+    assert torch.all(out[1] == 12345.0)
+    kb, vb = storage_bits(dev["k_cache"]), storage_bits(dev["v_cache"])
+    assert np.array_equal(kb[1], before[0][1]) and np.array_equal(vb[1], before[1][1])
+    got = storage_values(out)
+    for b in range(cfg.batch):
+        if b != 1:
+            assert rel_l2(got[b], ref["out"][b]) <= tol_for(cfg.dtype), b
