@@ -213,6 +213,20 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
         r.want = want;
         r.lo = half_batch;
         r.hi = 448;
+        // With a (sequence, kv head) pair for every CU already, a short
+        // sequence is not split (its chunks would only add merge work), long
+        // ones take chunks of at most 384 tokens, and the two-per-CU rule
+        // below stays off (it would give the ragged batch's sequences of
+        // 1-2K tokens chunks of up to 1024, which finish last).  GQA layer,
+        // batch 32, lengths U[256, 8192], on MI355X: at least two chunks of
+        // at most 448 tokens (two-per-CU rule on) 147.8 us per step; every
+        // sequence in chunks of 448, 384, 352 or 320 tokens 146.2, 144.6,
+        // 145.2, 145.4 us; 384 with the two-per-CU rule on 157.2 us.
+        const bool pair_per_cu = (long long)B * p->nkv >= 256;
+        if (pair_per_cu) {
+            r.want = 1;
+            r.hi = 384;
+        }
         // One query head per kv head: an attention workgroup loads one whole
         // buffer of 256 / (D/8) x 8 tokens per round trip, so a chunk is a
         // whole number of buffers (7B layer, batch 1, 1K tokens: 64-token
@@ -233,7 +247,8 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
         // round count is judged for the tokens the sequences hold.)
         const long long pairs = (long long)B * p->nkv;
         const long long two_per_cu = 2LL * attn_cus;
-        if (p->schedule == DAB_SCHEDULE_PHASED && attn_cus > 0 && attn_per_cu >= 2 && pairs <= two_per_cu) {
+        if (p->schedule == DAB_SCHEDULE_PHASED && attn_cus > 0 && attn_per_cu >= 2 && pairs <= two_per_cu &&
+            !pair_per_cu) {
             r.want2 = (int)(two_per_cu / pairs);
             r.hi2 = 1024;
             r.pairs = (int)pairs;

@@ -101,9 +101,12 @@ def test_residency_rule_leaves_other_shapes(plan_host):
     # long context, batch 1: at most 64 chunks per kv head, 512 chunks fit one round
     p = plan_host(1, 4096, 32, 8, 128, 16385, cus=256, per_cu=3)
     assert p["T"] == 256 and p["max_chunks"] == 64 and p["split_merge"]
-    # ragged batch 32 up to 8192 tokens: one round would need chunks over 1024 tokens; 448-token chunks
+    # ragged batch 32 up to 8192 tokens: one round would need chunks over 1024 tokens; with a (sequence,
+    # kv head) pair for every CU, 384-token chunks and no split of short sequences
     p = plan_host(32, 4096, 32, 8, 128, 8193, cus=256, per_cu=3)
-    assert p["T"] == 448 and p["max_chunks"] == 19 and p["split_merge"]
+    assert p["T"] == 384 and p["max_chunks"] == 22 and p["split_merge"]
+    assert plan_host(32, 4096, 32, 8, 128, 8193, cus=256, per_cu=3, probe=300)["T_at"] == 304   # one chunk
+    assert plan_host(16, 4096, 32, 8, 128, 8193, cus=256, per_cu=3, probe=300)["T_at"] == 80    # 128 pairs: four
 
 
 def test_chunks_cover_every_cached_token(plan_host):
