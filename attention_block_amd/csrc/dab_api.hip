@@ -125,6 +125,8 @@ dab::StepArgs step_args(const Plan& p, const void* hidden, const void* norm_w, c
     a.attn_ml = f(p.off_attn_ml);
     a.a = f(p.off_a);
     a.a16 = reinterpret_cast<uint16_t*>(ws + p.off_a16);
+    a.seq_chunk = p.schedule == DAB_SCHEDULE_PHASED || p.schedule == DAB_SCHEDULE_ATTN_OPROJ
+                      ? n(p.off_seq_chunk) : nullptr;
     a.B = p.B;
     a.H = p.H;
     a.nq = p.nq;

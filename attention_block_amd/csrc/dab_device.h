@@ -261,6 +261,36 @@ __device__ inline bool arrive_last(int* counter, int expected, int* s_flag) {
     return *s_flag != 0;
 }
 
+// Each sequence's split-KV chunk length and count, for the attention
+// launches that follow (workgroup 0 of the QKV kernel): the rule's integer
+// divisions are evaluated once per sequence instead of in front of every
+// chunk's first loads.  Invalid positions get a count of 0; nothing reads it.
+__device__ inline void publish_seq_chunks(const StepArgs& a) {
+    if (!a.seq_chunk || blockIdx.x != 0) return;
+    for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+        const int p = a.pos[b];
+        int len = 0, n = 0;
+        if (p >= 0 && p < a.pos_end) {
+            len = chunk_len(a.chunk, p);
+            n = p > 0 ? (p + len - 1) / len : 1;
+        }
+        a.seq_chunk[2 * b] = len;
+        a.seq_chunk[2 * b + 1] = n;
+    }
+}
+
+// A sequence's chunk length and count: from the QKV kernel's table where
+// there is one (request it before the position, so both loads overlap), else
+// from the rule.
+struct SeqChunk {
+    int len, n;
+};
+__device__ inline SeqChunk seq_chunk_of(const StepArgs& a, int b, int p, const int2* pre) {
+    if (pre) return SeqChunk{pre->x, pre->y};
+    const int len = chunk_len(a.chunk, p);
+    return SeqChunk{len, p > 0 ? (p + len - 1) / len : 1};
+}
+
 // A sequence's position is in the cache and within the max_position hint.
 __device__ inline bool pos_valid(const StepArgs& a, int b, int* p_out) {
     const int p = a.pos[b];
@@ -457,11 +487,13 @@ __device__ void attn_item(const StepArgs& a, int b, int g, int c, AttnShared<D, 
     using Geo = AttnGeom<D, G>;
     constexpr int LPR = Geo::LPR, NSLOT = Geo::NSLOT, U = Geo::U, HB = Geo::HB;
     const int nkv = a.nkv;
+    int2 pre;
+    if (a.seq_chunk) pre = reinterpret_cast<const int2*>(a.seq_chunk)[b];
     int p;
     if (!pos_valid(a, b, &p)) return;
     // chunks cover the p cached tokens; the last one also takes the new token
-    const int len = chunk_len(a.chunk, p);             // this sequence's chunk length
-    const int nchunk = p > 0 ? (p + len - 1) / len : 1;
+    const SeqChunk sc = seq_chunk_of(a, b, p, a.seq_chunk ? &pre : nullptr);
+    const int len = sc.len, nchunk = sc.n;             // this sequence's chunk length and count
     if (c >= nchunk) return;
     const int t0 = c * len;
     const int t1 = min(t0 + len, p);

@@ -55,6 +55,9 @@ struct StepArgs {
     // plan
     PanelPlanDev qkv, oproj;
     ChunkRule chunk;        // split-KV chunk length of each sequence, from its position (chunk_len)
+    int* seq_chunk;         // [B, 2] each sequence's chunk length and count, written by workgroup 0 of the
+                            // QKV kernel for the attention launches after it (phased and attention +
+                            // projection schedules), else null: the attention items evaluate the rule
     int maxc, attn_items;
     int split_merge;        // phased: chunk partials are merged by a kernel of their own
 #ifdef DAB_TRACE

@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void qkv_kernel(StepArgs a) {
     extern __shared__ f32x4 xs_raw[];
     __shared__ QkvShared<T, NB> sm;
     DAB_TRACE_POINT(a, 0);
+    publish_seq_chunks(a);
     int panel, bgi;
     if (panel_decode(a.qkv.nbg, a.qkv.panels, blockIdx.x, &panel, &bgi))
         qkv_panel<T, NB, EXACT, kQkvPlain>(a, panel, bgi, reinterpret_cast<float*>(xs_raw), sm);
@@ -149,9 +150,11 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
     DAB_TRACE_POINT(a, 0);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = blockIdx.x / a.nq, h = blockIdx.x - b * a.nq;
+    int2 pre;
+    if (a.seq_chunk) pre = reinterpret_cast<const int2*>(a.seq_chunk)[b];
     int p;
     if (!pos_valid(a, b, &p)) return;
-    const int nchunk = chunk_count(a.chunk, p);
+    const int nchunk = seq_chunk_of(a, b, p, a.seq_chunk ? &pre : nullptr).n;
     const size_t pbase = ((size_t)b * a.nq + h) * a.maxc;     // chunk cc: pbase + cc
     const int d = t % D, part = t / D;
     float v0[R];
@@ -225,6 +228,7 @@ __global__ __launch_bounds__(256) void oproj_kernel(StepArgs a) {
 template <bool QKV>
 __device__ inline void mfma_prologue(const StepArgs& a, u32x4* nw_raw, int threads) {
     if constexpr (QKV) {
+        publish_seq_chunks(a);
         for (int k = threadIdx.x * 8; k < a.H; k += threads * 8)
             nw_raw[k / 8] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.norm_w) + k);
         __syncthreads();
@@ -266,6 +270,7 @@ __global__ __launch_bounds__(kMfmaStrThreads) void mfma_str_kernel(StepArgs a) {
     __shared__ MfmaStrLds<TILES, NG> lds;
     DAB_TRACE_POINT(a, 0);
     if constexpr (!QKV) mfma_prologue<false>(a, nullptr, kMfmaStrThreads);
+    else publish_seq_chunks(a);
     const PanelPlanDev& g = QKV ? a.qkv : a.oproj;
     int panel, bgi;
     if (panel_decode(g.nbg, g.panels, blockIdx.x, &panel, &bgi))
@@ -277,6 +282,7 @@ template <int NG, int NWIN>
 __global__ __launch_bounds__(kMfmaStrThreads) void mfma_str_qkv24_kernel(StepArgs a) {
     __shared__ MfmaStrLds<2, NG> lds;
     DAB_TRACE_POINT(a, 0);
+    publish_seq_chunks(a);
     int panel, bgi;
     if (panel_decode(a.qkv.nbg, a.qkv.panels, blockIdx.x, &panel, &bgi)) mfma_str_qkv24<NG, NWIN>(a, panel, bgi, lds);
     DAB_TRACE_POINT(a, 3);

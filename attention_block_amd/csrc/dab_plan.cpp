@@ -297,6 +297,7 @@ dab_status make_plan(const dab_config* cfg, Plan* p, int attn_cus, int attn_per_
     p->off_attn_ml = take(sizeof(float) * (size_t)B * p->nq * p->max_chunks * 2);
     p->off_a = take(sizeof(float) * (size_t)B * p->n_q);
     p->off_a16 = take(sizeof(uint16_t) * (size_t)B * p->n_q);
+    p->off_seq_chunk = take(sizeof(int32_t) * 2 * (size_t)B);
     p->ws_bytes = off;
 
     const size_t e = (size_t)p->elem;

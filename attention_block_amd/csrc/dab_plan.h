@@ -132,7 +132,7 @@ struct Plan {
     // word is at offset 0
     size_t off_flags = 0, off_attn_cnt = 0, off_seq_ready = 0, off_ready_done = 0, off_head_cnt = 0;
     size_t off_q = 0, off_kv_new = 0;
-    size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0, off_a16 = 0;
+    size_t off_attn_o = 0, off_attn_ml = 0, off_a = 0, off_a16 = 0, off_seq_chunk = 0;
     size_t ws_bytes = 0;
 
     // byte extents of the caller's tensors (for alias checks)
